@@ -1,0 +1,176 @@
+"""The sink + rolling-window stream, float64, step by step.  Test infrastructure only.
+
+State is kept in the plainest form, independent of any device layout:
+
+* raw (pre-RoPE) K and V of every cached frame plus an explicit temporal position label;
+  RoPE is applied to keys at attention time;
+* the sinks as a list of S entries and the window as a chronological list (oldest first),
+  not a ring buffer.
+
+Sources and readings:
+
+* Sink frames + rolling window ([NEWS] algorithm item 1: the earliest frames' KV stay as sink
+  tokens, the rest of the cache rolls; [REPO] core components: ring-buffer KV cache with
+  sliding-window attention).  Keys of a chunk: every present sink, the last <= W committed
+  non-sink frames, and the chunk's own frames (block-causal inside the chunk).
+* Stream batch ([NEWS] system item 1, [WT] "可擴展的pipeline編排": B chunks at different noise
+  levels in one call, one finished frame per call; [REPO] quick example: denoise returns
+  nothing while the pipeline fills).  At step s the in-flight chunks are
+  c in [max(0, s-B+1), min(s, M-1)], element b = c - max(0, s-B+1); element 0 is the oldest
+  and is the one that finishes and is committed at the end of the step.
+* RoPE refresh ([WT] "自適應的sink和RoPE刷新": when the frame index passes a threshold the RoPE
+  phase is reset).  Reading: at the start of a step, while the newest in-flight frame f_new
+  satisfies f_new - b0 >= T_reset, b0 += T_reset and every cached label drops by T_reset.
+* Sink refresh (same sub-section: cosine similarity of the new chunk embedding against the
+  sink set; the least similar sink is refreshed when the similarity is below a threshold).
+  Reading: after the commit of frame f >= S, alpha_j = cos(h, e_j), j* = argmin (lowest index
+  on ties); if alpha_j* < tau the sink j* takes frame f's (K, V, label) for all layers and
+  e_j* = h.  Frame f also stays in the window.
+"""
+from __future__ import annotations
+
+import copy
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import rope
+from .attention import attention
+from .sink import decide
+
+
+def decode(cfg, x: np.ndarray) -> np.ndarray:
+    """Storage array (bf16 bit patterns or float32) -> float64 values."""
+    if cfg.dtype == "bf16":
+        return (np.asarray(x, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(x, np.float32).astype(np.float64)
+
+
+def schedule(cfg, s: int) -> dict:
+    """Chunks in flight at step s (element order), the chunk committed at its end, f_new."""
+    B, M, T = cfg.stream_batch, cfg.num_chunks, cfg.chunk_frames
+    lo, hi = max(0, s - B + 1), min(s, M - 1)
+    chunks = list(range(lo, hi + 1))
+    c0 = s - B + 1
+    return {"chunks": chunks,
+            "commit": c0 if 0 <= c0 < M else None,
+            "newest_frame": (hi + 1) * T - 1 if chunks else None}
+
+
+def ring_slot(cfg, frame: int) -> int:
+    """Cache slot of a committed frame: sinks are slots [0, S); frame f >= S lives at S + f mod W."""
+    S, W = cfg.sink_frames, cfg.window_frames
+    return frame if frame < S else S + frame % W
+
+
+@dataclass
+class Entry:
+    frame: int
+    label: int                                   # temporal RoPE position of the cached frame
+    kv: dict = field(default_factory=dict)       # layer -> (K_raw [N,H,d], V [N,H,d]) float64
+
+
+class OracleStream:
+    def __init__(self, cfg, layers=None):
+        self.cfg = cfg
+        self.layers = list(range(cfg.num_layers)) if layers is None else list(layers)
+        self.base = 0                                # b0
+        self.sinks: list[Entry | None] = [None] * cfg.sink_frames
+        self.sink_embed: list[np.ndarray | None] = [None] * cfg.sink_frames
+        self.window: list[Entry] = []
+        self.refresh_log: list[tuple[int, int]] = []          # (step, new b0)
+        self.sink_log: list[dict] = []
+        self.step = -1
+        self.plan = None
+
+    # ---- step start: schedule + RoPE refresh ---------------------------------------------
+    def begin_step(self, s: int) -> dict:
+        assert s == self.step + 1, "steps must be consecutive"
+        self.step = s
+        self.plan = schedule(self.cfg, s)
+        T_reset = self.cfg.rope_refresh_period
+        f_new = self.plan["newest_frame"]
+        while T_reset > 0 and f_new is not None and f_new - self.base >= T_reset:
+            self.base += T_reset
+            for e in self.cached_entries():
+                e.label -= T_reset
+            self.refresh_log.append((s, self.base))
+        return self.plan
+
+    def cached_entries(self) -> list[Entry]:
+        """Distinct cached entries: present sinks, then the window (oldest first)."""
+        return [e for e in self.sinks if e is not None] + list(self.window)
+
+    # ---- attention of one element ---------------------------------------------------------
+    def attend(self, layer: int, elem: int, q, k, v, rows=None, heads=None) -> np.ndarray:
+        """Output rows of element `elem` at the current step: float64 [len(rows), len(heads), d].
+
+        q, k, v are that element's fresh storage arrays [T'N, H, d] (pre-RoPE).
+        """
+        cfg = self.cfg
+        N, T = cfg.tokens, cfg.chunk_frames
+        chunk = self.plan["chunks"][elem]
+        rows = np.arange(T * N) if rows is None else np.asarray(rows)
+        heads = np.arange(cfg.num_heads) if heads is None else np.asarray(heads)
+        qd, kd, vd = decode(cfg, q), decode(cfg, k), decode(cfg, v)
+
+        # keys: cached entries at their labels, then the own chunk's frames at f - b0
+        k_parts, v_parts, key_frame = [], [], []
+        for e in self.cached_entries():
+            K_raw, V = e.kv[layer]
+            k_parts.append(rope.rope_frame(cfg, K_raw, e.label))
+            v_parts.append(V)
+            key_frame.append(np.full(N, -1))                     # always visible
+        own_frames = [chunk * T + t for t in range(T)]
+        for t, g in enumerate(own_frames):
+            k_parts.append(rope.rope_frame(cfg, kd[t * N:(t + 1) * N], g - self.base))
+            v_parts.append(vd[t * N:(t + 1) * N])
+            key_frame.append(np.full(N, g))
+        K_all = np.concatenate(k_parts)                            # [L, H, d]
+        V_all = np.concatenate(v_parts)
+        key_frame = np.concatenate(key_frame)
+
+        q_frame = chunk * T + rows // N
+        gh, gw = rope.token_grid(cfg.grid_h, cfg.grid_w)
+        phi = rope.angles(cfg, (q_frame - self.base).astype(np.float64), gh[rows % N], gw[rows % N])
+        Q_rot = rope.rotate_pairs(qd[rows], phi[:, None, :])       # [R, H, d]
+        mask = key_frame[None, :] <= q_frame[:, None]              # block-causal own chunk
+
+        out = np.empty((len(rows), len(heads), cfg.head_dim))
+        for i, h in enumerate(heads):
+            out[:, i], _ = attention(Q_rot[:, h], K_all[:, h], V_all[:, h], cfg.softmax_scale, mask)
+        return out
+
+    # ---- step end: commit + sink refresh ---------------------------------------------------
+    def end_step(self, commit_kv: dict | None = None, embedding=None):
+        """commit_kv: layer -> (k, v) storage arrays of element 0 at this step."""
+        cfg = self.cfg
+        c0 = self.plan["commit"]
+        if c0 is None:
+            return None
+        N, T, S, W = cfg.tokens, cfg.chunk_frames, cfg.sink_frames, cfg.window_frames
+        h = None if embedding is None else np.asarray(embedding, np.float32).astype(np.float64)
+        entry = None
+        for t in range(T):
+            f = c0 * T + t
+            entry = Entry(frame=f, label=f - self.base)
+            for layer in self.layers:
+                k, v = commit_kv[layer]
+                entry.kv[layer] = (decode(cfg, k)[t * N:(t + 1) * N], decode(cfg, v)[t * N:(t + 1) * N])
+            if f < S:
+                self.sinks[f] = entry
+                self.sink_embed[f] = h
+            else:
+                self.window.append(entry)
+                if len(self.window) > W:
+                    self.window.pop(0)
+        decision = None
+        if cfg.sink_threshold is not None and entry.frame >= S and S > 0:
+            j, alpha, replace = decide(h, self.sink_embed, cfg.sink_threshold)
+            if replace:
+                self.sinks[j] = copy.deepcopy(entry)
+                self.sink_embed[j] = h
+            decision = {"step": self.step, "chunk": c0, "frame": entry.frame, "slot": j,
+                        "alpha": alpha, "replaced": replace}
+            self.sink_log.append(decision)
+        return decision

@@ -1,0 +1,80 @@
+"""Pins of the oracle's sink refresh (oracle/sink.py and the stream's use of it)."""
+import json
+import math
+import pathlib
+
+import numpy as np
+import pytest
+
+import brute
+from oracle import sink
+from oracle import stream as ost
+from synth.configs import TINY_FP32
+
+GOLDEN = json.loads((pathlib.Path(__file__).parent / "golden" / "sink_script.json").read_text())
+
+
+@pytest.mark.parametrize("phi,replace", [(0.4, False), (0.45, False), (0.46, True), (0.5, True)])
+def test_constructed_angle_either_side_of_threshold(phi, replace):
+    # e = (1, 0, ...), h = (cos phi, sin phi, 0, ...) -> similarity cos phi; tau = 0.9 sits
+    # between cos 0.45 = 0.9004 and cos 0.46 = 0.8961.
+    e = np.zeros(64, np.float32)
+    e[0] = 1
+    h = np.zeros(64, np.float32)
+    h[0], h[1] = math.cos(phi), math.sin(phi)
+    j, alpha, rep = sink.decide(h, [e], 0.9)
+    assert j == 0 and rep is replace
+    assert alpha == pytest.approx(math.cos(phi), abs=1e-7)
+
+
+def test_least_similar_sink_is_chosen():
+    e0, e1, e2 = np.eye(3)
+    h = np.array([math.cos(0.5), math.sin(0.5), 0.0])
+    j, alpha, rep = sink.decide(h, [e0, e1, e2], 0.9)
+    assert j == 2 and alpha == 0.0 and rep                   # orthogonal to e2
+    j, alpha, _ = sink.decide(h, [e0, e1], 0.9)
+    assert j == 1 and alpha == pytest.approx(math.sin(0.5), abs=1e-15)
+
+
+def test_ties_zero_norm_and_strictness():
+    e = np.array([1.0, 0.0, 0.0, 0.0])
+    assert sink.decide(e, [e, e, e], 0.5) == (0, 1.0, False)
+    assert sink.cosine(np.zeros(4), e) == 0.0
+    c = GOLDEN["strict_threshold_case"]
+    j, alpha, rep = sink.decide(np.array(c["embedding"], float), [np.array(c["sink"], float)], c["tau"])
+    assert alpha == c["alpha"] and rep is c["replaced"]
+
+
+def _script_cfg():
+    return TINY_FP32.with_(sink_frames=GOLDEN["sink_frames"], window_frames=GOLDEN["window_frames"],
+                           sink_threshold=GOLDEN["tau"], embed_dim=4, rope_refresh_period=0,
+                           num_chunks=len(GOLDEN["embeddings"]))
+
+
+def test_scripted_sequence_matches_hand_derivation():
+    cfg = _script_cfg()
+    emb = [np.array(e, np.float32) for e in GOLDEN["embeddings"]]
+    st = ost.OracleStream(cfg, layers=[0])
+    from synth import inputs
+    for s in range(cfg.num_steps):
+        plan = st.begin_step(s)
+        _, k, v = inputs.qkv(cfg, s, 0, 0)
+        st.end_step({0: (k, v)}, emb[plan["commit"]])
+        want = GOLDEN["sink_frames_after_chunk"][plan["commit"]]
+        assert [None if e is None else e.frame for e in st.sinks] == want
+    got = [{"chunk": d["chunk"], "slot": d["slot"], "replaced": d["replaced"]} for d in st.sink_log]
+    want = [{"chunk": d["chunk"], "slot": d["slot"], "replaced": d["replaced"]} for d in GOLDEN["decisions"]]
+    assert got == want
+    for d, g in zip(st.sink_log, GOLDEN["decisions"]):
+        assert d["alpha"] == pytest.approx(g["alpha"], abs=1e-7)
+
+
+def test_replaced_sink_carries_the_frame_into_attention():
+    # after each replacement the keys are [the scripted sink frames | window | own chunk]
+    cfg = _script_cfg()
+    emb = [np.array(e, np.float32) for e in GOLDEN["embeddings"]]
+    st, outs = brute.run_oracle(cfg, embed_fn=lambda c: emb[c])
+    for s in range(1, cfg.num_steps):
+        sinks = [f for f in GOLDEN["sink_frames_after_chunk"][s - 1] if f is not None]
+        np.testing.assert_allclose(outs[(s, 0, 0)], brute.history_output(cfg, s, 0, 0, sink_frames=sinks),
+                                   atol=1e-12)

@@ -1,0 +1,126 @@
+"""Pins of the oracle's stream bookkeeping: schedule, ring model, RoPE refresh."""
+import numpy as np
+import pytest
+
+import brute
+from oracle import rope
+from oracle import stream as ost
+from oracle.attention import attention
+from synth import inputs
+from synth.configs import TINY_FP32, WAN13B_1LAYER, WAN13B_480P_B2
+
+
+def tiny(**kw):
+    base = dict(rope_refresh_period=0, sink_threshold=None, embed_dim=0, embed_kind=None)
+    base.update(kw)
+    return TINY_FP32.with_(**base)
+
+
+def test_schedule_fill_steady_drain():
+    # B = 4, M = 6: the pipeline fills for B-1 steps (nothing finishes), then one chunk
+    # finishes per step; after the last chunk enters, B-1 drain steps finish the rest.
+    cfg = tiny(stream_batch=4, num_chunks=6)
+    got = [ost.schedule(cfg, s) for s in range(cfg.num_steps)]
+    assert cfg.num_steps == 9
+    assert [g["chunks"] for g in got] == [[0], [0, 1], [0, 1, 2], [0, 1, 2, 3], [1, 2, 3, 4],
+                                          [2, 3, 4, 5], [3, 4, 5], [4, 5], [5]]
+    assert [g["commit"] for g in got] == [None, None, None, 0, 1, 2, 3, 4, 5]
+    assert [g["newest_frame"] for g in got] == [0, 1, 2, 3, 4, 5, 5, 5, 5]
+    cfg2 = tiny(stream_batch=2, num_chunks=3, chunk_frames=2)
+    assert [ost.schedule(cfg2, s)["newest_frame"] for s in range(4)] == [1, 3, 5, 5]
+
+
+@pytest.mark.parametrize("S,W", [(1, 8), (2, 6), (1, 4), (0, 3), (3, 1)])
+def test_ring_slots_hold_exactly_the_window(S, W):
+    # Commit frames one by one into both the oracle's chronological window and a ring indexed by
+    # ring_slot(): after every commit the ring's window slots hold exactly the window's frames.
+    cfg = tiny(sink_frames=S, window_frames=W)
+    ring = {}
+    window = []
+    for f in range(5 * W + S + 3):
+        slot = ost.ring_slot(cfg, f)
+        if f < S:
+            assert slot == f
+        else:
+            assert S <= slot < S + W
+            window.append(f)
+            window = window[-W:]
+        ring[slot] = f
+        assert sorted(ring[j] for j in range(S, S + W) if j in ring) == sorted(window)
+        assert [ring[j] for j in range(min(S, f + 1))] == list(range(min(S, f + 1)))
+
+
+def test_ring_order_attention_equals_chronological():
+    # after wraparound, attention over the keys in ring-slot order equals chronological order
+    cfg = tiny(sink_frames=1, window_frames=4, num_chunks=12)
+    st, outs = brute.run_oracle(cfg, steps=11)
+    st.begin_step(11)
+    q, k, v = inputs.qkv(cfg, 11, 0, 0)
+    want = st.attend(0, 0, q, k, v)
+    entries = sorted(st.cached_entries(), key=lambda e: ost.ring_slot(cfg, e.frame))
+    assert [e.frame for e in st.window] == [7, 8, 9, 10]
+    assert [ost.ring_slot(cfg, e.frame) for e in entries] == [0, 1, 2, 3, 4]
+    assert [e.frame for e in entries] == [0, 8, 9, 10, 7]
+    ks = [rope.rope_frame(cfg, e.kv[0][0], e.label) for e in entries]
+    vs = [e.kv[0][1] for e in entries]
+    ks.append(rope.rope_frame(cfg, brute.to_f64(cfg, k), 11))
+    vs.append(brute.to_f64(cfg, v))
+    qr = rope.rope_frame(cfg, brute.to_f64(cfg, q), 11)
+    K, V = np.concatenate(ks), np.concatenate(vs)
+    for h in range(cfg.num_heads):
+        o, _ = attention(qr[:, h], K[:, h], V[:, h], cfg.softmax_scale)
+        np.testing.assert_allclose(o, want[:, h], atol=1e-12)
+
+
+@pytest.mark.parametrize("period,B,M,expect", [
+    (8, 1, 12, [(8, 8)]),                                   # tiny fp32 workload: frame index 8
+    (32, 1, 64, [(32, 32)]),                                # Wan-1.3B single layer: every 32
+    (24, 2, 128, [(24, 24), (48, 48), (72, 72), (96, 96), (120, 120)]),   # 480p, B = 2
+    (4, 3, 10, [(4, 4), (8, 8)]),
+])
+def test_refresh_events(period, B, M, expect):
+    cfg = tiny(rope_refresh_period=period, stream_batch=B, num_chunks=M)
+    st = ost.OracleStream(cfg, layers=[])
+    for s in range(cfg.num_steps):
+        st.begin_step(s)
+        st.end_step({}, None)                               # no layers tracked: labels only
+    assert st.refresh_log == expect
+
+
+def test_refresh_makes_new_frame_position_zero_and_shifts_labels():
+    cfg = tiny(rope_refresh_period=8, num_chunks=12)
+    st, _ = brute.run_oracle(cfg, steps=8)
+    before = {e.frame: e.label for e in st.cached_entries()}
+    assert before == {0: 0, 4: 4, 5: 5, 6: 6, 7: 7}
+    st.begin_step(8)
+    after = {e.frame: e.label for e in st.cached_entries()}
+    assert st.base == 8
+    assert after == {f: p - 8 for f, p in before.items()}
+
+
+@pytest.mark.parametrize("B,period", [(1, 3), (2, 4), (3, 5)])
+def test_refresh_leaves_outputs_unchanged(B, period):
+    # rebasing every cached label and the query by the same constant leaves every score, hence
+    # every output, unchanged: the same stream with and without refresh must agree.
+    cfg = tiny(stream_batch=B, num_chunks=13)
+    _, plain = brute.run_oracle(cfg)
+    st, refreshed = brute.run_oracle(cfg.with_(rope_refresh_period=period))
+    assert len(st.refresh_log) >= 2
+    for key in plain:
+        np.testing.assert_allclose(refreshed[key], plain[key], atol=1e-12)
+
+
+def test_commit_labels_and_window_contents_over_a_stream():
+    cfg = tiny(sink_frames=2, window_frames=3, stream_batch=2, num_chunks=9, rope_refresh_period=4)
+    st = ost.OracleStream(cfg, layers=[0])
+    for s in range(cfg.num_steps):
+        plan = st.begin_step(s)
+        _, k, v = inputs.qkv(cfg, s, 0, 0)
+        st.end_step({0: (k, v)})
+        c0 = plan["commit"]
+        if c0 is not None:
+            committed = list(range(c0 + 1))
+            assert [e.frame for e in st.sinks if e] == committed[:2]
+            assert [e.frame for e in st.window] == [f for f in committed if f >= 2][-3:]
+            for e in st.cached_entries():
+                assert e.label == e.frame - st.base
