@@ -1,0 +1,211 @@
+/*
+ * sdv2.h - C ABI of the sink + rolling-KV chunk-attention library for AMD MI355X (gfx950).
+ *
+ * The operation: a causal video DiT streams latent frames in chunks of T' frames; a stream batch
+ * of B chunks at different noise levels runs in one call and the oldest one finishes each call.
+ * Every chunk attends over a KV cache made of S pinned "sink" frames, a rolling window of the W
+ * most recently finished frames, and its own chunk.  Keys carry a 3-axis (t, h, w) rotary
+ * position embedding whose temporal phase is periodically rebased ("RoPE refresh"); the sinks
+ * are refreshed when a new chunk embedding is too dissimilar to all of them; a per-frame motion
+ * estimate drives the noise-rate EMA.
+ *
+ * Pages this interface follows (title, section):
+ *  [WT]   "直播革命來了！StreamDiffusionV2" paper walkthrough (qq8o.cn), section "方法" (Method):
+ *         "SLO感知的批處理調度器" (SLO-aware batching scheduler: chunk size T, stream batch B,
+ *         B*T must not exceed the frames collected), "自適應的sink和RoPE刷新" (adaptive sink and
+ *         RoPE refresh), "運動感知的噪聲調度器" (motion-aware noise scheduler).
+ *  [NEWS] admirer.cn article on StreamDiffusionV2 (MLSys 2026), section "方法" (Method),
+ *         algorithm items 1 (sink tokens + rolling KV cache) and 2 (motion-aware noise),
+ *         system item 1 (pipelined batch denoising: one finished frame per DiT call).
+ *  [REPO] agentlenshq page "chenfengxu714/StreamDiffusionV2", section "核心组件" (core
+ *         components: ring-buffer KV cache with sliding-window attention) and "快速 Python 示例"
+ *         (quick example: encode -> denoise, which yields nothing while the pipeline fills).
+ *
+ * Conventions (all entry points):
+ *  - Return 0 (SDV2_OK) or a negative error code.  A failing call changes no host state and
+ *    launches nothing, except SDV2_EHIP from a launch, after which the cache must be destroyed.
+ *    The message of the last error on the calling thread: sdv2_last_error().
+ *  - Device pointers are caller-owned (the library never allocates or frees device memory);
+ *    they must stay valid while work that uses them is in flight.  The cache handle is
+ *    library-owned host memory, freed by sdv2_cache_destroy.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued asynchronously
+ *    on it; no call synchronises unless its comment says so.
+ *  - q, k, v and attention outputs are contiguous [nbatch][T'*N][H][head_dim] in the cache dtype
+ *    (fp32, or bf16 bit patterns rounded to nearest even), N = grid_h * grid_w tokens per frame,
+ *    token n at row n / grid_w, column n % grid_w.  Embeddings and latent frames are fp32.
+ *  - Step protocol (per stream step):
+ *        sdv2_rope_refresh  ->  for each layer: sdv2_cache_append, sdv2_chunk_attention
+ *        -> [sdv2_cache_commit -> [sdv2_sink_replace]]
+ *    Calls out of this order return SDV2_ESTATE and change nothing.
+ */
+#ifndef SDV2_H
+#define SDV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SDV2_OK = 0,
+  SDV2_EINVAL = -1, /* bad argument or configuration */
+  SDV2_ESTATE = -2, /* call out of the step protocol */
+  SDV2_EHIP = -3,   /* a HIP runtime call or kernel launch failed */
+  SDV2_ENOSPC = -4  /* a caller buffer is smaller than sdv2_cache_size() asks for */
+};
+
+enum { SDV2_F32 = 0, SDV2_BF16 = 1 };
+
+/* Library limits (validated by sdv2_config_validate). */
+enum {
+  SDV2_MAX_SLOTS_SHARED = 64, /* S + W */
+  SDV2_MAX_BATCH = 8,         /* B */
+  SDV2_MAX_SINKS = 16,        /* S */
+  SDV2_MAX_TPAIRS = 32        /* rope_dim_t / 2 */
+};
+
+typedef struct sdv2_config {
+  int32_t num_layers;
+  int32_t num_heads;     /* H */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t grid_h;        /* latent tokens per frame: N = grid_h * grid_w */
+  int32_t grid_w;
+  int32_t sink_frames;   /* S >= 0 */
+  int32_t window_frames; /* W >= 1 */
+  int32_t chunk_frames;  /* T': only 1 is supported */
+  int32_t stream_batch;  /* B in [1, SDV2_MAX_BATCH] */
+  int32_t rope_dim_t;    /* even; rope_dim_t + rope_dim_h + rope_dim_w == head_dim */
+  int32_t rope_dim_h;
+  int32_t rope_dim_w;
+  double rope_theta;     /* > 1 */
+  int32_t rope_refresh_period; /* T_reset >= 0; 0 = never */
+  int32_t dtype;         /* SDV2_F32 | SDV2_BF16 */
+  int32_t embed_dim;     /* D >= 0: chunk-embedding length; 0 = no sink refresh */
+  double sink_threshold; /* tau; NaN or -INFINITY = sink refresh off */
+} sdv2_config;
+
+/* Device layout of the KV cache (element offsets from d_kv, element = 2 or 4 bytes).
+ * Slots [0,S) are sinks, [S,S+W) the ring (frame f >= S lives in slot S + f mod W),
+ * [S+W, S+W+B) the staging slots of stream-batch elements 0..B-1.
+ *   K of (layer, slot, head, token n, dim i): k_offset(layer) + slot*slot_stride
+ *        + head*head_stride + n*head_dim + i                      (rows of head_dim)
+ *   V of (layer, slot, head, token n, dim i): v_offset(layer) + slot*slot_stride
+ *        + head*head_stride + i*tokens_padded + n                 (stored transposed)
+ * with k_offset(l) = l*layer_stride, v_offset(l) = l*layer_stride + slot_stride*slots.
+ * Tokens n in [N, tokens_padded) are zero padding. */
+typedef struct sdv2_layout {
+  int64_t slots;          /* S + W + B */
+  int64_t tokens_padded;  /* N rounded up to 64 */
+  int64_t elem_bytes;     /* 4 (fp32) or 2 (bf16) */
+  int64_t head_stride;    /* tokens_padded * head_dim */
+  int64_t slot_stride;    /* num_heads * head_stride */
+  int64_t layer_stride;   /* 2 * slots * slot_stride (K block then V block) */
+  int64_t kv_elems;       /* num_layers * layer_stride */
+} sdv2_layout;
+
+typedef struct sdv2_cache sdv2_cache;
+
+/* Check a configuration against the library limits.  Host only. */
+int sdv2_config_validate(const sdv2_config* cfg);
+
+/* Fill *out with the cache layout of cfg.  Host only. */
+int sdv2_cache_layout(const sdv2_config* cfg, sdv2_layout* out);
+
+/* Bytes the caller must allocate on the device: the KV cache (layout above), the metadata
+ * block (RoPE h/w tables, sink embeddings, the last sink decision) and the workspace
+ * (split-KV partial results).  Host only.  Any pointer may be NULL. */
+int sdv2_cache_size(const sdv2_config* cfg, size_t* kv_bytes, size_t* meta_bytes,
+                    size_t* workspace_bytes);
+
+/* Create a cache over caller-owned device buffers (sizes from sdv2_cache_size; 256-byte
+ * aligned).  Zero-fills d_kv and writes the h/w RoPE tables into d_meta on `stream`, then
+ * synchronises `stream` once.  On success *out owns host bookkeeping only. */
+int sdv2_cache_create(const sdv2_config* cfg, void* d_kv, size_t kv_bytes, void* d_meta,
+                      size_t meta_bytes, void* d_workspace, size_t workspace_bytes,
+                      void* stream, sdv2_cache** out);
+
+/* Free the handle (not the device buffers).  NULL is accepted. */
+int sdv2_cache_destroy(sdv2_cache* cache);
+
+/* Start a stream step ([WT] adaptive sink and RoPE refresh: the RoPE phase is reset when the
+ * frame index passes a threshold).  `newest_frame` is the last frame of the newest chunk in
+ * flight this step (non-decreasing over calls).  While newest_frame - b0 >= T_reset, the RoPE
+ * base b0 grows by T_reset and every cached key (sinks and window) is re-rotated in place by
+ * -T_reset on the temporal pairs, so scores are unchanged.  *applied (may be NULL) receives
+ * the number of rebases.  Must open every step, also when T_reset == 0. */
+int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied, void* stream);
+
+/* RoPE + append for one layer ([NEWS] algorithm item 1; [REPO] ring-buffer KV cache).
+ * Elements b = 0..nbatch-1 hold chunks first_chunk+b (b = 0 oldest); first_chunk must equal
+ * the number of chunks committed so far and first_chunk + nbatch - 1 the newest frame given
+ * to sdv2_rope_refresh.  d_q is rotated in place at temporal position frame - b0 (row h, col
+ * w); k is rotated likewise and written with v into the staging slot of element b.  Buffers:
+ * [nbatch][T'N][H][d] each; d_q read-write, d_k and d_v read-only.  Once per layer per step. */
+int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int32_t nbatch,
+                      void* d_q, const void* d_k, const void* d_v, void* stream);
+
+/* Chunk attention for one layer (after its append this step).  For each element b and head:
+ * out = softmax(scale * Q_rot K^T) V over the keys [present sinks | window | own chunk], with
+ * Q_rot = d_q_rot as rotated by sdv2_cache_append.  d_out: [nbatch][T'N][H][d], written.  The
+ * workspace given at create time is used for split-KV partial results (calls on one cache
+ * must not overlap in time). */
+int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
+                         void* d_out, float scale, void* stream);
+
+/* Commit the finished chunk (element 0, which must be `chunk`) for all layers: its staged K
+ * and V are copied into sink slot f if f < S, else into ring slot S + f mod W (evicting the
+ * frame W older).  Requires every layer appended this step. */
+int sdv2_cache_commit(sdv2_cache* cache, int64_t chunk, void* stream);
+
+/* Adaptive sink refresh after the commit of `frame` ([WT] adaptive sink and RoPE refresh).
+ * d_embed: fp32 [embed_dim] chunk embedding h (device).  If frame < S it becomes sink frame's
+ * embedding.  Otherwise, when tau is on: alpha_j = cos(h, e_j) for j < S (fp64; 0 if a norm is
+ * 0), j* = argmin (lowest j on ties); if alpha_j* < tau the committed frame's K/V are copied
+ * into sink j* for all layers and e_j* = h.  The decision is taken on the device.  If h_slot is
+ * non-NULL the call synchronises `stream` and returns j* if replaced, else -1 (h_alpha, may be
+ * NULL: alpha_j*); with h_slot NULL nothing synchronises and sdv2_cache_slot_info reports the
+ * sink slots as unknown (-2) from then on. */
+int sdv2_sink_replace(sdv2_cache* cache, int64_t frame, const float* d_embed, int32_t* h_slot,
+                      double* h_alpha, void* stream);
+
+/* Motion estimate ([NEWS] algorithm item 2; [WT] motion-aware noise scheduler): for t = 1 ..
+ * nframes-1, d_dist[t-1] = sqrt(sum_i (x_t[i] - x_{t-1}[i])^2 / elems_per_frame), summed in fp64
+ * in a fixed order.  d_frames: fp32 [nframes][elems_per_frame]; d_dist: fp64 [nframes-1];
+ * d_workspace: at least sdv2_motion_workspace_size() bytes.  Stateless. */
+int sdv2_motion_workspace_size(int32_t nframes, int64_t elems_per_frame, size_t* bytes);
+int sdv2_motion_l2(const float* d_frames, int32_t nframes, int64_t elems_per_frame,
+                   double* d_dist, void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Motion-aware noise rate ([WT] motion-aware noise scheduler), host scalars: dhat_t =
+ * min(1, max of the last k distances / sigma), target = s_max - (s_max - s_min) * dhat,
+ * s_t = lambda * target + (1 - lambda) * s_{t-1}, from s_0 = s0.  h_dist: [n] distances
+ * d_1..d_n; h_rate: [n] rates s_1..s_n.  Host only. */
+int sdv2_noise_schedule(const double* h_dist, int32_t n, double sigma, int32_t k, double lambda,
+                        double s_min, double s_max, double s0, double* h_rate);
+
+/* Host bookkeeping of one slot: committed frame (-1 empty, -2 unknown after an unsynchronised
+ * sink decision) and its temporal RoPE position label = frame - b0 at commit, shifted by every
+ * later rebase.  Staging slots report the frame staged this step.  Never synchronises. */
+int sdv2_cache_slot_info(const sdv2_cache* cache, int32_t slot, int64_t* frame, int32_t* tpos);
+
+/* RoPE base b0, chunks committed so far and rebases applied so far.  Any pointer may be NULL. */
+int sdv2_cache_state(const sdv2_cache* cache, int64_t* rope_base, int64_t* committed,
+                     int64_t* refreshes);
+
+/* Stream-batch schedule of step `step` for a stream of num_chunks chunks ([NEWS] system item 1;
+ * [REPO] quick example): in-flight chunks [first_chunk, first_chunk + nbatch), the chunk
+ * finished and committed at its end (-1 while the pipeline fills) and the newest in-flight
+ * frame (-1 past the end).  Host only. */
+int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int64_t* first_chunk,
+                   int32_t* nbatch, int64_t* commit_chunk, int64_t* newest_frame);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* sdv2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV2_H */

@@ -1,0 +1,122 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdv2 {
+
+constexpr int kMaxShared = 64;   // S + W
+constexpr int kMaxBatch = 8;     // B
+constexpr int kMaxSinks = 16;    // S
+constexpr int kMaxTPairs = 32;   // temporal RoPE pairs
+constexpr int kTileKeys = 64;    // key tile; tokens are padded to a multiple of it
+constexpr int kQTile = 128;      // query rows per attention workgroup (4 waves x 32)
+constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 <-> fp32 (bit patterns in uint16_t) -------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round two fp32 values to bf16 (nearest even, hardware v_cvt_pk_bf16_f32); low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Workgroup id -> work item such that consecutive work items run on the same XCD (each XCD
+// has its own L2): hardware sends workgroup i to XCD i % 8.  A bijection on [0, G).
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  const int xcd = bid % kNumXcd, per = G / kNumXcd, rem = G % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + bid / kNumXcd;
+}
+
+// ---- kernel argument blocks (passed by value) ----------------------------------------------
+struct AppendArgs {
+  void* q;                 // [nbatch][N][H][D], rotated in place
+  const void* k;
+  const void* v;
+  void* kv;                // cache base
+  int64_t k_layer_off;     // element offsets of this layer's K and V blocks
+  int64_t v_layer_off;
+  int64_t slot_stride;
+  int64_t head_stride;
+  const float2* tab_h;     // [grid_h][ph] (cos, sin)
+  const float2* tab_w;     // [grid_w][pw]
+  int N, Npad, H, grid_w, nbatch;
+  int staging_slot0;       // S + W
+  int pt, ph, pw;          // RoPE pairs per axis
+  float2 tcs[kMaxBatch][kMaxTPairs];   // temporal (cos, sin) per element and pair
+};
+
+struct AttnArgs {
+  const void* q;           // [nbatch][N][H][D] rotated queries
+  void* out;               // [nbatch][N][H][D]
+  const void* kv;
+  int64_t k_layer_off, v_layer_off, slot_stride, head_stride;
+  float* part_o;           // [nsplit][nbatch][H][N][D] fp32 (split-KV only)
+  float2* part_ml;         // [nsplit][nbatch][H][N] (m in log2 units, l)
+  int N, Npad, H, nbatch;
+  int nshared;             // cached frames attended (sinks + window)
+  int own_slot0;           // staging slot of element 0
+  int tiles_per_frame;     // Npad / kTileKeys
+  int total_tiles;         // (nshared + 1) * tiles_per_frame
+  int nsplit, qtiles;
+  float scale_log2;        // softmax scale * log2(e)
+  float scale;
+  int slots[kMaxShared];   // cache slots of the shared frames, in attention order
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float2* part_ml;
+  void* out;
+  int N, H, nbatch, nsplit;
+};
+
+struct RebaseArgs {
+  void* kv;
+  int64_t layer_stride, slot_stride, head_stride;
+  int L, H, N, pt, nslots;
+  int slots[kMaxShared];
+  float2 cs[kMaxTPairs];   // (cos, sin) of the rebase angle per temporal pair
+};
+
+struct CopyArgs {
+  char* kv;
+  int64_t layer_stride_bytes;
+  int64_t v_block_bytes;   // byte offset of the V block inside a layer
+  int64_t slot_bytes;      // bytes of one slot of K (= of V)
+  int src_slot;
+  int dst_slot;            // used when dst_from == nullptr
+  const int32_t* dst_from; // device decision: copy into slot *dst_from, skip if < 0
+  int L;
+};
+
+struct SinkArgs {
+  const float* h;          // [D] new chunk embedding
+  float* embeds;           // [S][D] sink embeddings
+  int32_t* decision;       // [0] = replaced slot or -1
+  double* alpha;           // [0] = alpha of the least similar sink
+  int S, D;
+  int store_slot;          // >= 0: store h as that sink's embedding, no decision
+  double tau;
+};
+
+// ---- launchers (defined in the .hip files) --------------------------------------------------
+hipError_t launch_rope_append(const AppendArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_rebase(const RebaseArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s);
+hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s);
+hipError_t launch_motion(const float* frames, int nframes, int64_t elems, double* dist,
+                         double* partials, int parts, hipStream_t s);
+int motion_parts(int64_t elems);
+
+}  // namespace sdv2

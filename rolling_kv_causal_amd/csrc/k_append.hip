@@ -1,0 +1,119 @@
+// Fused RoPE + append for one layer.
+//
+// q is rotated in place; k is rotated and written with v into the staging slot of its
+// stream-batch element ([NEWS] method, algorithm item 1: the new frames' KV enter the rolling
+// cache; [WT] adaptive sink and RoPE refresh: keys and queries carry the RoPE phase of their
+// frame index relative to the current base).  RoPE: interleaved pairs; the first pt pairs turn
+// by the temporal angle (per element, from the host), the next ph by the row angle and the last
+// pw by the column angle of the token (tables in device memory).
+//
+// One workgroup per (64-token tile, head, element); 16-byte loads and stores throughout.  K
+// rows go to the cache as [token][d]; V goes through LDS and leaves transposed as [d][token]
+// rows of the tile, so the attention kernel can read V^T fragments contiguously.
+#include "common.h"
+
+#include <type_traits>
+
+namespace sdv2 {
+
+template <bool BF16>
+__device__ __forceinline__ void rotate16(uint4& w, const float2* cs) {
+  if constexpr (BF16) {
+    uint32_t* u = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = bf16_bits_to_f32(u[j] & 0xffffu), y = bf16_bits_to_f32(u[j] >> 16);
+      u[j] = pack_bf16x2(x * cs[j].x - y * cs[j].y, x * cs[j].y + y * cs[j].x);
+    }
+  } else {
+    float* f = reinterpret_cast<float*>(&w);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float x = f[2 * j], y = f[2 * j + 1];
+      f[2 * j] = x * cs[j].x - y * cs[j].y;
+      f[2 * j + 1] = x * cs[j].y + y * cs[j].x;
+    }
+  }
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int VEC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int CH = D / VEC;                // chunks per row
+  constexpr int ROWS = 256 / CH;             // token rows per pass
+  constexpr int TILE = kTileKeys;
+  constexpr int VSTR = D + (BF16 ? 2 : 1);   // LDS row stride (elements): breaks bank aliasing
+  __shared__ T vs[TILE * VSTR];
+  __shared__ float2 tcs[kMaxTPairs];
+
+  const int n0 = blockIdx.x * TILE, head = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  if (tid < a.pt) tcs[tid] = a.tcs[b][tid];
+  __syncthreads();
+
+  const int c = tid % CH;
+  const int64_t kdst = a.k_layer_off + (int64_t)(a.staging_slot0 + b) * a.slot_stride +
+                       (int64_t)head * a.head_stride;
+#pragma unroll
+  for (int pass = 0; pass < TILE / ROWS; ++pass) {
+    const int row = pass * ROWS + tid / CH;
+    const int n = n0 + row;
+    uint32_t* vrow = reinterpret_cast<uint32_t*>(vs + row * VSTR + c * VEC);
+    if (n < a.N) {
+      const int hr = n / a.grid_w, wc = n - hr * a.grid_w;
+      float2 cs[VEC / 2];
+#pragma unroll
+      for (int j = 0; j < VEC / 2; ++j) {
+        const int p = c * (VEC / 2) + j;
+        cs[j] = p < a.pt ? tcs[p]
+                : p < a.pt + a.ph ? a.tab_h[hr * a.ph + (p - a.pt)]
+                                  : a.tab_w[wc * a.pw + (p - a.pt - a.ph)];
+      }
+      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
+      uint4 qv = *(const uint4*)((const T*)a.q + off);
+      uint4 kv = *(const uint4*)((const T*)a.k + off);
+      const uint4 vv = *(const uint4*)((const T*)a.v + off);
+      rotate16<BF16>(qv, cs);
+      rotate16<BF16>(kv, cs);
+      *(uint4*)((T*)a.q + off) = qv;
+      *(uint4*)((T*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv;
+      vrow[0] = vv.x; vrow[1] = vv.y; vrow[2] = vv.z; vrow[3] = vv.w;
+    } else {                                   // padding tokens of V^T stay zero
+      vrow[0] = 0u; vrow[1] = 0u; vrow[2] = 0u; vrow[3] = 0u;
+    }
+  }
+  __syncthreads();
+
+  // V^T rows: d-major, the tile's 64 tokens contiguous
+  constexpr int TCH = TILE / VEC;            // 16-byte chunks per V^T row of the tile
+  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)(a.staging_slot0 + b) * a.slot_stride +
+            (int64_t)head * a.head_stride + n0;
+  for (int idx = tid; idx < D * TCH; idx += 256) {
+    const int drow = idx / TCH, kc = idx % TCH;
+    T vals[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) vals[j] = vs[(kc * VEC + j) * VSTR + drow];
+    uint4 w;
+    __builtin_memcpy(&w, vals, sizeof(w));
+    *(uint4*)(vdst + (int64_t)drow * a.Npad + kc * VEC) = w;
+  }
+}
+
+hipError_t launch_rope_append(const AppendArgs& a, int head_dim, bool bf16, hipStream_t s) {
+  const dim3 grid((a.N + kTileKeys - 1) / kTileKeys, a.H, a.nbatch);
+  if (bf16) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((rope_append_kernel<true, 128>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((rope_append_kernel<true, 64>), grid, dim3(256), 0, s, a);
+  } else {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((rope_append_kernel<false, 128>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((rope_append_kernel<false, 64>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sdv2

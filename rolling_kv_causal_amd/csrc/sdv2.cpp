@@ -1,0 +1,598 @@
+// C ABI of the sink + rolling-KV chunk-attention library: validation, cache layout, host
+// bookkeeping (slot table, RoPE base, step protocol) and kernel launches.  See include/sdv2.h.
+#include "sdv2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace sdv2;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return SDV2_OK;
+}
+
+#define SDV2_HIP(call)                                                                         \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess) return fail(SDV2_EHIP, "%s: %s", #call, hipGetErrorString(e_));      \
+  } while (0)
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool tau_on(const sdv2_config& c) {
+  return !std::isnan(c.sink_threshold) && c.sink_threshold != -INFINITY;
+}
+
+int validate(const sdv2_config* c) {
+  if (!c) return fail(SDV2_EINVAL, "config is NULL");
+  if (c->num_layers < 1) return fail(SDV2_EINVAL, "num_layers must be >= 1");
+  if (c->num_heads < 1) return fail(SDV2_EINVAL, "num_heads must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(SDV2_EINVAL, "head_dim must be 64 or 128");
+  if (c->grid_h < 1 || c->grid_w < 1) return fail(SDV2_EINVAL, "grid_h and grid_w must be >= 1");
+  if ((int64_t)c->grid_h * c->grid_w > (1 << 20)) return fail(SDV2_EINVAL, "too many tokens per frame");
+  if (c->sink_frames < 0 || c->sink_frames > kMaxSinks)
+    return fail(SDV2_EINVAL, "sink_frames must be in [0, %d]", kMaxSinks);
+  if (c->window_frames < 1) return fail(SDV2_EINVAL, "window_frames must be >= 1");
+  if (c->sink_frames + c->window_frames > kMaxShared)
+    return fail(SDV2_EINVAL, "sink_frames + window_frames must be <= %d", kMaxShared);
+  if (c->chunk_frames != 1) return fail(SDV2_EINVAL, "chunk_frames must be 1");
+  if (c->stream_batch < 1 || c->stream_batch > kMaxBatch)
+    return fail(SDV2_EINVAL, "stream_batch must be in [1, %d]", kMaxBatch);
+  if (c->rope_dim_t < 0 || c->rope_dim_h < 0 || c->rope_dim_w < 0 || (c->rope_dim_t & 1) ||
+      (c->rope_dim_h & 1) || (c->rope_dim_w & 1))
+    return fail(SDV2_EINVAL, "rope dims must be even and >= 0");
+  if (c->rope_dim_t + c->rope_dim_h + c->rope_dim_w != c->head_dim)
+    return fail(SDV2_EINVAL, "rope dims must sum to head_dim");
+  if (c->rope_dim_t / 2 > kMaxTPairs) return fail(SDV2_EINVAL, "rope_dim_t must be <= %d", 2 * kMaxTPairs);
+  if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta))
+    return fail(SDV2_EINVAL, "rope_theta must be finite and > 1");
+  if (c->rope_refresh_period < 0) return fail(SDV2_EINVAL, "rope_refresh_period must be >= 0");
+  if (c->dtype != SDV2_F32 && c->dtype != SDV2_BF16) return fail(SDV2_EINVAL, "dtype must be F32 or BF16");
+  if (c->embed_dim < 0) return fail(SDV2_EINVAL, "embed_dim must be >= 0");
+  if (tau_on(*c) && (c->embed_dim < 1 || c->sink_frames < 1))
+    return fail(SDV2_EINVAL, "sink refresh needs embed_dim >= 1 and sink_frames >= 1");
+  return SDV2_OK;
+}
+
+sdv2_layout make_layout(const sdv2_config& c) {
+  sdv2_layout l;
+  const int64_t N = (int64_t)c.grid_h * c.grid_w;
+  l.slots = c.sink_frames + c.window_frames + c.stream_batch;
+  l.tokens_padded = align_up(N, kTileKeys);
+  l.elem_bytes = c.dtype == SDV2_BF16 ? 2 : 4;
+  l.head_stride = l.tokens_padded * c.head_dim;
+  l.slot_stride = c.num_heads * l.head_stride;
+  l.layer_stride = 2 * l.slots * l.slot_stride;
+  l.kv_elems = c.num_layers * l.layer_stride;
+  return l;
+}
+
+// Split-KV count for nbatch elements: enough workgroups for two per CU of a 256-CU part.
+constexpr int kTargetGroups = 2 * 256;
+constexpr int kMaxSplit = 16;
+int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles) {
+  if (c.dtype != SDV2_BF16) return 1;
+  const int64_t N = (int64_t)c.grid_h * c.grid_w;
+  const int64_t base = (int64_t)nbatch * c.num_heads * ((N + kQTile - 1) / kQTile);
+  int ns = base >= kTargetGroups ? 1 : (int)((kTargetGroups + base - 1) / base);
+  if (ns > kMaxSplit) ns = kMaxSplit;
+  if (ns > total_tiles) ns = total_tiles;
+  return ns < 1 ? 1 : ns;
+}
+
+struct MetaLayout {
+  int64_t tab_h, tab_w, embeds, decision, alpha, total;
+};
+
+MetaLayout meta_layout(const sdv2_config& c) {
+  MetaLayout m;
+  int64_t off = 0;
+  m.tab_h = off;
+  off = align_up(off + (int64_t)c.grid_h * (c.rope_dim_h / 2) * 8, kAlign);
+  m.tab_w = off;
+  off = align_up(off + (int64_t)c.grid_w * (c.rope_dim_w / 2) * 8, kAlign);
+  m.embeds = off;
+  off = align_up(off + (int64_t)c.sink_frames * c.embed_dim * 4, kAlign);
+  m.decision = off;
+  off = align_up(off + 16, kAlign);
+  m.alpha = off;
+  off = align_up(off + 16, kAlign);
+  m.total = off;
+  return m;
+}
+
+int64_t workspace_bytes(const sdv2_config& c) {
+  const int64_t N = (int64_t)c.grid_h * c.grid_w;
+  const int tiles = (c.sink_frames + c.window_frames + 1) * (int)(align_up(N, kTileKeys) / kTileKeys);
+  int64_t best = 0;
+  for (int nb = 1; nb <= c.stream_batch; ++nb) {
+    const int ns = choose_nsplit(c, nb, tiles);
+    if (ns < 2) continue;
+    const int64_t rows = (int64_t)ns * nb * c.num_heads * N;
+    const int64_t bytes = align_up(rows * c.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
+    if (bytes > best) best = bytes;
+  }
+  return best;
+}
+
+// omega_i = theta^(-2i / dim_axis)
+double omega(double theta, int i, int dim_axis) { return std::pow(theta, -2.0 * i / dim_axis); }
+
+enum State { kIdle = 0, kStep = 1, kCommitted = 2 };
+
+}  // namespace
+
+struct sdv2_cache {
+  sdv2_config cfg;
+  sdv2_layout lay;
+  MetaLayout meta;
+  char* kv;
+  char* meta_base;
+  char* ws;
+  int64_t ws_bytes;
+  int64_t N;
+  // bookkeeping
+  int64_t base = 0;            // RoPE base b0
+  int64_t committed = 0;       // chunks committed
+  int64_t refreshes = 0;
+  std::vector<int64_t> slot_frame;   // per slot; -1 empty, -2 unknown
+  std::vector<int64_t> slot_label;
+  std::vector<uint8_t> slot_written; // slot holds a committed frame (shared slots only)
+  bool sinks_unknown = false;
+  // step protocol
+  int state = kIdle;
+  bool started = false;
+  int64_t newest = -1;
+  int64_t step_first = -1;
+  int32_t step_nbatch = 0;
+  std::vector<uint8_t> appended;
+  int64_t last_commit_frame = -1;
+};
+
+namespace {
+
+int check_cache(const sdv2_cache* c) {
+  if (!c) return fail(SDV2_EINVAL, "cache is NULL");
+  return SDV2_OK;
+}
+
+// Present shared slots in attention order: sinks by slot index, then the ring by slot index.
+int shared_slots(const sdv2_cache* c, int* out) {
+  int n = 0;
+  const int SW = c->cfg.sink_frames + c->cfg.window_frames;
+  for (int s = 0; s < SW; ++s)
+    if (c->slot_written[s]) out[n++] = s;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdv2_config_validate(const sdv2_config* cfg) {
+  const int rc = validate(cfg);
+  return rc ? rc : ok();
+}
+
+int sdv2_cache_layout(const sdv2_config* cfg, sdv2_layout* out) {
+  if (int rc = validate(cfg)) return rc;
+  if (!out) return fail(SDV2_EINVAL, "out is NULL");
+  *out = make_layout(*cfg);
+  return ok();
+}
+
+int sdv2_cache_size(const sdv2_config* cfg, size_t* kv_bytes, size_t* meta_bytes,
+                    size_t* workspace) {
+  if (int rc = validate(cfg)) return rc;
+  const sdv2_layout l = make_layout(*cfg);
+  if (kv_bytes) *kv_bytes = (size_t)(l.kv_elems * l.elem_bytes);
+  if (meta_bytes) *meta_bytes = (size_t)meta_layout(*cfg).total;
+  if (workspace) *workspace = (size_t)workspace_bytes(*cfg);
+  return ok();
+}
+
+int sdv2_cache_create(const sdv2_config* cfg, void* d_kv, size_t kv_bytes, void* d_meta,
+                      size_t meta_bytes, void* d_workspace, size_t ws_bytes, void* stream,
+                      sdv2_cache** out) {
+  if (int rc = validate(cfg)) return rc;
+  if (!out) return fail(SDV2_EINVAL, "out is NULL");
+  size_t need_kv, need_meta, need_ws;
+  sdv2_cache_size(cfg, &need_kv, &need_meta, &need_ws);
+  if (!d_kv || !d_meta) return fail(SDV2_EINVAL, "d_kv and d_meta must not be NULL");
+  if (need_ws && !d_workspace) return fail(SDV2_EINVAL, "d_workspace must not be NULL");
+  if (((uintptr_t)d_kv | (uintptr_t)d_meta | (uintptr_t)d_workspace) % kAlign)
+    return fail(SDV2_EINVAL, "device buffers must be 256-byte aligned");
+  if (kv_bytes < need_kv) return fail(SDV2_ENOSPC, "kv buffer %zu < %zu bytes", kv_bytes, need_kv);
+  if (meta_bytes < need_meta) return fail(SDV2_ENOSPC, "meta buffer %zu < %zu bytes", meta_bytes, need_meta);
+  if (ws_bytes < need_ws) return fail(SDV2_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, need_ws);
+
+  const sdv2_config& c = *cfg;
+  const MetaLayout ml = meta_layout(c);
+  // h / w RoPE tables: (cos, sin) of pos * omega, computed in double, stored as fp32
+  std::vector<char> host(ml.total, 0);
+  float2* th = (float2*)(host.data() + ml.tab_h);
+  float2* tw = (float2*)(host.data() + ml.tab_w);
+  const int ph = c.rope_dim_h / 2, pw = c.rope_dim_w / 2;
+  for (int h = 0; h < c.grid_h; ++h)
+    for (int i = 0; i < ph; ++i) {
+      const double ang = h * omega(c.rope_theta, i, c.rope_dim_h);
+      th[h * ph + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  for (int w = 0; w < c.grid_w; ++w)
+    for (int i = 0; i < pw; ++i) {
+      const double ang = w * omega(c.rope_theta, i, c.rope_dim_w);
+      tw[w * pw + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  *(int32_t*)(host.data() + ml.decision) = -1;
+
+  hipStream_t s = (hipStream_t)stream;
+  SDV2_HIP(hipMemsetAsync(d_kv, 0, need_kv, s));
+  SDV2_HIP(hipMemcpyAsync(d_meta, host.data(), ml.total, hipMemcpyHostToDevice, s));
+  SDV2_HIP(hipStreamSynchronize(s));
+
+  sdv2_cache* cache = new sdv2_cache();
+  cache->cfg = c;
+  cache->lay = make_layout(c);
+  cache->meta = ml;
+  cache->kv = (char*)d_kv;
+  cache->meta_base = (char*)d_meta;
+  cache->ws = (char*)d_workspace;
+  cache->ws_bytes = (int64_t)ws_bytes;
+  cache->N = (int64_t)c.grid_h * c.grid_w;
+  cache->slot_frame.assign(cache->lay.slots, -1);
+  cache->slot_label.assign(cache->lay.slots, 0);
+  cache->slot_written.assign(cache->lay.slots, 0);
+  cache->appended.assign(c.num_layers, 0);
+  *out = cache;
+  return ok();
+}
+
+int sdv2_cache_destroy(sdv2_cache* cache) {
+  delete cache;
+  return ok();
+}
+
+int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  if (newest_frame < 0) return fail(SDV2_EINVAL, "newest_frame must be >= 0");
+  if (c->started && newest_frame < c->newest)
+    return fail(SDV2_ESTATE, "newest_frame %lld is older than the previous step's %lld",
+                (long long)newest_frame, (long long)c->newest);
+  if (newest_frame < c->committed)
+    return fail(SDV2_ESTATE, "newest_frame %lld is already committed", (long long)newest_frame);
+  const sdv2_config& cfg = c->cfg;
+  const int64_t T = cfg.rope_refresh_period;
+  int64_t count = 0;
+  if (T > 0 && newest_frame - c->base >= T) count = (newest_frame - c->base) / T;
+  if (count > 0) {
+    int slots[kMaxShared];
+    const int ns = shared_slots(c, slots);
+    if (ns > 0 && cfg.rope_dim_t > 0) {
+      RebaseArgs a{};
+      a.kv = c->kv;
+      a.layer_stride = c->lay.layer_stride;
+      a.slot_stride = c->lay.slot_stride;
+      a.head_stride = c->lay.head_stride;
+      a.L = cfg.num_layers;
+      a.H = cfg.num_heads;
+      a.N = (int)c->N;
+      a.pt = cfg.rope_dim_t / 2;
+      a.nslots = ns;
+      for (int i = 0; i < ns; ++i) a.slots[i] = slots[i];
+      const double delta = (double)(count * T);
+      for (int i = 0; i < a.pt; ++i) {
+        const double ang = -delta * omega(cfg.rope_theta, i, cfg.rope_dim_t);
+        a.cs[i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+      SDV2_HIP(launch_rebase(a, cfg.head_dim, cfg.dtype == SDV2_BF16, (hipStream_t)stream));
+    }
+    c->base += count * T;
+    c->refreshes += count;
+    for (int s = 0; s < cfg.sink_frames + cfg.window_frames; ++s)
+      if (c->slot_written[s]) c->slot_label[s] -= count * T;
+  }
+  c->started = true;
+  c->newest = newest_frame;
+  c->state = kStep;
+  c->step_first = -1;
+  c->step_nbatch = 0;
+  std::fill(c->appended.begin(), c->appended.end(), 0);
+  // staging slots hold nothing committed-visible until the appends of this step
+  for (int64_t s = cfg.sink_frames + cfg.window_frames; s < c->lay.slots; ++s) c->slot_frame[s] = -1;
+  if (applied) *applied = (int32_t)count;
+  return ok();
+}
+
+int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t nbatch,
+                      void* d_q, const void* d_k, const void* d_v, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  const sdv2_config& cfg = c->cfg;
+  if (c->state != kStep) return fail(SDV2_ESTATE, "append outside a step (call sdv2_rope_refresh first)");
+  if (layer < 0 || layer >= cfg.num_layers) return fail(SDV2_EINVAL, "layer %d out of range", layer);
+  if (nbatch < 1 || nbatch > cfg.stream_batch)
+    return fail(SDV2_EINVAL, "nbatch must be in [1, %d]", cfg.stream_batch);
+  if (!d_q || !d_k || !d_v) return fail(SDV2_EINVAL, "q, k and v must not be NULL");
+  if (((uintptr_t)d_q | (uintptr_t)d_k | (uintptr_t)d_v) & 15)
+    return fail(SDV2_EINVAL, "q, k and v must be 16-byte aligned");
+  if (first_chunk != c->committed)
+    return fail(SDV2_ESTATE, "first_chunk %lld must equal the committed count %lld",
+                (long long)first_chunk, (long long)c->committed);
+  if (first_chunk + nbatch - 1 != c->newest)
+    return fail(SDV2_ESTATE, "newest chunk %lld differs from the step's newest frame %lld",
+                (long long)(first_chunk + nbatch - 1), (long long)c->newest);
+  if (c->step_nbatch != 0 && (c->step_nbatch != nbatch || c->step_first != first_chunk))
+    return fail(SDV2_ESTATE, "nbatch/first_chunk differ between layers of one step");
+  if (c->appended[layer]) return fail(SDV2_ESTATE, "layer %d already appended this step", layer);
+
+  AppendArgs a{};
+  a.q = d_q;
+  a.k = d_k;
+  a.v = d_v;
+  a.kv = c->kv;
+  a.k_layer_off = layer * c->lay.layer_stride;
+  a.v_layer_off = a.k_layer_off + c->lay.slots * c->lay.slot_stride;
+  a.slot_stride = c->lay.slot_stride;
+  a.head_stride = c->lay.head_stride;
+  a.tab_h = (const float2*)(c->meta_base + c->meta.tab_h);
+  a.tab_w = (const float2*)(c->meta_base + c->meta.tab_w);
+  a.N = (int)c->N;
+  a.Npad = (int)c->lay.tokens_padded;
+  a.H = cfg.num_heads;
+  a.grid_w = cfg.grid_w;
+  a.nbatch = nbatch;
+  a.staging_slot0 = cfg.sink_frames + cfg.window_frames;
+  a.pt = cfg.rope_dim_t / 2;
+  a.ph = cfg.rope_dim_h / 2;
+  a.pw = cfg.rope_dim_w / 2;
+  for (int b = 0; b < nbatch; ++b) {
+    const double p = (double)(first_chunk + b - c->base);   // temporal position f - b0 (T' = 1)
+    for (int i = 0; i < a.pt; ++i) {
+      const double ang = p * omega(cfg.rope_theta, i, cfg.rope_dim_t);
+      a.tcs[b][i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  }
+  SDV2_HIP(launch_rope_append(a, cfg.head_dim, cfg.dtype == SDV2_BF16, (hipStream_t)stream));
+  c->appended[layer] = 1;
+  c->step_first = first_chunk;
+  c->step_nbatch = nbatch;
+  for (int b = 0; b < nbatch; ++b) {
+    c->slot_frame[a.staging_slot0 + b] = first_chunk + b;
+    c->slot_label[a.staging_slot0 + b] = first_chunk + b - c->base;
+  }
+  return ok();
+}
+
+int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q_rot,
+                         void* d_out, float scale, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  const sdv2_config& cfg = c->cfg;
+  if (c->state != kStep) return fail(SDV2_ESTATE, "attention outside a step or after the commit");
+  if (layer < 0 || layer >= cfg.num_layers) return fail(SDV2_EINVAL, "layer %d out of range", layer);
+  if (!c->appended[layer]) return fail(SDV2_ESTATE, "layer %d not appended this step", layer);
+  if (nbatch != c->step_nbatch) return fail(SDV2_EINVAL, "nbatch %d differs from the append's %d", nbatch, c->step_nbatch);
+  if (!d_q_rot || !d_out) return fail(SDV2_EINVAL, "q_rot and out must not be NULL");
+  if (((uintptr_t)d_q_rot | (uintptr_t)d_out) & 15) return fail(SDV2_EINVAL, "q_rot and out must be 16-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SDV2_EINVAL, "scale must be finite and > 0");
+
+  const bool bf16 = cfg.dtype == SDV2_BF16;
+  AttnArgs a{};
+  a.q = d_q_rot;
+  a.out = d_out;
+  a.kv = c->kv;
+  a.k_layer_off = layer * c->lay.layer_stride;
+  a.v_layer_off = a.k_layer_off + c->lay.slots * c->lay.slot_stride;
+  a.slot_stride = c->lay.slot_stride;
+  a.head_stride = c->lay.head_stride;
+  a.N = (int)c->N;
+  a.Npad = (int)c->lay.tokens_padded;
+  a.H = cfg.num_heads;
+  a.nbatch = nbatch;
+  a.nshared = shared_slots(c, a.slots);
+  a.own_slot0 = cfg.sink_frames + cfg.window_frames;
+  a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
+  a.total_tiles = (a.nshared + 1) * a.tiles_per_frame;
+  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles);
+  a.qtiles = (int)((c->N + kQTile - 1) / kQTile);
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * c->N;
+  if (a.nsplit > 1) {
+    const int64_t need = align_up(rows * cfg.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
+    if (need > c->ws_bytes) return fail(SDV2_ENOSPC, "workspace too small for %d splits", a.nsplit);
+    a.part_o = (float*)c->ws;
+    a.part_ml = (float2*)(c->ws + align_up(rows * cfg.head_dim * 4, kAlign));
+  }
+  SDV2_HIP(launch_attention(a, cfg.head_dim, bf16, (hipStream_t)stream));
+  if (a.nsplit > 1) {
+    CombineArgs m{a.part_o, a.part_ml, d_out, a.N, a.H, nbatch, a.nsplit};
+    SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));
+  }
+  return ok();
+}
+
+int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  const sdv2_config& cfg = c->cfg;
+  if (c->state != kStep) return fail(SDV2_ESTATE, "commit outside a step or twice in one step");
+  for (int l = 0; l < cfg.num_layers; ++l)
+    if (!c->appended[l]) return fail(SDV2_ESTATE, "layer %d not appended this step", l);
+  if (chunk != c->step_first) return fail(SDV2_ESTATE, "only element 0 (chunk %lld) can be committed", (long long)c->step_first);
+  const int64_t f = chunk;   // T' = 1
+  const int S = cfg.sink_frames, W = cfg.window_frames;
+  const int dst = f < S ? (int)f : S + (int)(f % W);
+  CopyArgs a{};
+  a.kv = c->kv;
+  a.layer_stride_bytes = c->lay.layer_stride * c->lay.elem_bytes;
+  a.v_block_bytes = c->lay.slots * c->lay.slot_stride * c->lay.elem_bytes;
+  a.slot_bytes = c->lay.slot_stride * c->lay.elem_bytes;
+  a.src_slot = S + W;
+  a.dst_slot = dst;
+  a.dst_from = nullptr;
+  a.L = cfg.num_layers;
+  SDV2_HIP(launch_copy_slots(a, (hipStream_t)stream));
+  c->slot_frame[dst] = f;
+  c->slot_label[dst] = f - c->base;
+  c->slot_written[dst] = 1;
+  c->committed = chunk + 1;
+  c->last_commit_frame = f;
+  c->state = kCommitted;
+  return ok();
+}
+
+int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_t* h_slot,
+                      double* h_alpha, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  const sdv2_config& cfg = c->cfg;
+  if (c->state != kCommitted) return fail(SDV2_ESTATE, "sink_replace must follow a commit");
+  if (frame != c->last_commit_frame) return fail(SDV2_ESTATE, "frame %lld is not the committed frame %lld",
+                                                  (long long)frame, (long long)c->last_commit_frame);
+  if (cfg.embed_dim < 1) return fail(SDV2_EINVAL, "the cache has no chunk embeddings (embed_dim 0)");
+  if (!d_embed) return fail(SDV2_EINVAL, "d_embed must not be NULL");
+  const int S = cfg.sink_frames, W = cfg.window_frames;
+  hipStream_t s = (hipStream_t)stream;
+  SinkArgs a{};
+  a.h = d_embed;
+  a.embeds = (float*)(c->meta_base + c->meta.embeds);
+  a.decision = (int32_t*)(c->meta_base + c->meta.decision);
+  a.alpha = (double*)(c->meta_base + c->meta.alpha);
+  a.S = S;
+  a.D = cfg.embed_dim;
+  a.tau = cfg.sink_threshold;
+  const bool decide = frame >= S && tau_on(cfg);
+  if (frame < S) {
+    a.store_slot = (int)frame;
+    SDV2_HIP(launch_sink_decide(a, s));
+  } else if (decide) {
+    a.store_slot = -1;
+    SDV2_HIP(launch_sink_decide(a, s));
+    CopyArgs cp{};
+    cp.kv = c->kv;
+    cp.layer_stride_bytes = c->lay.layer_stride * c->lay.elem_bytes;
+    cp.v_block_bytes = c->lay.slots * c->lay.slot_stride * c->lay.elem_bytes;
+    cp.slot_bytes = c->lay.slot_stride * c->lay.elem_bytes;
+    cp.src_slot = S + (int)(frame % W);
+    cp.dst_slot = -1;
+    cp.dst_from = a.decision;
+    cp.L = cfg.num_layers;
+    SDV2_HIP(launch_copy_slots(cp, s));
+  }
+  int32_t slot = -1;
+  double alpha = 1.0;
+  if (decide && h_slot) {
+    SDV2_HIP(hipMemcpyAsync(&slot, a.decision, sizeof(slot), hipMemcpyDeviceToHost, s));
+    SDV2_HIP(hipMemcpyAsync(&alpha, a.alpha, sizeof(alpha), hipMemcpyDeviceToHost, s));
+    SDV2_HIP(hipStreamSynchronize(s));
+    if (slot >= 0) {
+      c->slot_frame[slot] = frame;
+      c->slot_label[slot] = c->slot_label[S + (int)(frame % W)];
+    }
+  } else if (decide) {
+    c->sinks_unknown = true;
+  }
+  if (h_slot) *h_slot = slot;
+  if (h_alpha) *h_alpha = alpha;
+  c->state = kIdle;
+  return ok();
+}
+
+int sdv2_motion_workspace_size(int32_t nframes, int64_t elems_per_frame, size_t* bytes) {
+  if (nframes < 2) return fail(SDV2_EINVAL, "nframes must be >= 2");
+  if (elems_per_frame < 1) return fail(SDV2_EINVAL, "elems_per_frame must be >= 1");
+  if (!bytes) return fail(SDV2_EINVAL, "bytes is NULL");
+  *bytes = (size_t)(nframes - 1) * motion_parts(elems_per_frame) * sizeof(double);
+  return ok();
+}
+
+int sdv2_motion_l2(const float* d_frames, int32_t nframes, int64_t elems_per_frame, double* d_dist,
+                   void* d_workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  if (int rc = sdv2_motion_workspace_size(nframes, elems_per_frame, &need)) return rc;
+  if (!d_frames || !d_dist || !d_workspace) return fail(SDV2_EINVAL, "frames, dist and workspace must not be NULL");
+  if (workspace_bytes < need) return fail(SDV2_ENOSPC, "motion workspace %zu < %zu bytes", workspace_bytes, need);
+  if (nframes - 1 > 65535) return fail(SDV2_EINVAL, "at most 65536 frames per call");
+  if (((uintptr_t)d_dist | (uintptr_t)d_workspace) & 7) return fail(SDV2_EINVAL, "dist and workspace must be 8-byte aligned");
+  if ((uintptr_t)d_frames & 3) return fail(SDV2_EINVAL, "frames must be 4-byte aligned");
+  SDV2_HIP(launch_motion(d_frames, nframes, elems_per_frame, d_dist, (double*)d_workspace,
+                         motion_parts(elems_per_frame), (hipStream_t)stream));
+  return ok();
+}
+
+int sdv2_noise_schedule(const double* h_dist, int32_t n, double sigma, int32_t k, double lambda,
+                        double s_min, double s_max, double s0, double* h_rate) {
+  if (n < 0 || (n > 0 && (!h_dist || !h_rate))) return fail(SDV2_EINVAL, "bad distance/rate arrays");
+  if (!(sigma > 0.0) || k < 1) return fail(SDV2_EINVAL, "sigma must be > 0 and k >= 1");
+  if (!(lambda > 0.0 && lambda <= 1.0)) return fail(SDV2_EINVAL, "lambda must be in (0, 1]");
+  double s = s0;
+  for (int32_t t = 0; t < n; ++t) {
+    double m = 0.0;
+    for (int32_t i = (t - k + 1 > 0 ? t - k + 1 : 0); i <= t; ++i) m = h_dist[i] > m ? h_dist[i] : m;
+    const double dhat = m / sigma < 1.0 ? m / sigma : 1.0;
+    const double target = s_max - (s_max - s_min) * dhat;
+    s = lambda * target + (1.0 - lambda) * s;
+    h_rate[t] = s;
+  }
+  return ok();
+}
+
+int sdv2_cache_slot_info(const sdv2_cache* c, int32_t slot, int64_t* frame, int32_t* tpos) {
+  if (int rc = check_cache(c)) return rc;
+  if (slot < 0 || slot >= c->lay.slots) return fail(SDV2_EINVAL, "slot %d out of range", slot);
+  int64_t f = c->slot_frame[slot];
+  int64_t p = c->slot_label[slot];
+  if (c->sinks_unknown && slot < c->cfg.sink_frames && f >= 0) f = -2;
+  if (frame) *frame = f;
+  if (tpos) *tpos = (int32_t)p;
+  return ok();
+}
+
+int sdv2_cache_state(const sdv2_cache* c, int64_t* rope_base, int64_t* committed, int64_t* refreshes) {
+  if (int rc = check_cache(c)) return rc;
+  if (rope_base) *rope_base = c->base;
+  if (committed) *committed = c->committed;
+  if (refreshes) *refreshes = c->refreshes;
+  return ok();
+}
+
+int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int64_t* first_chunk,
+                   int32_t* nbatch, int64_t* commit_chunk, int64_t* newest_frame) {
+  if (int rc = validate(cfg)) return rc;
+  if (num_chunks < 1 || step < 0) return fail(SDV2_EINVAL, "num_chunks must be >= 1 and step >= 0");
+  const int64_t B = cfg->stream_batch;
+  const int64_t lo = step - B + 1 > 0 ? step - B + 1 : 0;
+  const int64_t hi = step < num_chunks - 1 ? step : num_chunks - 1;
+  const int64_t nb = hi >= lo ? hi - lo + 1 : 0;
+  const int64_t c0 = step - B + 1;
+  if (first_chunk) *first_chunk = nb > 0 ? lo : -1;
+  if (nbatch) *nbatch = (int32_t)nb;
+  if (commit_chunk) *commit_chunk = (c0 >= 0 && c0 < num_chunks) ? c0 : -1;
+  if (newest_frame) *newest_frame = nb > 0 ? hi : -1;   // T' = 1
+  return ok();
+}
+
+const char* sdv2_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

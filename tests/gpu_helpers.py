@@ -1,0 +1,164 @@
+"""Drive the HIP path and the oracle side by side on the same seeded inputs (GPU tests only)."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+from oracle import rope as orope
+from oracle import stream as ost
+from rolling_kv_causal_amd import sdv2
+from rolling_kv_causal_amd.stream import StreamRunner
+from synth import inputs
+
+BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS = 2e-2, 2e-3, 1e-5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(cfg, arr):
+    if cfg.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def host64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bf16_bits_of(x64: np.ndarray) -> np.ndarray:
+    """bf16-exact float64 values -> their bit patterns."""
+    return (np.asarray(x64, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def assert_close(cfg, got, want, what, scale=1.0):
+    err = np.abs(np.asarray(got, np.float64) - want)
+    if cfg.dtype == "fp32":
+        assert err.max() <= FP32_MAX_ABS * scale, f"{what}: max-abs {err.max():.3g}"
+    else:
+        assert err.max() <= BF16_MAX_ABS * scale, f"{what}: max-abs {err.max():.3g}"
+        assert err.mean() <= BF16_MEAN_ABS * scale, f"{what}: mean-abs {err.mean():.3g}"
+    return float(err.max())
+
+
+class Harness:
+    """GPU stream + oracle stream.  Layers in `layers` get seeded numpy inputs for element 0 at
+    every step (so the oracle knows every cached frame) and for all elements at checked steps;
+    other (layer, element) pairs get device-side random inputs."""
+
+    def __init__(self, cfg, layers, num_chunks=None, seed=1234):
+        self.cfg = cfg
+        self.layers = list(layers)
+        self.M = cfg.num_chunks if num_chunks is None else num_chunks
+        self.ccfg = sdv2.config_of(cfg)
+        self.run = StreamRunner(self.ccfg, cfg.num_chunks, cfg.softmax_scale)
+        self.st = ost.OracleStream(cfg, layers=self.layers)
+        self.gen = torch.Generator(device="cuda")
+        self.gen.manual_seed(seed)
+        self.np_inputs = {}
+        self.refresh_applied = {}
+        self.decisions = {}
+        self.step_no = -1
+
+    def _random(self, nb):
+        shape = (nb, self.cfg.chunk_rows, self.cfg.num_heads, self.cfg.head_dim)
+        x = torch.randn(shape, generator=self.gen, device="cuda")
+        return x.to(self.run.dtype)
+
+    def step(self, s, full=False):
+        """Advance both sides one step; full = numpy inputs for every element of the layers."""
+        cfg = self.cfg
+        plan = self.st.begin_step(s)
+        nb = len(plan["chunks"])
+        self.np_inputs = {}
+        for layer in self.layers:
+            for b in (range(nb) if full else [0]):
+                self.np_inputs[(layer, b)] = inputs.qkv(cfg, s, layer, b)
+
+        def qkv(s_, layer, nb_):
+            out = []
+            for j in range(3):
+                t = self._random(nb_)
+                for b in range(nb_):
+                    if (layer, b) in self.np_inputs:
+                        t[b] = dev(cfg, self.np_inputs[(layer, b)][j])
+                out.append(t)
+            return tuple(out)
+
+        emb = None
+        if cfg.embed_dim > 0:
+            emb = lambda c: dev(cfg, inputs.chunk_embedding(cfg, c))
+        info = self.run.step(s, qkv, embed=emb)
+        self.refresh_applied[s] = info["refreshed"]
+        commit_kv = {layer: self.np_inputs[(layer, 0)][1:] for layer in self.layers}
+        h = inputs.chunk_embedding(cfg, plan["commit"]) if (cfg.embed_dim > 0 and plan["commit"] is not None) else None
+        self._pending = (plan, info, commit_kv, h)
+        self.step_no = s
+        return plan, info
+
+    def finish_step(self):
+        plan, info, commit_kv, h = self._pending
+        dec = self.st.end_step(commit_kv, h)
+        if dec is not None:
+            self.decisions[plan["commit"]] = (dec, info["sink"])
+            want = dec["slot"] if dec["replaced"] else -1
+            assert info["sink"][0] == want, f"sink decision chunk {plan['commit']}: gpu {info['sink']} oracle {dec}"
+            assert abs(info["sink"][1] - dec["alpha"]) <= 1e-9, (info["sink"], dec)
+        # refresh events must match the oracle's
+        n_ref = sum(1 for (s_, _) in self.st.refresh_log if s_ == self.step_no)
+        assert self.refresh_applied[self.step_no] == n_ref, (self.step_no, self.refresh_applied[self.step_no], n_ref)
+        return dec
+
+    def check_outputs(self, rows=None, heads=None):
+        """Compare the current step's outputs of every element on the checked layers."""
+        cfg = self.cfg
+        plan = self.st.plan
+        worst = 0.0
+        for layer in self.layers:
+            for b in range(len(plan["chunks"])):
+                q, k, v = self.np_inputs[(layer, b)]
+                ref = self.st.attend(layer, b, q, k, v, rows=rows, heads=heads)
+                got = self.run.out[layer, b]
+                if rows is not None:
+                    got = got[torch.as_tensor(rows, device="cuda")]
+                if heads is not None:
+                    got = got[:, torch.as_tensor(heads, device="cuda")]
+                worst = max(worst, assert_close(cfg, host64(got), ref, f"out step {self.step_no} layer {layer} elem {b}"))
+        return worst
+
+    def check_cache(self, layers=None):
+        """Slot table bit-exact, V bytes bit-exact, K_rot within tolerance, for cached frames."""
+        cfg = self.cfg
+        N = cfg.tokens
+        r = len(self.st.refresh_log)
+        cache = self.run.cache
+        base, committed, refreshes = cache.state()
+        assert base == self.st.base and refreshes == r
+        entries = [(j, e) for j, e in enumerate(self.st.sinks) if e is not None]
+        entries += [(ost.ring_slot(cfg, e.frame), e) for e in self.st.window]
+        for layer in (self.layers if layers is None else layers):
+            Kg, Vg = cache.k_view(layer), cache.v_view(layer)
+            for slot, e in entries:
+                assert cache.slot_info(slot) == (e.frame, e.label), (slot, cache.slot_info(slot), e.frame, e.label)
+                k_ref = orope.rope_frame(cfg, e.kv[layer][0], e.label)
+                k_got = host64(Kg[slot, :, :N, :].permute(1, 0, 2))
+                assert_close(cfg, k_got, k_ref, f"K slot {slot} frame {e.frame}", scale=1 + r)
+                v_got = Vg[slot, :, :, :N].permute(2, 0, 1).contiguous()
+                if cfg.dtype == "bf16":
+                    got_bits = v_got.view(torch.int16).cpu().numpy().view(np.uint16)
+                    assert np.array_equal(got_bits, bf16_bits_of(e.kv[layer][1])), f"V bytes slot {slot}"
+                else:
+                    assert np.array_equal(v_got.cpu().numpy(), np.asarray(e.kv[layer][1], np.float32)), f"V slot {slot}"
+            # zero padding of the token axis stays zero
+            if cache.layout.tokens_padded > N:
+                assert torch.count_nonzero(Kg[:, :, N:, :]) == 0 and torch.count_nonzero(Vg[:, :, :, N:]) == 0
+
+
+def sample_rows(N, n=40, seed=0):
+    g = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, N // 2, N - 2, N - 1]
+    return np.array(sorted(set([x for x in fixed if 0 <= x < N] + list(g.choice(N, min(n, N), replace=False)))))

@@ -1,0 +1,143 @@
+"""GPU parity: the HIP path against the float64 oracle on the same seeded inputs.
+
+Bars: bit-exact slot table, V bytes, refresh events and sink decisions; outputs and cached K
+within max-abs 1e-5 (fp32) or max-abs 2e-2 and mean-abs 2e-3 (bf16, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Harness, log, sample_rows
+from oracle import motion as omotion
+from rolling_kv_causal_amd import sdv2
+from synth import configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(**kw):
+    base = dict(rope_refresh_period=0, sink_threshold=None, embed_dim=0, embed_kind=None)
+    base.update(kw)
+    return configs.TINY_FP32.with_(**base)
+
+
+def _stream(cfg, steps, layers=(0,), check=lambda s: True, rows=None, cache_check=lambda s: True):
+    h = Harness(cfg, layers)
+    worst = 0.0
+    for s in range(steps):
+        full = check(s)
+        h.step(s, full=full)
+        if full:
+            worst = max(worst, h.check_outputs(rows=rows))
+        h.finish_step()
+        if cache_check(s):
+            h.check_cache()
+    log(f"{cfg.name}: {steps} steps, worst max-abs {worst:.3g}, refreshes {h.st.refresh_log}")
+    return h
+
+
+def test_tiny_fp32_full_stream():
+    # 12 chunks: the ring wraps twice, refresh at frame 8, the sink refreshed by cosine rule
+    cfg = configs.TINY_FP32
+    h = _stream(cfg, cfg.num_steps)
+    assert h.st.refresh_log == [(8, 8)]
+    assert len(h.decisions) == cfg.num_chunks - cfg.sink_frames
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5, grid_w=13,
+         num_heads=3, sink_frames=2, window_frames=3, stream_batch=3, rope_refresh_period=5, num_chunks=14,
+         softmax_scale=128 ** -0.5),
+    dict(dtype="bf16", head_dim=64, grid_h=9, grid_w=11, num_heads=2, sink_frames=0, window_frames=2,
+         stream_batch=2, num_chunks=9, num_layers=2),
+    dict(dtype="fp32", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=3, grid_w=7,
+         num_heads=2, sink_frames=1, window_frames=1, stream_batch=4, rope_refresh_period=3, num_chunks=10),
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=12, grid_w=25,
+         num_heads=4, sink_frames=3, window_frames=2, stream_batch=1, num_chunks=9, embed_dim=16,
+         sink_threshold=0.2, embed_kind="iid", softmax_scale=128 ** -0.5),
+], ids=["bf16-ragged-B3-refresh", "bf16-d64-S0", "fp32-d128-W1-B4", "bf16-sinks-iid"])
+def test_small_ragged_streams(kw):
+    # token counts that are not multiples of the 64-key tile or the 128-row query tile,
+    # degenerate windows (W = 1, S = 0), B up to 4, and several layers
+    cfg = _small(**kw)
+    _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
+
+
+def test_wan13b_single_layer_full_size():
+    cfg = configs.WAN13B_1LAYER
+    checked = {0, 1, 8, 9, 10, 31, 32, 33, cfg.num_steps - 1}
+    rows = sample_rows(cfg.tokens, n=48)
+    h = _stream(cfg, cfg.num_steps, check=lambda s: s in checked, rows=rows,
+                cache_check=lambda s: s in checked)
+    assert h.st.refresh_log == [(32, 32)]
+
+
+def test_wan13b_30layer_b4_full_size():
+    cfg = configs.WAN13B_30LAYER_B4
+    checked = {3, 12, 13}
+    rows = sample_rows(cfg.tokens, n=24, seed=1)
+    _stream(cfg, 14, layers=(0, 29), check=lambda s: s in checked, rows=rows,
+            cache_check=lambda s: s in checked)
+
+
+def test_wan13b_480p_b2_full_size_with_refresh():
+    cfg = configs.WAN13B_480P_B2
+    checked = {2, 10, 24, 25}
+    rows = sample_rows(cfg.tokens, n=24, seed=2)
+    h = _stream(cfg, 26, layers=(0,), check=lambda s: s in checked, rows=rows,
+                cache_check=lambda s: s in checked)
+    assert h.st.refresh_log == [(24, 24)]
+
+
+def test_wan14b_40layer_b4_full_size_with_sink_refresh():
+    cfg = configs.WAN14B_40LAYER_B4
+    steps = 40
+    rows = sample_rows(cfg.tokens, n=16, seed=3)
+    h = Harness(cfg, layers=(0,))
+    replaced = kept = 0
+    for s in range(steps):
+        full = s in (12, steps - 1)
+        h.step(s, full=full)
+        if full:
+            h.check_outputs(rows=rows, heads=np.arange(0, 40, 3))
+        dec = h.finish_step()
+        if dec is not None:
+            replaced += dec["replaced"]
+            kept += not dec["replaced"]
+        if full:
+            h.check_cache()
+    log(f"{cfg.name}: sink decisions replaced {replaced} kept {kept}")
+    assert replaced >= 1 and kept >= 1
+
+
+def test_motion_l2_and_noise_schedule():
+    cfg = configs.WAN13B_480P_B2
+    m = cfg.motion
+    frames = inputs.motion_frames(cfg)
+    x = torch.from_numpy(frames).cuda()
+    F = m.frames - 1
+    dist = torch.empty(F, dtype=torch.float64, device="cuda")
+    ws = torch.empty(sdv2.sdv2_motion_workspace_size(m.frames, m.elems), dtype=torch.uint8, device="cuda")
+    sdv2.sdv2_motion_l2(x, m.frames, m.elems, dist, ws)
+    got = dist.cpu().numpy()
+    want = omotion.frame_distances(frames)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+    rate = sdv2.sdv2_noise_schedule(list(got), m.sigma, m.window, m.lam, m.s_min, m.s_max, m.s_max)
+    np.testing.assert_allclose(rate, omotion.noise_schedule(want, m.sigma, m.window, m.lam, m.s_min, m.s_max),
+                               rtol=1e-12)
+    # odd element count and unaligned base take the scalar path
+    sdv2.sdv2_motion_l2(x.view(-1)[1:1 + 3 * 1001], 3, 1001, dist, ws)
+    want2 = omotion.frame_distances(frames.reshape(-1)[1:1 + 3 * 1001].reshape(3, 1001))
+    np.testing.assert_allclose(dist[:2].cpu().numpy(), want2, rtol=1e-12)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    cfg = configs.WAN13B_1LAYER.with_(num_chunks=12)
+    outs = []
+    for _ in range(2):
+        h = Harness(cfg, layers=(0,))
+        for s in range(cfg.num_steps):
+            h.step(s)
+            h.finish_step()
+        outs.append(h.run.out.clone())
+    assert torch.equal(outs[0], outs[1])

@@ -1,0 +1,132 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol, and its
+host-only entry points (validation, layout, schedule, noise schedule) behave as documented.
+No kernel is launched here."""
+import math
+import pathlib
+import re
+
+import numpy as np
+import pytest
+
+from oracle import motion as omotion
+from oracle import stream as ost
+from rolling_kv_causal_amd import sdv2
+from synth import configs
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "sdv2.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sdv2_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 17
+    L = sdv2.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # the binding exposes the same names
+    assert all(hasattr(sdv2, n) for n in names)
+
+
+def test_struct_layout_matches_header():
+    # field order and types of sdv2_config / sdv2_layout as declared in the header
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct sdv2_config \{(.*?)\} sdv2_config;", text, re.S).group(1)
+    fields = re.findall(r"(int32_t|double)\s+([^;]+);", body)
+    names = []
+    for ty, decl in fields:
+        names += [(ty, n.strip()) for n in decl.split(",")]
+    want = [(("double" if f[1] is sdv2.ctypes.c_double else "int32_t"), f[0]) for f in sdv2.Config._fields_]
+    assert names == want
+
+
+@pytest.mark.parametrize("c", configs.ALL, ids=lambda c: c.name)
+def test_workload_configs_validate_and_size(c):
+    cfg = sdv2.config_of(c)
+    sdv2.sdv2_config_validate(cfg)
+    kv, meta, ws = sdv2.sdv2_cache_size(cfg)
+    L = sdv2.sdv2_cache_layout(cfg)
+    N = c.grid_h * c.grid_w
+    assert L.tokens_padded % 64 == 0 and N <= L.tokens_padded < N + 64
+    assert L.slots == c.sink_frames + c.window_frames + c.stream_batch
+    assert L.layer_stride == 2 * L.slots * c.num_heads * L.tokens_padded * c.head_dim
+    assert kv == c.num_layers * L.layer_stride * (2 if c.dtype == "bf16" else 4)
+    assert meta > 0 and ws >= 0
+
+
+def test_wan14b_cache_is_about_8_4_gb_plus_staging():
+    # 40 layers x (1 sink + 8 window + 1 chunk) frames x 1024 tokens x 40 heads x 128 x 2 (K, V)
+    # x 2 bytes = 8.39 GB; the cache also holds B = 4 staging frames.
+    c = configs.WAN14B_40LAYER_B4
+    kv, _, _ = sdv2.sdv2_cache_size(sdv2.config_of(c))
+    per_frame = 40 * 1024 * 40 * 128 * 2 * 2
+    assert kv == per_frame * (1 + 8 + 4)
+    assert abs(per_frame * 10 / 1e9 - 8.39) < 0.01
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, sdv2.SDV2_EINVAL), ("num_layers", 0, sdv2.SDV2_EINVAL),
+    ("window_frames", 0, sdv2.SDV2_EINVAL), ("chunk_frames", 2, sdv2.SDV2_EINVAL),
+    ("stream_batch", 9, sdv2.SDV2_EINVAL), ("rope_dim_t", 46, sdv2.SDV2_EINVAL),
+    ("rope_dim_h", 41, sdv2.SDV2_EINVAL), ("rope_theta", 1.0, sdv2.SDV2_EINVAL),
+    ("dtype", 7, sdv2.SDV2_EINVAL), ("sink_frames", 17, sdv2.SDV2_EINVAL),
+    ("rope_refresh_period", -1, sdv2.SDV2_EINVAL), ("grid_w", 0, sdv2.SDV2_EINVAL),
+])
+def test_invalid_configs_are_rejected(field, value, code):
+    cfg = sdv2.config_of(configs.WAN13B_1LAYER)
+    setattr(cfg, field, value)
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_config_validate(cfg)
+    assert e.value.code == code and sdv2.sdv2_last_error()
+
+
+def test_sink_threshold_needs_embeddings():
+    cfg = sdv2.config_of(configs.WAN13B_1LAYER)
+    cfg.sink_threshold = 0.5
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_config_validate(cfg)
+    cfg.embed_dim = 8
+    sdv2.sdv2_config_validate(cfg)
+    cfg.sink_threshold = -math.inf              # off again
+    cfg.embed_dim = 0
+    sdv2.sdv2_config_validate(cfg)
+
+
+@pytest.mark.parametrize("B,M", [(1, 5), (2, 7), (4, 6), (4, 2), (8, 11)])
+def test_plan_step_matches_oracle_schedule(B, M):
+    c = configs.WAN13B_1LAYER.with_(stream_batch=B, num_chunks=M)
+    cfg = sdv2.config_of(c)
+    for s in range(M + B + 1):
+        first, nb, commit, newest = sdv2.sdv2_plan_step(cfg, M, s)
+        want = ost.schedule(c, s)
+        assert nb == len(want["chunks"])
+        if nb:
+            assert list(range(first, first + nb)) == want["chunks"]
+            assert newest == want["newest_frame"]
+        assert commit == (want["commit"] if want["commit"] is not None else -1)
+
+
+def test_noise_schedule_matches_oracle():
+    g = np.random.default_rng(0)
+    d = np.abs(g.standard_normal(50)) * 0.4
+    for sigma, k, lam in [(1.0, 4, 0.9), (0.3, 1, 0.5), (2.0, 7, 1.0)]:
+        got = sdv2.sdv2_noise_schedule(list(d), sigma, k, lam, 0.25, 1.0, 1.0)
+        np.testing.assert_allclose(got, omotion.noise_schedule(d, sigma, k, lam, 0.25, 1.0), rtol=1e-14)
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_noise_schedule([0.1], 0.0, 4, 0.9, 0.25, 1.0, 1.0)
+
+
+def test_motion_workspace_size_and_errors():
+    assert sdv2.sdv2_motion_workspace_size(129, 99840) == 128 * 7 * 8
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_motion_workspace_size(1, 10)
+
+
+def test_null_handle_and_bad_arguments_fail_cleanly():
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_cache_slot_info(None, 0)
+    assert e.value.code == sdv2.SDV2_EINVAL
+    sdv2.sdv2_cache_destroy(None)
