@@ -31,6 +31,8 @@
 
 namespace sdv2 {
 
+constexpr float kLazy = 8.0f;   // lazy-rescale margin of the running max (log2 units)
+
 // LDS row of key `key` within a 64-key tile: swap bits 2 and 3 of the key index.
 __device__ __forceinline__ int perm_key(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
@@ -163,9 +165,22 @@ void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    // Lazy rescale: the running max m_run only moves when the tile max exceeds it by more than
+    // kLazy (log2 units), so exponentials stay <= 2^kLazy and O/l is unchanged (both use m_run).
+    // Once the max has settled no tile rescales O.
+    const float m_tile = mx * sl;
+    const bool grow = m_tile > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {          // wave-uniform branch
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    }
+    const float m_new = m_run;
 
     uint32_t pw0[8], pw1[8];
     float ps = 0.f;
@@ -179,11 +194,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       pw0[v / 2] = pack_bf16x2(p0, p1);
       pw1[v / 2] = pack_bf16x2(p2, p3);
     }
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    l_run += ps;
 
     // P^T operands: 16-key step kk of key block kb covers accumulator entries 8kk..8kk+7
     const bf16x8 pb00 = __builtin_bit_cast(bf16x8, make_uint4(pw0[0], pw0[1], pw0[2], pw0[3]));

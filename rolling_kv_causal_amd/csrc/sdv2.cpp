@@ -91,17 +91,31 @@ sdv2_layout make_layout(const sdv2_config& c) {
   return l;
 }
 
-// Split-KV count for nbatch elements: enough workgroups for two per CU of a 256-CU part.
-constexpr int kTargetGroups = 2 * 256;
+// Split-KV count for nbatch elements.  The grid runs in rounds of kSlots workgroups (256 CUs of
+// MI355X x 2 resident workgroups); a split count costs rounds x tiles-per-split tile steps plus
+// the fp32 partial results it writes and the combine reads back.  The constants are measured
+// on MI355X: about 2 us per 64-key tile step of a workgroup, ~5 TB/s for the partial traffic.
+constexpr int kSlots = 2 * 256;
 constexpr int kMaxSplit = 16;
+constexpr double kTileUs = 2.0, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles) {
   if (c.dtype != SDV2_BF16) return 1;
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
   const int64_t base = (int64_t)nbatch * c.num_heads * ((N + kQTile - 1) / kQTile);
-  int ns = base >= kTargetGroups ? 1 : (int)((kTargetGroups + base - 1) / base);
-  if (ns > kMaxSplit) ns = kMaxSplit;
-  if (ns > total_tiles) ns = total_tiles;
-  return ns < 1 ? 1 : ns;
+  const int64_t rows = (int64_t)nbatch * c.num_heads * N;
+  int best = 1;
+  double best_cost = 1e300;
+  for (int ns = 1; ns <= kMaxSplit && ns <= total_tiles; ++ns) {
+    const int64_t rounds = (base * ns + kSlots - 1) / kSlots;
+    const int64_t per = (total_tiles + ns - 1) / ns;
+    double cost = (double)(rounds * per) * kTileUs;
+    if (ns > 1) cost += (double)ns * rows * (2.0 * (c.head_dim * 4 + 8)) / kPartialBytesPerUs + kCombineUs;
+    if (cost < best_cost * 0.98) {   // prefer fewer splits unless clearly cheaper
+      best_cost = cost;
+      best = ns;
+    }
+  }
+  return best;
 }
 
 struct MetaLayout {
@@ -127,15 +141,17 @@ MetaLayout meta_layout(const sdv2_config& c) {
 
 int64_t workspace_bytes(const sdv2_config& c) {
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
-  const int tiles = (c.sink_frames + c.window_frames + 1) * (int)(align_up(N, kTileKeys) / kTileKeys);
+  const int tpf = (int)(align_up(N, kTileKeys) / kTileKeys);
   int64_t best = 0;
-  for (int nb = 1; nb <= c.stream_batch; ++nb) {
-    const int ns = choose_nsplit(c, nb, tiles);
-    if (ns < 2) continue;
-    const int64_t rows = (int64_t)ns * nb * c.num_heads * N;
-    const int64_t bytes = align_up(rows * c.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
-    if (bytes > best) best = bytes;
-  }
+  // every (nbatch, frames present) the stream can reach, warm-up included
+  for (int nb = 1; nb <= c.stream_batch; ++nb)
+    for (int frames = 1; frames <= c.sink_frames + c.window_frames + 1; ++frames) {
+      const int ns = choose_nsplit(c, nb, frames * tpf);
+      if (ns < 2) continue;
+      const int64_t rows = (int64_t)ns * nb * c.num_heads * N;
+      const int64_t bytes = align_up(rows * c.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
+      if (bytes > best) best = bytes;
+    }
   return best;
 }
 
