@@ -11,7 +11,7 @@ constexpr int kMaxBatch = 8;     // B
 constexpr int kMaxSinks = 16;    // S
 constexpr int kMaxTPairs = 32;   // temporal RoPE pairs
 constexpr int kTileKeys = 64;    // key tile; tokens are padded to a multiple of it
-constexpr int kQTile = 128;      // query rows per attention workgroup (4 waves x 32)
+constexpr int kQTile = 256;      // query rows per attention workgroup (8 waves x 32)
 constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

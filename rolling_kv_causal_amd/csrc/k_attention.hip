@@ -32,24 +32,70 @@
 namespace sdv2 {
 
 constexpr float kLazy = 8.0f;   // lazy-rescale margin of the running max (log2 units)
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 // LDS row of key `key` within a 64-key tile: swap bits 2 and 3 of the key index.
 __device__ __forceinline__ int perm_key(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+// Byte offset of 16-byte chunk c of row R in an LDS tile whose rows are RB bytes (256 or 128).
+// The LDS has 64 four-byte banks (a 256-byte period): 256-byte rows XOR the chunk index with
+// (R & 15); 128-byte rows are paired into 256-byte double rows J = R >> 1 whose 16 chunk
+// positions are XORed with (J & 15).  Either way the 16 lanes that read one chunk column of 16
+// consecutive rows hit 16 different bank groups.
+template <int RB>
+__device__ __forceinline__ int lds_chunk(int R, int c) {
+  if constexpr (RB == 256) return R * 256 + ((c ^ (R & 15)) << 4);
+  else return (R >> 1) * 256 + (((((R & 1) << 3) | c) ^ ((R >> 1) & 15)) << 4);
+}
+// Inverse: LDS chunk position pos -> (row, logical chunk).
+template <int RB>
+__device__ __forceinline__ void lds_chunk_inv(int pos, int& R, int& c) {
+  if constexpr (RB == 256) {
+    R = pos >> 4;
+    c = (pos & 15) ^ (R & 15);
+  } else {
+    const int J = pos >> 4, p = (pos & 15) ^ (J & 15);
+    R = 2 * J + (p >> 3);
+    c = p & 7;
+  }
+}
+
+// Tile walk of one split: frame f, tile k within the frame, element offset of the frame's
+// (slot, head) block.  Frames are [shared frames..., own staging frame].
+struct TileCursor {
+  int f, k;
+  int64_t base;
+};
+
+// Ping-pong schedule.  A workgroup is 8 waves = 2 groups of 4 (wave w runs on SIMD w % 4, so
+// every SIMD holds one wave of each group); every wave owns 32 query rows, so the 256 rows of
+// the workgroup share each K/V tile staged in LDS.  Per tile k a wave runs an MFMA phase
+// M(k) = {O^T += V^T(k-1) P^T(k-1); S^T(k) = K(k) Q^T} and a VALU phase V(k) = {row max,
+// exponentials, row sums of S(k) -> P(k)}.  Group B runs half a tile behind group A and
+// workgroup barriers separate the phases, so while one wave of a SIMD issues MFMAs the other
+// issues the softmax: phase 2m is {A: M(m), B: V(m-1)}, phase 2m+1 is {A: V(m), B: M(m)}.
+// LDS rings of two K and two V^T tiles: K(m+1) and V(m) stream in during phases 2m and 2m+1
+// (direct global->LDS loads issued by all waves at the start of phase 2m, awaited before the
+// barrier that ends phase 2m+1), into slots whose previous tiles were last read in phase 2m-1.
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
-  constexpr int KSTR = D + 8;            // LDS row stride of the K tile (elements)
-  constexpr int VSTR = kTileKeys + 8;    // LDS row stride of the V^T tile
-  constexpr int K_ELEMS = kTileKeys * KSTR;
-  constexpr int V_ELEMS = D * VSTR;
-  constexpr int BUF = K_ELEMS + V_ELEMS;
-  constexpr int NLD = D / 32;            // 16-byte chunks per thread per tile (K and V each)
-  static_assert(NLD == 2 || NLD == 4, "head_dim 64 or 128");
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  constexpr int KD = D / 16;                  // 16-wide k steps over d (QK)
+  constexpr int DB = D / 32;                  // 32-row d blocks of O^T (PV)
+  constexpr int KRB = D * 2;                  // bytes per K row
+  constexpr int K_BYTES = kTileKeys * KRB;
+  constexpr int V_BYTES = D * kTileKeys * 2;  // V^T tile: D rows of 128 bytes
+  constexpr int NW = 8;                       // waves per workgroup
+  constexpr int KLD = K_BYTES / 1024 / NW;    // 1 KB wave loads per wave per K tile
+  constexpr int VLD = V_BYTES / 1024 / NW;
+  static_assert(KLD >= 1 && VLD >= 1 && (D == 64 || D == 128), "head_dim 64 or 128");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * K_BYTES + 2 * V_BYTES];
+  char* const ldsK = lds;
+  char* const ldsV = lds + 2 * K_BYTES;
+  typedef __attribute__((address_space(3))) void lds_void;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int qtile = w % a.qtiles;
@@ -59,18 +105,20 @@ void attn_bf16_kernel(const AttnArgs a) {
   const int split = rest % a.nsplit;
   const int head = rest / a.nsplit;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                  // 0 = group A, 1 = group B
   const int g = lane >> 5, r = lane & 31;
   const int qrow = qtile * kQTile + wave * 32 + r;
   const bool qvalid = qrow < a.N;
 
   // Q^T operand: lane (g, r) holds Q[row r][kd*16 + 8g .. +7] for every 16-wide k step.
-  bf16x8 qf[D / 16];
+  bf16x8 qf[KD];
   {
     const uint16_t* qp = (const uint16_t*)a.q +
                          ((int64_t)(elem * a.N + (qvalid ? qrow : 0)) * a.H + head) * D + g * 8;
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
+    for (int kd = 0; kd < KD; ++kd) {
       const uint4 v = qvalid ? *(const uint4*)(qp + kd * 16) : make_uint4(0, 0, 0, 0);
       qf[kd] = __builtin_bit_cast(bf16x8, v);
     }
@@ -78,81 +126,138 @@ void attn_bf16_kernel(const AttnArgs a) {
 
   const int t_begin = (int)((int64_t)split * a.total_tiles / a.nsplit);
   const int t_end = (int)((int64_t)(split + 1) * a.total_tiles / a.nsplit);
-  const uint16_t* kvb = (const uint16_t*)a.kv;
+  const int ntiles = t_end - t_begin;         // >= 1 (nsplit <= total_tiles)
+  const int last = ntiles - 1;
+  const char* kvb = (const char*)a.kv;
+  const int64_t head_off = (int64_t)head * a.head_stride;
+  auto frame_base = [&](int f) -> int64_t {
+    const int slot = f < a.nshared ? a.slots[f] : a.own_slot0 + elem;
+    return (int64_t)slot * a.slot_stride + head_off;
+  };
+  auto cursor_at = [&](int tile) -> TileCursor {
+    TileCursor c;
+    c.f = tile / a.tiles_per_frame;
+    c.k = tile - c.f * a.tiles_per_frame;
+    c.base = frame_base(c.f);
+    return c;
+  };
+  auto advance = [&](TileCursor& c) {
+    if (++c.k == a.tiles_per_frame) {
+      c.k = 0;
+      ++c.f;
+      c.base = frame_base(c.f);
+    }
+  };
 
-  // Prefetch registers for one K tile and one V^T tile (16-byte chunks c = i*256 + tid).
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
-#define SDV2_LOAD_TILE(tile_)                                                                  \
-  do {                                                                                         \
-    const int f_ = (tile_) / a.tiles_per_frame;                                                \
-    const int n0_ = ((tile_) - f_ * a.tiles_per_frame) * kTileKeys;                            \
-    const int slot_ = f_ < a.nshared ? a.slots[f_] : a.own_slot0 + elem;                       \
-    const int64_t sh_ = (int64_t)slot_ * a.slot_stride + (int64_t)head * a.head_stride;        \
-    const uint16_t* kp_ = kvb + a.k_layer_off + sh_ + (int64_t)n0_ * D;                        \
-    const uint16_t* vp_ = kvb + a.v_layer_off + sh_ + n0_;                                     \
-    rk0 = *(const u32x4*)(kp_ + ((0 * 256 + tid) / KCH) * D + ((0 * 256 + tid) % KCH) * 8);    \
-    rk1 = *(const u32x4*)(kp_ + ((1 * 256 + tid) / KCH) * D + ((1 * 256 + tid) % KCH) * 8);    \
-    rv0 = *(const u32x4*)(vp_ + (int64_t)((0 * 256 + tid) / 8) * a.Npad + (tid % 8) * 8);      \
-    rv1 = *(const u32x4*)(vp_ + (int64_t)((1 * 256 + tid) / 8) * a.Npad + (tid % 8) * 8);      \
-    if constexpr (NLD == 4) {                                                                  \
-      rk2 = *(const u32x4*)(kp_ + ((2 * 256 + tid) / KCH) * D + ((2 * 256 + tid) % KCH) * 8);  \
-      rk3 = *(const u32x4*)(kp_ + ((3 * 256 + tid) / KCH) * D + ((3 * 256 + tid) % KCH) * 8);  \
-      rv2 = *(const u32x4*)(vp_ + (int64_t)((2 * 256 + tid) / 8) * a.Npad + (tid % 8) * 8);    \
-      rv3 = *(const u32x4*)(vp_ + (int64_t)((3 * 256 + tid) / 8) * a.Npad + (tid % 8) * 8);    \
-    }                                                                                          \
-  } while (0)
-#define SDV2_STORE_TILE(buf_)                                                                  \
-  do {                                                                                         \
-    uint16_t* kt_ = lds + (buf_) * BUF;                                                        \
-    uint16_t* vt_ = kt_ + K_ELEMS;                                                             \
-    *(u32x4*)(kt_ + perm_key((0 * 256 + tid) / KCH) * KSTR + ((0 * 256 + tid) % KCH) * 8) = rk0; \
-    *(u32x4*)(kt_ + perm_key((1 * 256 + tid) / KCH) * KSTR + ((1 * 256 + tid) % KCH) * 8) = rk1; \
-    *(u32x4*)(vt_ + ((0 * 256 + tid) / 8) * VSTR + (tid % 8) * 8) = rv0;                       \
-    *(u32x4*)(vt_ + ((1 * 256 + tid) / 8) * VSTR + (tid % 8) * 8) = rv1;                       \
-    if constexpr (NLD == 4) {                                                                  \
-      *(u32x4*)(kt_ + perm_key((2 * 256 + tid) / KCH) * KSTR + ((2 * 256 + tid) % KCH) * 8) = rk2; \
-      *(u32x4*)(kt_ + perm_key((3 * 256 + tid) / KCH) * KSTR + ((3 * 256 + tid) % KCH) * 8) = rk3; \
-      *(u32x4*)(vt_ + ((2 * 256 + tid) / 8) * VSTR + (tid % 8) * 8) = rv2;                     \
-      *(u32x4*)(vt_ + ((3 * 256 + tid) / 8) * VSTR + (tid % 8) * 8) = rv3;                     \
-    }                                                                                          \
-  } while (0)
+  // Per-lane byte offsets of the tile fills (loop invariant)
+  uint32_t koff[KLD], voff[VLD];
+#pragma unroll
+  for (int i = 0; i < KLD; ++i) {
+    int R, c;
+    lds_chunk_inv<KRB>((wave * KLD + i) * 64 + lane, R, c);
+    koff[i] = (uint32_t)(perm_key(R) * KRB + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    int R, c;
+    lds_chunk_inv<128>((wave * VLD + i) * 64 + lane, R, c);
+    voff[i] = (uint32_t)(R * a.Npad * 2 + c * 16);
+  }
+  auto fill_k = [&](const TileCursor& c, int buf) {
+    const char* src = kvb + (a.k_layer_off + c.base + (int64_t)c.k * kTileKeys * D) * 2;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
+                                       (lds_void*)(ldsK + buf * K_BYTES + (wave * KLD + i) * 1024), 16, 0, 0);
+  };
+  auto fill_v = [&](const TileCursor& c, int buf) {
+    const char* src = kvb + (a.v_layer_off + c.base + (int64_t)c.k * kTileKeys) * 2;
+#pragma unroll
+    for (int i = 0; i < VLD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
+                                       (lds_void*)(ldsV + buf * V_BYTES + (wave * VLD + i) * 1024), 16, 0, 0);
+  };
+  // Per-lane LDS read offsets (loop invariant)
+  int kro[KD], vro[4];
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd) kro[kd] = lds_chunk<KRB>(r, 2 * kd + g);   // + 32 rows for kb = 1
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) vro[ch] = lds_chunk<128>(r, 2 * ch + g);   // + 4096 B per d block
 
   const float sl = a.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[D / 32];
+  f32x16 o[DB];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
+  for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  f32x16 s0, s1;                              // S^T of the current tile: keys [0,32), [32,64)
+  bf16x8 pb00, pb01, pb10, pb11;              // P^T operands of the previous tile
 
-  SDV2_LOAD_TILE(t_begin);
-  SDV2_STORE_TILE(0);
-  __syncthreads();
+  // MFMA phase of tile k.  PV: group i = d block i (4 fragments, 4 MFMAs); QK: group j = k
+  // steps 2j, 2j+1 (4 fragments, 4 MFMAs).  Fragment reads run one group ahead of the MFMAs;
+  // sched_barrier fences keep the compiler from hoisting more reads (registers).
+  bf16x8 fa0, fa1, fa2, fa3, fb0, fb1, fb2, fb3;
+#define SDV2_PV_READ(i_, f0, f1, f2, f3)                                                       \
+  do {                                                                                         \
+    const char* vr_ = vt + (i_) * 4096;                                                        \
+    f0 = *(const bf16x8*)(vr_ + vro[0]); f1 = *(const bf16x8*)(vr_ + vro[1]);                  \
+    f2 = *(const bf16x8*)(vr_ + vro[2]); f3 = *(const bf16x8*)(vr_ + vro[3]);                  \
+  } while (0)
+#define SDV2_PV_MFMA(i_, f0, f1, f2, f3)                                                       \
+  do {                                                                                         \
+    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, pb00, o[i_], 0, 0, 0);                 \
+    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, pb01, o[i_], 0, 0, 0);                 \
+    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, pb10, o[i_], 0, 0, 0);                 \
+    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, pb11, o[i_], 0, 0, 0);                 \
+  } while (0)
+#define SDV2_QK_READ(j_, f0, f1, f2, f3)                                                       \
+  do {                                                                                         \
+    f0 = *(const bf16x8*)(kt + kro[2 * (j_)]);                                                 \
+    f1 = *(const bf16x8*)(kt + 32 * KRB + kro[2 * (j_)]);                                      \
+    f2 = *(const bf16x8*)(kt + kro[2 * (j_) + 1]);                                             \
+    f3 = *(const bf16x8*)(kt + 32 * KRB + kro[2 * (j_) + 1]);                                  \
+  } while (0)
+#define SDV2_QK_MFMA(j_, f0, f1, f2, f3)                                                       \
+  do {                                                                                         \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[2 * (j_)], s0, 0, 0, 0);               \
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[2 * (j_)], s1, 0, 0, 0);               \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, qf[2 * (j_) + 1], s0, 0, 0, 0);           \
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, qf[2 * (j_) + 1], s1, 0, 0, 0);           \
+  } while (0)
+#define SDV2_MFMA_PHASE(k_)                                                                    \
+  do {                                                                                         \
+    if ((k_) >= 1) {                                                                           \
+      const char* vt = ldsV + (((k_) - 1) & 1) * V_BYTES;                                      \
+      SDV2_PV_READ(0, fa0, fa1, fa2, fa3);                                                     \
+      _Pragma("unroll") for (int i_ = 0; i_ < DB; i_ += 2) {                                   \
+        SDV2_PV_READ(i_ + 1, fb0, fb1, fb2, fb3);                                              \
+        SDV2_PV_MFMA(i_, fa0, fa1, fa2, fa3);                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (i_ + 2 < DB) SDV2_PV_READ(i_ + 2, fa0, fa1, fa2, fa3);                             \
+        SDV2_PV_MFMA(i_ + 1, fb0, fb1, fb2, fb3);                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+    }                                                                                          \
+    if ((k_) <= last) {                                                                        \
+      const char* kt = ldsK + ((k_) & 1) * K_BYTES;                                            \
+      _Pragma("unroll") for (int v_ = 0; v_ < 16; ++v_) { s0[v_] = 0.f; s1[v_] = 0.f; }        \
+      SDV2_QK_READ(0, fa0, fa1, fa2, fa3);                                                     \
+      _Pragma("unroll") for (int j_ = 0; j_ < KD / 2; j_ += 2) {                               \
+        SDV2_QK_READ(j_ + 1, fb0, fb1, fb2, fb3);                                              \
+        SDV2_QK_MFMA(j_, fa0, fa1, fa2, fa3);                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (j_ + 2 < KD / 2) SDV2_QK_READ(j_ + 2, fa0, fa1, fa2, fa3);                         \
+        SDV2_QK_MFMA(j_ + 1, fb0, fb1, fb2, fb3);                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
 
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const int buf = (tile - t_begin) & 1;
-    const bool more = tile + 1 < t_end;
-    if (more) SDV2_LOAD_TILE(tile + 1);
-    const uint16_t* kt = lds + buf * BUF;
-    const uint16_t* vt = kt + K_ELEMS;
-
-    // S^T for keys [0,32) and [32,64) of the tile (rows permuted, see perm_key)
-    f32x16 s0, s1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-#pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd) {
-      const bf16x8 a0 = *(const bf16x8*)(kt + r * KSTR + kd * 16 + g * 8);
-      const bf16x8 a1 = *(const bf16x8*)(kt + (32 + r) * KSTR + kd * 16 + g * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kd], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kd], s1, 0, 0, 0);
-    }
-    // lane (g, r), accumulator v holds key 16*(v/8) + 8g + v%8 (+32 for s1) of query r
-
-    const int f = tile / a.tiles_per_frame;
-    const int nvalid = a.N - (tile - f * a.tiles_per_frame) * kTileKeys;
-    if (nvalid < kTileKeys) {                       // ragged last tile of a frame
+  // VALU phase of the current tile: masked row max, lazy rescale, exponentials -> P^T, row
+  // sums.  lane (g, r), accumulator v holds key 16*(v/8) + 8g + v%8 (+32 for s1) of query r.
+  auto valu_phase = [&](int nvalid) {
+    if (nvalid < kTileKeys) {                 // ragged last tile of a frame
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = 16 * (v >> 3) + 8 * g + (v & 7);
@@ -160,59 +265,89 @@ void attn_bf16_kernel(const AttnArgs a) {
         if (key + 32 >= nvalid) s1[v] = -INFINITY;
       }
     }
-
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescale: the running max m_run only moves when the tile max exceeds it by more than
-    // kLazy (log2 units), so exponentials stay <= 2^kLazy and O/l is unchanged (both use m_run).
-    // Once the max has settled no tile rescales O.
+    // Lazy rescale: the running max only moves when a tile max exceeds it by more than kLazy
+    // (log2 units), so exponentials stay <= 2^kLazy and O/l is unchanged (both use m_run).
     const float m_tile = mx * sl;
     const bool grow = m_tile > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(grow)) {          // wave-uniform branch
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch, rare once the max settles
       const float m_new = grow ? m_tile : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
     }
-    const float m_new = m_run;
-
     uint32_t pw0[8], pw1[8];
     float ps = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[v], sl, -m_new));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -m_new));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[v], sl, -m_new));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -m_new));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[v], sl, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -m_run));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[v], sl, -m_run));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -m_run));
       ps += (p0 + p1) + (p2 + p3);
       pw0[v / 2] = pack_bf16x2(p0, p1);
       pw1[v / 2] = pack_bf16x2(p2, p3);
     }
     l_run += ps;
+    pb00 = __builtin_bit_cast(bf16x8, make_uint4(pw0[0], pw0[1], pw0[2], pw0[3]));
+    pb01 = __builtin_bit_cast(bf16x8, make_uint4(pw0[4], pw0[5], pw0[6], pw0[7]));
+    pb10 = __builtin_bit_cast(bf16x8, make_uint4(pw1[0], pw1[1], pw1[2], pw1[3]));
+    pb11 = __builtin_bit_cast(bf16x8, make_uint4(pw1[4], pw1[5], pw1[6], pw1[7]));
+  };
 
-    // P^T operands: 16-key step kk of key block kb covers accumulator entries 8kk..8kk+7
-    const bf16x8 pb00 = __builtin_bit_cast(bf16x8, make_uint4(pw0[0], pw0[1], pw0[2], pw0[3]));
-    const bf16x8 pb01 = __builtin_bit_cast(bf16x8, make_uint4(pw0[4], pw0[5], pw0[6], pw0[7]));
-    const bf16x8 pb10 = __builtin_bit_cast(bf16x8, make_uint4(pw1[0], pw1[1], pw1[2], pw1[3]));
-    const bf16x8 pb11 = __builtin_bit_cast(bf16x8, make_uint4(pw1[4], pw1[5], pw1[6], pw1[7]));
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const uint16_t* vr = vt + (i * 32 + r) * VSTR + g * 8;
-      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + 0), pb00, o[i], 0, 0, 0);
-      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + 16), pb01, o[i], 0, 0, 0);
-      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + 32), pb10, o[i], 0, 0, 0);
-      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vr + 48), pb11, o[i], 0, 0, 0);
+  // Loads of "phase pair" m: K(m+1) and V(m) into their ring slots (every wave its share).
+  TileCursor kc = cursor_at(t_begin);         // K tile of the next loads
+  TileCursor vc = kc;                         // V tile of the next loads
+  TileCursor sc = kc;                         // tile of this wave's next VALU phase
+  auto loads = [&](int m) {
+    if (m + 1 <= last) {
+      advance(kc);
+      fill_k(kc, (m + 1) & 1);
     }
+    if (m <= last) {
+      fill_v(vc, m & 1);
+      if (m + 1 <= last) advance(vc);
+    }
+  };
 
-    if (more) SDV2_STORE_TILE(buf ^ 1);
+  // prologue: K(0) resident before phase 0; group B idles through phase 0 (it issues its
+  // share of the phase-0 loads there)
+  fill_k(kc, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (grp == 1) {
+    loads(0);
     __syncthreads();
   }
+  // Each wave runs M(0), V(0), M(1), ..., V(n-1), M(n).  Loads of pair m are issued at the
+  // start of even phase 2m (A: M(m); B: V(m-1)) and awaited at the end of odd phase 2m+1
+  // (A: V(m); B: M(m)), so every wave passes the same barriers with its loads complete.
+  for (int k = 0; k <= ntiles; ++k) {
+    if (grp == 0) loads(k);
+    SDV2_MFMA_PHASE(k);
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (k == ntiles && grp == 1) break;       // B's last phase was M(n)
+    if (grp == 1) loads(k + 1);
+    if (k <= last) {
+      valu_phase(a.N - sc.k * kTileKeys);
+      if (k < last) advance(sc);
+    }
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+#undef SDV2_PV_READ
+#undef SDV2_PV_MFMA
+#undef SDV2_QK_READ
+#undef SDV2_QK_MFMA
+#undef SDV2_MFMA_PHASE
 
   // lane (g, r), accumulator v of o[i] holds O^T[d = 32i + 8(v/4) + 4g + v%4][query r]
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -221,7 +356,7 @@ void attn_bf16_kernel(const AttnArgs a) {
   if (a.nsplit == 1) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * a.N + qrow) * a.H + head) * D + 4 * g;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         uint2 w2;
@@ -233,7 +368,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * a.N + qrow;
     float* po = a.part_o + prow * D + 4 * g;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
         *(float4*)(po + 32 * i + 8 * a4) =
@@ -241,8 +376,6 @@ void attn_bf16_kernel(const AttnArgs a) {
                         o[i][4 * a4 + 3] * inv);
     if (g == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
   }
-#undef SDV2_LOAD_TILE
-#undef SDV2_STORE_TILE
 }
 
 // Merge split-KV partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - max m).
@@ -350,9 +483,9 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool bf16, hipStrea
   if (bf16) {
     const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
     if (head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
   } else {
     const int grid = a.nbatch * a.H * ((a.N + 63) / 64);
     if (head_dim == 128)

@@ -92,12 +92,13 @@ sdv2_layout make_layout(const sdv2_config& c) {
 }
 
 // Split-KV count for nbatch elements.  The grid runs in rounds of kSlots workgroups (256 CUs of
-// MI355X x 2 resident workgroups); a split count costs rounds x tiles-per-split tile steps plus
-// the fp32 partial results it writes and the combine reads back.  The constants are measured
-// on MI355X: about 2 us per 64-key tile step of a workgroup, ~5 TB/s for the partial traffic.
-constexpr int kSlots = 2 * 256;
+// MI355X, one 8-wave workgroup each); a split count costs rounds x tiles-per-split tile steps
+// plus the fp32 partial results it writes and the combine reads back.  The constants are
+// measured on MI355X: about 1.2 us per 64-key tile step of a 256-row workgroup and ~5 TB/s for
+// the partial traffic.
+constexpr int kSlots = 256;
 constexpr int kMaxSplit = 16;
-constexpr double kTileUs = 2.0, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
+constexpr double kTileUs = 1.2, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles) {
   if (c.dtype != SDV2_BF16) return 1;
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
