@@ -87,8 +87,9 @@ typedef struct sdv2_config {
 } sdv2_config;
 
 /* Device layout of the KV cache (element offsets from d_kv, element = 2 or 4 bytes).
- * Slots [0,S) are sinks, [S,S+W) the ring (frame f >= S lives in slot S + f mod W),
- * [S+W, S+W+B) the staging slots of stream-batch elements 0..B-1.
+ * Slots [0,S) are sinks, [S,S+W+1) the ring (frame f >= S lives in slot S + f mod (W+1);
+ * W of these slots hold the window, the spare one receives the frame being finished), and
+ * [S+W+1, S+W+B) the staging slots of stream-batch elements 1..B-1 (element b in S+W+b).
  *   K of (layer, slot, head, token n, dim i): k_offset(layer) + slot*slot_stride
  *        + head*head_stride + n*head_dim + i                      (rows of head_dim)
  *   V of (layer, slot, head, token n, dim i): v_offset(layer) + slot*slot_stride
@@ -96,7 +97,7 @@ typedef struct sdv2_config {
  * with k_offset(l) = l*layer_stride, v_offset(l) = l*layer_stride + slot_stride*slots.
  * Tokens n in [N, tokens_padded) are zero padding. */
 typedef struct sdv2_layout {
-  int64_t slots;          /* S + W + B */
+  int64_t slots;          /* S + (W + 1) + (B - 1) */
   int64_t tokens_padded;  /* N rounded up to 64 */
   int64_t elem_bytes;     /* 4 (fp32) or 2 (bf16) */
   int64_t head_stride;    /* tokens_padded * head_dim */
@@ -141,7 +142,9 @@ int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied,
  * Elements b = 0..nbatch-1 hold chunks first_chunk+b (b = 0 oldest); first_chunk must equal
  * the number of chunks committed so far and first_chunk + nbatch - 1 the newest frame given
  * to sdv2_rope_refresh.  d_q is rotated in place at temporal position frame - b0 (row h, col
- * w); k is rotated likewise and written with v into the staging slot of element b.  Buffers:
+ * w); k is rotated likewise and written with v: element 0 into the slot its frame keeps once
+ * committed (sink slot f, or ring slot S + f mod (W+1), which holds no attended frame), the
+ * others into their staging slots.  Buffers:
  * [nbatch][T'N][H][d] each; d_q read-write, d_k and d_v read-only.  Once per layer per step. */
 int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int32_t nbatch,
                       void* d_q, const void* d_k, const void* d_v, void* stream);
@@ -154,9 +157,10 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
 int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream);
 
-/* Commit the finished chunk (element 0, which must be `chunk`) for all layers: its staged K
- * and V are copied into sink slot f if f < S, else into ring slot S + f mod W (evicting the
- * frame W older).  Requires every layer appended this step. */
+/* Commit the finished chunk (element 0, which must be `chunk`) for all layers: from the next
+ * step on, its K and V (already in sink slot f if f < S, else in ring slot S + f mod (W+1)) are
+ * attended and the frame W older leaves the window.  Requires every layer appended this step.
+ * Host bookkeeping only: no device work is queued on `stream`. */
 int sdv2_cache_commit(sdv2_cache* cache, int64_t chunk, void* stream);
 
 /* Adaptive sink refresh after the commit of `frame` ([WT] adaptive sink and RoPE refresh).
@@ -187,7 +191,9 @@ int sdv2_noise_schedule(const double* h_dist, int32_t n, double sigma, int32_t k
 
 /* Host bookkeeping of one slot: committed frame (-1 empty, -2 unknown after an unsynchronised
  * sink decision) and its temporal RoPE position label = frame - b0 at commit, shifted by every
- * later rebase.  Staging slots report the frame staged this step.  Never synchronises. */
+ * later rebase.  A slot written by an append and not (yet) committed reports the chunk staged
+ * there (staging slots, and element 0's sink or ring slot before its commit).  Never
+ * synchronises. */
 int sdv2_cache_slot_info(const sdv2_cache* cache, int32_t slot, int64_t* frame, int32_t* tpos);
 
 /* RoPE base b0, chunks committed so far and rebases applied so far.  Any pointer may be NULL. */

@@ -49,7 +49,7 @@ struct AppendArgs {
   const float2* tab_h;     // [grid_h][ph] (cos, sin)
   const float2* tab_w;     // [grid_w][pw]
   int N, Npad, H, grid_w, nbatch;
-  int staging_slot0;       // S + W
+  int dst_slot[kMaxBatch]; // slot each element's K and V are written to
   int pt, ph, pw;          // RoPE pairs per axis
   float2 tcs[kMaxBatch][kMaxTPairs];   // temporal (cos, sin) per element and pair
 };
@@ -63,7 +63,7 @@ struct AttnArgs {
   float2* part_ml;         // [nsplit][nbatch][H][N] (m in log2 units, l)
   int N, Npad, H, nbatch;
   int nshared;             // cached frames attended (sinks + window)
-  int own_slot0;           // staging slot of element 0
+  int own_slot[kMaxBatch]; // slot holding each element's own chunk
   int tiles_per_frame;     // Npad / kTileKeys
   int total_tiles;         // (nshared + 1) * tiles_per_frame
   int nsplit, qtiles;

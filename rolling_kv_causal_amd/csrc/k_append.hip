@@ -53,41 +53,53 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   __syncthreads();
 
   const int c = tid % CH;
-  const int64_t kdst = a.k_layer_off + (int64_t)(a.staging_slot0 + b) * a.slot_stride +
+  const int64_t kdst = a.k_layer_off + (int64_t)a.dst_slot[b] * a.slot_stride +
                        (int64_t)head * a.head_stride;
+  constexpr int PASSES = TILE / ROWS;
+  // Every global load of the tile is issued before the first store: q is rotated in place,
+  // so loads placed after a store could not be hoisted by the compiler and each pass would
+  // cost a full memory round trip.
+  uint4 qv[PASSES], kv[PASSES], vv[PASSES];
+  float2 cs[PASSES][VEC / 2];
 #pragma unroll
-  for (int pass = 0; pass < TILE / ROWS; ++pass) {
-    const int row = pass * ROWS + tid / CH;
-    const int n = n0 + row;
-    uint32_t* vrow = reinterpret_cast<uint32_t*>(vs + row * VSTR + c * VEC);
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int n = n0 + pass * ROWS + tid / CH;
     if (n < a.N) {
+      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
+      qv[pass] = *(const uint4*)((const T*)a.q + off);
+      kv[pass] = *(const uint4*)((const T*)a.k + off);
+      vv[pass] = *(const uint4*)((const T*)a.v + off);
       const int hr = n / a.grid_w, wc = n - hr * a.grid_w;
-      float2 cs[VEC / 2];
 #pragma unroll
       for (int j = 0; j < VEC / 2; ++j) {
         const int p = c * (VEC / 2) + j;
-        cs[j] = p < a.pt ? tcs[p]
-                : p < a.pt + a.ph ? a.tab_h[hr * a.ph + (p - a.pt)]
-                                  : a.tab_w[wc * a.pw + (p - a.pt - a.ph)];
+        cs[pass][j] = p < a.pt ? tcs[p]
+                      : p < a.pt + a.ph ? a.tab_h[hr * a.ph + (p - a.pt)]
+                                        : a.tab_w[wc * a.pw + (p - a.pt - a.ph)];
       }
-      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
-      uint4 qv = *(const uint4*)((const T*)a.q + off);
-      uint4 kv = *(const uint4*)((const T*)a.k + off);
-      const uint4 vv = *(const uint4*)((const T*)a.v + off);
-      rotate16<BF16>(qv, cs);
-      rotate16<BF16>(kv, cs);
-      *(uint4*)((T*)a.q + off) = qv;
-      *(uint4*)((T*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv;
-      vrow[0] = vv.x; vrow[1] = vv.y; vrow[2] = vv.z; vrow[3] = vv.w;
     } else {                                   // padding tokens of V^T stay zero
-      vrow[0] = 0u; vrow[1] = 0u; vrow[2] = 0u; vrow[3] = 0u;
+      vv[pass] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int row = pass * ROWS + tid / CH;
+    const int n = n0 + row;
+    uint32_t* vrow = reinterpret_cast<uint32_t*>(vs + row * VSTR + c * VEC);
+    vrow[0] = vv[pass].x; vrow[1] = vv[pass].y; vrow[2] = vv[pass].z; vrow[3] = vv[pass].w;
+    if (n < a.N) {
+      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
+      rotate16<BF16>(qv[pass], cs[pass]);
+      rotate16<BF16>(kv[pass], cs[pass]);
+      *(uint4*)((T*)a.q + off) = qv[pass];
+      *(uint4*)((T*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv[pass];
     }
   }
   __syncthreads();
 
   // V^T rows: d-major, the tile's 64 tokens contiguous
   constexpr int TCH = TILE / VEC;            // 16-byte chunks per V^T row of the tile
-  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)(a.staging_slot0 + b) * a.slot_stride +
+  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)a.dst_slot[b] * a.slot_stride +
             (int64_t)head * a.head_stride + n0;
   for (int idx = tid; idx < D * TCH; idx += 256) {
     const int drow = idx / TCH, kc = idx % TCH;

@@ -131,7 +131,7 @@ void attn_bf16_kernel(const AttnArgs a) {
   const char* kvb = (const char*)a.kv;
   const int64_t head_off = (int64_t)head * a.head_stride;
   auto frame_base = [&](int f) -> int64_t {
-    const int slot = f < a.nshared ? a.slots[f] : a.own_slot0 + elem;
+    const int slot = f < a.nshared ? a.slots[f] : a.own_slot[elem];
     return (int64_t)slot * a.slot_stride + head_off;
   };
   auto cursor_at = [&](int tile) -> TileCursor {
@@ -331,7 +331,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   // (A: V(m); B: M(m)), so every wave passes the same barriers with its loads complete.
   for (int k = 0; k <= ntiles; ++k) {
     if (grp == 0) loads(k);
+    __builtin_amdgcn_s_setprio(2);            // MFMA phase first in issue arbitration
     SDV2_MFMA_PHASE(k);
+    __builtin_amdgcn_s_setprio(0);
     if (grp == 1) __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (k == ntiles && grp == 1) break;       // B's last phase was M(n)
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float* kvb = (const float*)a.kv;
   for (int f = 0; f <= a.nshared; ++f) {
-    const int slot = f < a.nshared ? a.slots[f] : a.own_slot0 + elem;
+    const int slot = f < a.nshared ? a.slots[f] : a.own_slot[elem];
     const int64_t sh = (int64_t)slot * a.slot_stride + (int64_t)head * a.head_stride;
     const float* kp = kvb + a.k_layer_off + sh;
     const float* vp = kvb + a.v_layer_off + sh;

@@ -197,11 +197,22 @@ int check_cache(const sdv2_cache* c) {
   return SDV2_OK;
 }
 
+// Slot of frame f once committed: sink slot f for f < S, else one of W + 1 ring slots.  The
+// ring holds one slot more than the window: the slot of the frame being finished holds a frame
+// that already left the window, so the append writes element 0 to its final slot and the commit
+// moves no data.
+int home_slot(const sdv2_config& c, int64_t f) {
+  return f < c.sink_frames ? (int)f : c.sink_frames + (int)(f % (c.window_frames + 1));
+}
+
+// Sinks and ring slots; the staging slots of elements 1..B-1 follow.
+int shared_region(const sdv2_config& c) { return c.sink_frames + c.window_frames + 1; }
+
 // Present shared slots in attention order: sinks by slot index, then the ring by slot index.
 int shared_slots(const sdv2_cache* c, int* out) {
   int n = 0;
-  const int SW = c->cfg.sink_frames + c->cfg.window_frames;
-  for (int s = 0; s < SW; ++s)
+  const int R = shared_region(c->cfg);
+  for (int s = 0; s < R; ++s)
     if (c->slot_written[s]) out[n++] = s;
   return n;
 }
@@ -329,7 +340,7 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
     }
     c->base += count * T;
     c->refreshes += count;
-    for (int s = 0; s < cfg.sink_frames + cfg.window_frames; ++s)
+    for (int s = 0; s < shared_region(cfg); ++s)
       if (c->slot_written[s]) c->slot_label[s] -= count * T;
   }
   c->started = true;
@@ -339,7 +350,7 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
   c->step_nbatch = 0;
   std::fill(c->appended.begin(), c->appended.end(), 0);
   // staging slots hold nothing committed-visible until the appends of this step
-  for (int64_t s = cfg.sink_frames + cfg.window_frames; s < c->lay.slots; ++s) c->slot_frame[s] = -1;
+  for (int64_t s = shared_region(cfg); s < c->lay.slots; ++s) c->slot_frame[s] = -1;
   if (applied) *applied = (int32_t)count;
   return ok();
 }
@@ -381,7 +392,12 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   a.H = cfg.num_heads;
   a.grid_w = cfg.grid_w;
   a.nbatch = nbatch;
-  a.staging_slot0 = cfg.sink_frames + cfg.window_frames;
+  // element 0 goes to the slot its frame keeps once committed, the others to staging slots
+  for (int b = 0; b < nbatch; ++b)
+    a.dst_slot[b] = b == 0 ? home_slot(cfg, first_chunk) : cfg.sink_frames + cfg.window_frames + b;
+  if (c->slot_written[a.dst_slot[0]])
+    return fail(SDV2_ESTATE, "internal: slot %d of chunk %lld is still attended", a.dst_slot[0],
+                (long long)first_chunk);
   a.pt = cfg.rope_dim_t / 2;
   a.ph = cfg.rope_dim_h / 2;
   a.pw = cfg.rope_dim_w / 2;
@@ -397,8 +413,8 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   c->step_first = first_chunk;
   c->step_nbatch = nbatch;
   for (int b = 0; b < nbatch; ++b) {
-    c->slot_frame[a.staging_slot0 + b] = first_chunk + b;
-    c->slot_label[a.staging_slot0 + b] = first_chunk + b - c->base;
+    c->slot_frame[a.dst_slot[b]] = first_chunk + b;
+    c->slot_label[a.dst_slot[b]] = first_chunk + b - c->base;
   }
   return ok();
 }
@@ -429,7 +445,8 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
   a.H = cfg.num_heads;
   a.nbatch = nbatch;
   a.nshared = shared_slots(c, a.slots);
-  a.own_slot0 = cfg.sink_frames + cfg.window_frames;
+  for (int b = 0; b < nbatch; ++b)
+    a.own_slot[b] = b == 0 ? home_slot(cfg, c->step_first) : cfg.sink_frames + cfg.window_frames + b;
   a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
   a.total_tiles = (a.nshared + 1) * a.tiles_per_frame;
   a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles);
@@ -458,19 +475,15 @@ int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {
   for (int l = 0; l < cfg.num_layers; ++l)
     if (!c->appended[l]) return fail(SDV2_ESTATE, "layer %d not appended this step", l);
   if (chunk != c->step_first) return fail(SDV2_ESTATE, "only element 0 (chunk %lld) can be committed", (long long)c->step_first);
+  (void)stream;              // the appends already wrote the frame to its slot
   const int64_t f = chunk;   // T' = 1
   const int S = cfg.sink_frames, W = cfg.window_frames;
-  const int dst = f < S ? (int)f : S + (int)(f % W);
-  CopyArgs a{};
-  a.kv = c->kv;
-  a.layer_stride_bytes = c->lay.layer_stride * c->lay.elem_bytes;
-  a.v_block_bytes = c->lay.slots * c->lay.slot_stride * c->lay.elem_bytes;
-  a.slot_bytes = c->lay.slot_stride * c->lay.elem_bytes;
-  a.src_slot = S + W;
-  a.dst_slot = dst;
-  a.dst_from = nullptr;
-  a.L = cfg.num_layers;
-  SDV2_HIP(launch_copy_slots(a, (hipStream_t)stream));
+  const int dst = home_slot(cfg, f);
+  if (f - W >= S) {          // frame f - W leaves the window
+    const int old = home_slot(cfg, f - W);
+    c->slot_written[old] = 0;
+    c->slot_frame[old] = -1;
+  }
   c->slot_frame[dst] = f;
   c->slot_label[dst] = f - c->base;
   c->slot_written[dst] = 1;
@@ -489,7 +502,7 @@ int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_
                                                   (long long)frame, (long long)c->last_commit_frame);
   if (cfg.embed_dim < 1) return fail(SDV2_EINVAL, "the cache has no chunk embeddings (embed_dim 0)");
   if (!d_embed) return fail(SDV2_EINVAL, "d_embed must not be NULL");
-  const int S = cfg.sink_frames, W = cfg.window_frames;
+  const int S = cfg.sink_frames;
   hipStream_t s = (hipStream_t)stream;
   SinkArgs a{};
   a.h = d_embed;
@@ -511,7 +524,7 @@ int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_
     cp.layer_stride_bytes = c->lay.layer_stride * c->lay.elem_bytes;
     cp.v_block_bytes = c->lay.slots * c->lay.slot_stride * c->lay.elem_bytes;
     cp.slot_bytes = c->lay.slot_stride * c->lay.elem_bytes;
-    cp.src_slot = S + (int)(frame % W);
+    cp.src_slot = home_slot(cfg, frame);
     cp.dst_slot = -1;
     cp.dst_from = a.decision;
     cp.L = cfg.num_layers;
@@ -525,7 +538,7 @@ int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_
     SDV2_HIP(hipStreamSynchronize(s));
     if (slot >= 0) {
       c->slot_frame[slot] = frame;
-      c->slot_label[slot] = c->slot_label[S + (int)(frame % W)];
+      c->slot_label[slot] = c->slot_label[home_slot(cfg, frame)];
     }
   } else if (decide) {
     c->sinks_unknown = true;

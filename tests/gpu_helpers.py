@@ -139,7 +139,14 @@ class Harness:
         base, committed, refreshes = cache.state()
         assert base == self.st.base and refreshes == r
         entries = [(j, e) for j, e in enumerate(self.st.sinks) if e is not None]
-        entries += [(ost.ring_slot(cfg, e.frame), e) for e in self.st.window]
+        entries += [(lib_slot(cfg, e.frame), e) for e in self.st.window]
+        # every other sink / ring slot is empty, or holds the staged (not yet committed) chunk
+        # written there by this step's append
+        held = {slot for slot, _ in entries}
+        for slot in range(cfg.sink_frames + cfg.window_frames + 1):
+            if slot not in held:
+                f = cache.slot_info(slot)[0]
+                assert f == -1 or (f == committed and slot == lib_slot(cfg, committed)), (slot, f, committed)
         for layer in (self.layers if layers is None else layers):
             Kg, Vg = cache.k_view(layer), cache.v_view(layer)
             for slot, e in entries:
@@ -156,6 +163,14 @@ class Harness:
             # zero padding of the token axis stays zero
             if cache.layout.tokens_padded > N:
                 assert torch.count_nonzero(Kg[:, :, N:, :]) == 0 and torch.count_nonzero(Vg[:, :, :, N:]) == 0
+
+
+def lib_slot(cfg, frame):
+    """Physical slot of a committed frame in the library's cache layout (sdv2.h): sink slot f for
+    f < S, else ring slot S + f mod (W + 1).  The pages' ring has W slots; the library keeps one
+    spare so the frame being finished can be written in place."""
+    S, W = cfg.sink_frames, cfg.window_frames
+    return frame if frame < S else S + frame % (W + 1)
 
 
 def sample_rows(N, n=40, seed=0):
