@@ -32,6 +32,7 @@
 namespace sdv2 {
 
 constexpr float kLazy = 8.0f;   // lazy-rescale margin of the running max (log2 units)
+constexpr float kLazyMass = 256.0f;   // 2^kLazy: bound on a lane's sum of exponentials
 // s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
@@ -63,11 +64,12 @@ __device__ __forceinline__ void lds_chunk_inv(int pos, int& R, int& c) {
   }
 }
 
-// Tile walk of one split: frame f, tile k within the frame, element offset of the frame's
-// (slot, head) block.  Frames are [shared frames..., own staging frame].
+// Tile walk of one split: frame f, tile k within the frame, and the addresses of the tile's
+// K rows and V^T columns.  Frames are [shared frames..., own chunk].
 struct TileCursor {
   int f, k;
-  int64_t base;
+  const char* kp;
+  const char* vp;
 };
 
 // Ping-pong schedule.  A workgroup is 8 waves = 2 groups of 4 (wave w runs on SIMD w % 4, so
@@ -130,22 +132,34 @@ void attn_bf16_kernel(const AttnArgs a) {
   const int last = ntiles - 1;
   const char* kvb = (const char*)a.kv;
   const int64_t head_off = (int64_t)head * a.head_stride;
-  auto frame_base = [&](int f) -> int64_t {
-    const int slot = f < a.nshared ? a.slots[f] : a.own_slot[elem];
-    return (int64_t)slot * a.slot_stride + head_off;
+  // Slot of frame f in lane f (frames >= 64 can only be the own chunk), read back with
+  // readlane: the tile walk issues no scalar memory load, whose wait would also drain the
+  // LDS queue.
+  const int own = a.own_slot[elem];
+  const int slot_lane = lane < a.nshared ? a.slots[lane] : own;
+  const char* const kblk = kvb + (a.k_layer_off + head_off) * 2;
+  const char* const vblk = kvb + (a.v_layer_off + head_off) * 2;
+  const int64_t slot_bytes = a.slot_stride * 2;
+  auto frame_at = [&](TileCursor& c) {
+    const int slot = c.f < a.nshared ? __builtin_amdgcn_readlane(slot_lane, c.f & 63) : own;
+    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * 2);
+    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * 2);
   };
   auto cursor_at = [&](int tile) -> TileCursor {
     TileCursor c;
     c.f = tile / a.tiles_per_frame;
     c.k = tile - c.f * a.tiles_per_frame;
-    c.base = frame_base(c.f);
+    frame_at(c);
     return c;
   };
   auto advance = [&](TileCursor& c) {
     if (++c.k == a.tiles_per_frame) {
       c.k = 0;
       ++c.f;
-      c.base = frame_base(c.f);
+      frame_at(c);
+    } else {
+      c.kp += kTileKeys * D * 2;
+      c.vp += kTileKeys * 2;
     }
   };
 
@@ -164,14 +178,14 @@ void attn_bf16_kernel(const AttnArgs a) {
     voff[i] = (uint32_t)(R * a.Npad * 2 + c * 16);
   }
   auto fill_k = [&](const TileCursor& c, int buf) {
-    const char* src = kvb + (a.k_layer_off + c.base + (int64_t)c.k * kTileKeys * D) * 2;
+    const char* src = c.kp;
 #pragma unroll
     for (int i = 0; i < KLD; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
                                        (lds_void*)(ldsK + buf * K_BYTES + (wave * KLD + i) * 1024), 16, 0, 0);
   };
   auto fill_v = [&](const TileCursor& c, int buf) {
-    const char* src = kvb + (a.v_layer_off + c.base + (int64_t)c.k * kTileKeys) * 2;
+    const char* src = c.vp;
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
@@ -192,66 +206,54 @@ void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
   f32x16 s0, s1;                              // S^T of the current tile: keys [0,32), [32,64)
-  bf16x8 pb00, pb01, pb10, pb11;              // P^T operands of the previous tile
+  bf16x8 pb00 = {}, pb01 = {}, pb10 = {}, pb11 = {};   // P^T operands of the previous tile
 
-  // MFMA phase of tile k.  PV: group i = d block i (4 fragments, 4 MFMAs); QK: group j = k
-  // steps 2j, 2j+1 (4 fragments, 4 MFMAs).  Fragment reads run one group ahead of the MFMAs;
-  // sched_barrier fences keep the compiler from hoisting more reads (registers).
-  bf16x8 fa0, fa1, fa2, fa3, fb0, fb1, fb2, fb3;
-#define SDV2_PV_READ(i_, f0, f1, f2, f3)                                                       \
+  // MFMA phase of tile k: 16 PV fragments (d block t/4, key step t%4) then 16 QK fragments
+  // (k step u/2, key block u%2), one MFMA each.  Fragment reads run kAhead fragments ahead of
+  // their MFMA, and sched_group_barrier fixes the interleave (one MFMA, one LDS read), so each
+  // MFMA waits only for its own operand instead of the whole LDS queue.
+  constexpr int NPV = DB * 4, NQK = KD * 2, NF = NPV + NQK, kAhead = 8;
+#define SDV2_FRAG(t_)                                                                          \
+  ((t_) < NPV ? *(const bf16x8*)(vt + ((t_) / 4) * 4096 + vro[(t_) % 4])                       \
+              : *(const bf16x8*)(kt + (((t_) - NPV) % 2) * 32 * KRB + kro[((t_) - NPV) / 2]))
+#define SDV2_FRAG_MFMA(t_, f_)                                                                 \
   do {                                                                                         \
-    const char* vr_ = vt + (i_) * 4096;                                                        \
-    f0 = *(const bf16x8*)(vr_ + vro[0]); f1 = *(const bf16x8*)(vr_ + vro[1]);                  \
-    f2 = *(const bf16x8*)(vr_ + vro[2]); f3 = *(const bf16x8*)(vr_ + vro[3]);                  \
+    if ((t_) < NPV) {                                                                          \
+      const bf16x8 pb_ = ((t_) % 4 == 0) ? pb00 : ((t_) % 4 == 1) ? pb01 : ((t_) % 4 == 2) ? pb10 : pb11; \
+      o[(t_) / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f_, pb_, o[(t_) / 4], 0, 0, 0);    \
+    } else if ((((t_) - NPV) % 2) == 0) {                                                      \
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f_, qf[((t_) - NPV) / 2],                   \
+                                                   (t_) - NPV < 2 ? f32x16{} : s0, 0, 0, 0);   \
+    } else {                                                                                   \
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f_, qf[((t_) - NPV) / 2],                   \
+                                                   (t_) - NPV < 2 ? f32x16{} : s1, 0, 0, 0);   \
+    }                                                                                          \
   } while (0)
-#define SDV2_PV_MFMA(i_, f0, f1, f2, f3)                                                       \
+  // fragments t in [T0, T1) of tile k's phase.  Every phase runs all of them, which keeps a
+  // single code path (and the accumulators in place): M(0) adds V^T P^T with P = 0 over a
+  // zeroed V^T slot, and the S^T of M(n) is never used.
+#define SDV2_MFMA_RUN(k_, T0, T1)                                                              \
   do {                                                                                         \
-    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, pb00, o[i_], 0, 0, 0);                 \
-    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, pb01, o[i_], 0, 0, 0);                 \
-    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, pb10, o[i_], 0, 0, 0);                 \
-    o[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, pb11, o[i_], 0, 0, 0);                 \
-  } while (0)
-#define SDV2_QK_READ(j_, f0, f1, f2, f3)                                                       \
-  do {                                                                                         \
-    f0 = *(const bf16x8*)(kt + kro[2 * (j_)]);                                                 \
-    f1 = *(const bf16x8*)(kt + 32 * KRB + kro[2 * (j_)]);                                      \
-    f2 = *(const bf16x8*)(kt + kro[2 * (j_) + 1]);                                             \
-    f3 = *(const bf16x8*)(kt + 32 * KRB + kro[2 * (j_) + 1]);                                  \
-  } while (0)
-#define SDV2_QK_MFMA(j_, f0, f1, f2, f3)                                                       \
-  do {                                                                                         \
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[2 * (j_)], s0, 0, 0, 0);               \
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[2 * (j_)], s1, 0, 0, 0);               \
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, qf[2 * (j_) + 1], s0, 0, 0, 0);           \
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, qf[2 * (j_) + 1], s1, 0, 0, 0);           \
+    const char* vt = ldsV + (((k_) - 1) & 1) * V_BYTES;                                        \
+    const char* kt = ldsK + ((k_) & 1) * K_BYTES;                                              \
+    (void)vt; (void)kt;                                                                        \
+    bf16x8 fr_[NF];                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+    _Pragma("unroll") for (int t_ = T0; t_ < T0 + kAhead && t_ < T1; ++t_) fr_[t_] = SDV2_FRAG(t_); \
+    _Pragma("unroll") for (int t_ = T0; t_ < T1; ++t_) {                                       \
+      SDV2_FRAG_MFMA(t_, fr_[t_]);                                                             \
+      if (t_ + kAhead < T1) fr_[t_ + kAhead] = SDV2_FRAG(t_ + kAhead);                         \
+    }                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x100, (T1 - T0) < kAhead ? (T1 - T0) : kAhead, 0);   \
+    _Pragma("unroll") for (int t_ = T0; t_ < T1; ++t_) {                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+      if (t_ + kAhead < T1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
   } while (0)
 #define SDV2_MFMA_PHASE(k_)                                                                    \
   do {                                                                                         \
-    if ((k_) >= 1) {                                                                           \
-      const char* vt = ldsV + (((k_) - 1) & 1) * V_BYTES;                                      \
-      SDV2_PV_READ(0, fa0, fa1, fa2, fa3);                                                     \
-      _Pragma("unroll") for (int i_ = 0; i_ < DB; i_ += 2) {                                   \
-        SDV2_PV_READ(i_ + 1, fb0, fb1, fb2, fb3);                                              \
-        SDV2_PV_MFMA(i_, fa0, fa1, fa2, fa3);                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (i_ + 2 < DB) SDV2_PV_READ(i_ + 2, fa0, fa1, fa2, fa3);                             \
-        SDV2_PV_MFMA(i_ + 1, fb0, fb1, fb2, fb3);                                              \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-      }                                                                                        \
-    }                                                                                          \
-    if ((k_) <= last) {                                                                        \
-      const char* kt = ldsK + ((k_) & 1) * K_BYTES;                                            \
-      _Pragma("unroll") for (int v_ = 0; v_ < 16; ++v_) { s0[v_] = 0.f; s1[v_] = 0.f; }        \
-      SDV2_QK_READ(0, fa0, fa1, fa2, fa3);                                                     \
-      _Pragma("unroll") for (int j_ = 0; j_ < KD / 2; j_ += 2) {                               \
-        SDV2_QK_READ(j_ + 1, fb0, fb1, fb2, fb3);                                              \
-        SDV2_QK_MFMA(j_, fa0, fa1, fa2, fa3);                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-        if (j_ + 2 < KD / 2) SDV2_QK_READ(j_ + 2, fa0, fa1, fa2, fa3);                         \
-        SDV2_QK_MFMA(j_ + 1, fb0, fb1, fb2, fb3);                                              \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
-      }                                                                                        \
-    }                                                                                          \
+    SDV2_MFMA_RUN(k_, 0, NF);                                                                  \
   } while (0)
 
   // VALU phase of the current tile: masked row max, lazy rescale, exponentials -> P^T, row
@@ -265,16 +267,36 @@ void attn_bf16_kernel(const AttnArgs a) {
         if (key + 32 >= nvalid) s1[v] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    // Exponentials at the running max m_run.  The row max is only taken (and m_run moved,
+    // with O and l rescaled) when a lane's sum of exponentials leaves [0, 2^kLazy]: on the
+    // first tile (m_run = -inf gives inf or NaN) or once scores pass m_run by a margin.  So
+    // exponentials stay <= 2^kLazy and O/l is unchanged (both use m_run).  Row sums are taken
+    // from the rounded bf16 P that the PV product uses.
+    uint32_t pw0[8], pw1[8];
+    float ps;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#define SDV2_EXPS()                                                                            \
+    do {                                                                                       \
+      _Pragma("unroll") for (int v = 0; v < 16; v += 2) {                                      \
+        pw0[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[v], sl, -m_run)),              \
+                                 __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -m_run)));         \
+        pw1[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[v], sl, -m_run)),              \
+                                 __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -m_run)));         \
+      }                                                                                        \
+      float sa = 0.f, sb = 0.f;                                                                \
+      _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
+        sa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw0[j]), ones, sa, false); \
+        sb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw1[j]), ones, sb, false); \
+      }                                                                                        \
+      ps = sa + sb;                                                                            \
+    } while (0)
+    SDV2_EXPS();
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kLazyMass))) {   // wave-uniform, rare
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescale: the running max only moves when a tile max exceeds it by more than kLazy
-    // (log2 units), so exponentials stay <= 2^kLazy and O/l is unchanged (both use m_run).
-    const float m_tile = mx * sl;
-    const bool grow = m_tile > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch, rare once the max settles
-      const float m_new = grow ? m_tile : m_run;
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -282,19 +304,9 @@ void attn_bf16_kernel(const AttnArgs a) {
       for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      SDV2_EXPS();
     }
-    uint32_t pw0[8], pw1[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[v], sl, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -m_run));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[v], sl, -m_run));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -m_run));
-      ps += (p0 + p1) + (p2 + p3);
-      pw0[v / 2] = pack_bf16x2(p0, p1);
-      pw1[v / 2] = pack_bf16x2(p2, p3);
-    }
+#undef SDV2_EXPS
     l_run += ps;
     pb00 = __builtin_bit_cast(bf16x8, make_uint4(pw0[0], pw0[1], pw0[2], pw0[3]));
     pb01 = __builtin_bit_cast(bf16x8, make_uint4(pw0[4], pw0[5], pw0[6], pw0[7]));
@@ -320,6 +332,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   // prologue: K(0) resident before phase 0; group B idles through phase 0 (it issues its
   // share of the phase-0 loads there)
   fill_k(kc, 0);
+  // V^T slot 1 is read by M(0) (with P = 0) before V(1) arrives: make it finite
+  reinterpret_cast<uint4*>(ldsV + V_BYTES)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (V_BYTES > 512 * 16) reinterpret_cast<uint4*>(ldsV + V_BYTES)[tid + 512] = make_uint4(0u, 0u, 0u, 0u);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   if (grp == 1) {
@@ -345,10 +360,9 @@ void attn_bf16_kernel(const AttnArgs a) {
     if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
-#undef SDV2_PV_READ
-#undef SDV2_PV_MFMA
-#undef SDV2_QK_READ
-#undef SDV2_QK_MFMA
+#undef SDV2_FRAG
+#undef SDV2_FRAG_MFMA
+#undef SDV2_MFMA_RUN
 #undef SDV2_MFMA_PHASE
 
   // lane (g, r), accumulator v of o[i] holds O^T[d = 32i + 8(v/4) + 4g + v%4][query r]
