@@ -39,12 +39,17 @@ def attn_source_hash() -> str:
     return hashlib.sha256(p.read_bytes()).hexdigest()[:16]
 
 
+def visible_keys(c, t):
+    """Keys a query of own-chunk frame t sees: sinks + window + own frames 0..t (block-causal)."""
+    return (c.sink_frames + c.window_frames + t + 1) * c.tokens
+
+
 def workload_numbers(c):
     N = c.tokens
     L = (c.sink_frames + c.window_frames + c.chunk_frames) * N
     B = c.stream_batch
     eb = 2 if c.dtype == "bf16" else 4
-    flops_layer = 4 * B * c.num_heads * c.chunk_rows * L * c.head_dim
+    flops_layer = 4 * B * c.num_heads * N * c.head_dim * sum(visible_keys(c, t) for t in range(c.chunk_frames))
     # algorithmic bytes of one attention call: Q + O, the shared sink+window K/V read once, and
     # each element's own chunk K/V
     qo = 2 * B * c.chunk_rows * c.num_heads * c.head_dim * eb
@@ -118,7 +123,8 @@ def run_gpu(c, steps, warmup, pool=2):
             if embeds is not None:
                 if timed_parts:
                     a, b = ev_pair("sink_replace"); a.record()
-                run.cache.sink_replace(commit, embeds[commit % len(embeds)], sync=False)
+                last = (commit + 1) * c.chunk_frames - 1          # the chunk's last frame
+                run.cache.sink_replace(last, embeds[commit % len(embeds)], sync=False)
                 if timed_parts:
                     b.record()
             if motion is not None:
@@ -177,7 +183,7 @@ def cpu_baseline(c, budget_s=12.0):
     st.begin_step(steady)
     q, k, v = inputs.qkv(c, steady, 0, 0)
     calls, t_used = 0, 0.0
-    rows = c.chunk_rows
+    rows = c.tokens                                # frame 0's query rows
     while t_used < budget_s and calls < 64:
         # one element's attention over the full key set, a slice of the rows at a time
         n = max(1, min(rows, 64 if c.num_heads > 12 else 128))
@@ -188,7 +194,7 @@ def cpu_baseline(c, budget_s=12.0):
         t_used += time.perf_counter() - t0
         calls += 1
         last_rows = len(sel)
-    L = (c.sink_frames + c.window_frames + 1) * c.tokens
+    L = visible_keys(c, 0)                         # the sampled rows are frame 0's
     flops = calls * 4 * last_rows * c.num_heads * L * c.head_dim
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{calls} oracle attend calls of {last_rows} query rows x {c.num_heads} heads over "

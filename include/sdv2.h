@@ -60,8 +60,8 @@ enum { SDV2_F32 = 0, SDV2_BF16 = 1 };
 
 /* Library limits (validated by sdv2_config_validate). */
 enum {
-  SDV2_MAX_SLOTS_SHARED = 64, /* S + W */
-  SDV2_MAX_BATCH = 8,         /* B */
+  SDV2_MAX_SLOTS_SHARED = 64, /* S + W + T' */
+  SDV2_MAX_BATCH = 8,         /* B, and B * T' */
   SDV2_MAX_SINKS = 16,        /* S */
   SDV2_MAX_TPAIRS = 32        /* rope_dim_t / 2 */
 };
@@ -74,7 +74,7 @@ typedef struct sdv2_config {
   int32_t grid_w;
   int32_t sink_frames;   /* S >= 0 */
   int32_t window_frames; /* W >= 1 */
-  int32_t chunk_frames;  /* T': only 1 is supported */
+  int32_t chunk_frames;  /* T' >= 1 frames per chunk, B * T' <= SDV2_MAX_BATCH */
   int32_t stream_batch;  /* B in [1, SDV2_MAX_BATCH] */
   int32_t rope_dim_t;    /* even; rope_dim_t + rope_dim_h + rope_dim_w == head_dim */
   int32_t rope_dim_h;
@@ -87,9 +87,10 @@ typedef struct sdv2_config {
 } sdv2_config;
 
 /* Device layout of the KV cache (element offsets from d_kv, element = 2 or 4 bytes).
- * Slots [0,S) are sinks, [S,S+W+1) the ring (frame f >= S lives in slot S + f mod (W+1);
- * W of these slots hold the window, the spare one receives the frame being finished), and
- * [S+W+1, S+W+B) the staging slots of stream-batch elements 1..B-1 (element b in S+W+b).
+ * Slots [0,S) are sinks, [S,S+W+T') the ring (frame f >= S lives in slot S + f mod (W+T');
+ * W of these slots hold the window, the T' spare ones receive the chunk being finished), and
+ * [S+W+T', S+W+B*T') the staging slots of stream-batch elements 1..B-1 (frame t of element b
+ * in S+W+b*T'+t).
  *   K of (layer, slot, head, token n, dim i): k_offset(layer) + slot*slot_stride
  *        + head*head_stride + n*head_dim + i                      (rows of head_dim)
  *   V of (layer, slot, head, token n, dim i): v_offset(layer) + slot*slot_stride
@@ -97,7 +98,7 @@ typedef struct sdv2_config {
  * with k_offset(l) = l*layer_stride, v_offset(l) = l*layer_stride + slot_stride*slots.
  * Tokens n in [N, tokens_padded) are zero padding. */
 typedef struct sdv2_layout {
-  int64_t slots;          /* S + (W + 1) + (B - 1) */
+  int64_t slots;          /* S + (W + T') + (B - 1) T' */
   int64_t tokens_padded;  /* N rounded up to 64 */
   int64_t elem_bytes;     /* 4 (fp32) or 2 (bf16) */
   int64_t head_stride;    /* tokens_padded * head_dim */
@@ -139,11 +140,12 @@ int sdv2_cache_destroy(sdv2_cache* cache);
 int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied, void* stream);
 
 /* RoPE + append for one layer ([NEWS] algorithm item 1; [REPO] ring-buffer KV cache).
- * Elements b = 0..nbatch-1 hold chunks first_chunk+b (b = 0 oldest); first_chunk must equal
- * the number of chunks committed so far and first_chunk + nbatch - 1 the newest frame given
- * to sdv2_rope_refresh.  d_q is rotated in place at temporal position frame - b0 (row h, col
- * w); k is rotated likewise and written with v: element 0 into the slot its frame keeps once
- * committed (sink slot f, or ring slot S + f mod (W+1), which holds no attended frame), the
+ * Elements b = 0..nbatch-1 hold chunks first_chunk+b (b = 0 oldest) of T' frames each, frame
+ * f = chunk*T' + t in rows [t*N, (t+1)*N); first_chunk must equal the number of chunks
+ * committed so far and (first_chunk + nbatch)*T' - 1 the newest frame given to
+ * sdv2_rope_refresh.  d_q is rotated in place at temporal position f - b0 (row h, col w); k is
+ * rotated likewise and written with v: element 0's frames into the slots they keep once
+ * committed (sink slot f, or ring slot S + f mod (W+T'), which hold no attended frame), the
  * others into their staging slots.  Buffers:
  * [nbatch][T'N][H][d] each; d_q read-write, d_k and d_v read-only.  Once per layer per step. */
 int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int32_t nbatch,
@@ -151,23 +153,26 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
 
 /* Chunk attention for one layer (after its append this step).  For each element b and head:
  * out = softmax(scale * Q_rot K^T) V over the keys [present sinks | window | own chunk], with
- * Q_rot = d_q_rot as rotated by sdv2_cache_append.  d_out: [nbatch][T'N][H][d], written.  The
+ * Q_rot = d_q_rot as rotated by sdv2_cache_append; inside the own chunk a query of frame t sees
+ * the keys of frames 0..t (block-causal).  d_out: [nbatch][T'N][H][d], written.  The
  * workspace given at create time is used for split-KV partial results (calls on one cache
  * must not overlap in time). */
 int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream);
 
 /* Commit the finished chunk (element 0, which must be `chunk`) for all layers: from the next
- * step on, its K and V (already in sink slot f if f < S, else in ring slot S + f mod (W+1)) are
- * attended and the frame W older leaves the window.  Requires every layer appended this step.
- * Host bookkeeping only: no device work is queued on `stream`. */
+ * step on, its T' frames' K and V (already in sink slot f if f < S, else in ring slot
+ * S + f mod (W+T')) are attended, and for each of them the frame W older leaves the window.
+ * Requires every layer appended this step.  Host bookkeeping only: no device work is queued on
+ * `stream`. */
 int sdv2_cache_commit(sdv2_cache* cache, int64_t chunk, void* stream);
 
-/* Adaptive sink refresh after the commit of `frame` ([WT] adaptive sink and RoPE refresh).
- * d_embed: fp32 [embed_dim] chunk embedding h (device).  If frame < S it becomes sink frame's
- * embedding.  Otherwise, when tau is on: alpha_j = cos(h, e_j) for j < S (fp64; 0 if a norm is
- * 0), j* = argmin (lowest j on ties); if alpha_j* < tau the committed frame's K/V are copied
- * into sink j* for all layers and e_j* = h.  The decision is taken on the device.  If h_slot is
+/* Adaptive sink refresh after a commit ([WT] adaptive sink and RoPE refresh).  `frame` is the
+ * last frame of the committed chunk.  d_embed: fp32 [embed_dim] chunk embedding h (device).
+ * Every frame of the chunk below S became a sink and gets h as its embedding.  Then, if
+ * frame >= S and tau is on: alpha_j = cos(h, e_j) for j < S (fp64; 0 if a norm is 0), j* =
+ * argmin (lowest j on ties); if alpha_j* < tau frame `frame`'s K/V are copied into sink j* for
+ * all layers and e_j* = h.  The decision is taken on the device.  If h_slot is
  * non-NULL the call synchronises `stream` and returns j* if replaced, else -1 (h_alpha, may be
  * NULL: alpha_j*); with h_slot NULL nothing synchronises and sdv2_cache_slot_info reports the
  * sink slots as unknown (-2) from then on. */
@@ -203,7 +208,7 @@ int sdv2_cache_state(const sdv2_cache* cache, int64_t* rope_base, int64_t* commi
 /* Stream-batch schedule of step `step` for a stream of num_chunks chunks ([NEWS] system item 1;
  * [REPO] quick example): in-flight chunks [first_chunk, first_chunk + nbatch), the chunk
  * finished and committed at its end (-1 while the pipeline fills) and the newest in-flight
- * frame (-1 past the end).  Host only. */
+ * frame, the last frame of the newest chunk (-1 past the end).  Host only. */
 int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int64_t* first_chunk,
                    int32_t* nbatch, int64_t* commit_chunk, int64_t* newest_frame);
 

@@ -38,7 +38,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 
 // ---- kernel argument blocks (passed by value) ----------------------------------------------
 struct AppendArgs {
-  void* q;                 // [nbatch][N][H][D], rotated in place
+  void* q;                 // [nbatch][T*N][H][D], rotated in place
   const void* k;
   const void* v;
   void* kv;                // cache base
@@ -49,23 +49,25 @@ struct AppendArgs {
   const float2* tab_h;     // [grid_h][ph] (cos, sin)
   const float2* tab_w;     // [grid_w][pw]
   int N, Npad, H, grid_w, nbatch;
-  int dst_slot[kMaxBatch]; // slot each element's K and V are written to
+  int T;                   // frames per chunk; nbatch * T <= kMaxBatch
+  int dst_slot[kMaxBatch]; // slot of frame t of element b, index b * T + t
   int pt, ph, pw;          // RoPE pairs per axis
-  float2 tcs[kMaxBatch][kMaxTPairs];   // temporal (cos, sin) per element and pair
+  float2 tcs[kMaxBatch][kMaxTPairs];   // temporal (cos, sin) per frame (b * T + t) and pair
 };
 
 struct AttnArgs {
-  const void* q;           // [nbatch][N][H][D] rotated queries
-  void* out;               // [nbatch][N][H][D]
+  const void* q;           // [nbatch][T*N][H][D] rotated queries
+  void* out;               // [nbatch][T*N][H][D]
   const void* kv;
   int64_t k_layer_off, v_layer_off, slot_stride, head_stride;
-  float* part_o;           // [nsplit][nbatch][H][N][D] fp32 (split-KV only)
-  float2* part_ml;         // [nsplit][nbatch][H][N] (m in log2 units, l)
-  int N, Npad, H, nbatch;
+  float* part_o;           // [nsplit][nbatch][H][T*N][D] fp32 (split-KV only)
+  float2* part_ml;         // [nsplit][nbatch][H][T*N] (m in log2 units, l)
+  int N, Npad, H, nbatch;  // N: tokens per frame
+  int T;                   // frames per chunk (block-causal inside the chunk)
   int nshared;             // cached frames attended (sinks + window)
-  int own_slot[kMaxBatch]; // slot holding each element's own chunk
+  int own_slot[kMaxBatch]; // slot of own-chunk frame t of element b, index b * T + t
   int tiles_per_frame;     // Npad / kTileKeys
-  int total_tiles;         // (nshared + 1) * tiles_per_frame
+  int total_tiles;         // (nshared + T) * tiles_per_frame
   int nsplit, qtiles;
   float scale_log2;        // softmax scale * log2(e)
   float scale;
@@ -76,7 +78,7 @@ struct CombineArgs {
   const float* part_o;
   const float2* part_ml;
   void* out;
-  int N, H, nbatch, nsplit;
+  int N, H, nbatch, nsplit;  // N: query rows per (element, head)
 };
 
 struct RebaseArgs {

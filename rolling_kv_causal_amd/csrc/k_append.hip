@@ -7,9 +7,10 @@
 // by the temporal angle (per element, from the host), the next ph by the row angle and the last
 // pw by the column angle of the token (tables in device memory).
 //
-// One workgroup per (64-token tile, head, element); 16-byte loads and stores throughout.  K
-// rows go to the cache as [token][d]; V goes through LDS and leaves transposed as [d][token]
-// rows of the tile, so the attention kernel can read V^T fragments contiguously.
+// One workgroup per (frame of the chunk, 64-token tile of the frame, head, element); 16-byte
+// loads and stores throughout.  K rows go to the cache as [token][d]; V goes through LDS and
+// leaves transposed as [d][token] rows of the tile, so the attention kernel can read V^T
+// fragments contiguously.  Frame t of element b has its own slot and temporal angle.
 #include "common.h"
 
 #include <type_traits>
@@ -47,13 +48,16 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   __shared__ T vs[TILE * VSTR];
   __shared__ float2 tcs[kMaxTPairs];
 
-  const int n0 = blockIdx.x * TILE, head = blockIdx.y, b = blockIdx.z;
+  const int tiles = (a.N + TILE - 1) / TILE;
+  const int t = blockIdx.x / tiles;                // frame of the chunk
+  const int n0 = (blockIdx.x - t * tiles) * TILE, head = blockIdx.y, b = blockIdx.z;
+  const int fr = b * a.T + t;                      // frame index within the call
   const int tid = threadIdx.x;
-  if (tid < a.pt) tcs[tid] = a.tcs[b][tid];
+  if (tid < a.pt) tcs[tid] = a.tcs[fr][tid];
   __syncthreads();
 
   const int c = tid % CH;
-  const int64_t kdst = a.k_layer_off + (int64_t)a.dst_slot[b] * a.slot_stride +
+  const int64_t kdst = a.k_layer_off + (int64_t)a.dst_slot[fr] * a.slot_stride +
                        (int64_t)head * a.head_stride;
   constexpr int PASSES = TILE / ROWS;
   // Every global load of the tile is issued before the first store: q is rotated in place,
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   for (int pass = 0; pass < PASSES; ++pass) {
     const int n = n0 + pass * ROWS + tid / CH;
     if (n < a.N) {
-      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
+      const int64_t off = ((int64_t)(fr * a.N + n) * a.H + head) * D + c * VEC;
       qv[pass] = *(const uint4*)((const T*)a.q + off);
       kv[pass] = *(const uint4*)((const T*)a.k + off);
       vv[pass] = *(const uint4*)((const T*)a.v + off);
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
     uint32_t* vrow = reinterpret_cast<uint32_t*>(vs + row * VSTR + c * VEC);
     vrow[0] = vv[pass].x; vrow[1] = vv[pass].y; vrow[2] = vv[pass].z; vrow[3] = vv[pass].w;
     if (n < a.N) {
-      const int64_t off = ((int64_t)(b * a.N + n) * a.H + head) * D + c * VEC;
+      const int64_t off = ((int64_t)(fr * a.N + n) * a.H + head) * D + c * VEC;
       rotate16<BF16>(qv[pass], cs[pass]);
       rotate16<BF16>(kv[pass], cs[pass]);
       *(uint4*)((T*)a.q + off) = qv[pass];
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
 
   // V^T rows: d-major, the tile's 64 tokens contiguous
   constexpr int TCH = TILE / VEC;            // 16-byte chunks per V^T row of the tile
-  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)a.dst_slot[b] * a.slot_stride +
+  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)a.dst_slot[fr] * a.slot_stride +
             (int64_t)head * a.head_stride + n0;
   for (int idx = tid; idx < D * TCH; idx += 256) {
     const int drow = idx / TCH, kc = idx % TCH;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
 }
 
 hipError_t launch_rope_append(const AppendArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  const dim3 grid((a.N + kTileKeys - 1) / kTileKeys, a.H, a.nbatch);
+  const dim3 grid(a.T * ((a.N + kTileKeys - 1) / kTileKeys), a.H, a.nbatch);
   if (bf16) {
     if (head_dim == 128)
       hipLaunchKernelGGL((rope_append_kernel<true, 128>), grid, dim3(256), 0, s, a);

@@ -31,8 +31,7 @@
 
 namespace sdv2 {
 
-constexpr float kLazy = 8.0f;   // lazy-rescale margin of the running max (log2 units)
-constexpr float kLazyMass = 256.0f;   // 2^kLazy: bound on a lane's sum of exponentials
+constexpr float kLazyMass = 256.0f;   // 2^8: bound on a lane's sum of exponentials
 // s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
@@ -111,14 +110,17 @@ void attn_bf16_kernel(const AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;                  // 0 = group A, 1 = group B
   const int g = lane >> 5, r = lane & 31;
+  const int R = a.T * a.N;                    // query rows per element (T frames of N tokens)
   const int qrow = qtile * kQTile + wave * 32 + r;
-  const bool qvalid = qrow < a.N;
+  const bool qvalid = qrow < R;
+  const int tq = qrow / a.N;                  // the row's frame within the chunk
+  const int tq_wave = (qtile * kQTile + wave * 32) / a.N;   // lowest frame of the wave's rows
 
   // Q^T operand: lane (g, r) holds Q[row r][kd*16 + 8g .. +7] for every 16-wide k step.
   bf16x8 qf[KD];
   {
     const uint16_t* qp = (const uint16_t*)a.q +
-                         ((int64_t)(elem * a.N + (qvalid ? qrow : 0)) * a.H + head) * D + g * 8;
+                         ((int64_t)(elem * R + (qvalid ? qrow : 0)) * a.H + head) * D + g * 8;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
       const uint4 v = qvalid ? *(const uint4*)(qp + kd * 16) : make_uint4(0, 0, 0, 0);
@@ -126,22 +128,27 @@ void attn_bf16_kernel(const AttnArgs a) {
     }
   }
 
-  const int t_begin = (int)((int64_t)split * a.total_tiles / a.nsplit);
-  const int t_end = (int)((int64_t)(split + 1) * a.total_tiles / a.nsplit);
-  const int ntiles = t_end - t_begin;         // >= 1 (nsplit <= total_tiles)
+  // Block-causal chunk: the walk [shared frames..., own frames 0..T-1] ends with the last own
+  // frame a row of this query tile sees; the host keeps nsplit <= (nshared + 1) tiles per frame,
+  // so every split has a tile.
+  const int tq_hi = min(a.T - 1, (qtile * kQTile + kQTile - 1) / a.N);
+  const int tiles_q = (a.nshared + tq_hi + 1) * a.tiles_per_frame;
+  const int t_begin = (int)((int64_t)split * tiles_q / a.nsplit);
+  const int t_end = (int)((int64_t)(split + 1) * tiles_q / a.nsplit);
+  const int ntiles = t_end - t_begin;         // >= 1
   const int last = ntiles - 1;
   const char* kvb = (const char*)a.kv;
   const int64_t head_off = (int64_t)head * a.head_stride;
-  // Slot of frame f in lane f (frames >= 64 can only be the own chunk), read back with
-  // readlane: the tile walk issues no scalar memory load, whose wait would also drain the
-  // LDS queue.
-  const int own = a.own_slot[elem];
-  const int slot_lane = lane < a.nshared ? a.slots[lane] : own;
+  // Slot of frame f in lane f (shared frames, then the T own frames; the host keeps
+  // S + W + T <= 64), read back with readlane: the tile walk issues no scalar memory load,
+  // whose wait would also drain the LDS queue.
+  const int own_i = min(max(lane - a.nshared, 0), a.T - 1);
+  const int slot_lane = lane < a.nshared ? a.slots[lane] : a.own_slot[elem * a.T + own_i];
   const char* const kblk = kvb + (a.k_layer_off + head_off) * 2;
   const char* const vblk = kvb + (a.v_layer_off + head_off) * 2;
   const int64_t slot_bytes = a.slot_stride * 2;
   auto frame_at = [&](TileCursor& c) {
-    const int slot = c.f < a.nshared ? __builtin_amdgcn_readlane(slot_lane, c.f & 63) : own;
+    const int slot = __builtin_amdgcn_readlane(slot_lane, c.f & 63);
     c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * 2);
     c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * 2);
   };
@@ -258,7 +265,11 @@ void attn_bf16_kernel(const AttnArgs a) {
 
   // VALU phase of the current tile: masked row max, lazy rescale, exponentials -> P^T, row
   // sums.  lane (g, r), accumulator v holds key 16*(v/8) + 8g + v%8 (+32 for s1) of query r.
-  auto valu_phase = [&](int nvalid) {
+  auto valu_phase = [&](int nvalid, int tk) {
+    if (tk > tq_wave && tk > tq) {            // own frame tk is after this row's frame
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s0[v] = s1[v] = -INFINITY;
+    }
     if (nvalid < kTileKeys) {                 // ragged last tile of a frame
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -275,13 +286,13 @@ void attn_bf16_kernel(const AttnArgs a) {
     uint32_t pw0[8], pw1[8];
     float ps;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#define SDV2_EXPS()                                                                            \
+#define SDV2_EXPS(M_)                                                                          \
     do {                                                                                       \
       _Pragma("unroll") for (int v = 0; v < 16; v += 2) {                                      \
-        pw0[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[v], sl, -m_run)),              \
-                                 __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -m_run)));         \
-        pw1[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[v], sl, -m_run)),              \
-                                 __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -m_run)));         \
+        pw0[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[v], sl, -(M_))),               \
+                                 __builtin_amdgcn_exp2f(fmaf(s0[v + 1], sl, -(M_))));          \
+        pw1[v / 2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[v], sl, -(M_))),               \
+                                 __builtin_amdgcn_exp2f(fmaf(s1[v + 1], sl, -(M_))));          \
       }                                                                                        \
       float sa = 0.f, sb = 0.f;                                                                \
       _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
@@ -290,21 +301,22 @@ void attn_bf16_kernel(const AttnArgs a) {
       }                                                                                        \
       ps = sa + sb;                                                                            \
     } while (0)
-    SDV2_EXPS();
+    SDV2_EXPS(m_run);
     if (__builtin_amdgcn_ballot_w64(!(ps <= kLazyMass))) {   // wave-uniform, rare
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // a row that has seen only masked keys keeps m_run = -inf and gets P = 0
       const float m_new = fmaxf(m_run, mx * sl);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      SDV2_EXPS();
+      SDV2_EXPS(m_run == -INFINITY ? 0.f : m_run);
     }
 #undef SDV2_EXPS
     l_run += ps;
@@ -354,7 +366,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     if (k == ntiles && grp == 1) break;       // B's last phase was M(n)
     if (grp == 1) loads(k + 1);
     if (k <= last) {
-      valu_phase(a.N - sc.k * kTileKeys);
+      valu_phase(a.N - sc.k * kTileKeys, sc.f - a.nshared);
       if (k < last) advance(sc);
     }
     if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -368,9 +380,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   // lane (g, r), accumulator v of o[i] holds O^T[d = 32i + 8(v/4) + 4g + v%4][query r]
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // 0: no visible key in this split
   if (a.nsplit == 1) {
-    uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * a.N + qrow) * a.H + head) * D + 4 * g;
+    uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * R + qrow) * a.H + head) * D + 4 * g;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -381,7 +393,7 @@ void attn_bf16_kernel(const AttnArgs a) {
         *(uint2*)(op + 32 * i + 8 * a4) = w2;
       }
   } else {
-    const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * a.N + qrow;
+    const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + qrow;
     float* po = a.part_o + prow * D + 4 * g;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
@@ -433,16 +445,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
   constexpr int KT = 32;
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
-  const int qtiles = (a.N + 63) / 64;
+  const int R = a.T * a.N;                    // query rows per element
+  const int qtiles = (R + 63) / 64;
   const int qtile = blockIdx.x % qtiles;
   const int head = (blockIdx.x / qtiles) % a.H;
   const int elem = blockIdx.x / (qtiles * a.H);
   const int lane = threadIdx.x;
   const int n = qtile * 64 + lane;
-  const bool valid = n < a.N;
+  const bool valid = n < R;
+  const int tq = n / a.N;                     // the row's frame within the chunk
+  const int tq_hi = min(a.T - 1, (qtile * 64 + 63) / a.N);
 
   float q[D], o[D];
-  const float* qp = (const float*)a.q + ((int64_t)(elem * a.N + (valid ? n : 0)) * a.H + head) * D;
+  const float* qp = (const float*)a.q + ((int64_t)(elem * R + (valid ? n : 0)) * a.H + head) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     q[d] = valid ? qp[d] : 0.f;
@@ -450,8 +465,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const float* kvb = (const float*)a.kv;
-  for (int f = 0; f <= a.nshared; ++f) {
-    const int slot = f < a.nshared ? a.slots[f] : a.own_slot[elem];
+  for (int f = 0; f <= a.nshared + tq_hi; ++f) {   // block-causal inside the chunk
+    const int slot = f < a.nshared ? a.slots[f] : a.own_slot[elem * a.T + f - a.nshared];
+    const bool seen = f - a.nshared <= tq;
     const int64_t sh = (int64_t)slot * a.slot_stride + (int64_t)head * a.head_stride;
     const float* kp = kvb + a.k_layer_off + sh;
     const float* vp = kvb + a.v_layer_off + sh;
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int d = 0; d < D; ++d) acc = fmaf(q[d], ks[j][d], acc);
-        s[j] = j < nv ? acc * a.scale : -INFINITY;
+        s[j] = (j < nv && seen) ? acc * a.scale : -INFINITY;
         mx = fmaxf(mx, s[j]);
       }
       const float m_new = fmaxf(m, mx);
@@ -489,7 +505,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     }
   }
   if (!valid) return;
-  float* op = (float*)a.out + ((int64_t)(elem * a.N + n) * a.H + head) * D;
+  float* op = (float*)a.out + ((int64_t)(elem * R + n) * a.H + head) * D;
   const float inv = 1.f / l;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
@@ -503,7 +519,7 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool bf16, hipStrea
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
   } else {
-    const int grid = a.nbatch * a.H * ((a.N + 63) / 64);
+    const int grid = a.nbatch * a.H * ((a.T * a.N + 63) / 64);
     if (head_dim == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(64), 0, s, a);
     else

@@ -57,11 +57,13 @@ int validate(const sdv2_config* c) {
   if (c->sink_frames < 0 || c->sink_frames > kMaxSinks)
     return fail(SDV2_EINVAL, "sink_frames must be in [0, %d]", kMaxSinks);
   if (c->window_frames < 1) return fail(SDV2_EINVAL, "window_frames must be >= 1");
-  if (c->sink_frames + c->window_frames > kMaxShared)
-    return fail(SDV2_EINVAL, "sink_frames + window_frames must be <= %d", kMaxShared);
-  if (c->chunk_frames != 1) return fail(SDV2_EINVAL, "chunk_frames must be 1");
+  if (c->chunk_frames < 1) return fail(SDV2_EINVAL, "chunk_frames must be >= 1");
+  if (c->sink_frames + c->window_frames + c->chunk_frames > kMaxShared)
+    return fail(SDV2_EINVAL, "sink_frames + window_frames + chunk_frames must be <= %d", kMaxShared);
   if (c->stream_batch < 1 || c->stream_batch > kMaxBatch)
     return fail(SDV2_EINVAL, "stream_batch must be in [1, %d]", kMaxBatch);
+  if ((int64_t)c->stream_batch * c->chunk_frames > kMaxBatch)
+    return fail(SDV2_EINVAL, "stream_batch * chunk_frames must be <= %d", kMaxBatch);
   if (c->rope_dim_t < 0 || c->rope_dim_h < 0 || c->rope_dim_w < 0 || (c->rope_dim_t & 1) ||
       (c->rope_dim_h & 1) || (c->rope_dim_w & 1))
     return fail(SDV2_EINVAL, "rope dims must be even and >= 0");
@@ -81,7 +83,7 @@ int validate(const sdv2_config* c) {
 sdv2_layout make_layout(const sdv2_config& c) {
   sdv2_layout l;
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
-  l.slots = c.sink_frames + c.window_frames + c.stream_batch;
+  l.slots = c.sink_frames + c.window_frames + (int64_t)c.stream_batch * c.chunk_frames;
   l.tokens_padded = align_up(N, kTileKeys);
   l.elem_bytes = c.dtype == SDV2_BF16 ? 2 : 4;
   l.head_stride = l.tokens_padded * c.head_dim;
@@ -99,14 +101,17 @@ sdv2_layout make_layout(const sdv2_config& c) {
 constexpr int kSlots = 256;
 constexpr int kMaxSplit = 16;
 constexpr double kTileUs = 1.2, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
-int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles) {
+// total_tiles: key tiles of the longest query tile; min_tiles: of the shortest (block-causal
+// chunks end the walk at a query tile's last own frame), which bounds the split count so that
+// every split has at least one tile.
+int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_tiles) {
   if (c.dtype != SDV2_BF16) return 1;
-  const int64_t N = (int64_t)c.grid_h * c.grid_w;
-  const int64_t base = (int64_t)nbatch * c.num_heads * ((N + kQTile - 1) / kQTile);
-  const int64_t rows = (int64_t)nbatch * c.num_heads * N;
+  const int64_t R = (int64_t)c.chunk_frames * c.grid_h * c.grid_w;   // query rows per element
+  const int64_t base = (int64_t)nbatch * c.num_heads * ((R + kQTile - 1) / kQTile);
+  const int64_t rows = (int64_t)nbatch * c.num_heads * R;
   int best = 1;
   double best_cost = 1e300;
-  for (int ns = 1; ns <= kMaxSplit && ns <= total_tiles; ++ns) {
+  for (int ns = 1; ns <= kMaxSplit && ns <= min_tiles; ++ns) {
     const int64_t rounds = (base * ns + kSlots - 1) / kSlots;
     const int64_t per = (total_tiles + ns - 1) / ns;
     double cost = (double)(rounds * per) * kTileUs;
@@ -144,12 +149,12 @@ int64_t workspace_bytes(const sdv2_config& c) {
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
   const int tpf = (int)(align_up(N, kTileKeys) / kTileKeys);
   int64_t best = 0;
-  // every (nbatch, frames present) the stream can reach, warm-up included
+  // every (nbatch, shared frames present) the stream can reach, warm-up included
   for (int nb = 1; nb <= c.stream_batch; ++nb)
-    for (int frames = 1; frames <= c.sink_frames + c.window_frames + 1; ++frames) {
-      const int ns = choose_nsplit(c, nb, frames * tpf);
+    for (int shared = 0; shared <= c.sink_frames + c.window_frames; ++shared) {
+      const int ns = choose_nsplit(c, nb, (shared + c.chunk_frames) * tpf, (shared + 1) * tpf);
       if (ns < 2) continue;
-      const int64_t rows = (int64_t)ns * nb * c.num_heads * N;
+      const int64_t rows = (int64_t)ns * nb * c.num_heads * c.chunk_frames * N;
       const int64_t bytes = align_up(rows * c.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
       if (bytes > best) best = bytes;
     }
@@ -197,16 +202,25 @@ int check_cache(const sdv2_cache* c) {
   return SDV2_OK;
 }
 
-// Slot of frame f once committed: sink slot f for f < S, else one of W + 1 ring slots.  The
-// ring holds one slot more than the window: the slot of the frame being finished holds a frame
-// that already left the window, so the append writes element 0 to its final slot and the commit
-// moves no data.
+// Slot of frame f once committed: sink slot f for f < S, else one of W + T' ring slots.  The
+// ring holds T' slots more than the window: the slots of the chunk being finished hold frames
+// that already left the window, so the append writes element 0 to its final slots and the
+// commit moves no data.
 int home_slot(const sdv2_config& c, int64_t f) {
-  return f < c.sink_frames ? (int)f : c.sink_frames + (int)(f % (c.window_frames + 1));
+  return f < c.sink_frames ? (int)f
+                           : c.sink_frames + (int)(f % (c.window_frames + c.chunk_frames));
 }
 
 // Sinks and ring slots; the staging slots of elements 1..B-1 follow.
-int shared_region(const sdv2_config& c) { return c.sink_frames + c.window_frames + 1; }
+int shared_region(const sdv2_config& c) {
+  return c.sink_frames + c.window_frames + c.chunk_frames;
+}
+
+// Slot of frame t of element b's chunk at a step whose element 0 holds chunk `first`.
+int chunk_slot(const sdv2_config& c, int64_t first, int b, int t) {
+  return b == 0 ? home_slot(c, first * c.chunk_frames + t)
+                : c.sink_frames + c.window_frames + b * c.chunk_frames + t;
+}
 
 // Present shared slots in attention order: sinks by slot index, then the ring by slot index.
 int shared_slots(const sdv2_cache* c, int* out) {
@@ -310,7 +324,7 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
   if (c->started && newest_frame < c->newest)
     return fail(SDV2_ESTATE, "newest_frame %lld is older than the previous step's %lld",
                 (long long)newest_frame, (long long)c->newest);
-  if (newest_frame < c->committed)
+  if (newest_frame < c->committed * c->cfg.chunk_frames)
     return fail(SDV2_ESTATE, "newest_frame %lld is already committed", (long long)newest_frame);
   const sdv2_config& cfg = c->cfg;
   const int64_t T = cfg.rope_refresh_period;
@@ -369,9 +383,10 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   if (first_chunk != c->committed)
     return fail(SDV2_ESTATE, "first_chunk %lld must equal the committed count %lld",
                 (long long)first_chunk, (long long)c->committed);
-  if (first_chunk + nbatch - 1 != c->newest)
-    return fail(SDV2_ESTATE, "newest chunk %lld differs from the step's newest frame %lld",
-                (long long)(first_chunk + nbatch - 1), (long long)c->newest);
+  const int Tc = cfg.chunk_frames;
+  if ((first_chunk + nbatch) * Tc - 1 != c->newest)
+    return fail(SDV2_ESTATE, "newest chunk's last frame %lld differs from the step's newest frame %lld",
+                (long long)((first_chunk + nbatch) * Tc - 1), (long long)c->newest);
   if (c->step_nbatch != 0 && (c->step_nbatch != nbatch || c->step_first != first_chunk))
     return fail(SDV2_ESTATE, "nbatch/first_chunk differ between layers of one step");
   if (c->appended[layer]) return fail(SDV2_ESTATE, "layer %d already appended this step", layer);
@@ -392,30 +407,35 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   a.H = cfg.num_heads;
   a.grid_w = cfg.grid_w;
   a.nbatch = nbatch;
-  // element 0 goes to the slot its frame keeps once committed, the others to staging slots
+  a.T = Tc;
+  // element 0 goes to the slots its frames keep once committed, the others to staging slots
   for (int b = 0; b < nbatch; ++b)
-    a.dst_slot[b] = b == 0 ? home_slot(cfg, first_chunk) : cfg.sink_frames + cfg.window_frames + b;
-  if (c->slot_written[a.dst_slot[0]])
-    return fail(SDV2_ESTATE, "internal: slot %d of chunk %lld is still attended", a.dst_slot[0],
-                (long long)first_chunk);
+    for (int t = 0; t < Tc; ++t) a.dst_slot[b * Tc + t] = chunk_slot(cfg, first_chunk, b, t);
+  for (int t = 0; t < Tc; ++t)
+    if (c->slot_written[a.dst_slot[t]])
+      return fail(SDV2_ESTATE, "internal: slot %d of chunk %lld is still attended", a.dst_slot[t],
+                  (long long)first_chunk);
   a.pt = cfg.rope_dim_t / 2;
   a.ph = cfg.rope_dim_h / 2;
   a.pw = cfg.rope_dim_w / 2;
-  for (int b = 0; b < nbatch; ++b) {
-    const double p = (double)(first_chunk + b - c->base);   // temporal position f - b0 (T' = 1)
-    for (int i = 0; i < a.pt; ++i) {
-      const double ang = p * omega(cfg.rope_theta, i, cfg.rope_dim_t);
-      a.tcs[b][i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+  for (int b = 0; b < nbatch; ++b)
+    for (int t = 0; t < Tc; ++t) {
+      const double p = (double)((first_chunk + b) * Tc + t - c->base);   // position f - b0
+      for (int i = 0; i < a.pt; ++i) {
+        const double ang = p * omega(cfg.rope_theta, i, cfg.rope_dim_t);
+        a.tcs[b * Tc + t][i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
     }
-  }
   SDV2_HIP(launch_rope_append(a, cfg.head_dim, cfg.dtype == SDV2_BF16, (hipStream_t)stream));
   c->appended[layer] = 1;
   c->step_first = first_chunk;
   c->step_nbatch = nbatch;
-  for (int b = 0; b < nbatch; ++b) {
-    c->slot_frame[a.dst_slot[b]] = first_chunk + b;
-    c->slot_label[a.dst_slot[b]] = first_chunk + b - c->base;
-  }
+  for (int b = 0; b < nbatch; ++b)
+    for (int t = 0; t < Tc; ++t) {
+      const int64_t f = (first_chunk + b) * Tc + t;
+      c->slot_frame[a.dst_slot[b * Tc + t]] = f;
+      c->slot_label[a.dst_slot[b * Tc + t]] = f - c->base;
+    }
   return ok();
 }
 
@@ -445,15 +465,17 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
   a.H = cfg.num_heads;
   a.nbatch = nbatch;
   a.nshared = shared_slots(c, a.slots);
+  const int Tc = cfg.chunk_frames;
+  a.T = Tc;
   for (int b = 0; b < nbatch; ++b)
-    a.own_slot[b] = b == 0 ? home_slot(cfg, c->step_first) : cfg.sink_frames + cfg.window_frames + b;
+    for (int t = 0; t < Tc; ++t) a.own_slot[b * Tc + t] = chunk_slot(cfg, c->step_first, b, t);
   a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
-  a.total_tiles = (a.nshared + 1) * a.tiles_per_frame;
-  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles);
-  a.qtiles = (int)((c->N + kQTile - 1) / kQTile);
+  a.total_tiles = (a.nshared + Tc) * a.tiles_per_frame;
+  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
+  a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * c->N;
+  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
   if (a.nsplit > 1) {
     const int64_t need = align_up(rows * cfg.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
     if (need > c->ws_bytes) return fail(SDV2_ENOSPC, "workspace too small for %d splits", a.nsplit);
@@ -462,7 +484,7 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
   }
   SDV2_HIP(launch_attention(a, cfg.head_dim, bf16, (hipStream_t)stream));
   if (a.nsplit > 1) {
-    CombineArgs m{a.part_o, a.part_ml, d_out, a.N, a.H, nbatch, a.nsplit};
+    CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.nsplit};
     SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));
   }
   return ok();
@@ -475,20 +497,22 @@ int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {
   for (int l = 0; l < cfg.num_layers; ++l)
     if (!c->appended[l]) return fail(SDV2_ESTATE, "layer %d not appended this step", l);
   if (chunk != c->step_first) return fail(SDV2_ESTATE, "only element 0 (chunk %lld) can be committed", (long long)c->step_first);
-  (void)stream;              // the appends already wrote the frame to its slot
-  const int64_t f = chunk;   // T' = 1
-  const int S = cfg.sink_frames, W = cfg.window_frames;
-  const int dst = home_slot(cfg, f);
-  if (f - W >= S) {          // frame f - W leaves the window
-    const int old = home_slot(cfg, f - W);
-    c->slot_written[old] = 0;
-    c->slot_frame[old] = -1;
+  (void)stream;              // the appends already wrote the frames to their slots
+  const int S = cfg.sink_frames, W = cfg.window_frames, Tc = cfg.chunk_frames;
+  for (int t = 0; t < Tc; ++t) {
+    const int64_t f = chunk * Tc + t;
+    if (f - W >= S) {        // frame f - W leaves the window
+      const int old = home_slot(cfg, f - W);
+      c->slot_written[old] = 0;
+      c->slot_frame[old] = -1;
+    }
+    const int dst = home_slot(cfg, f);
+    c->slot_frame[dst] = f;
+    c->slot_label[dst] = f - c->base;
+    c->slot_written[dst] = 1;
   }
-  c->slot_frame[dst] = f;
-  c->slot_label[dst] = f - c->base;
-  c->slot_written[dst] = 1;
   c->committed = chunk + 1;
-  c->last_commit_frame = f;
+  c->last_commit_frame = (chunk + 1) * Tc - 1;
   c->state = kCommitted;
   return ok();
 }
@@ -513,10 +537,12 @@ int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_
   a.D = cfg.embed_dim;
   a.tau = cfg.sink_threshold;
   const bool decide = frame >= S && tau_on(cfg);
-  if (frame < S) {
-    a.store_slot = (int)frame;
+  // the chunk's frames below S became sinks: h is their embedding
+  for (int64_t f = frame - cfg.chunk_frames + 1; f <= frame && f < S; ++f) {
+    a.store_slot = (int)f;
     SDV2_HIP(launch_sink_decide(a, s));
-  } else if (decide) {
+  }
+  if (decide) {
     a.store_slot = -1;
     SDV2_HIP(launch_sink_decide(a, s));
     CopyArgs cp{};
@@ -619,7 +645,7 @@ int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int
   if (first_chunk) *first_chunk = nb > 0 ? lo : -1;
   if (nbatch) *nbatch = (int32_t)nb;
   if (commit_chunk) *commit_chunk = (c0 >= 0 && c0 < num_chunks) ? c0 : -1;
-  if (newest_frame) *newest_frame = nb > 0 ? hi : -1;   // T' = 1
+  if (newest_frame) *newest_frame = nb > 0 ? (hi + 1) * cfg->chunk_frames - 1 : -1;
   return ok();
 }
 

@@ -22,7 +22,8 @@ class StreamRunner:
         self.cache = sdv2.Cache(cfg, device=device)
         self.dtype = torch.bfloat16 if cfg.dtype == sdv2.SDV2_BF16 else torch.float32
         self.N = cfg.grid_h * cfg.grid_w
-        self.out = torch.empty((cfg.num_layers, cfg.stream_batch, self.N, cfg.num_heads, cfg.head_dim),
+        self.rows = cfg.chunk_frames * self.N     # query rows per element: T' frames of N tokens
+        self.out = torch.empty((cfg.num_layers, cfg.stream_batch, self.rows, cfg.num_heads, cfg.head_dim),
                                dtype=self.dtype, device=device)
 
     @property
@@ -34,7 +35,7 @@ class StreamRunner:
 
     def step(self, s: int, qkv: Callable[[int, int, int], tuple], embed: Optional[Callable] = None,
              sink_sync: bool = True) -> dict:
-        """Run step s.  qkv(s, layer, nbatch) -> (q, k, v) device tensors [nbatch][N][H][d]
+        """Run step s.  qkv(s, layer, nbatch) -> (q, k, v) device tensors [nbatch][T'N][H][d]
         (q is rotated in place).  embed(chunk) -> fp32 device embedding or None."""
         first, nb, commit, newest = self.plan(s)
         info = {"first": first, "nbatch": nb, "commit": commit, "refreshed": 0, "sink": None}
@@ -50,5 +51,6 @@ class StreamRunner:
             if embed is not None and self.cfg.embed_dim > 0:
                 e = embed(commit)
                 if e is not None:
-                    info["sink"] = self.cache.sink_replace(commit, e, sync=sink_sync)
+                    last = (commit + 1) * self.cfg.chunk_frames - 1   # the chunk's last frame
+                    info["sink"] = self.cache.sink_replace(last, e, sync=sink_sync)
         return info

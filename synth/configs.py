@@ -121,5 +121,15 @@ WAN14B_40LAYER_B4 = StreamConfig(
     embed_dim=5120, sink_threshold=0.95, embed_kind="scenes", scene_change_prob=0.08,
     scene_noise=0.05)
 
-ALL = [TINY_FP32, WAN13B_1LAYER, WAN13B_30LAYER_B4, WAN13B_480P_B2, WAN14B_40LAYER_B4]
+# T' = 2 frames per chunk with B = 2: the same four frames per step as the B = 4 workload, with
+# block-causal attention inside each chunk ([WT] SLO-aware batching scheduler: chunk size T' and
+# stream batch B are the two latency knobs).
+WAN13B_30LAYER_T2B2 = StreamConfig(
+    name="wan13b_512_30layer_t2b2", cfg_id=6, num_layers=30, num_heads=12, head_dim=128,
+    grid_h=32, grid_w=32, sink_frames=1, window_frames=8, chunk_frames=2, stream_batch=2,
+    rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, rope_theta=10000.0, rope_refresh_period=0,
+    dtype="bf16", num_chunks=64, q_prescale=1.0, softmax_scale=1.0 / math.sqrt(128))
+
+ALL = [TINY_FP32, WAN13B_1LAYER, WAN13B_30LAYER_B4, WAN13B_480P_B2, WAN14B_40LAYER_B4,
+       WAN13B_30LAYER_T2B2]
 BY_NAME = {c.name: c for c in ALL}

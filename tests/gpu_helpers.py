@@ -140,13 +140,15 @@ class Harness:
         assert base == self.st.base and refreshes == r
         entries = [(j, e) for j, e in enumerate(self.st.sinks) if e is not None]
         entries += [(lib_slot(cfg, e.frame), e) for e in self.st.window]
-        # every other sink / ring slot is empty, or holds the staged (not yet committed) chunk
-        # written there by this step's append
+        # every other sink / ring slot is empty, or holds a frame of the staged (not yet
+        # committed) chunk written there by this step's append
         held = {slot for slot, _ in entries}
-        for slot in range(cfg.sink_frames + cfg.window_frames + 1):
+        T = cfg.chunk_frames
+        for slot in range(cfg.sink_frames + cfg.window_frames + T):
             if slot not in held:
                 f = cache.slot_info(slot)[0]
-                assert f == -1 or (f == committed and slot == lib_slot(cfg, committed)), (slot, f, committed)
+                assert f == -1 or (committed * T <= f < (committed + 1) * T and slot == lib_slot(cfg, f)), \
+                    (slot, f, committed)
         for layer in (self.layers if layers is None else layers):
             Kg, Vg = cache.k_view(layer), cache.v_view(layer)
             for slot, e in entries:
@@ -167,10 +169,10 @@ class Harness:
 
 def lib_slot(cfg, frame):
     """Physical slot of a committed frame in the library's cache layout (sdv2.h): sink slot f for
-    f < S, else ring slot S + f mod (W + 1).  The pages' ring has W slots; the library keeps one
-    spare so the frame being finished can be written in place."""
+    f < S, else ring slot S + f mod (W + T').  The pages' ring has W slots; the library keeps T'
+    spare ones so the chunk being finished can be written in place."""
     S, W = cfg.sink_frames, cfg.window_frames
-    return frame if frame < S else S + frame % (W + 1)
+    return frame if frame < S else S + frame % (W + cfg.chunk_frames)
 
 
 def sample_rows(N, n=40, seed=0):

@@ -63,6 +63,36 @@ def test_small_ragged_streams(kw):
     _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
 
 
+@pytest.mark.parametrize("kw", [
+    dict(dtype="fp32", chunk_frames=2, grid_h=5, grid_w=7, num_heads=2, sink_frames=1, window_frames=3,
+         stream_batch=2, rope_refresh_period=5, num_chunks=8, num_layers=2),
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, chunk_frames=3, grid_h=6,
+         grid_w=13, num_heads=3, sink_frames=2, window_frames=4, stream_batch=2, num_chunks=10, embed_dim=16,
+         sink_threshold=0.2, embed_kind="iid", softmax_scale=128 ** -0.5),
+    dict(dtype="bf16", chunk_frames=4, grid_h=9, grid_w=9, num_heads=2, sink_frames=0, window_frames=2,
+         stream_batch=2, num_chunks=7),
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, chunk_frames=2, grid_h=12,
+         grid_w=12, num_heads=4, sink_frames=1, window_frames=2, stream_batch=4, rope_refresh_period=3,
+         num_chunks=9, softmax_scale=128 ** -0.5),
+], ids=["fp32-T2-B2-refresh", "bf16-T3-sinks-straddle", "bf16-T4-W2-S0", "bf16-T2-B4-refresh"])
+def test_block_causal_chunks(kw):
+    # T' frames per chunk: block-causal own chunk, T' frames per append and commit, a chunk that
+    # straddles the sink boundary, a window shorter than the chunk, B * T' at its limit of 8
+    cfg = _small(**kw)
+    h = _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
+    if cfg.sink_threshold is not None:
+        assert len(h.decisions) == cfg.num_chunks
+
+
+def test_wan13b_30layer_t2b2_full_size():
+    # split-KV with block-causal query tiles: splits of frame-0 rows end before own frame 1
+    cfg = configs.WAN13B_30LAYER_T2B2
+    checked = {1, 9, 10}
+    rows = sample_rows(cfg.chunk_rows, n=32, seed=4)
+    _stream(cfg, 11, layers=(0, 29), check=lambda s: s in checked, rows=rows,
+            cache_check=lambda s: s in checked)
+
+
 def test_wan13b_single_layer_full_size():
     cfg = configs.WAN13B_1LAYER
     checked = {0, 1, 8, 9, 10, 31, 32, 33, cfg.num_steps - 1}

@@ -51,7 +51,7 @@ def test_workload_configs_validate_and_size(c):
     L = sdv2.sdv2_cache_layout(cfg)
     N = c.grid_h * c.grid_w
     assert L.tokens_padded % 64 == 0 and N <= L.tokens_padded < N + 64
-    assert L.slots == c.sink_frames + c.window_frames + c.stream_batch
+    assert L.slots == c.sink_frames + c.window_frames + c.stream_batch * c.chunk_frames
     assert L.layer_stride == 2 * L.slots * c.num_heads * L.tokens_padded * c.head_dim
     assert kv == c.num_layers * L.layer_stride * (2 if c.dtype == "bf16" else 4)
     assert meta > 0 and ws >= 0
@@ -69,7 +69,8 @@ def test_wan14b_cache_is_about_8_4_gb_plus_staging():
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, sdv2.SDV2_EINVAL), ("num_layers", 0, sdv2.SDV2_EINVAL),
-    ("window_frames", 0, sdv2.SDV2_EINVAL), ("chunk_frames", 2, sdv2.SDV2_EINVAL),
+    ("window_frames", 0, sdv2.SDV2_EINVAL), ("chunk_frames", 0, sdv2.SDV2_EINVAL),
+    ("chunk_frames", 9, sdv2.SDV2_EINVAL), ("window_frames", 63, sdv2.SDV2_EINVAL),
     ("stream_batch", 9, sdv2.SDV2_EINVAL), ("rope_dim_t", 46, sdv2.SDV2_EINVAL),
     ("rope_dim_h", 41, sdv2.SDV2_EINVAL), ("rope_theta", 1.0, sdv2.SDV2_EINVAL),
     ("dtype", 7, sdv2.SDV2_EINVAL), ("sink_frames", 17, sdv2.SDV2_EINVAL),
@@ -95,9 +96,26 @@ def test_sink_threshold_needs_embeddings():
     sdv2.sdv2_config_validate(cfg)
 
 
-@pytest.mark.parametrize("B,M", [(1, 5), (2, 7), (4, 6), (4, 2), (8, 11)])
-def test_plan_step_matches_oracle_schedule(B, M):
-    c = configs.WAN13B_1LAYER.with_(stream_batch=B, num_chunks=M)
+def test_chunk_frames_limits():
+    # B * T' <= 8 and S + W + T' <= 64; T' > 1 sizes T' slots per element
+    c = configs.WAN13B_1LAYER.with_(chunk_frames=2, stream_batch=4)
+    cfg = sdv2.config_of(c)
+    sdv2.sdv2_config_validate(cfg)
+    assert sdv2.sdv2_cache_layout(cfg).slots == 1 + 8 + 4 * 2
+    cfg.stream_batch = 5
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_config_validate(cfg)
+    cfg = sdv2.config_of(configs.WAN13B_1LAYER.with_(chunk_frames=8, window_frames=55, sink_frames=1))
+    sdv2.sdv2_config_validate(cfg)
+    cfg.window_frames = 56
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_config_validate(cfg)
+
+
+@pytest.mark.parametrize("B,M,T", [(1, 5, 1), (2, 7, 1), (4, 6, 1), (4, 2, 1), (8, 11, 1),
+                                   (1, 5, 2), (2, 7, 3), (4, 6, 2), (2, 3, 4)])
+def test_plan_step_matches_oracle_schedule(B, M, T):
+    c = configs.WAN13B_1LAYER.with_(stream_batch=B, num_chunks=M, chunk_frames=T)
     cfg = sdv2.config_of(c)
     for s in range(M + B + 1):
         first, nb, commit, newest = sdv2.sdv2_plan_step(cfg, M, s)
