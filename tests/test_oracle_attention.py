@@ -53,10 +53,12 @@ def test_no_eviction_equals_full_causal_history(B, T):
             np.testing.assert_allclose(outs[(s, 0, b)], brute.history_output(cfg, s, b, 0), atol=1e-12)
 
 
-@pytest.mark.parametrize("S,W,B", [(1, 4, 1), (2, 3, 2), (1, 2, 4), (0, 3, 1), (3, 1, 2)])
-def test_sink_and_window_match_history(S, W, B):
-    # keys = the first S frames + the last W committed non-sink frames + own chunk
-    cfg = tiny(sink_frames=S, window_frames=W, stream_batch=B, num_chunks=11)
+@pytest.mark.parametrize("S,W,B,T", [(1, 4, 1, 1), (2, 3, 2, 1), (1, 2, 4, 1), (0, 3, 1, 1), (3, 1, 2, 1),
+                                     (2, 3, 2, 2), (1, 2, 2, 3), (2, 4, 1, 3)])
+def test_sink_and_window_match_history(S, W, B, T):
+    # keys = the first S frames + the last W committed non-sink frames + own chunk (block-causal);
+    # T > 1 covers a window shorter than the chunk and a chunk straddling the sink boundary
+    cfg = tiny(sink_frames=S, window_frames=W, stream_batch=B, chunk_frames=T, num_chunks=11 if T == 1 else 7)
     st, outs = brute.run_oracle(cfg)
     for s in range(cfg.num_steps):
         for b in range(len(ost.schedule(cfg, s)["chunks"])):

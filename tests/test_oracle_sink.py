@@ -78,3 +78,25 @@ def test_replaced_sink_carries_the_frame_into_attention():
         sinks = [f for f in GOLDEN["sink_frames_after_chunk"][s - 1] if f is not None]
         np.testing.assert_allclose(outs[(s, 0, 0)], brute.history_output(cfg, s, 0, 0, sink_frames=sinks),
                                    atol=1e-12)
+
+
+def test_chunk_of_two_frames_decides_on_its_last_frame():
+    # T' = 2, S = 1: chunk 0 = frames 0, 1.  Frame 0 becomes the sink with e_0 = h_0; the decision
+    # on frame 1 compares h_0 with itself (alpha = 1, kept).  Chunk 1 (frames 2, 3) has h_1
+    # orthogonal to h_0 (alpha = 0 < tau): sink 0 takes frame 3, the chunk's last frame.  Chunk 2
+    # repeats h_1 (alpha = 1, kept).  Attention must then use frame 3 as the sink.
+    D = 8
+    h0 = np.zeros(D, np.float32); h0[0] = 1.0
+    h1 = np.zeros(D, np.float32); h1[1] = 1.0
+    emb = [h0, h1, h1, h1, h1]
+    cfg = TINY_FP32.with_(chunk_frames=2, stream_batch=1, sink_frames=1, window_frames=3, num_chunks=5,
+                          rope_refresh_period=0, embed_dim=D, sink_threshold=0.5, embed_kind="iid")
+    st, outs = brute.run_oracle(cfg, embed_fn=lambda c: emb[c])
+    got = [(d["chunk"], d["frame"], d["replaced"], d["alpha"]) for d in st.sink_log]
+    assert got == [(0, 1, False, 1.0), (1, 3, True, 0.0), (2, 5, False, 1.0), (3, 7, False, 1.0),
+                   (4, 9, False, 1.0)]
+    assert st.sinks[0].frame == 3
+    np.testing.assert_allclose(st.sink_embed[0], h1)
+    for s in range(2, cfg.num_steps):
+        np.testing.assert_allclose(outs[(s, 0, 0)], brute.history_output(cfg, s, 0, 0, sink_frames=[3]),
+                                   atol=1e-12)
