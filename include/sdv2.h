@@ -83,6 +83,8 @@ typedef struct sdv2_config {
   int32_t rope_refresh_period; /* T_reset >= 0; 0 = never */
   int32_t dtype;         /* SDV2_F32 | SDV2_BF16 */
   int32_t embed_dim;     /* D >= 0: chunk-embedding length; 0 = no sink refresh */
+  int32_t rope_pin_sinks; /* 0: a RoPE refresh rebases every cached key; 1: sinks keep their
+                             labels (pinned anchors), only the window is rebased */
   double sink_threshold; /* tau; NaN or -INFINITY = sink refresh off */
 } sdv2_config;
 
@@ -135,7 +137,9 @@ int sdv2_cache_destroy(sdv2_cache* cache);
  * frame index passes a threshold).  `newest_frame` is the last frame of the newest chunk in
  * flight this step (non-decreasing over calls).  While newest_frame - b0 >= T_reset, the RoPE
  * base b0 grows by T_reset and every cached key (sinks and window) is re-rotated in place by
- * -T_reset on the temporal pairs, so scores are unchanged.  *applied (may be NULL) receives
+ * -T_reset on the temporal pairs, so scores are unchanged.  With rope_pin_sinks the sinks are
+ * left as they are: their labels stay, so the query-to-sink distance drops by T_reset (the
+ * anchors are reset with the phase).  *applied (may be NULL) receives
  * the number of rebases.  Must open every step, also when T_reset == 0. */
 int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied, void* stream);
 

@@ -21,6 +21,9 @@ Sources and readings:
 * RoPE refresh ([WT] "自適應的sink和RoPE刷新": when the frame index passes a threshold the RoPE
   phase is reset).  Reading: at the start of a step, while the newest in-flight frame f_new
   satisfies f_new - b0 >= T_reset, b0 += T_reset and every cached label drops by T_reset.
+  Alternative reading (cfg.rope_pin_sinks; the same passage speaks of resetting the temporal
+  anchors): only the window's labels drop, the sinks keep theirs, so the distance from the
+  current frame to the sinks resets with the phase.
 * Sink refresh (same sub-section: cosine similarity of the new chunk embedding against the
   sink set; the least similar sink is refreshed when the similarity is below a threshold).
   Reading: after the commit of frame f >= S, alpha_j = cos(h, e_j), j* = argmin (lowest index
@@ -92,7 +95,8 @@ class OracleStream:
         f_new = self.plan["newest_frame"]
         while T_reset > 0 and f_new is not None and f_new - self.base >= T_reset:
             self.base += T_reset
-            for e in self.cached_entries():
+            moved = self.window if self.cfg.rope_pin_sinks else self.cached_entries()
+            for e in moved:
                 e.label -= T_reset
             self.refresh_log.append((s, self.base))
         return self.plan

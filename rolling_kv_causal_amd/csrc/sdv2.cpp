@@ -75,6 +75,7 @@ int validate(const sdv2_config* c) {
   if (c->rope_refresh_period < 0) return fail(SDV2_EINVAL, "rope_refresh_period must be >= 0");
   if (c->dtype != SDV2_F32 && c->dtype != SDV2_BF16) return fail(SDV2_EINVAL, "dtype must be F32 or BF16");
   if (c->embed_dim < 0) return fail(SDV2_EINVAL, "embed_dim must be >= 0");
+  if (c->rope_pin_sinks != 0 && c->rope_pin_sinks != 1) return fail(SDV2_EINVAL, "rope_pin_sinks must be 0 or 1");
   if (tau_on(*c) && (c->embed_dim < 1 || c->sink_frames < 1))
     return fail(SDV2_EINVAL, "sink refresh needs embed_dim >= 1 and sink_frames >= 1");
   return SDV2_OK;
@@ -331,8 +332,11 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
   int64_t count = 0;
   if (T > 0 && newest_frame - c->base >= T) count = (newest_frame - c->base) / T;
   if (count > 0) {
-    int slots[kMaxShared];
-    const int ns = shared_slots(c, slots);
+    // every attended slot, or only the window when the sinks are pinned
+    int all[kMaxShared], slots[kMaxShared], ns = 0;
+    const int na = shared_slots(c, all);
+    for (int i = 0; i < na; ++i)
+      if (!cfg.rope_pin_sinks || all[i] >= cfg.sink_frames) slots[ns++] = all[i];
     if (ns > 0 && cfg.rope_dim_t > 0) {
       RebaseArgs a{};
       a.kv = c->kv;
@@ -354,7 +358,7 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
     }
     c->base += count * T;
     c->refreshes += count;
-    for (int s = 0; s < shared_region(cfg); ++s)
+    for (int s = cfg.rope_pin_sinks ? cfg.sink_frames : 0; s < shared_region(cfg); ++s)
       if (c->slot_written[s]) c->slot_label[s] -= count * T;
   }
   c->started = true;

@@ -27,7 +27,8 @@ class Config(ctypes.Structure):
                 ("rope_dim_t", ctypes.c_int32), ("rope_dim_h", ctypes.c_int32),
                 ("rope_dim_w", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("rope_refresh_period", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("embed_dim", ctypes.c_int32), ("sink_threshold", ctypes.c_double)]
+                ("embed_dim", ctypes.c_int32), ("rope_pin_sinks", ctypes.c_int32),
+                ("sink_threshold", ctypes.c_double)]
 
 
 class Layout(ctypes.Structure):
@@ -108,12 +109,12 @@ def _stream(stream) -> int:
 def make_config(*, num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                 chunk_frames=1, stream_batch=1, rope_dim_t, rope_dim_h, rope_dim_w,
                 rope_theta=10000.0, rope_refresh_period=0, dtype="bf16", embed_dim=0,
-                sink_threshold=None, **_ignored) -> Config:
+                rope_pin_sinks=False, sink_threshold=None, **_ignored) -> Config:
     """Build the C config; dtype "bf16"/"fp32"; sink_threshold None = sink refresh off."""
     return Config(num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                   chunk_frames, stream_batch, rope_dim_t, rope_dim_h, rope_dim_w, float(rope_theta),
                   rope_refresh_period, SDV2_BF16 if dtype == "bf16" else SDV2_F32, embed_dim,
-                  float("nan") if sink_threshold is None else float(sink_threshold))
+                  int(bool(rope_pin_sinks)), float("nan") if sink_threshold is None else float(sink_threshold))
 
 
 def config_of(obj) -> Config:

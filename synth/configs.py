@@ -63,6 +63,7 @@ class StreamConfig:
     scene_change_prob: float = 0.0
     scene_noise: float = 0.0
     motion: Optional[MotionConfig] = None
+    rope_pin_sinks: bool = False      # refresh leaves the sinks' labels pinned (alternative reading)
 
     @property
     def tokens(self) -> int:          # N tokens per latent frame

@@ -62,23 +62,39 @@ def committed_frame_kv(cfg, frame, layer):
     return to_f64(cfg, k)[r:r + N], to_f64(cfg, v)[r:r + N]
 
 
-def history_output(cfg, s, elem, layer, sink_frames=None):
-    """Output of one element at step s from the frame history, for streams without RoPE refresh.
+def refresh_base(cfg, step):
+    """RoPE base b0 at a step, from the schedule alone: the largest multiple of T_reset not
+    above the newest in-flight frame (0 without refresh)."""
+    T_reset = cfg.rope_refresh_period
+    if T_reset == 0:
+        return 0
+    f_new = (min(step, cfg.num_chunks - 1) + 1) * cfg.chunk_frames - 1
+    return T_reset * (f_new // T_reset)
+
+
+def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False):
+    """Output of one element at step s from the frame history.
 
     Keys: sinks = the first S frames (or the frames listed in sink_frames), window = the last W
     committed non-sink frames, own chunk block-causal; every frame rotated at its absolute
-    index (no refresh, so b0 = 0).
+    index.  Without pinned_sinks the stream has no refresh.  With pinned_sinks the stream may
+    refresh and the sinks keep the label they had when committed, f - b0(commit step); since
+    scores depend only on position differences, that is a sink placed at absolute position
+    f - b0(commit step) + b0(s) against everything else at its absolute index.
     """
-    assert cfg.rope_refresh_period == 0
+    assert pinned_sinks or cfg.rope_refresh_period == 0
     T, N, B, S, W = cfg.chunk_frames, cfg.tokens, cfg.stream_batch, cfg.sink_frames, cfg.window_frames
     chunk = max(0, s - B + 1) + elem
     n_committed = max(0, s - B + 1) * T                    # frames of chunks already committed
     sinks = list(range(min(S, n_committed))) if sink_frames is None else list(sink_frames)
     frames = sinks + list(range(max(S, n_committed - W), n_committed))
     k_parts, v_parts, kf = [], [], []
-    for f in frames:
+    for i, f in enumerate(frames):
         k, v = committed_frame_kv(cfg, f, layer)
-        k_parts.append(frame_rope(cfg, k, f))
+        pos = f
+        if pinned_sinks and i < len(sinks):
+            pos = f - refresh_base(cfg, f // T + B - 1) + refresh_base(cfg, s)
+        k_parts.append(frame_rope(cfg, k, pos))
         v_parts.append(v)
         kf.append(np.full(N, -1))
     q, k, v = (to_f64(cfg, a) for a in inputs.qkv(cfg, s, layer, elem))

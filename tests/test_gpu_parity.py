@@ -84,6 +84,21 @@ def test_block_causal_chunks(kw):
         assert len(h.decisions) == cfg.num_chunks
 
 
+@pytest.mark.parametrize("kw", [
+    dict(dtype="fp32", rope_refresh_period=3, sink_frames=2, window_frames=3, stream_batch=2, num_chunks=12,
+         rope_pin_sinks=True),
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5, grid_w=13,
+         num_heads=3, sink_frames=1, window_frames=3, stream_batch=2, chunk_frames=2, rope_refresh_period=4,
+         num_chunks=10, embed_dim=16, sink_threshold=0.2, embed_kind="iid", softmax_scale=128 ** -0.5,
+         rope_pin_sinks=True),
+], ids=["fp32-pinned-refresh", "bf16-pinned-T2-sink-refresh"])
+def test_pinned_sink_refresh(kw):
+    # refresh rebases only the window; the sinks' labels (checked in the slot table) stay
+    cfg = _small(**kw)
+    h = _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
+    assert len(h.st.refresh_log) >= 2
+
+
 def test_wan13b_30layer_t2b2_full_size():
     # split-KV with block-causal query tiles: splits of frame-0 rows end before own frame 1
     cfg = configs.WAN13B_30LAYER_T2B2

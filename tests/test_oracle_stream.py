@@ -124,3 +124,37 @@ def test_commit_labels_and_window_contents_over_a_stream():
             assert [e.frame for e in st.window] == [f for f in committed if f >= 2][-3:]
             for e in st.cached_entries():
                 assert e.label == e.frame - st.base
+
+
+@pytest.mark.parametrize("S,B,T,period", [(1, 1, 1, 3), (2, 2, 1, 4), (2, 2, 2, 3), (1, 3, 1, 2)])
+def test_pinned_sinks_match_history(S, B, T, period):
+    # alternative refresh reading: the sinks keep their labels across refreshes.  Outputs must
+    # equal the history brute force with each sink placed at f - b0(commit step) + b0(step).
+    cfg = tiny(sink_frames=S, window_frames=3, stream_batch=B, chunk_frames=T, num_chunks=10,
+               rope_refresh_period=period, rope_pin_sinks=True)
+    st, outs = brute.run_oracle(cfg)
+    assert len(st.refresh_log) >= 2
+    for e in st.sinks:                            # the label at commit, never moved since
+        assert e.label == e.frame - brute.refresh_base(cfg, e.frame // T + B - 1)
+    for s in range(cfg.num_steps):
+        for b in range(len(ost.schedule(cfg, s)["chunks"])):
+            np.testing.assert_allclose(outs[(s, 0, b)], brute.history_output(cfg, s, b, 0, pinned_sinks=True),
+                                       atol=1e-12)
+
+
+def test_pinned_sinks_equal_rebased_sinks_without_refresh():
+    cfg = tiny(sink_frames=2, window_frames=3, stream_batch=2, num_chunks=8)
+    _, a = brute.run_oracle(cfg)
+    _, b = brute.run_oracle(cfg.with_(rope_pin_sinks=True))
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_pinned_and_rebased_sinks_part_at_the_first_refresh():
+    # the two readings agree until the first refresh (step 3: frame 3 reaches T_reset = 3) and
+    # differ afterwards, when the pinned sinks sit closer to the query
+    cfg = tiny(sink_frames=1, window_frames=3, num_chunks=10, rope_refresh_period=3)
+    _, a = brute.run_oracle(cfg)
+    _, b = brute.run_oracle(cfg.with_(rope_pin_sinks=True))
+    differ = sorted(k[0] for k in a if not np.allclose(a[k], b[k], atol=1e-9))
+    assert differ and differ[0] == 3
