@@ -226,6 +226,26 @@ def calibration_copy(nbytes=1 << 30):
     log(f"bench: calibration copy of {nbytes} bytes done")
 
 
+SLO_GRID = [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2), (1, 4), (2, 4), (1, 8)]
+
+
+def slo_table(base, steps, warmup, target_fps, deadline_s):
+    """Measured step latency L(B, T') of a workload over a (B, T') grid, the library's fit
+    L = c0 + c1 B T' and its SLO-aware choice ([WT] SLO-aware batching scheduler)."""
+    from rolling_kv_causal_amd import sdv2
+    rows = []
+    for B, T in SLO_GRID:
+        c = base.with_(stream_batch=B, chunk_frames=T, num_chunks=max(64, 4 * B))
+        g = run_gpu(c, steps, warmup)
+        rows.append({"B": B, "T": T, "frames": B * T, "ms_per_step": round(g["ms_per_step"], 4),
+                     "fps": round(B * T / (g["ms_per_step"] * 1e-3), 1)})
+        log(f"bench: slo B={B} T'={T} {g['ms_per_step']:.3f} ms/step")
+    c0, c1 = sdv2.sdv2_latency_fit([r["frames"] for r in rows], [r["ms_per_step"] * 1e-3 for r in rows])
+    pick = sdv2.sdv2_slo_select(c0, c1, target_fps, deadline_s, 8, 8, 8)
+    return {"workload": base.name, "grid": rows, "fit_c0_s": c0, "fit_c1_s_per_frame": c1,
+            "target_fps": target_fps, "deadline_s": deadline_s, "choice": pick}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +255,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a 1 GiB plain copy first (scales HBM counters in rocprofv3 runs)")
+    ap.add_argument("--slo-table", action="store_true",
+                    help="measure L(B, T') over a grid on --workload, fit it and print the SLO-aware choice")
+    ap.add_argument("--pin-sinks", action="store_true",
+                    help="pinned-sink RoPE refresh: the refresh rebases only the window")
+    ap.add_argument("--target-fps", type=float, default=30.0)
+    ap.add_argument("--deadline-ms", type=float, default=100.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -245,6 +271,12 @@ def main():
 
     from synth import configs
     c = configs.BY_NAME[args.workload]
+    if args.pin_sinks:
+        c = c.with_(rope_pin_sinks=True)
+    if args.slo_table:
+        print(json.dumps(slo_table(c, min(args.steps, 20), min(args.warmup, 5), args.target_fps,
+                                   args.deadline_ms * 1e-3)), flush=True)
+        return
     wn = workload_numbers(c)
     log(f"bench: workload {c.name}, {args.steps} timed steps after {args.warmup} warmup")
     if args.calibration_copy:
@@ -266,7 +298,7 @@ def main():
                    "head_dim": c.head_dim, "tokens_per_frame": c.tokens, "sink_frames": c.sink_frames,
                    "window_frames": c.window_frames, "chunk_frames": c.chunk_frames,
                    "stream_batch": c.stream_batch, "keys_per_query": wn["keys"],
-                   "rope_refresh_period": c.rope_refresh_period,
+                   "rope_refresh_period": c.rope_refresh_period, "rope_pin_sinks": c.rope_pin_sinks,
                    "sink_threshold": c.sink_threshold, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,

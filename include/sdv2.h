@@ -198,6 +198,25 @@ int sdv2_motion_l2(const float* d_frames, int32_t nframes, int64_t elems_per_fra
 int sdv2_noise_schedule(const double* h_dist, int32_t n, double sigma, int32_t k, double lambda,
                         double s_min, double s_max, double s0, double* h_rate);
 
+/* SLO-aware choice of stream batch B and chunk size T' ([WT] SLO-aware batching scheduler: the
+ * step latency L(T', B) is parameter plus activation traffic over an effective bandwidth, the
+ * activations growing linearly in B*T'; f = B*T'/L; B*T' must not exceed the frames collected).
+ * Host only.
+ * sdv2_latency_fit: least-squares L = c0 + c1 * frames from n >= 2 measured steps (frames =
+ *   B*T' of each, at least two distinct values; latency in seconds).
+ * sdv2_slo_select: over 1 <= B <= max_batch, 1 <= T' <= max_chunk with B*T' <= frames_ready and
+ *   B*T' <= SDV2_MAX_BATCH: L = c0 + c1*B*T', f = B*T'/L, a frame's latency = B*L (its chunk is in
+ *   flight for B steps) + (T'-1)/target_fps (waiting for its chunk's frames).  Feasible: f >=
+ *   target_fps and latency <= deadline_s.  Returns the feasible candidate of highest f (f within a
+ *   relative 1e-12 counts as equal; ties: lower latency, then smaller B) with *feasible = 1, else
+ *   the highest-f candidate with *feasible = 0.  Outputs may be NULL except B and T.  Errors:
+ *   SDV2_EINVAL if a candidate's L <= 0, target_fps <= 0 or no candidate exists. */
+int sdv2_latency_fit(const int32_t* h_frames, const double* h_latency_s, int32_t n, double* c0,
+                     double* c1);
+int sdv2_slo_select(double c0, double c1, double target_fps, double deadline_s, int32_t frames_ready,
+                    int32_t max_batch, int32_t max_chunk, int32_t* B, int32_t* T, double* fps,
+                    double* latency_s, int32_t* feasible);
+
 /* Host bookkeeping of one slot: committed frame (-1 empty, -2 unknown after an unsynchronised
  * sink decision) and its temporal RoPE position label = frame - b0 at commit, shifted by every
  * later rebase.  A slot written by an append and not (yet) committed reports the chunk staged

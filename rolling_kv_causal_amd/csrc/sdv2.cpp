@@ -618,6 +618,62 @@ int sdv2_noise_schedule(const double* h_dist, int32_t n, double sigma, int32_t k
   return ok();
 }
 
+int sdv2_latency_fit(const int32_t* h_frames, const double* h_latency_s, int32_t n, double* c0,
+                     double* c1) {
+  if (n < 2 || !h_frames || !h_latency_s || !c0 || !c1)
+    return fail(SDV2_EINVAL, "need n >= 2 measurements and non-NULL arrays");
+  double mx = 0.0, my = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    mx += h_frames[i];
+    my += h_latency_s[i];
+  }
+  mx /= n;
+  my /= n;
+  double sxx = 0.0, sxy = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double dx = h_frames[i] - mx;
+    sxx += dx * dx;
+    sxy += dx * (h_latency_s[i] - my);
+  }
+  if (!(sxx > 0.0)) return fail(SDV2_EINVAL, "the measurements need at least two distinct frame counts");
+  *c1 = sxy / sxx;
+  *c0 = my - *c1 * mx;
+  return ok();
+}
+
+int sdv2_slo_select(double c0, double c1, double target_fps, double deadline_s, int32_t frames_ready,
+                    int32_t max_batch, int32_t max_chunk, int32_t* B, int32_t* T, double* fps,
+                    double* latency_s, int32_t* feasible) {
+  if (!B || !T) return fail(SDV2_EINVAL, "B and T must not be NULL");
+  if (!(target_fps > 0.0)) return fail(SDV2_EINVAL, "target_fps must be > 0");
+  const int32_t cap = frames_ready < kMaxBatch ? frames_ready : kMaxBatch;
+  struct Cand { int b, t; double f, lat; };
+  Cand best{0, 0, 0.0, 0.0}, best_any{0, 0, 0.0, 0.0};
+  bool have = false, have_any = false;
+  auto better = [](const Cand& c, const Cand& ref) {
+    if (c.f > ref.f * (1.0 + 1e-12)) return true;
+    if (c.f < ref.f * (1.0 - 1e-12)) return false;
+    return c.lat < ref.lat || (c.lat == ref.lat && c.b < ref.b);
+  };
+  for (int b = 1; b <= max_batch; ++b)
+    for (int t = 1; t <= max_chunk; ++t) {
+      if (b * t > cap) continue;
+      const double L = c0 + c1 * b * t;
+      if (!(L > 0.0)) return fail(SDV2_EINVAL, "latency model gives L <= 0 at B*T' = %d", b * t);
+      const Cand c{b, t, b * t / L, b * L + (t - 1) / target_fps};
+      if (!have_any || better(c, best_any)) best_any = c, have_any = true;
+      if (c.f >= target_fps && c.lat <= deadline_s && (!have || better(c, best))) best = c, have = true;
+    }
+  if (!have_any) return fail(SDV2_EINVAL, "no (B, T') candidate: check frames_ready, max_batch, max_chunk");
+  const Cand& r = have ? best : best_any;
+  *B = r.b;
+  *T = r.t;
+  if (fps) *fps = r.f;
+  if (latency_s) *latency_s = r.lat;
+  if (feasible) *feasible = have ? 1 : 0;
+  return ok();
+}
+
 int sdv2_cache_slot_info(const sdv2_cache* c, int32_t slot, int64_t* frame, int32_t* tpos) {
   if (int rc = check_cache(c)) return rc;
   if (slot < 0 || slot >= c->lay.slots) return fail(SDV2_EINVAL, "slot %d out of range", slot);

@@ -60,6 +60,8 @@ _PROTOS = {
     "sdv2_motion_workspace_size": [_I32, _I64, ctypes.POINTER(_SZ)],
     "sdv2_motion_l2": [_P, _I32, _I64, _P, _P, _SZ, _P],
     "sdv2_noise_schedule": [_P, _I32, _D, _I32, _D, _D, _D, _D, _P],
+    "sdv2_latency_fit": [_P, _P, _I32, _P, _P],
+    "sdv2_slo_select": [_D, _D, _D, _D, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "sdv2_cache_slot_info": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)],
     "sdv2_cache_state": [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "sdv2_plan_step": [ctypes.POINTER(Config), _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I32),
@@ -188,6 +190,24 @@ def sdv2_motion_workspace_size(nframes: int, elems_per_frame: int) -> int:
 def sdv2_motion_l2(frames, nframes: int, elems_per_frame: int, dist, workspace, stream=None) -> None:
     _call("sdv2_motion_l2", _ptr(frames), nframes, elems_per_frame, _ptr(dist), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def sdv2_latency_fit(frames, latency_s) -> tuple[float, float]:
+    n = len(frames)
+    f = (ctypes.c_int32 * max(n, 1))(*frames)
+    y = (ctypes.c_double * max(n, 1))(*latency_s)
+    c0, c1 = _D(), _D()
+    _call("sdv2_latency_fit", ctypes.cast(f, _P), ctypes.cast(y, _P), n, ctypes.addressof(c0), ctypes.addressof(c1))
+    return c0.value, c1.value
+
+
+def sdv2_slo_select(c0, c1, target_fps, deadline_s, frames_ready, max_batch, max_chunk) -> dict:
+    B, T, feas = _I32(), _I32(), _I32()
+    fps, lat = _D(), _D()
+    _call("sdv2_slo_select", c0, c1, target_fps, deadline_s, frames_ready, max_batch, max_chunk,
+          ctypes.addressof(B), ctypes.addressof(T), ctypes.addressof(fps), ctypes.addressof(lat),
+          ctypes.addressof(feas))
+    return {"B": B.value, "T": T.value, "fps": fps.value, "latency": lat.value, "feasible": bool(feas.value)}
 
 
 def sdv2_noise_schedule(dist, sigma: float, k: int, lam: float, s_min: float, s_max: float, s0: float):

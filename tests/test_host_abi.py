@@ -148,3 +148,36 @@ def test_null_handle_and_bad_arguments_fail_cleanly():
         sdv2.sdv2_cache_slot_info(None, 0)
     assert e.value.code == sdv2.SDV2_EINVAL
     sdv2.sdv2_cache_destroy(None)
+
+
+def test_latency_fit_and_slo_select_match_the_oracle():
+    from oracle import slo
+    g = np.random.default_rng(7)
+    for _ in range(300):
+        n = int(g.integers(2, 9))
+        frames = [int(x) for x in g.integers(1, 9, n)]
+        if len(set(frames)) < 2:
+            frames[-1] = frames[0] % 8 + 1
+        lat = [0.002 + 0.001 * x + float(g.normal(0, 2e-4)) for x in frames]
+        c0, c1 = sdv2.sdv2_latency_fit(frames, lat)
+        o0, o1 = slo.fit_latency(frames, lat)
+        assert c0 == pytest.approx(o0, abs=1e-12) and c1 == pytest.approx(o1, abs=1e-12)
+        c0, c1 = abs(c0) + 1e-4, abs(c1)
+        args = (float(g.uniform(10, 2000)), float(g.uniform(0.005, 0.2)), int(g.integers(1, 10)),
+                int(g.integers(1, 9)), int(g.integers(1, 9)))
+        got = sdv2.sdv2_slo_select(c0, c1, *args)
+        want = slo.select(c0, c1, *args)
+        assert (got["B"], got["T"], got["feasible"]) == (want["B"], want["T"], want["feasible"])
+        assert got["fps"] == pytest.approx(want["fps"], rel=1e-12)
+        assert got["latency"] == pytest.approx(want["latency"], rel=1e-12)
+
+
+def test_slo_select_errors():
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_latency_fit([2, 2, 2], [0.1, 0.2, 0.3])         # one distinct frame count
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_slo_select(-0.01, 0.001, 100.0, 1.0, 8, 8, 8)    # L <= 0 for small B T'
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_slo_select(0.01, 0.001, 0.0, 1.0, 8, 8, 8)       # target_fps <= 0
+    with pytest.raises(sdv2.SDV2Error):
+        sdv2.sdv2_slo_select(0.01, 0.001, 100.0, 1.0, 0, 8, 8)     # no frames ready
