@@ -29,6 +29,12 @@ Sources and readings:
   Reading: after the commit of frame f >= S, alpha_j = cos(h, e_j), j* = argmin (lowest index
   on ties); if alpha_j* < tau the sink j* takes frame f's (K, V, label) for all layers and
   e_j* = h.  Frame f also stays in the window.
+* FP8 cache (cfg.kv_fp8; [REPO] future work and [WT] trade-offs name an FP8 KV cache without a
+  format).  Reading: the cache holds what the exact stream would hold, each element rounded to
+  OCP e4m3 (oracle.fp8): a key is rotated at its label and then rounded, a value is rounded;
+  this covers the chunk's own frames as well, since they are read from the cache.  A RoPE
+  refresh turns each stored key's temporal pairs by -T_reset and rounds again (the stored
+  keys are all the cache has).  Queries, scores and outputs keep their own precision.
 """
 from __future__ import annotations
 
@@ -37,6 +43,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from . import fp8 as ofp8
 from . import rope
 from .attention import attention
 from .sink import decide
@@ -70,7 +77,8 @@ def ring_slot(cfg, frame: int) -> int:
 class Entry:
     frame: int
     label: int                                   # temporal RoPE position of the cached frame
-    kv: dict = field(default_factory=dict)       # layer -> (K_raw [N,H,d], V [N,H,d]) float64
+    # layer -> (K, V) float64 [N,H,d]: K raw (pre-RoPE), or rotated at `label` and e4m3 in FP8 mode
+    kv: dict = field(default_factory=dict)
 
 
 class OracleStream:
@@ -85,6 +93,7 @@ class OracleStream:
         self.sink_log: list[dict] = []
         self.step = -1
         self.plan = None
+        self.kv_fp8 = bool(getattr(cfg, "kv_fp8", False))
 
     # ---- step start: schedule + RoPE refresh ---------------------------------------------
     def begin_step(self, s: int) -> dict:
@@ -98,8 +107,28 @@ class OracleStream:
             moved = self.window if self.cfg.rope_pin_sinks else self.cached_entries()
             for e in moved:
                 e.label -= T_reset
+                if self.kv_fp8:
+                    e.kv = {layer: (self._turn_back(K, T_reset), V) for layer, (K, V) in e.kv.items()}
             self.refresh_log.append((s, self.base))
         return self.plan
+
+    def _turn_back(self, K: np.ndarray, T_reset: int) -> np.ndarray:
+        """Stored (rotated, e4m3) keys of a frame whose label drops by T_reset: the temporal
+        pairs turn by -T_reset * omega (the row and column pairs by angle 0), then round."""
+        phi = rope.angles(self.cfg, -float(T_reset), 0.0, 0.0)
+        return ofp8.round_fp8(rope.rotate_pairs(K, phi))
+
+    def _stored(self, K_raw: np.ndarray, V: np.ndarray, label: int):
+        """What the cache keeps for a frame at a label: raw K and V (exact mode, RoPE applied
+        when attending), or the rotated key and the value rounded to e4m3."""
+        if self.kv_fp8:
+            return ofp8.round_fp8(rope.rope_frame(self.cfg, K_raw, label)), ofp8.round_fp8(V)
+        return K_raw, V
+
+    def key_rot(self, e: Entry, layer: int, heads=slice(None)) -> np.ndarray:
+        """Rotated key of a cached entry at its label (the given heads)."""
+        K = e.kv[layer][0][:, heads]
+        return K if self.kv_fp8 else rope.rope_frame(self.cfg, K, e.label)
 
     def cached_entries(self) -> list[Entry]:
         """Distinct cached entries: present sinks, then the window (oldest first)."""
@@ -116,19 +145,20 @@ class OracleStream:
         chunk = self.plan["chunks"][elem]
         rows = np.arange(T * N) if rows is None else np.asarray(rows)
         heads = np.arange(cfg.num_heads) if heads is None else np.asarray(heads)
-        qd, kd, vd = decode(cfg, q), decode(cfg, k), decode(cfg, v)
+        # heads are independent: only the requested ones are formed
+        qd, kd, vd = (decode(cfg, x)[:, heads] for x in (q, k, v))
 
         # keys: cached entries at their labels, then the own chunk's frames at f - b0
         k_parts, v_parts, key_frame = [], [], []
         for e in self.cached_entries():
-            K_raw, V = e.kv[layer]
-            k_parts.append(rope.rope_frame(cfg, K_raw, e.label))
-            v_parts.append(V)
+            k_parts.append(self.key_rot(e, layer, heads))
+            v_parts.append(e.kv[layer][1][:, heads])
             key_frame.append(np.full(N, -1))                     # always visible
         own_frames = [chunk * T + t for t in range(T)]
         for t, g in enumerate(own_frames):
-            k_parts.append(rope.rope_frame(cfg, kd[t * N:(t + 1) * N], g - self.base))
-            v_parts.append(vd[t * N:(t + 1) * N])
+            own = self._stored(kd[t * N:(t + 1) * N], vd[t * N:(t + 1) * N], g - self.base)
+            k_parts.append(own[0] if self.kv_fp8 else rope.rope_frame(cfg, own[0], g - self.base))
+            v_parts.append(own[1])
             key_frame.append(np.full(N, g))
         K_all = np.concatenate(k_parts)                            # [L, H, d]
         V_all = np.concatenate(v_parts)
@@ -141,8 +171,8 @@ class OracleStream:
         mask = key_frame[None, :] <= q_frame[:, None]              # block-causal own chunk
 
         out = np.empty((len(rows), len(heads), cfg.head_dim))
-        for i, h in enumerate(heads):
-            out[:, i], _ = attention(Q_rot[:, h], K_all[:, h], V_all[:, h], cfg.softmax_scale, mask)
+        for i in range(len(heads)):
+            out[:, i], _ = attention(Q_rot[:, i], K_all[:, i], V_all[:, i], cfg.softmax_scale, mask)
         return out
 
     # ---- step end: commit + sink refresh ---------------------------------------------------
@@ -160,7 +190,8 @@ class OracleStream:
             entry = Entry(frame=f, label=f - self.base)
             for layer in self.layers:
                 k, v = commit_kv[layer]
-                entry.kv[layer] = (decode(cfg, k)[t * N:(t + 1) * N], decode(cfg, v)[t * N:(t + 1) * N])
+                entry.kv[layer] = self._stored(decode(cfg, k)[t * N:(t + 1) * N],
+                                               decode(cfg, v)[t * N:(t + 1) * N], entry.label)
             if f < S:
                 self.sinks[f] = entry
                 self.sink_embed[f] = h

@@ -64,6 +64,7 @@ class StreamConfig:
     scene_noise: float = 0.0
     motion: Optional[MotionConfig] = None
     rope_pin_sinks: bool = False      # refresh leaves the sinks' labels pinned (alternative reading)
+    kv_fp8: bool = False              # bf16 activations with an OCP e4m3 KV cache
 
     @property
     def tokens(self) -> int:          # N tokens per latent frame

@@ -53,6 +53,16 @@ def sdpa(q, k, v, scale, mask=None):
     return np.moveaxis(o.numpy(), 0, 1)
 
 
+def round_e4m3(x):
+    """Round to OCP e4m3 another way than oracle.fp8's table search: scale by the quantum of x's
+    binade (3 mantissa bits; the subnormal quantum 2^-9 below 2^-6), round half to even,
+    saturate at 448."""
+    x = np.asarray(x, np.float64)
+    _, e = np.frexp(x)                                  # |x| in [2^(e-1), 2^e)
+    q = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    return np.clip(np.round(x / q) * q, -448.0, 448.0)
+
+
 def committed_frame_kv(cfg, frame, layer):
     """K, V (float64 [N,H,d]) of a frame as committed: element 0's inputs at step c + B - 1."""
     T, N, B = cfg.chunk_frames, cfg.tokens, cfg.stream_batch
@@ -72,7 +82,7 @@ def refresh_base(cfg, step):
     return T_reset * (f_new // T_reset)
 
 
-def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False):
+def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False, fp8=False):
     """Output of one element at step s from the frame history.
 
     Keys: sinks = the first S frames (or the frames listed in sink_frames), window = the last W
@@ -81,7 +91,15 @@ def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False):
     refresh and the sinks keep the label they had when committed, f - b0(commit step); since
     scores depend only on position differences, that is a sink placed at absolute position
     f - b0(commit step) + b0(s) against everything else at its absolute index.
+
+    fp8: the e4m3 cache, where rounding makes scores depend on the labels themselves, so every
+    position is taken relative to b0(s).  A cached key is rotated at its commit-time label
+    f - b0(commit step), rounded, then turned back by T_reset and rounded once per refresh
+    since; values and the own chunk's keys are rounded once.
     """
+    if fp8:
+        assert not pinned_sinks
+        return _history_output_fp8(cfg, s, elem, layer, sink_frames)
     assert pinned_sinks or cfg.rope_refresh_period == 0
     T, N, B, S, W = cfg.chunk_frames, cfg.tokens, cfg.stream_batch, cfg.sink_frames, cfg.window_frames
     chunk = max(0, s - B + 1) + elem
@@ -104,6 +122,36 @@ def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False):
         v_parts.append(v[t * N:(t + 1) * N])
         kf.append(np.full(N, g))
     q_rot = np.concatenate([frame_rope(cfg, q[t * N:(t + 1) * N], chunk * T + t) for t in range(T)])
+    qf = chunk * T + np.arange(T * N) // N
+    mask = np.concatenate(kf)[None, :] <= qf[:, None]
+    return sdpa(q_rot, np.concatenate(k_parts), np.concatenate(v_parts), cfg.softmax_scale, mask)
+
+
+def _history_output_fp8(cfg, s, elem, layer, sink_frames):
+    T, N, B, S, W = cfg.chunk_frames, cfg.tokens, cfg.stream_batch, cfg.sink_frames, cfg.window_frames
+    T_reset = cfg.rope_refresh_period
+    chunk = max(0, s - B + 1) + elem
+    n_committed = max(0, s - B + 1) * T
+    sinks = list(range(min(S, n_committed))) if sink_frames is None else list(sink_frames)
+    frames = sinks + list(range(max(S, n_committed - W), n_committed))
+    b_s = refresh_base(cfg, s)
+    k_parts, v_parts, kf = [], [], []
+    for f in frames:
+        k, v = committed_frame_kv(cfg, f, layer)
+        b_c = refresh_base(cfg, f // T + B - 1)
+        key = round_e4m3(frame_rope(cfg, k, f - b_c))
+        for _ in range((b_s - b_c) // T_reset if T_reset else 0):
+            key = round_e4m3(complex_rope(cfg, key, -T_reset, 0, 0))
+        k_parts.append(key)
+        v_parts.append(round_e4m3(v))
+        kf.append(np.full(N, -1))
+    q, k, v = (to_f64(cfg, a) for a in inputs.qkv(cfg, s, layer, elem))
+    for t in range(T):
+        g = chunk * T + t
+        k_parts.append(round_e4m3(frame_rope(cfg, k[t * N:(t + 1) * N], g - b_s)))
+        v_parts.append(round_e4m3(v[t * N:(t + 1) * N]))
+        kf.append(np.full(N, g))
+    q_rot = np.concatenate([frame_rope(cfg, q[t * N:(t + 1) * N], chunk * T + t - b_s) for t in range(T)])
     qf = chunk * T + np.arange(T * N) // N
     mask = np.concatenate(kf)[None, :] <= qf[:, None]
     return sdpa(q_rot, np.concatenate(k_parts), np.concatenate(v_parts), cfg.softmax_scale, mask)
