@@ -48,13 +48,14 @@ def workload_numbers(c):
     N = c.tokens
     L = (c.sink_frames + c.window_frames + c.chunk_frames) * N
     B = c.stream_batch
-    eb = 2 if c.dtype == "bf16" else 4
+    eb = 2 if c.dtype == "bf16" else 4                 # activations (Q, O)
+    kb = 1 if c.kv_fp8 else eb                          # cache elements (K, V)
     flops_layer = 4 * B * c.num_heads * N * c.head_dim * sum(visible_keys(c, t) for t in range(c.chunk_frames))
     # algorithmic bytes of one attention call: Q + O, the shared sink+window K/V read once, and
     # each element's own chunk K/V
     qo = 2 * B * c.chunk_rows * c.num_heads * c.head_dim * eb
-    shared = 2 * (c.sink_frames + c.window_frames) * N * c.num_heads * c.head_dim * eb
-    own = 2 * B * c.chunk_rows * c.num_heads * c.head_dim * eb
+    shared = 2 * (c.sink_frames + c.window_frames) * N * c.num_heads * c.head_dim * kb
+    own = 2 * B * c.chunk_rows * c.num_heads * c.head_dim * kb
     return {"keys": L, "flops_per_layer": flops_layer, "attn_bytes_per_layer": qo + shared + own}
 
 
@@ -259,6 +260,8 @@ def main():
                     help="measure L(B, T') over a grid on --workload, fit it and print the SLO-aware choice")
     ap.add_argument("--pin-sinks", action="store_true",
                     help="pinned-sink RoPE refresh: the refresh rebases only the window")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="OCP e4m3 KV cache (bf16 queries, scores and outputs)")
     ap.add_argument("--target-fps", type=float, default=30.0)
     ap.add_argument("--deadline-ms", type=float, default=100.0)
     args = ap.parse_args()
@@ -273,6 +276,8 @@ def main():
     c = configs.BY_NAME[args.workload]
     if args.pin_sinks:
         c = c.with_(rope_pin_sinks=True)
+    if args.kv_fp8:
+        c = c.with_(kv_fp8=True, name=c.name + "_kvfp8")
     if args.slo_table:
         print(json.dumps(slo_table(c, min(args.steps, 20), min(args.warmup, 5), args.target_fps,
                                    args.deadline_ms * 1e-3)), flush=True)
@@ -299,10 +304,12 @@ def main():
                    "window_frames": c.window_frames, "chunk_frames": c.chunk_frames,
                    "stream_batch": c.stream_batch, "keys_per_query": wn["keys"],
                    "rope_refresh_period": c.rope_refresh_period, "rope_pin_sinks": c.rope_pin_sinks,
+                   "kv_cache": "e4m3" if c.kv_fp8 else c.dtype,
                    "sink_threshold": c.sink_threshold, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "sdv2_chunk_attention (attn_bf16_kernel + combine_kernel)",
+                     "kernel": "sdv2_chunk_attention (attn_bf16_kernel%s + combine_kernel)"
+                               % ("<128, e4m3 cache>" if c.kv_fp8 else ""),
                      "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3)},
         "chunk_attention_calls_per_s": round(c.num_layers / (ms * 1e-3), 1),
         "latent_frames_per_s": round(c.chunk_frames / (ms * 1e-3), 2),

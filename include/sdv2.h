@@ -56,7 +56,12 @@ enum {
   SDV2_ENOSPC = -4  /* a caller buffer is smaller than sdv2_cache_size() asks for */
 };
 
-enum { SDV2_F32 = 0, SDV2_BF16 = 1 };
+enum {
+  SDV2_F32 = 0,          /* fp32 activations and cache */
+  SDV2_BF16 = 1,         /* bf16 activations and cache */
+  SDV2_BF16_KV_FP8 = 2   /* bf16 activations, OCP e4m3 cache (head_dim 128): K_rot and V are
+                            rounded to nearest even, saturated at +-448; fp32 accumulation */
+};
 
 /* Library limits (validated by sdv2_config_validate). */
 enum {
@@ -81,14 +86,14 @@ typedef struct sdv2_config {
   int32_t rope_dim_w;
   double rope_theta;     /* > 1 */
   int32_t rope_refresh_period; /* T_reset >= 0; 0 = never */
-  int32_t dtype;         /* SDV2_F32 | SDV2_BF16 */
+  int32_t dtype;         /* SDV2_F32 | SDV2_BF16 | SDV2_BF16_KV_FP8 */
   int32_t embed_dim;     /* D >= 0: chunk-embedding length; 0 = no sink refresh */
   int32_t rope_pin_sinks; /* 0: a RoPE refresh rebases every cached key; 1: sinks keep their
                              labels (pinned anchors), only the window is rebased */
   double sink_threshold; /* tau; NaN or -INFINITY = sink refresh off */
 } sdv2_config;
 
-/* Device layout of the KV cache (element offsets from d_kv, element = 2 or 4 bytes).
+/* Device layout of the KV cache (element offsets from d_kv, element = 4, 2 or 1 bytes).
  * Slots [0,S) are sinks, [S,S+W+T') the ring (frame f >= S lives in slot S + f mod (W+T');
  * W of these slots hold the window, the T' spare ones receive the chunk being finished), and
  * [S+W+T', S+W+B*T') the staging slots of stream-batch elements 1..B-1 (frame t of element b
@@ -98,11 +103,13 @@ typedef struct sdv2_config {
  *   V of (layer, slot, head, token n, dim i): v_offset(layer) + slot*slot_stride
  *        + head*head_stride + i*tokens_padded + n                 (stored transposed)
  * with k_offset(l) = l*layer_stride, v_offset(l) = l*layer_stride + slot_stride*slots.
+ * e4m3 cache: within each group of 32 dims of a K row, and of 32 tokens of a V^T row inside a
+ * 64-token tile, element 32p + 16h + 8g + e is stored at 32p + 16g + 8h + e.
  * Tokens n in [N, tokens_padded) are zero padding. */
 typedef struct sdv2_layout {
   int64_t slots;          /* S + (W + T') + (B - 1) T' */
   int64_t tokens_padded;  /* N rounded up to 64 */
-  int64_t elem_bytes;     /* 4 (fp32) or 2 (bf16) */
+  int64_t elem_bytes;     /* 4 (fp32), 2 (bf16) or 1 (e4m3) */
   int64_t head_stride;    /* tokens_padded * head_dim */
   int64_t slot_stride;    /* num_heads * head_stride */
   int64_t layer_stride;   /* 2 * slots * slot_stride (K block then V block) */
@@ -137,7 +144,9 @@ int sdv2_cache_destroy(sdv2_cache* cache);
  * frame index passes a threshold).  `newest_frame` is the last frame of the newest chunk in
  * flight this step (non-decreasing over calls).  While newest_frame - b0 >= T_reset, the RoPE
  * base b0 grows by T_reset and every cached key (sinks and window) is re-rotated in place by
- * -T_reset on the temporal pairs, so scores are unchanged.  With rope_pin_sinks the sinks are
+ * -T_reset on the temporal pairs, so scores are unchanged (e4m3 cache: up to the rounding of
+ * the re-rotated keys, which are widened, turned in fp32 and rounded again).  With
+ * rope_pin_sinks the sinks are
  * left as they are: their labels stay, so the query-to-sink distance drops by T_reset (the
  * anchors are reset with the phase).  *applied (may be NULL) receives
  * the number of rebases.  Must open every step, also when T_reset == 0. */
@@ -148,7 +157,8 @@ int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied,
  * f = chunk*T' + t in rows [t*N, (t+1)*N); first_chunk must equal the number of chunks
  * committed so far and (first_chunk + nbatch)*T' - 1 the newest frame given to
  * sdv2_rope_refresh.  d_q is rotated in place at temporal position f - b0 (row h, col w); k is
- * rotated likewise and written with v: element 0's frames into the slots they keep once
+ * rotated likewise (e4m3 cache: in fp32, then rounded) and written with v: element 0's frames
+ * into the slots they keep once
  * committed (sink slot f, or ring slot S + f mod (W+T'), which hold no attended frame), the
  * others into their staging slots.  Buffers:
  * [nbatch][T'N][H][d] each; d_q read-write, d_k and d_v read-only.  Once per layer per step. */

@@ -29,6 +29,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Cache element types: fp32, bf16, or OCP e4m3 (with bf16 activations).
+constexpr int kKvF32 = 0, kKvBF16 = 1, kKvFP8 = 2;
+
+// e4m3 cache layout: inside each group of 32 elements (32 dims of a K row; 32 tokens of a V^T
+// row within a 64-token tile) element 32p + 16h + 8g + e is stored at 32p + 16g + 8h + e (bits
+// 3 and 4 swapped; its own inverse).  A 16-byte read at 32p + 16g then holds the 8 elements
+// lane half g needs for the two 16-wide MFMA k steps 2p and 2p + 1.
+__host__ __device__ __forceinline__ int fp8_pos(int i) {
+  return (i & ~24) | ((i & 8) << 1) | ((i & 16) >> 1);
+}
+
+// Four fp32 values -> four OCP e4m3 bytes (low byte first): round to nearest even, saturated
+// at +-448 (the conversion instruction itself turns values past the last rounding interval
+// into NaN).
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // Workgroup id -> work item such that consecutive work items run on the same XCD (each XCD
 // has its own L2): hardware sends workgroup i to XCD i % 8.  A bijection on [0, G).
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
@@ -111,10 +134,10 @@ struct SinkArgs {
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------------------------
-hipError_t launch_rope_append(const AppendArgs& a, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_rope_append(const AppendArgs& a, int head_dim, int kv, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
-hipError_t launch_rebase(const RebaseArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_rebase(const RebaseArgs& a, int head_dim, int kv, hipStream_t s);
 hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s);
 hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s);
 hipError_t launch_motion(const float* frames, int nframes, int64_t elems, double* dist,

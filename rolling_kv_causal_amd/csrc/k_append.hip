@@ -37,9 +37,24 @@ __device__ __forceinline__ void rotate16(uint4& w, const float2* cs) {
   }
 }
 
-template <bool BF16, int D>
+// The 8 values of a 16-byte bf16 chunk rotated in fp32 (pairs as in rotate16), for the e4m3 path
+// which rounds once from fp32.
+__device__ __forceinline__ void rotate8_f32(const uint4& w, const float2* cs, float* out) {
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(&w);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x = bf16_bits_to_f32(u[j] & 0xffffu), y = bf16_bits_to_f32(u[j] >> 16);
+    out[2 * j] = x * cs[j].x - y * cs[j].y;
+    out[2 * j + 1] = x * cs[j].y + y * cs[j].x;
+  }
+}
+
+// KV: cache element type (kKvF32, kKvBF16, kKvFP8); q, k, v are fp32 for kKvF32, else bf16.
+template <int KV, int D>
 __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr bool BF16 = KV != kKvF32;
+  using T = typename std::conditional<BF16, uint16_t, float>::type;   // activations
+  using TC = typename std::conditional<KV == kKvFP8, uint8_t, T>::type;  // cache elements
   constexpr int VEC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int CH = D / VEC;                // chunks per row
   constexpr int ROWS = 256 / CH;             // token rows per pass
@@ -94,41 +109,56 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
     if (n < a.N) {
       const int64_t off = ((int64_t)(fr * a.N + n) * a.H + head) * D + c * VEC;
       rotate16<BF16>(qv[pass], cs[pass]);
-      rotate16<BF16>(kv[pass], cs[pass]);
       *(uint4*)((T*)a.q + off) = qv[pass];
-      *(uint4*)((T*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv[pass];
+      if constexpr (KV == kKvFP8) {            // 8 dims -> one 8-byte unit at its e4m3 position
+        float kr[8];
+        rotate8_f32(kv[pass], cs[pass], kr);
+        const uint2 w = make_uint2(pack_fp8x4(kr[0], kr[1], kr[2], kr[3]),
+                                   pack_fp8x4(kr[4], kr[5], kr[6], kr[7]));
+        *(uint2*)((TC*)a.kv + kdst + (int64_t)n * D + fp8_pos(c * VEC)) = w;
+      } else {
+        rotate16<BF16>(kv[pass], cs[pass]);
+        *(uint4*)((TC*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv[pass];
+      }
     }
   }
   __syncthreads();
 
-  // V^T rows: d-major, the tile's 64 tokens contiguous
-  constexpr int TCH = TILE / VEC;            // 16-byte chunks per V^T row of the tile
-  T* vdst = (T*)a.kv + a.v_layer_off + (int64_t)a.dst_slot[fr] * a.slot_stride +
-            (int64_t)head * a.head_stride + n0;
+  // V^T rows: d-major, the tile's 64 tokens contiguous (e4m3: in fp8_pos order)
+  constexpr int TVEC = 16 / (int)sizeof(TC);  // cache elements per 16-byte store
+  constexpr int TCH = TILE / TVEC;            // 16-byte chunks per V^T row of the tile
+  TC* vdst = (TC*)a.kv + a.v_layer_off + (int64_t)a.dst_slot[fr] * a.slot_stride +
+             (int64_t)head * a.head_stride + n0;
   for (int idx = tid; idx < D * TCH; idx += 256) {
     const int drow = idx / TCH, kc = idx % TCH;
-    T vals[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) vals[j] = vs[(kc * VEC + j) * VSTR + drow];
     uint4 w;
-    __builtin_memcpy(&w, vals, sizeof(w));
-    *(uint4*)(vdst + (int64_t)drow * a.Npad + kc * VEC) = w;
+    if constexpr (KV == kKvFP8) {
+      float f[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) f[j] = bf16_bits_to_f32(vs[fp8_pos(kc * 16 + j) * VSTR + drow]);
+      w = make_uint4(pack_fp8x4(f[0], f[1], f[2], f[3]), pack_fp8x4(f[4], f[5], f[6], f[7]),
+                     pack_fp8x4(f[8], f[9], f[10], f[11]), pack_fp8x4(f[12], f[13], f[14], f[15]));
+    } else {
+      T vals[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) vals[j] = vs[(kc * VEC + j) * VSTR + drow];
+      __builtin_memcpy(&w, vals, sizeof(w));
+    }
+    *(uint4*)(vdst + (int64_t)drow * a.Npad + kc * TVEC) = w;
   }
 }
 
-hipError_t launch_rope_append(const AppendArgs& a, int head_dim, bool bf16, hipStream_t s) {
+hipError_t launch_rope_append(const AppendArgs& a, int head_dim, int kv, hipStream_t s) {
   const dim3 grid(a.T * ((a.N + kTileKeys - 1) / kTileKeys), a.H, a.nbatch);
-  if (bf16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((rope_append_kernel<true, 128>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((rope_append_kernel<true, 64>), grid, dim3(256), 0, s, a);
+#define SDV2_APPEND(KV_, D_) hipLaunchKernelGGL((rope_append_kernel<KV_, D_>), grid, dim3(256), 0, s, a)
+  if (kv == kKvFP8) {
+    if (head_dim == 128) SDV2_APPEND(kKvFP8, 128); else SDV2_APPEND(kKvFP8, 64);
+  } else if (kv == kKvBF16) {
+    if (head_dim == 128) SDV2_APPEND(kKvBF16, 128); else SDV2_APPEND(kKvBF16, 64);
   } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((rope_append_kernel<false, 128>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((rope_append_kernel<false, 64>), grid, dim3(256), 0, s, a);
+    if (head_dim == 128) SDV2_APPEND(kKvF32, 128); else SDV2_APPEND(kKvF32, 64);
   }
+#undef SDV2_APPEND
   return hipGetLastError();
 }
 

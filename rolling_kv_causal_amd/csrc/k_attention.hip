@@ -48,7 +48,8 @@ __device__ __forceinline__ int perm_key(int key) {
 template <int RB>
 __device__ __forceinline__ int lds_chunk(int R, int c) {
   if constexpr (RB == 256) return R * 256 + ((c ^ (R & 15)) << 4);
-  else return (R >> 1) * 256 + (((((R & 1) << 3) | c) ^ ((R >> 1) & 15)) << 4);
+  else if constexpr (RB == 128) return (R >> 1) * 256 + (((((R & 1) << 3) | c) ^ ((R >> 1) & 15)) << 4);
+  else return R * 64 + ((c ^ ((R >> 2) & 3)) << 4);   // 64-byte rows: 16 rows x 1 chunk column
 }
 // Inverse: LDS chunk position pos -> (row, logical chunk).
 template <int RB>
@@ -56,10 +57,13 @@ __device__ __forceinline__ void lds_chunk_inv(int pos, int& R, int& c) {
   if constexpr (RB == 256) {
     R = pos >> 4;
     c = (pos & 15) ^ (R & 15);
-  } else {
+  } else if constexpr (RB == 128) {
     const int J = pos >> 4, p = (pos & 15) ^ (J & 15);
     R = 2 * J + (p >> 3);
     c = p & 7;
+  } else {
+    R = pos >> 2;
+    c = (pos & 3) ^ ((R >> 2) & 3);
   }
 }
 
@@ -81,21 +85,45 @@ struct TileCursor {
 // LDS rings of two K and two V^T tiles: K(m+1) and V(m) stream in during phases 2m and 2m+1
 // (direct global->LDS loads issued by all waves at the start of phase 2m, awaited before the
 // barrier that ends phase 2m+1), into slots whose previous tiles were last read in phase 2m-1.
-template <int D>
+// KV = kKvBF16: bf16 cache; kKvFP8: e4m3 cache (head_dim 128).  The e4m3 tiles land in a
+// staging area (each wave 1 KB of K and 1 KB of V^T, the bytes it loaded itself); once its
+// loads are in, the wave widens exactly those bytes to bf16 into the ring slots, so every
+// element is converted once per workgroup and the MFMA phase is the bf16 one.
+template <int D, int KV>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
+  constexpr bool F8 = KV == kKvFP8;
+  constexpr int EB = F8 ? 1 : 2;              // bytes per cache element in HBM
   constexpr int KD = D / 16;                  // 16-wide k steps over d (QK)
   constexpr int DB = D / 32;                  // 32-row d blocks of O^T (PV)
-  constexpr int KRB = D * 2;                  // bytes per K row
+  constexpr int KRB = D * 2;                  // bytes per K row in LDS (bf16)
+  constexpr int VRB = kTileKeys * 2;          // bytes per V^T row of a tile in LDS (bf16)
   constexpr int K_BYTES = kTileKeys * KRB;
-  constexpr int V_BYTES = D * kTileKeys * 2;  // V^T tile: D rows of 128 bytes
+  constexpr int V_BYTES = D * VRB;
+  constexpr int KG_BYTES = kTileKeys * D * EB;   // bytes of a K (V^T) tile in HBM
   constexpr int NW = 8;                       // waves per workgroup
-  constexpr int KLD = K_BYTES / 1024 / NW;    // 1 KB wave loads per wave per K tile
-  constexpr int VLD = V_BYTES / 1024 / NW;
-  static_assert(KLD >= 1 && VLD >= 1 && (D == 64 || D == 128), "head_dim 64 or 128");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * K_BYTES + 2 * V_BYTES];
+  constexpr int KLD = KG_BYTES / 1024 / NW;   // 1 KB wave loads per wave per K tile
+  constexpr int VLD = KLD;
+  static_assert(KLD >= 1 && (D == 64 || D == 128), "head_dim 64 or 128");
+  static_assert(!F8 || (D == 128 && KLD == 1), "e4m3 cache: head_dim 128");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * K_BYTES + 2 * V_BYTES + (F8 ? 2 * KG_BYTES : 0)];
   char* const ldsK = lds;
   char* const ldsV = lds + 2 * K_BYTES;
+  char* const ldsS = lds + 2 * K_BYTES + 2 * V_BYTES;   // e4m3 staging: K, then V^T
+  // 16 e4m3 bytes -> the bf16 values of bytes 0-7 (lo) and 8-15 (hi), exactly
+#define SDV2_WIDEN(w_, lo_, hi_)                                                               \
+  do {                                                                                         \
+    const bf16x2 a0_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).x, 1.f, false);     \
+    const bf16x2 a1_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).x, 1.f, true);      \
+    const bf16x2 a2_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).y, 1.f, false);     \
+    const bf16x2 a3_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).y, 1.f, true);      \
+    const bf16x2 b0_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).z, 1.f, false);     \
+    const bf16x2 b1_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).z, 1.f, true);      \
+    const bf16x2 b2_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).w, 1.f, false);     \
+    const bf16x2 b3_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).w, 1.f, true);      \
+    lo_ = bf16x8{a0_.x, a0_.y, a1_.x, a1_.y, a2_.x, a2_.y, a3_.x, a3_.y};                      \
+    hi_ = bf16x8{b0_.x, b0_.y, b1_.x, b1_.y, b2_.x, b2_.y, b3_.x, b3_.y};                      \
+  } while (0)
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -144,13 +172,13 @@ void attn_bf16_kernel(const AttnArgs a) {
   // whose wait would also drain the LDS queue.
   const int own_i = min(max(lane - a.nshared, 0), a.T - 1);
   const int slot_lane = lane < a.nshared ? a.slots[lane] : a.own_slot[elem * a.T + own_i];
-  const char* const kblk = kvb + (a.k_layer_off + head_off) * 2;
-  const char* const vblk = kvb + (a.v_layer_off + head_off) * 2;
-  const int64_t slot_bytes = a.slot_stride * 2;
+  const char* const kblk = kvb + (a.k_layer_off + head_off) * EB;
+  const char* const vblk = kvb + (a.v_layer_off + head_off) * EB;
+  const int64_t slot_bytes = a.slot_stride * EB;
   auto frame_at = [&](TileCursor& c) {
     const int slot = __builtin_amdgcn_readlane(slot_lane, c.f & 63);
-    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * 2);
-    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * 2);
+    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * EB);
+    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * EB);
   };
   auto cursor_at = [&](int tile) -> TileCursor {
     TileCursor c;
@@ -165,45 +193,88 @@ void attn_bf16_kernel(const AttnArgs a) {
       ++c.f;
       frame_at(c);
     } else {
-      c.kp += kTileKeys * D * 2;
-      c.vp += kTileKeys * 2;
+      c.kp += kTileKeys * D * EB;
+      c.vp += kTileKeys * EB;
     }
   };
 
-  // Per-lane byte offsets of the tile fills (loop invariant)
+  // Per-lane byte offsets of the tile fills (loop invariant).  bf16: LDS row R of a K tile
+  // holds key perm_key(R), its chunks placed by lds_chunk.  e4m3 (one 1 KB load per tile
+  // each): lane (row kr8, chunk kc8) of K, lane (row vr8, chunk vc8) of V^T, in lane order
+  // in the staging area.
+  const int kr8 = wave * 8 + (lane >> 3), kc8 = lane & 7;     // 8 rows of 128 bytes per wave
+  const int vr8 = wave * 16 + (lane >> 2), vc8 = lane & 3;    // 16 rows of 64 bytes per wave
   uint32_t koff[KLD], voff[VLD];
 #pragma unroll
   for (int i = 0; i < KLD; ++i) {
     int R, c;
-    lds_chunk_inv<KRB>((wave * KLD + i) * 64 + lane, R, c);
-    koff[i] = (uint32_t)(perm_key(R) * KRB + c * 16);
+    if constexpr (F8) {
+      R = kr8;
+      c = kc8;
+    } else {
+      lds_chunk_inv<KRB>((wave * KLD + i) * 64 + lane, R, c);
+    }
+    koff[i] = (uint32_t)(perm_key(R) * D * EB + c * 16);
   }
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
     int R, c;
-    lds_chunk_inv<128>((wave * VLD + i) * 64 + lane, R, c);
-    voff[i] = (uint32_t)(R * a.Npad * 2 + c * 16);
+    if constexpr (F8) {
+      R = vr8;
+      c = vc8;
+    } else {
+      lds_chunk_inv<VRB>((wave * VLD + i) * 64 + lane, R, c);
+    }
+    voff[i] = (uint32_t)(R * a.Npad * EB + c * 16);
   }
+  char* const kdst = F8 ? ldsS : ldsK;
+  char* const vdst = F8 ? ldsS + KG_BYTES : ldsV;
+  constexpr int KDST = F8 ? 0 : K_BYTES, VDST = F8 ? 0 : V_BYTES;   // per ring slot
   auto fill_k = [&](const TileCursor& c, int buf) {
     const char* src = c.kp;
 #pragma unroll
     for (int i = 0; i < KLD; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src + koff[i]),
-                                       (lds_void*)(ldsK + buf * K_BYTES + (wave * KLD + i) * 1024), 16, 0, 0);
+                                       (lds_void*)(kdst + buf * KDST + (wave * KLD + i) * 1024), 16, 0, 0);
   };
   auto fill_v = [&](const TileCursor& c, int buf) {
     const char* src = c.vp;
 #pragma unroll
     for (int i = 0; i < VLD; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
-                                       (lds_void*)(ldsV + buf * V_BYTES + (wave * VLD + i) * 1024), 16, 0, 0);
+                                       (lds_void*)(vdst + buf * VDST + (wave * VLD + i) * 1024), 16, 0, 0);
   };
-  // Per-lane LDS read offsets (loop invariant)
+  // e4m3: after this wave's loads are in, widen its staged bytes into ring slots kslot / vslot
+  // (-1: none).  An e4m3 chunk c = 2p + h of a row holds, in the cache's byte order, elements
+  // 32p + 8h + [0, 8) and 32p + 16 + 8h + [0, 8): bf16 chunks 4p + h and 4p + 2 + h.
+  auto widen_staged = [&](int kslot, int vslot) {
+    if constexpr (F8) {
+      if (kslot >= 0) {
+        const uint4 w = *(const uint4*)(ldsS + wave * 1024 + lane * 16);
+        bf16x8 lo, hi;
+        SDV2_WIDEN(w, lo, hi);
+        char* const kt = ldsK + kslot * K_BYTES;
+        const int p = kc8 >> 1, h = kc8 & 1;
+        *(bf16x8*)(kt + lds_chunk<KRB>(kr8, 4 * p + h)) = lo;
+        *(bf16x8*)(kt + lds_chunk<KRB>(kr8, 4 * p + 2 + h)) = hi;
+      }
+      if (vslot >= 0) {
+        const uint4 w = *(const uint4*)(ldsS + KG_BYTES + wave * 1024 + lane * 16);
+        bf16x8 lo, hi;
+        SDV2_WIDEN(w, lo, hi);
+        char* const vt = ldsV + vslot * V_BYTES;
+        const int p = vc8 >> 1, h = vc8 & 1;
+        *(bf16x8*)(vt + lds_chunk<VRB>(vr8, 4 * p + h)) = lo;
+        *(bf16x8*)(vt + lds_chunk<VRB>(vr8, 4 * p + 2 + h)) = hi;
+      }
+    }
+  };
+  // Per-lane LDS read offsets (loop invariant): one 16-byte chunk per fragment.
   int kro[KD], vro[4];
 #pragma unroll
   for (int kd = 0; kd < KD; ++kd) kro[kd] = lds_chunk<KRB>(r, 2 * kd + g);   // + 32 rows for kb = 1
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) vro[ch] = lds_chunk<128>(r, 2 * ch + g);   // + 4096 B per d block
+  for (int ch = 0; ch < 4; ++ch) vro[ch] = lds_chunk<VRB>(r, 2 * ch + g);   // + 32 rows per d block
 
   const float sl = a.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
@@ -221,7 +292,7 @@ void attn_bf16_kernel(const AttnArgs a) {
   // MFMA waits only for its own operand instead of the whole LDS queue.
   constexpr int NPV = DB * 4, NQK = KD * 2, NF = NPV + NQK, kAhead = 8;
 #define SDV2_FRAG(t_)                                                                          \
-  ((t_) < NPV ? *(const bf16x8*)(vt + ((t_) / 4) * 4096 + vro[(t_) % 4])                       \
+  ((t_) < NPV ? *(const bf16x8*)(vt + ((t_) / 4) * 32 * VRB + vro[(t_) % 4])                   \
               : *(const bf16x8*)(kt + (((t_) - NPV) % 2) * 32 * KRB + kro[((t_) - NPV) / 2]))
 #define SDV2_FRAG_MFMA(t_, f_)                                                                 \
   do {                                                                                         \
@@ -258,10 +329,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     }                                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                         \
   } while (0)
-#define SDV2_MFMA_PHASE(k_)                                                                    \
-  do {                                                                                         \
-    SDV2_MFMA_RUN(k_, 0, NF);                                                                  \
-  } while (0)
+#define SDV2_MFMA_PHASE(k_) SDV2_MFMA_RUN(k_, 0, NF)
 
   // VALU phase of the current tile: masked row max, lazy rescale, exponentials -> P^T, row
   // sums.  lane (g, r), accumulator v holds key 16*(v/8) + 8g + v%8 (+32 for s1) of query r.
@@ -330,24 +398,35 @@ void attn_bf16_kernel(const AttnArgs a) {
   TileCursor kc = cursor_at(t_begin);         // K tile of the next loads
   TileCursor vc = kc;                         // V tile of the next loads
   TileCursor sc = kc;                         // tile of this wave's next VALU phase
+  int pend_k = -1, pend_v = -1;               // ring slots of this wave's loads in flight (e4m3)
   auto loads = [&](int m) {
     if (m + 1 <= last) {
       advance(kc);
       fill_k(kc, (m + 1) & 1);
+      pend_k = (m + 1) & 1;
     }
     if (m <= last) {
       fill_v(vc, m & 1);
+      pend_v = m & 1;
       if (m + 1 <= last) advance(vc);
     }
+  };
+  // wait for this wave's loads; e4m3: widen them into their slots (before the barrier)
+  auto loads_in = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    widen_staged(pend_k, pend_v);
+    pend_k = pend_v = -1;
   };
 
   // prologue: K(0) resident before phase 0; group B idles through phase 0 (it issues its
   // share of the phase-0 loads there)
   fill_k(kc, 0);
+  pend_k = 0;
   // V^T slot 1 is read by M(0) (with P = 0) before V(1) arrives: make it finite
-  reinterpret_cast<uint4*>(ldsV + V_BYTES)[tid] = make_uint4(0u, 0u, 0u, 0u);
-  if (V_BYTES > 512 * 16) reinterpret_cast<uint4*>(ldsV + V_BYTES)[tid + 512] = make_uint4(0u, 0u, 0u, 0u);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+  for (int i = 0; i < V_BYTES / (512 * 16); ++i)
+    reinterpret_cast<uint4*>(ldsV + V_BYTES)[tid + 512 * i] = make_uint4(0u, 0u, 0u, 0u);
+  loads_in();
   __syncthreads();
   if (grp == 1) {
     loads(0);
@@ -361,7 +440,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     __builtin_amdgcn_s_setprio(2);            // MFMA phase first in issue arbitration
     SDV2_MFMA_PHASE(k);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (grp == 1) loads_in();
     __syncthreads();
     if (k == ntiles && grp == 1) break;       // B's last phase was M(n)
     if (grp == 1) loads(k + 1);
@@ -369,12 +448,13 @@ void attn_bf16_kernel(const AttnArgs a) {
       valu_phase(a.N - sc.k * kTileKeys, sc.f - a.nshared);
       if (k < last) advance(sc);
     }
-    if (grp == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (grp == 0) loads_in();
     __syncthreads();
   }
 #undef SDV2_FRAG
 #undef SDV2_FRAG_MFMA
 #undef SDV2_MFMA_RUN
+#undef SDV2_WIDEN
 #undef SDV2_MFMA_PHASE
 
   // lane (g, r), accumulator v of o[i] holds O^T[d = 32i + 8(v/4) + 4g + v%4][query r]
@@ -511,13 +591,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  if (bf16) {
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s) {
+  if (kv != kKvF32) {
     const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
-    if (head_dim == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(512), 0, s, a);
+    if (kv == kKvFP8)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, kKvFP8>), dim3(grid), dim3(512), 0, s, a);
+    else if (head_dim == 128)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, kKvBF16>), dim3(grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<64, kKvBF16>), dim3(grid), dim3(512), 0, s, a);
   } else {
     const int grid = a.nbatch * a.H * ((a.T * a.N + 63) / 64);
     if (head_dim == 128)

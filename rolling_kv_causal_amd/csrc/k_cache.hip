@@ -37,7 +37,7 @@ hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s) {
 // [WT] adaptive sink and RoPE refresh: the RoPE phase is reset once the frame index passes the
 // threshold; rotating every cached key by -delta on the temporal pairs (queries are rotated at
 // the new base by the append) keeps every score unchanged.
-template <bool BF16>
+template <int KV>
 __global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) {
   __shared__ float2 cs[kMaxTPairs];
   if ((int)threadIdx.x < a.pt) cs[threadIdx.x] = a.cs[threadIdx.x];
@@ -50,10 +50,16 @@ __global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) 
     const int p = (int)(i % a.pt);
     const int64_t rowi = i / a.pt;
     const int n = (int)(rowi % a.N), h = (int)(rowi / a.N);
+    // dims 2p, 2p+1 stay adjacent in the e4m3 order (fp8_pos keeps bits 0-2)
+    const int dpos = KV == kKvFP8 ? fp8_pos(2 * p) : 2 * p;
     const int64_t off = layer * a.layer_stride + slot * a.slot_stride + h * a.head_stride +
-                        (int64_t)n * D + 2 * p;
+                        (int64_t)n * D + dpos;
     const float c = cs[p].x, sn = cs[p].y;
-    if constexpr (BF16) {
+    if constexpr (KV == kKvFP8) {
+      uint16_t* ptr = (uint16_t*)((uint8_t*)a.kv + off);
+      const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)*ptr, false);
+      *ptr = (uint16_t)(pack_fp8x4(v.x * c - v.y * sn, v.x * sn + v.y * c, 0.f, 0.f) & 0xffffu);
+    } else if constexpr (KV == kKvBF16) {
       uint32_t* ptr = (uint32_t*)((uint16_t*)a.kv + off);
       const uint32_t w = *ptr;
       const float x = bf16_bits_to_f32(w & 0xffffu), y = bf16_bits_to_f32(w >> 16);
@@ -66,15 +72,17 @@ __global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) 
   }
 }
 
-hipError_t launch_rebase(const RebaseArgs& a, int head_dim, bool bf16, hipStream_t s) {
+hipError_t launch_rebase(const RebaseArgs& a, int head_dim, int kv, hipStream_t s) {
   const int64_t npairs = (int64_t)a.H * a.N * a.pt;
   int gx = (int)((npairs + 256 * 4 - 1) / (256 * 4));
   gx = gx < 1 ? 1 : gx > 1024 ? 1024 : gx;
   const dim3 grid(gx, a.nslots * a.L);
-  if (bf16)
-    hipLaunchKernelGGL(rebase_kernel<true>, grid, dim3(256), 0, s, a, head_dim);
+  if (kv == kKvFP8)
+    hipLaunchKernelGGL(rebase_kernel<kKvFP8>, grid, dim3(256), 0, s, a, head_dim);
+  else if (kv == kKvBF16)
+    hipLaunchKernelGGL(rebase_kernel<kKvBF16>, grid, dim3(256), 0, s, a, head_dim);
   else
-    hipLaunchKernelGGL(rebase_kernel<false>, grid, dim3(256), 0, s, a, head_dim);
+    hipLaunchKernelGGL(rebase_kernel<kKvF32>, grid, dim3(256), 0, s, a, head_dim);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@
 
 using namespace sdv2;
 
+static_assert(SDV2_F32 == kKvF32 && SDV2_BF16 == kKvBF16 && SDV2_BF16_KV_FP8 == kKvFP8,
+              "the config dtype codes are the kernels' cache types");
+
 namespace {
 
 thread_local std::string g_error;
@@ -73,7 +76,10 @@ int validate(const sdv2_config* c) {
   if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta))
     return fail(SDV2_EINVAL, "rope_theta must be finite and > 1");
   if (c->rope_refresh_period < 0) return fail(SDV2_EINVAL, "rope_refresh_period must be >= 0");
-  if (c->dtype != SDV2_F32 && c->dtype != SDV2_BF16) return fail(SDV2_EINVAL, "dtype must be F32 or BF16");
+  if (c->dtype != SDV2_F32 && c->dtype != SDV2_BF16 && c->dtype != SDV2_BF16_KV_FP8)
+    return fail(SDV2_EINVAL, "dtype must be F32, BF16 or BF16_KV_FP8");
+  if (c->dtype == SDV2_BF16_KV_FP8 && c->head_dim != 128)
+    return fail(SDV2_EINVAL, "the e4m3 cache needs head_dim 128");
   if (c->embed_dim < 0) return fail(SDV2_EINVAL, "embed_dim must be >= 0");
   if (c->rope_pin_sinks != 0 && c->rope_pin_sinks != 1) return fail(SDV2_EINVAL, "rope_pin_sinks must be 0 or 1");
   if (tau_on(*c) && (c->embed_dim < 1 || c->sink_frames < 1))
@@ -86,7 +92,7 @@ sdv2_layout make_layout(const sdv2_config& c) {
   const int64_t N = (int64_t)c.grid_h * c.grid_w;
   l.slots = c.sink_frames + c.window_frames + (int64_t)c.stream_batch * c.chunk_frames;
   l.tokens_padded = align_up(N, kTileKeys);
-  l.elem_bytes = c.dtype == SDV2_BF16 ? 2 : 4;
+  l.elem_bytes = c.dtype == SDV2_F32 ? 4 : c.dtype == SDV2_BF16 ? 2 : 1;
   l.head_stride = l.tokens_padded * c.head_dim;
   l.slot_stride = c.num_heads * l.head_stride;
   l.layer_stride = 2 * l.slots * l.slot_stride;
@@ -106,7 +112,7 @@ constexpr double kTileUs = 1.2, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 // chunks end the walk at a query tile's last own frame), which bounds the split count so that
 // every split has at least one tile.
 int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_tiles) {
-  if (c.dtype != SDV2_BF16) return 1;
+  if (c.dtype == SDV2_F32) return 1;
   const int64_t R = (int64_t)c.chunk_frames * c.grid_h * c.grid_w;   // query rows per element
   const int64_t base = (int64_t)nbatch * c.num_heads * ((R + kQTile - 1) / kQTile);
   const int64_t rows = (int64_t)nbatch * c.num_heads * R;
@@ -354,7 +360,7 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
         const double ang = -delta * omega(cfg.rope_theta, i, cfg.rope_dim_t);
         a.cs[i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
       }
-      SDV2_HIP(launch_rebase(a, cfg.head_dim, cfg.dtype == SDV2_BF16, (hipStream_t)stream));
+      SDV2_HIP(launch_rebase(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
     }
     c->base += count * T;
     c->refreshes += count;
@@ -430,7 +436,7 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
         a.tcs[b * Tc + t][i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
       }
     }
-  SDV2_HIP(launch_rope_append(a, cfg.head_dim, cfg.dtype == SDV2_BF16, (hipStream_t)stream));
+  SDV2_HIP(launch_rope_append(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
   c->appended[layer] = 1;
   c->step_first = first_chunk;
   c->step_nbatch = nbatch;
@@ -455,7 +461,6 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
   if (((uintptr_t)d_q_rot | (uintptr_t)d_out) & 15) return fail(SDV2_EINVAL, "q_rot and out must be 16-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SDV2_EINVAL, "scale must be finite and > 0");
 
-  const bool bf16 = cfg.dtype == SDV2_BF16;
   AttnArgs a{};
   a.q = d_q_rot;
   a.out = d_out;
@@ -486,7 +491,7 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
     a.part_o = (float*)c->ws;
     a.part_ml = (float2*)(c->ws + align_up(rows * cfg.head_dim * 4, kAlign));
   }
-  SDV2_HIP(launch_attention(a, cfg.head_dim, bf16, (hipStream_t)stream));
+  SDV2_HIP(launch_attention(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
   if (a.nsplit > 1) {
     CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.nsplit};
     SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));

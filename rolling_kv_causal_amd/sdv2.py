@@ -15,7 +15,7 @@ from typing import Optional
 _LIB_PATH = pathlib.Path(__file__).resolve().parent / "libsdv2.so"
 
 SDV2_OK, SDV2_EINVAL, SDV2_ESTATE, SDV2_EHIP, SDV2_ENOSPC = 0, -1, -2, -3, -4
-SDV2_F32, SDV2_BF16 = 0, 1
+SDV2_F32, SDV2_BF16, SDV2_BF16_KV_FP8 = 0, 1, 2
 ERROR_NAMES = {SDV2_EINVAL: "EINVAL", SDV2_ESTATE: "ESTATE", SDV2_EHIP: "EHIP", SDV2_ENOSPC: "ENOSPC"}
 
 
@@ -111,18 +111,21 @@ def _stream(stream) -> int:
 def make_config(*, num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                 chunk_frames=1, stream_batch=1, rope_dim_t, rope_dim_h, rope_dim_w,
                 rope_theta=10000.0, rope_refresh_period=0, dtype="bf16", embed_dim=0,
-                rope_pin_sinks=False, sink_threshold=None, **_ignored) -> Config:
-    """Build the C config; dtype "bf16"/"fp32"; sink_threshold None = sink refresh off."""
+                rope_pin_sinks=False, sink_threshold=None, kv_fp8=False, **_ignored) -> Config:
+    """Build the C config; dtype "bf16"/"fp32" (activations); kv_fp8 with bf16: e4m3 cache;
+    sink_threshold None = sink refresh off."""
+    code = SDV2_F32 if dtype != "bf16" else (SDV2_BF16_KV_FP8 if kv_fp8 else SDV2_BF16)
     return Config(num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                   chunk_frames, stream_batch, rope_dim_t, rope_dim_h, rope_dim_w, float(rope_theta),
-                  rope_refresh_period, SDV2_BF16 if dtype == "bf16" else SDV2_F32, embed_dim,
+                  rope_refresh_period, code, embed_dim,
                   int(bool(rope_pin_sinks)), float("nan") if sink_threshold is None else float(sink_threshold))
 
 
 def config_of(obj) -> Config:
     """C config from any object carrying the config's field names as attributes."""
     names = [f[0] for f in Config._fields_]
-    return make_config(**{n: getattr(obj, n) for n in names})
+    kw = {n: getattr(obj, n) for n in names}
+    return make_config(kv_fp8=getattr(obj, "kv_fp8", False), **kw)
 
 
 # ---- entry points (same names as the C ABI) ----------------------------------------------------
@@ -254,7 +257,8 @@ class Cache:
         self.meta = torch.empty(meta_b, dtype=torch.uint8, device=device)
         self.ws = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=device)
         self.handle = sdv2_cache_create(cfg, self.kv, self.meta, self.ws, stream)
-        self.torch_dtype = torch.bfloat16 if cfg.dtype == SDV2_BF16 else torch.float32
+        # cache element type: fp32, bf16, or e4m3 bytes
+        self.torch_dtype = {SDV2_F32: torch.float32, SDV2_BF16: torch.bfloat16}.get(cfg.dtype, torch.uint8)
 
     def close(self):
         if self.handle:

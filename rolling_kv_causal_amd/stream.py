@@ -20,7 +20,7 @@ class StreamRunner:
         self.num_chunks = num_chunks
         self.scale = scale
         self.cache = sdv2.Cache(cfg, device=device)
-        self.dtype = torch.bfloat16 if cfg.dtype == sdv2.SDV2_BF16 else torch.float32
+        self.dtype = torch.float32 if cfg.dtype == sdv2.SDV2_F32 else torch.bfloat16   # activations
         self.N = cfg.grid_h * cfg.grid_w
         self.rows = cfg.chunk_frames * self.N     # query rows per element: T' frames of N tokens
         self.out = torch.empty((cfg.num_layers, cfg.stream_batch, self.rows, cfg.num_heads, cfg.head_dim),

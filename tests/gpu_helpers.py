@@ -7,6 +7,7 @@ import time
 import numpy as np
 import torch
 
+from oracle import fp8 as ofp8
 from oracle import rope as orope
 from oracle import stream as ost
 from rolling_kv_causal_amd import sdv2
@@ -33,6 +34,24 @@ def host64(t) -> np.ndarray:
 def bf16_bits_of(x64: np.ndarray) -> np.ndarray:
     """bf16-exact float64 values -> their bit patterns."""
     return (np.asarray(x64, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def fp8_pos(i):
+    """Byte position of element i in an e4m3 row of the cache (sdv2.h: bits 3 and 4 of i swap;
+    the map is its own inverse, so it also gives the element at position i)."""
+    i = np.asarray(i)
+    return (i & ~24) | ((i & 8) << 1) | ((i & 16) >> 1)
+
+
+def check_fp8_keys(got, want, refreshes, what):
+    """Rotated e4m3 keys [.., d]: almost all bytes equal; where the kernel's fp32 rotation and the
+    oracle's float64 one round to neighbouring codes (near-midpoint values, compounded by the
+    re-rounding of each refresh), each pair stays within an e4m3 ulp per rounding."""
+    same = np.mean(got == want)
+    assert same >= 1 - 1e-3, f"{what}: only {same:.5f} of the key bytes agree"
+    err = np.hypot(got[..., 0::2] - want[..., 0::2], got[..., 1::2] - want[..., 1::2])
+    norm = np.hypot(want[..., 0::2], want[..., 1::2])
+    assert np.all(err <= (refreshes + 1) * (2.0 ** -3 * norm + 2.0 ** -8)), f"{what}: key pair off by {err.max():.3g}"
 
 
 def assert_close(cfg, got, want, what, scale=1.0):
@@ -149,6 +168,8 @@ class Harness:
                 f = cache.slot_info(slot)[0]
                 assert f == -1 or (committed * T <= f < (committed + 1) * T and slot == lib_slot(cfg, f)), \
                     (slot, f, committed)
+        if self.st.kv_fp8:
+            return self._check_cache_fp8(entries, r, layers)
         for layer in (self.layers if layers is None else layers):
             Kg, Vg = cache.k_view(layer), cache.v_view(layer)
             for slot, e in entries:
@@ -164,6 +185,26 @@ class Harness:
                     assert np.array_equal(v_got.cpu().numpy(), np.asarray(e.kv[layer][1], np.float32)), f"V slot {slot}"
             # zero padding of the token axis stays zero
             if cache.layout.tokens_padded > N:
+                assert torch.count_nonzero(Kg[:, :, N:, :]) == 0 and torch.count_nonzero(Vg[:, :, :, N:]) == 0
+
+
+    def _check_cache_fp8(self, entries, r, layers):
+        """e4m3 cache: V bytes bit-exact against the oracle's encoding, K per check_fp8_keys,
+        padding tokens zero; rows read back through the documented byte permutation."""
+        cfg, cache = self.cfg, self.run.cache
+        N, D, Npad = cfg.tokens, cfg.head_dim, cache.layout.tokens_padded
+        dperm = torch.as_tensor(fp8_pos(np.arange(D)), device="cuda")
+        tperm = torch.as_tensor(fp8_pos(np.arange(Npad)), device="cuda")
+        for layer in (self.layers if layers is None else layers):
+            Kg = cache.k_view(layer)[..., dperm]                     # [slot][H][Npad][d], d in order
+            Vg = cache.v_view(layer)[..., tperm]                     # [slot][H][d][Npad], tokens in order
+            for slot, e in entries:
+                assert cache.slot_info(slot) == (e.frame, e.label), (slot, cache.slot_info(slot), e.frame, e.label)
+                k_codes = Kg[slot, :, :N, :].permute(1, 0, 2).cpu().numpy()
+                check_fp8_keys(ofp8.decode(k_codes), e.kv[layer][0], r, f"K slot {slot} frame {e.frame}")
+                v_codes = Vg[slot, :, :, :N].permute(2, 0, 1).cpu().numpy()
+                assert np.array_equal(v_codes, ofp8.encode(e.kv[layer][1])), f"V bytes slot {slot}"
+            if Npad > N:
                 assert torch.count_nonzero(Kg[:, :, N:, :]) == 0 and torch.count_nonzero(Vg[:, :, :, N:]) == 0
 
 

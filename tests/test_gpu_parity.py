@@ -99,6 +99,51 @@ def test_pinned_sink_refresh(kw):
     assert len(h.st.refresh_log) >= 2
 
 
+_D128 = dict(dtype="bf16", kv_fp8=True, head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
+             softmax_scale=128 ** -0.5)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(grid_h=5, grid_w=13, num_heads=3, sink_frames=2, window_frames=3, stream_batch=3,
+         rope_refresh_period=5, num_chunks=14),
+    dict(chunk_frames=2, grid_h=12, grid_w=12, num_heads=4, sink_frames=1, window_frames=2, stream_batch=4,
+         rope_refresh_period=3, num_chunks=9, num_layers=2),
+    dict(chunk_frames=3, grid_h=6, grid_w=13, num_heads=3, sink_frames=2, window_frames=4, stream_batch=2,
+         num_chunks=10, embed_dim=16, sink_threshold=0.2, embed_kind="iid"),
+    dict(grid_h=7, grid_w=9, num_heads=2, sink_frames=1, window_frames=3, stream_batch=2, chunk_frames=2,
+         rope_refresh_period=4, num_chunks=10, rope_pin_sinks=True),
+], ids=["ragged-B3-refresh", "T2-B4-refresh", "T3-sink-refresh", "pinned-T2"])
+def test_fp8_kv_cache(kw):
+    # e4m3 cache: token counts off the 32-token byte-permutation blocks, refresh re-rounding,
+    # block-causal chunks, sink replacement (a byte copy) and pinned sinks
+    cfg = _small(**dict(_D128, **kw))
+    h = _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
+    assert len(h.st.refresh_log) >= (2 if cfg.rope_refresh_period else 0)
+
+
+def test_fp8_kv_wan13b_single_layer_full_size():
+    # the headline shape with an e4m3 cache, through the refresh at frame 32
+    cfg = configs.WAN13B_1LAYER.with_(kv_fp8=True)
+    checked = {1, 9, 31, 32, 33}
+    rows = sample_rows(cfg.tokens, n=48, seed=5)
+    h = _stream(cfg, 34, check=lambda s: s in checked, rows=rows, cache_check=lambda s: s in checked)
+    assert h.st.refresh_log == [(32, 32)]
+
+
+def test_fp8_kv_wan14b_40layer_b4_full_size():
+    cfg = configs.WAN14B_40LAYER_B4.with_(kv_fp8=True, sink_threshold=None, embed_dim=0, embed_kind=None)
+    rows = sample_rows(cfg.tokens, n=16, seed=6)
+    h = Harness(cfg, layers=(39,))                       # the last layer: largest cache offsets
+    for s in range(12):
+        full = s in (3, 11)
+        h.step(s, full=full)
+        if full:
+            h.check_outputs(rows=rows, heads=np.arange(0, 40, 3))
+        h.finish_step()
+        if full:
+            h.check_cache()
+
+
 def test_wan13b_30layer_t2b2_full_size():
     # split-KV with block-causal query tiles: splits of frame-0 rows end before own frame 1
     cfg = configs.WAN13B_30LAYER_T2B2

@@ -84,6 +84,21 @@ def test_invalid_configs_are_rejected(field, value, code):
     assert e.value.code == code and sdv2.sdv2_last_error()
 
 
+def test_fp8_cache_config():
+    # e4m3 cache: dtype code 2, one byte per element, head_dim 128 only
+    c = configs.WAN14B_40LAYER_B4.with_(kv_fp8=True)
+    cfg = sdv2.config_of(c)
+    assert cfg.dtype == sdv2.SDV2_BF16_KV_FP8
+    sdv2.sdv2_config_validate(cfg)
+    kv, _, _ = sdv2.sdv2_cache_size(cfg)
+    assert kv == sdv2.sdv2_cache_size(sdv2.config_of(configs.WAN14B_40LAYER_B4))[0] // 2
+    assert sdv2.config_of(c.with_(dtype="fp32")).dtype == sdv2.SDV2_F32      # fp32 runs keep fp32
+    cfg = sdv2.config_of(configs.TINY_FP32.with_(dtype="bf16", kv_fp8=True))  # head_dim 64
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_config_validate(cfg)
+    assert e.value.code == sdv2.SDV2_EINVAL and "128" in sdv2.sdv2_last_error()
+
+
 def test_sink_threshold_needs_embeddings():
     cfg = sdv2.config_of(configs.WAN13B_1LAYER)
     cfg.sink_threshold = 0.5
