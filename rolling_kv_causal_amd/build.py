@@ -13,7 +13,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libsdv2.so"
-SOURCES = ["sdv2.cpp", "k_append.hip", "k_attention.hip", "k_cache.hip"]
+SOURCES = ["sdv2.cpp", "k_append.hip", "k_attention.hip", "k_attention_w64.hip", "k_cache.hip"]
 ARCH = "gfx950"
 
 

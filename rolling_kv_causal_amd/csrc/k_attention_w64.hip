@@ -1,0 +1,288 @@
+// Chunk attention, bf16 cache, head_dim 128: one wave per SIMD, 64 query rows per wave.
+//
+// Same operation and split-KV interface as attn_bf16_kernel ([NEWS] method, algorithm item 1;
+// [REPO] core components; [WT] SLO-aware batching scheduler names FlashAttention as the exact
+// tiled evaluation): O = softmax(scale * Q_rot K^T) V over [sinks | window | own chunk], the
+// own chunk block-causal, one 256-row query tile of one (element, head) per workgroup.
+//
+// Why 64 rows per wave: with 32 rows every 1 KB K or V^T fragment read from LDS feeds one
+// MFMA, and one wave cannot read LDS fast enough to keep the matrix core busy.  With 64 rows
+// (two 32-row blocks qb) every fragment feeds two MFMAs.  The state then needs
+//   O^T 128 + Q^T 64 (AGPRs) and S^T 64 + P^T 2 x 32 + fragments 48 (VGPRs),
+// which fits one wave per SIMD only.  The softmax of tile t is interleaved with the MFMAs of
+// the same wave (P V of tile t-1), so the wave overlaps its own VALU and matrix work.  That
+// needs an instruction order and a register assignment the compiler does not produce, so the
+// whole tile loop (tile walk, global->LDS loads, waits, barriers, the 64 MFMAs and 32 fragment
+// reads of a tile, the softmax, masks and the rare rescale) is one generated asm program
+// (attn_w64_asm.h, written by gen_attn_w64.py, which documents the register plan and the
+// gfx950 hazard rules it keeps) over registers named by the asm operands.  The C++ around it
+// loads Q^T, computes lane constants and the first loads, and writes the outputs.
+//
+// Per tile t (iteration t = 0..n-1, n tiles in the split):
+//   QK(t): S^T = K(t) Q^T;  PV(t-1): O^T += V^T(t-1) P^T(t-1);  softmax(t): P^T(t) from S^T
+// with P(-1) = 0 over a zeroed V^T slot, then a last P V-only step.  LDS rings of three K and
+// three V^T tiles: iteration t loads K(t+2) and V(t+1) into the slots of K(t-1) and V(t-2)
+// after the barrier that follows everyone's reads of them; a wave waits for its own loads
+// (vmcnt) two iterations after issue, before that iteration's barrier.
+//
+// Softmax: base 2 with the lazy-max rule of the other kernel: exponentials at the running max
+// m; only when a lane's tile sum of the bf16-rounded P leaves [0, 256] (first tile, NaN, or a
+// score far above m) is the row max taken and O, l rescaled.  Masks (ragged last tile of a
+// frame, block-causal own frames) are applied to the packed P words by AND with per-lane masks.
+#include "common.h"
+#include "attn_tiles.h"
+#include "attn_w64_asm.h"
+
+namespace sdv2 {
+
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef int i32x32 __attribute__((ext_vector_type(32)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x12 __attribute__((ext_vector_type(12)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// s_waitcnt immediate: vmcnt(n), lgkmcnt and expcnt at their maxima
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void attn_w64_kernel(const AttnArgs a) {
+  constexpr int D = 128, KRB = 256, VRB = 128;
+  constexpr int K_BYTES = kTileKeys * KRB, V_BYTES = D * VRB, NBUF = 3;
+  constexpr int LD = K_BYTES / 1024 / 4;      // 1 KB loads per wave per tile (K; the same for V^T)
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * (K_BYTES + V_BYTES)];
+  char* const ldsK = lds;
+  char* const ldsV = lds + NBUF * K_BYTES;
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int qtile = w % a.qtiles;
+  int rest = w / a.qtiles;
+  const int elem = rest % a.nbatch;
+  rest /= a.nbatch;
+  const int split = rest % a.nsplit;
+  const int head = rest / a.nsplit;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r = lane & 31;
+  const int R = a.T * a.N;                    // query rows per element
+  const int wrow = qtile * kQTile + wave * 64;   // first row of the wave
+  int row[2], tq[2];
+  bool valid[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    row[qb] = wrow + 32 * qb + r;
+    valid[qb] = row[qb] < R;
+    tq[qb] = row[qb] / a.N;
+  }
+  const int tq_wave = wrow / a.N;             // lowest frame of the wave's rows
+
+  // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb].
+  i32x32 q0, q1;
+  {
+    const uint16_t* qb0 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[0] ? row[0] : 0)) * a.H + head) * D + 8 * g;
+    const uint16_t* qb1 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[1] ? row[1] : 0)) * a.H + head) * D + 8 * g;
+#pragma unroll
+    for (int kd = 0; kd < 8; ++kd) {
+      const uint4 x = valid[0] ? *(const uint4*)(qb0 + 16 * kd) : make_uint4(0, 0, 0, 0);
+      const uint4 y = valid[1] ? *(const uint4*)(qb1 + 16 * kd) : make_uint4(0, 0, 0, 0);
+      q0[4 * kd] = x.x; q0[4 * kd + 1] = x.y; q0[4 * kd + 2] = x.z; q0[4 * kd + 3] = x.w;
+      q1[4 * kd] = y.x; q1[4 * kd + 1] = y.y; q1[4 * kd + 2] = y.z; q1[4 * kd + 3] = y.w;
+    }
+  }
+
+  // Tile range of this split (as in attn_bf16_kernel: the walk ends with the last own frame a
+  // row of the query tile sees).
+  const int tq_hi = min(a.T - 1, (qtile * kQTile + kQTile - 1) / a.N);
+  const int tiles_q = (a.nshared + tq_hi + 1) * a.tiles_per_frame;
+  const int t_begin = (int)((int64_t)split * tiles_q / a.nsplit);
+  const int t_end = (int)((int64_t)(split + 1) * tiles_q / a.nsplit);
+  const int n = t_end - t_begin;              // >= 1
+  const char* kvb = (const char*)a.kv;
+  const int64_t head_off = (int64_t)head * a.head_stride;
+  const int own_i = min(max(lane - a.nshared, 0), a.T - 1);
+  const int slot_lane = lane < a.nshared ? a.slots[lane] : a.own_slot[elem * a.T + own_i];
+  const char* const kblk = kvb + (a.k_layer_off + head_off) * 2;
+  const char* const vblk = kvb + (a.v_layer_off + head_off) * 2;
+  const int64_t slot_bytes = a.slot_stride * 2;
+  auto frame_at = [&](TileCursor& c) {
+    const int slot = __builtin_amdgcn_readlane(slot_lane, c.f & 63);
+    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * 2);
+    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * 2);
+  };
+  auto cursor_at = [&](int tile) -> TileCursor {
+    TileCursor c;
+    c.f = tile / a.tiles_per_frame;
+    c.k = tile - c.f * a.tiles_per_frame;
+    frame_at(c);
+    return c;
+  };
+  auto advance = [&](TileCursor& c) {
+    if (++c.k == a.tiles_per_frame) {
+      c.k = 0;
+      ++c.f;
+      frame_at(c);
+    } else {
+      c.kp += kTileKeys * D * 2;
+      c.vp += kTileKeys * 2;
+    }
+  };
+
+  // Global->LDS loads: wave w fills 1 KB pieces w*LD .. w*LD+LD-1 of each tile.
+  uint32_t koff[LD], voff[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    int Rr, c;
+    lds_chunk_inv<KRB>((wave * LD + i) * 64 + lane, Rr, c);
+    koff[i] = (uint32_t)(perm_key(Rr) * KRB + c * 16);
+    lds_chunk_inv<VRB>((wave * LD + i) * 64 + lane, Rr, c);
+    voff[i] = (uint32_t)(Rr * a.Npad * 2 + c * 16);
+  }
+  auto fill_k = [&](const TileCursor& c, int slot) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(c.kp + koff[i]),
+                                       (lds_void*)(ldsK + slot * K_BYTES + (wave * LD + i) * 1024), 16, 0, 0);
+  };
+  auto fill_v = [&](const TileCursor& c, int slot) {
+#pragma unroll
+    for (int i = 0; i < LD; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(c.vp + voff[i]),
+                                       (lds_void*)(ldsV + slot * V_BYTES + (wave * LD + i) * 1024), 16, 0, 0);
+  };
+
+  // Prologue: V^T slot 2 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
+  // slot 1, V(0) into slot 0.
+#pragma unroll
+  for (int i = 0; i < V_BYTES / (256 * 16); ++i)
+    reinterpret_cast<uint4*>(ldsV + 2 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  const TileCursor c0 = cursor_at(t_begin);
+  TileCursor kc = c0;
+  fill_k(kc, 0);
+  if (n > 1) {
+    advance(kc);
+    fill_k(kc, 1);
+  }
+  fill_v(c0, 0);
+
+  // The tile loop (generated asm, see gen_attn_w64.py).  Its state lives in the registers
+  // named by the operands below; the compiler sees one statement.
+  i32x8 kaddr;                                // LDS addresses of K fragments per k step (slot 0)
+  i32x4 vaddr;                                // LDS addresses of V^T fragments per key step (slot 2)
+  i32x4 lanec;                                // 8g, frame of the row per qb, (lane ^ 32) * 4
+  i32x4 koffv, voffv;
+  {
+    const uint32_t kb = (uint32_t)(uintptr_t)ldsK, vb = (uint32_t)(uintptr_t)ldsV;
+#pragma unroll
+    for (int kd = 0; kd < 8; ++kd) kaddr[kd] = (int)(kb + lds_chunk<KRB>(r, 2 * kd + g));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vaddr[ks] = (int)(vb + 2 * V_BYTES + lds_chunk<VRB>(r, 2 * ks + g));
+    lanec[0] = 8 * g;
+    lanec[1] = tq[0];
+    lanec[2] = tq[1];
+    lanec[3] = (lane ^ 32) * 4;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      koffv[i] = (int)koff[i];
+      voffv[i] = (int)voff[i];
+    }
+  }
+  f32x32 o0, o1, o2, o3, s0, s1;
+  i32x32 p0, p1, frg;
+  i32x16 frg2;
+  i32x12 tmp;
+  f32x2 mrun, lrun;
+  f32x4 tsum;
+  i32x16 rmask;
+  i32x2 cmask;
+  // scalar state: cursors (frame, tile in frame) of the last K and V^T tiles loaded and of the
+  // tile t, iteration t, ring offsets, read-slot indices, loads in flight
+  int kf = kc.f, kk = kc.k, vf = c0.f, vk = c0.k, sf = c0.f, sk = c0.k, t = 0;
+  int krd = 0, vrd = 2, kl = K_BYTES, vl = 0, nlprev = (n > 1 ? 2 : 1) * LD;
+  const uint64_t kblk64 = (uint64_t)(uintptr_t)kblk, vblk64 = (uint64_t)(uintptr_t)vblk;
+  const int slotb = (int)slot_bytes, tpf = a.tiles_per_frame, nshared = a.nshared, Ntok = a.N;
+  const int mk = (int)((uint32_t)(uintptr_t)ldsK + wave * LD * 1024);
+  const int mv = (int)((uint32_t)(uintptr_t)ldsV + wave * LD * 1024);
+  const float sl = a.scale_log2;
+  const int ones = 0x3F803F80;                // bf16 (1, 1)
+  unsigned long long trig;
+  int x, y, nvalid, tk, kstep, vstep, nl, mflag, m0save, stmp;
+  asm volatile(SDV2_W64_LOOP
+               : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
+                 "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),
+                 "={v[128:159]}"(frg), "={v[160:175]}"(frg2), "+{v[176:183]}"(kaddr),
+                 "+{v[184:187]}"(vaddr), "={v[188:199]}"(tmp), "={v[200:201]}"(mrun),
+                 "={v[202:205]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),
+                 "={v[228:229]}"(lrun),
+                 [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk), [sf] "+s"(sf),
+                 [sk] "+s"(sk), [t] "+s"(t), [krd] "+s"(krd), [vrd] "+s"(vrd), [kl] "+s"(kl),
+                 [vl] "+s"(vl), [nlprev] "+s"(nlprev),
+                 [trig] "=&s"(trig), [x] "=&s"(x), [y] "=&s"(y), [nvalid] "=&s"(nvalid),
+                 [tk] "=&s"(tk), [kstep] "=&s"(kstep), [vstep] "=&s"(vstep), [nl] "=&s"(nl),
+                 [mflag] "=&s"(mflag), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
+               : "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec),
+                 "{v[230:233]}"(koffv), "{v[234:237]}"(voffv), "{v238}"(slot_lane),
+                 [n] "s"(n), [tpf] "s"(tpf), [nshared] "s"(nshared), [N] "s"(Ntok),
+                 [tqw] "s"(tq_wave), [kblk] "s"(kblk64), [vblk] "s"(vblk64), [slotb] "s"(slotb),
+                 [mk] "s"(mk), [mv] "s"(mv), [sl] "s"(sl), [ones] "s"(ones)
+               : "vcc", "scc", "memory");
+  (void)frg;
+  (void)frg2;
+  (void)tmp;
+  (void)s0;
+  (void)s1;
+  (void)p0;
+  (void)p1;
+  (void)tsum;
+  (void)rmask;
+  (void)cmask;
+  (void)trig;
+
+  // Epilogue.  Lane (g, r), element v of o[db][qb] (o_db[16 qb + v]) holds
+  // O^T[d = 32 db + 8 (v / 4) + 4 g + v % 4][row r of block qb].
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    if (!valid[qb]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    auto ov = [&](int db, int i) { return db == 0 ? o0[i] : db == 1 ? o1[i] : db == 2 ? o2[i] : o3[i]; };
+    if (a.nsplit == 1) {
+      uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * R + row[qb]) * a.H + head) * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int i0 = 16 * qb + 4 * a4;
+          uint2 w2;
+          w2.x = pack_bf16x2(ov(db, i0) * inv, ov(db, i0 + 1) * inv);
+          w2.y = pack_bf16x2(ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
+          *(uint2*)(op + 32 * db + 8 * a4) = w2;
+        }
+    } else {
+      const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + row[qb];
+      float* po = a.part_o + prow * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int i0 = 16 * qb + 4 * a4;
+          *(float4*)(po + 32 * db + 8 * a4) =
+              make_float4(ov(db, i0) * inv, ov(db, i0 + 1) * inv, ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
+        }
+      if (g == 0) a.part_ml[prow] = make_float2(mrun[qb], l_tot);
+    }
+  }
+}
+
+hipError_t launch_attention_w64(const AttnArgs& a, hipStream_t s) {
+  const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
+  hipLaunchKernelGGL(attn_w64_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sdv2

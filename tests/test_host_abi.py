@@ -196,3 +196,13 @@ def test_slo_select_errors():
         sdv2.sdv2_slo_select(0.01, 0.001, 0.0, 1.0, 8, 8, 8)       # target_fps <= 0
     with pytest.raises(sdv2.SDV2Error):
         sdv2.sdv2_slo_select(0.01, 0.001, 100.0, 1.0, 0, 8, 8)     # no frames ready
+
+
+def test_generated_attention_asm_is_current():
+    # attn_w64_asm.h is the output of gen_attn_w64.py (which also checks its hazard rules)
+    import pathlib
+    import subprocess
+    import sys
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    out = subprocess.run([sys.executable, "gen_attn_w64.py"], cwd=csrc, capture_output=True, text=True, check=True)
+    assert out.stdout == (csrc / "attn_w64_asm.h").read_text()
