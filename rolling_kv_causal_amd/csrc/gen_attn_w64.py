@@ -1,4 +1,4 @@
-"""Writes attn_w64_asm.h: the per-tile instruction streams of the 64-row attention kernel.
+"""Writes attn_w64_asm.h: the tile loop of the 64-row attention kernel as one asm program.
 
 Run from this directory (`python3 gen_attn_w64.py > attn_w64_asm.h`); the header is committed
 and a host test checks that it matches this script's output.
@@ -7,52 +7,58 @@ One wave owns 64 query rows (two 32-row blocks qb) of one (element, head).  Per 
 issues 64 MFMAs 32x32x16 bf16 fed by 32 LDS fragment reads (each read feeds both row blocks):
   QK:  S^T[kb][qb] = K[kb] Q^T[qb]      16 K reads (kb-major, 8 k steps each)
   PV:  O^T[db][qb] += V^T[db] P^T[qb]   16 V^T reads (key step ks-major, d block db)
-and, interleaved with the PV MFMAs, the softmax of the tile's S: exp2(S*scale_log2 - m) rounded
-to bf16 P^T words for the next tile's PV, with per-lane tile sums by dot2 over the packed P.
+and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete after the
+16th), the softmax of the tile's S: exp2(S*scale_log2 - m) rounded to bf16 P^T words for the
+next tile's PV, with per-lane tile sums.
 
-Blocks (one asm statement each; every state register is an asm operand, so the compiler never
-moves them):
-  TILE_P{pp}, TILE_MASKED_P{pp}  QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp,
-                                 the lazy test (trig != 0: some lane's tile sum left [0, 256]),
-                                 l += tile sums when trig == 0, LDS address steps
-  RARE_P{pc}, RARE_MASKED_P{pc}  the rescale: masked row max, m, alpha, O and l scaled, P of
-                                 the tile recomputed into buffer pc, l += its sums
-  PV_ONLY_P{pp}                  the last PV
-The masked variants AND every P word with a ragged-tile mask (keys >= nvalid) and a per-row-
-block causal mask (own frame tk after the row's frame), both computed at the block start.
+Iteration t (every state register is an asm operand, so the compiler never moves them):
+  wait for the loads of iteration t-2, barrier; branch on mflag(t) to the masked variant
+  tile block: QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this wave's eight
+    1 KB tile loads (K(t+2), V^T(t+1)) spread over the stream, and, in the free issue slots of
+    the QK part, the scalar set-up of iteration t+1 (load cursors, bases and ring slots, the
+    walk cursor and mflag of tile t+1, LDS read address steps); then the lazy test
+    (trig != 0: some lane's tile sum left [0, 256] or is not finite)
+  trig == 0: l += tile sums; otherwise (out of line) the rescale: masked row max, m, alpha,
+    O and l scaled, P of the tile recomputed into buffer 1-pp, l += its sums
+After the loop the last PV.  Set-up values alternate between two register sets by iteration
+parity, so the loads of iteration t read one set while the stream writes the other.  The
+masked variant ANDs every P word with a ragged-tile mask (keys >= nvalid) and a per-row-block
+causal mask (own frame tk after the row's frame), both computed at the block start.
 
 Register plan (per lane):
   a[0:127]    O^T  o[db][qb] at a[(2db+qb)*16 .. +15]
   a[128:191]  Q^T  q[qb][kd] at a[128 + (8qb+kd)*4 .. +3]
   v[0:63]     S^T  s[kb][qb] at v[(2kb+qb)*16 .. +15]
   v[64:127]   P^T  two buffers, p[qb][ks] at base + (4qb+ks)*4, base 64 or 96
-  v[128:175]  fragment ring, 12 slots of 4 (also DMA offsets and rare-path temporaries)
+  v[128:175]  fragment ring, 12 slots of 4 (also rare-path temporaries)
   v[176:183]  K fragment LDS addresses per k step kd;  v[184:187] V^T addresses per key step
   v[188:199]  temporaries
-  v[200:201]  m per qb (running max, log2 units);  v[202:205] tile sums (two per qb)
+  v[200:201]  m per qb (running max, log2 units)
   v[206:221]  ragged masks of the 16 P words of a row block;  v[222:223] causal mask per qb
   v[224] 8g;  v[225:226] frame of the lane's row per qb;  v[227] (lane ^ 32) * 4
   v[228:229]  l per qb;  v[230:237] K and V^T lane offsets of the tile loads;  v238 frame slots
+  v[248:255]  tile sums, four per qb
+  s[84:91]    global bases of the K and V^T tile loads, two sets by iteration parity
 
 Hazards kept by construction (gfx950, counted in issued instructions): an MFMA result is read
-by no VALU or MFMA A/B operand within 12 instructions (checked below; S of kb = 1 is complete
-after MFMA 31 and first read at MFMA 48; the rare block starts with 16 wait states); VALU-
-written P words are read by MFMAs of the next tile only; an exponential's result is read at
-least one instruction later; a dot2 result is read by an instruction other than the next
-dot2 of the same sum only after 3 wait states (gfx950 does not interlock it: reading the sums
-right after the last dot2 lost its update, measured);
-a fragment slot is refilled at least 12 instructions after the
-last MFMA that reads it (an MFMA may read its A operand after issue, so 8 reads in flight use
-a ring of 12 slots);
-same-accumulator MFMAs chain back to back (allowed); VOP3 forms read at most one SGPR.
+by no VALU or MFMA A/B operand within 12 instructions (checked below; the rare block starts
+with 16 wait states); VALU-written P words are read by MFMAs of the next tile only; an
+exponential's result is read at least one instruction later; a fragment slot is refilled at
+least 12 instructions after the last MFMA that reads it (an MFMA may read its A operand after
+issue, so 8 reads in flight use a ring of 12 slots); an LDS DMA load does not directly follow
+a write of m0; same-accumulator MFMAs chain back to back (allowed); VOP3 forms read at most one
+SGPR.  Measured on gfx950 and avoided: a dot2 (v_dot2_f32_bf16) waits for the MFMA in flight
+to finish, and its result is not interlocked for a non-dot2 reader (3 wait states needed).
 """
 import sys
 
 KA = 8                                           # fragment reads in flight
 RING = 12                                        # fragment slots: a slot is refilled 4 reads after its last use
 FR, KADDR, VADDR = 128, 176, 184
-TMP, M, TS, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 202, 206, 222, 224, 225, 227, 228
+TMP, M, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 206, 222, 224, 225, 227, 228
+TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
+SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
 
 
 def o_reg(db, qb):
@@ -102,6 +108,8 @@ def word_key(j):
 
 
 def k_reads():
+    # kb-major: S^T of key block 0 is complete after the first 16 MFMAs, so the softmax of its
+    # half of the tile overlaps the key block 1 MFMAs
     return [("K", kb, kd) for kb in range(2) for kd in range(8)]
 
 
@@ -132,12 +140,14 @@ def mfma_pair(r, slot, pp):
 
 
 def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
-    """Groups of 4 values (kb-major, so the kb = 0 half only needs the first 16 QK MFMAs):
-    4 FMAs, 4 exponentials, 2 packs into P words (masked: AND with the word's ragged mask and
-    the row block's causal mask), 2 dot2 row sums into the two sums of the row block.  mreg(qb): register holding m; sums(qb, i):
-    the two tile-sum accumulators."""
+    """Groups of 4 values: 4 FMAs, 4 exponentials, 2 packs into P words, 4 adds into the four
+    tile sums of the row block.  Unmasked, the sums add the fp32 exponentials; masked, every P
+    word is ANDed with its ragged-tile mask and the row block's causal mask and the sums add
+    the two bf16 halves of the masked words, so masked keys add nothing.  (Row sums by dot2
+    would be shorter, but gfx950 holds a dot2 back until the MFMA in flight has finished.)
+    mreg(qb): register holding m; sums(qb, i): the four tile-sum accumulators."""
     mreg = mreg or (lambda qb: f"v{M + qb}")
-    sums = sums or (lambda qb, i: f"v{TS + 2 * qb + i}")
+    sums = sums or (lambda qb, i: f"v{TS + 4 * qb + i}")
     ops = []
     gi = 0
     for kb in range(2):
@@ -160,11 +170,11 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                             j = ks * 4 + w0 + wi
                             ops.append(f"v_and_b32 {w}, {w}, v{RMASK + j}")
                             ops.append(f"v_and_b32 {w}, {w}, v{CMASK + qb}")
-                    # word 0 into sum 0, word 1 into sum 1: a sum is accumulated again only
-                    # one group (>= 10 instructions) later (dependent dot2 need spacing)
-                    for i, wd in enumerate(words):
-                        acc = sums(qb, i)
-                        ops.append(f"v_dot2_f32_bf16 {acc}, {wd}, %[ones], {acc}")
+                        for wi, w in enumerate(words):
+                            ops.append(f"v_lshlrev_b32 {t[2 * wi]}, 16, {w}")
+                            ops.append(f"v_and_b32 {t[2 * wi + 1]}, 0xffff0000, {w}")
+                    for j in range(4):
+                        ops.append(f"v_add_f32 {sums(qb, j)}, {sums(qb, j)}, {t[j]}")
     return ops
 
 
@@ -187,57 +197,69 @@ def mask_setup():
     return lines
 
 
-def stream(reads, pp, valu):
-    """Reads KA ahead of their MFMAs; VALU ops spread evenly over the PV MFMAs."""
+def stream(reads, pp, valu, dma=None, valu_from=0, extra=None):
+    """Reads KA ahead of their MFMAs; VALU ops spread evenly over the MFMAs from index
+    valu_from on.  dma maps a read index i to (m0 setup, tile load): the setup follows the MFMA
+    pair of read i and the load the LDS read issued after it, so the tile loads of a wave are
+    spread over the tile instead of queueing behind the other waves' loads at the texture unit.
+    extra maps a read index to instructions placed after its MFMA pair (scalar bookkeeping,
+    each list self-contained in its use of SCC)."""
+    dma = dma or {}
+    extra = extra or {}
     lines = []
     for i in range(min(KA, len(reads))):
         lines.append(read_instr(reads[i], i % RING))
     issued = min(KA, len(reads))
-    pv_first = next(i for i, r in enumerate(reads) if r[0] == "V")
-    n_pv_mfma = 2 * (len(reads) - pv_first)
-    per = [0] * n_pv_mfma
+    n_mfma = 2 * len(reads)
+    per = [0] * n_mfma
     for i in range(len(valu)):
-        per[i * n_pv_mfma // len(valu)] += 1
+        per[valu_from + i * (n_mfma - valu_from) // len(valu)] += 1
     vi = 0
     for i, r in enumerate(reads):
         lines.append(f"s_waitcnt lgkmcnt({min(issued - (i + 1), 15)})")
         for j, m in enumerate(mfma_pair(r, i % RING, pp)):
             lines.append(m)
-            if i >= pv_first:
-                k = 2 * (i - pv_first) + j
-                for _ in range(per[k]):
-                    lines.append(valu[vi])
-                    vi += 1
+            for _ in range(per[2 * i + j]):
+                lines.append(valu[vi])
+                vi += 1
+        lines += extra.get(i, [])
+        if i in dma:
+            lines.append(dma[i][0])
         if i + KA < len(reads):
             lines.append(read_instr(reads[i + KA], (i + KA) % RING))
             issued += 1
+        elif i in dma:
+            lines.append("s_nop 0")
+        if i in dma:
+            lines.append(dma[i][1])
     assert vi == len(valu)
     lines.append("s_waitcnt lgkmcnt(0)")
     return lines
 
 
-def tile_block(pp, masked, tag=""):
+def tile_block(pp, par, masked):
+    """QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this iteration's tile
+    loads (parity par) and the next iteration's scalar set-up, then the lazy test (trig != 0:
+    some lane's tile sum left [0, 256] or is not finite)."""
     pc = 1 - pp
     lines = mask_setup() if masked else []
-    lines += [f"v_mov_b32 v{TS + i}, 0" for i in range(4)]
-    lines += stream(k_reads() + v_reads(), pp, softmax_ops(pc, masked))
-    # lazy test and the common-path row sums (a dot2 result is read by another VALU op only
-    # after 3 wait states)
-    lines += ["s_nop 3",
-              f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
-              f"v_add_f32 v{TMP + 1}, v{TS + 2}, v{TS + 3}",
+    extra = {2: load_setup("K", 1 - par, 3)[:8], 3: load_setup("K", 1 - par, 3)[8:],
+             4: load_setup("V", 1 - par, 2)[:8], 5: load_setup("V", 1 - par, 2)[8:],
+             6: walk_setup(1 - par, True),
+             7: [f"v_mov_b32 v{TS + i}, 0" for i in range(8)],
+             8: read_step("K"), 24: read_step("V")}
+    lines += stream(k_reads() + v_reads(), pp, softmax_ops(pc, masked), tile_loads(par), SM_FROM, extra)
+    lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
+              f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
+              f"v_add_f32 v{TMP + 2}, v{TS + 2}, v{TS + 3}",
+              f"v_add_f32 v{TMP + 3}, v{TS + 6}, v{TS + 7}",
+              f"v_add_f32 v{TMP}, v{TMP}, v{TMP + 2}",
+              f"v_add_f32 v{TMP + 1}, v{TMP + 1}, v{TMP + 3}",
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP}",
               "s_mov_b64 %[trig], vcc",
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP + 1}",
               "s_or_b64 %[trig], %[trig], vcc",
-              "s_cmp_eq_u64 %[trig], 0",
-              f"s_cbranch_scc0 .Lw64_keep{tag}_%=",
-              f"v_add_f32 v{L}, v{L}, v{TMP}",
-              f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}",
-              f".Lw64_keep{tag}_%=:"]
-    lines += [f"v_add_u32 v{KADDR + kd}, %[kstep], v{KADDR + kd}" for kd in range(8)]
-    lines += [f"v_add_u32 v{VADDR + ks}, %[vstep], v{VADDR + ks}" for ks in range(4)]
-    lines.append("s_nop 11")
+              "s_nop 11"]
     return lines
 
 
@@ -281,12 +303,10 @@ def rare_block(pc, masked):
             lines += [f"v_mul_f32 {tmps[i]}, {tmps[i]}, {al}" for i in range(4)]
             lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
         # P of the tile at the new m, and its sums
-        s0, s1 = "v140", "v141"
-        lines += [f"v_mov_b32 {s0}, 0", f"v_mov_b32 {s1}, 0"]
-        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: mm,
-                             sums=lambda _q, i: s0 if i == 0 else s1)
-        lines += ["s_nop 3", f"v_add_f32 v{L + qb}, v{L + qb}, {s0}", f"v_add_f32 v{L + qb}, v{L + qb}, {s1}"]
-    lines.append("s_nop 3")
+        ss = [f"v{140 + i}" for i in range(4)]
+        lines += [f"v_mov_b32 {x}, 0" for x in ss]
+        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: mm, sums=lambda _q, i: ss[i])
+        lines += [f"v_add_f32 v{L + qb}, v{L + qb}, {x}" for x in ss]
     return lines
 
 
@@ -295,7 +315,7 @@ def init_block():
     lines = [f"v_accvgpr_write_b32 a{i}, 0" for i in range(128)]
     lines += [f"v_mov_b32 v{i}, 0" for i in range(128)]
     lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
-    lines += [f"v_mov_b32 v{i}, 0" for i in list(range(TS, CMASK + 2)) + [L, L + 1]]
+    lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
     return lines
 
 
@@ -306,13 +326,19 @@ def pv_only_block(pp):
 def check_hazards(lines):
     """An MFMA result is not read by a VALU op within 12 instructions; a register an MFMA reads
     is not overwritten by an LDS read within 12 instructions; an exponential's result is not
-    read by the next instruction."""
+    read by the next instruction; a dot2 result is read by another op only after 3 wait
+    states; an LDS DMA load does not directly follow the write of m0."""
     last_write = {}
     last_exp = {}
     last_mfma_read = {}
     last_dot = {}
+    last_m0 = -100
     for idx, l in enumerate(lines):
         op = l.split()[0] if l.split() else ""
+        if op.startswith("s_") and op != "s_nop" and len(l.split()) > 1 and l.split()[1].rstrip(",") == "m0":
+            last_m0 = idx
+        if op.startswith("global_load_lds"):
+            assert idx - last_m0 >= 2, (l, "m0 written by the previous instruction")
         if op.startswith("v_mfma"):
             dst = l.split()[1].rstrip(",")
             lo = int(dst[2:].split(":")[0])
@@ -353,100 +379,113 @@ def check_hazards(lines):
             last_exp = {k: v - n for k, v in last_exp.items()}
             last_mfma_read = {k: v - n for k, v in last_mfma_read.items()}
             last_dot = {k: v - n for k, v in last_dot.items()}
+            last_m0 -= n
 
 
 KOFF, VOFF, SLOTL = 230, 234, 238
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
 
 
-def wait_loads(tag):
-    """Own loads of K(t), V(t-1) in: vmcnt(nlprev), nlprev in {0, 4, 8}."""
-    return ["s_cmp_eq_u32 %[nlprev], 8", f"s_cbranch_scc1 .Lw64_w8{tag}_%=",
-            "s_cmp_eq_u32 %[nlprev], 4", f"s_cbranch_scc1 .Lw64_w4{tag}_%=",
-            "s_waitcnt vmcnt(0)", f"s_branch .Lw64_wd{tag}_%=",
-            f".Lw64_w8{tag}_%=:", "s_waitcnt vmcnt(8)", f"s_branch .Lw64_wd{tag}_%=",
-            f".Lw64_w4{tag}_%=:", "s_waitcnt vmcnt(4)",
-            f".Lw64_wd{tag}_%=:"]
+BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
 
 
-def dma(kind, tag):
-    """Load the next K (t+2) or V^T (t+1) tile if it exists: advance the cursor, offset of the
-    tile inside the (layer, head) block, four 1 KB loads of this wave's share into ring slot
-    (offset kl / vl, advanced first), lane offsets koff / voff."""
-    f, k, blk, lo, off, ahead, mbase, colb = (("kf", "kk", "kblk", "kl", KOFF, 2, "mk", 14) if kind == "K"
-                                              else ("vf", "vk", "vblk", "vl", VOFF, 1, "mv", 7))
-    skip = f".Lw64_no{kind}{tag}_%="
-    lines = [f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", f"s_cbranch_scc0 {skip}",
-             f"s_add_u32 %[{k}], %[{k}], 1", f"s_cmp_eq_u32 %[{k}], %[tpf]",
-             f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0",
-             f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]",
-             "s_mul_i32 %[x], %[x], %[slotb]",
-             f"s_lshl_b32 %[y], %[{k}], {colb}",       # tile within the frame: 16 KB of K rows / 128 B of V^T columns
-             "s_add_u32 %[x], %[x], %[y]",
-             f"s_add_u32 %[{lo}], %[{lo}], {KTILE}", f"s_cmp_eq_u32 %[{lo}], {3 * KTILE}",
-             f"s_cselect_b32 %[{lo}], 0, %[{lo}]",
-             f"s_add_u32 m0, %[{mbase}], %[{lo}]"]
-    for i in range(4):
-        lines += [f"v_add_u32 v{128 + 4 * (kind == 'V') + i}, %[x], v{off + i}"]
-    for i in range(4):
-        if i:
-            lines.append("s_add_u32 m0, m0, 1024")
-        lines.append(f"global_load_lds_dwordx4 v{128 + 4 * (kind == 'V') + i}, %[{blk}]")
-    lines += ["s_add_u32 %[nl], %[nl], 4", f"{skip}:"]
-    return lines
+def tile_loads(par):
+    """Read index -> (m0 setup, load) of this wave's four 1 KB K loads (after reads 1, 5, 9, 13)
+    and four V^T loads (after reads 17, 21, 25, 29); m0 holds the LDS destination, the SGPR
+    pair of parity par the global tile base and v[230:237] the lane offsets."""
+    d = {}
+    for first, m0reg, base, v0 in ((1, f"dk{par}", BASE[par][0], KOFF), (17, f"dv{par}", BASE[par][1], VOFF)):
+        for i in range(4):
+            setup = f"s_mov_b32 m0, %[{m0reg}]" if i == 0 else "s_add_u32 m0, m0, 1024"
+            d[first + 4 * i] = (setup, f"global_load_lds_dwordx4 v{v0 + i}, s[{base}:{base + 1}]")
+    return d
 
 
-def iteration(pp, tag):
-    """Iteration t < n (P buffer pp read by PV(t-1), P(t) written into 1 - pp)."""
-    pc = 1 - pp
-    lines = wait_loads(tag) + ["s_barrier", "s_mov_b32 %[nl], 0"]
-    lines += dma("K", tag) + dma("V", tag)
-    lines += ["s_mov_b32 %[nlprev], %[nl]",
-              # tile t: valid keys, own frame index, masked?
-              "s_lshl_b32 %[x], %[sk], 6", "s_sub_i32 %[nvalid], %[N], %[x]",
+def load_setup(kind, par, ahead):
+    """Set-up of the loads of K (t + ahead) or V^T (t + ahead) for the iteration of parity par:
+    the cursor advances when that tile exists (otherwise the loads repeat the last tile, a valid
+    address, into the free slot, so every iteration issues eight loads and one vmcnt serves
+    all), the ring slot advances, and the global base and LDS destination are set."""
+    f, k, lo, mbase, colb, blo, bhi, d, base = (
+        ("kf", "kk", "kl", "mk", 14, "kblo", "kbhi", f"dk{par}", BASE[par][0]) if kind == "K"
+        else ("vf", "vk", "vl", "mv", 7, "vblo", "vbhi", f"dv{par}", BASE[par][1]))
+    return [f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0",
+            f"s_add_u32 %[{k}], %[{k}], %[y]", f"s_cmp_eq_u32 %[{k}], %[tpf]",
+            f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0",
+            f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]",
+            # tile offset in the (layer, head) block: slot * slot bytes + tile (16 KB of K rows or
+            # 128 B of V^T columns)
+            "s_mul_i32 %[x], %[x], %[slotb]",
+            f"s_lshl_b32 %[y], %[{k}], {colb}",
+            "s_add_u32 %[x], %[x], %[y]",
+            f"s_add_u32 s{base}, %[{blo}], %[x]", f"s_addc_u32 s{base + 1}, %[{bhi}], 0",
+            f"s_add_u32 %[{lo}], %[{lo}], {KTILE}", f"s_cmp_eq_u32 %[{lo}], {3 * KTILE}",
+            f"s_cselect_b32 %[{lo}], 0, %[{lo}]",
+            f"s_add_u32 %[{d}], %[{mbase}], %[{lo}]"]
+
+
+def walk_setup(par, advance):
+    """Tile t+1 of the softmax walk (tile 0 when advance is False): cursor, valid keys, own frame
+    index tk, and mflag of parity par (1: ragged or partly causal, take the masked block)."""
+    lines = []
+    if advance:
+        lines += ["s_add_u32 %[x], %[t], 1", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0",
+                  "s_add_u32 %[sk], %[sk], %[y]", "s_cmp_eq_u32 %[sk], %[tpf]",
+                  "s_cselect_b32 %[sk], 0, %[sk]", "s_addc_u32 %[sf], %[sf], 0"]
+    lines += ["s_lshl_b32 %[x], %[sk], 6", "s_sub_i32 %[nvalid], %[N], %[x]",
               "s_min_i32 %[nvalid], %[nvalid], 64",
               "s_sub_i32 %[tk], %[sf], %[nshared]",
-              "s_cmp_lt_i32 %[nvalid], 64", "s_cselect_b32 %[mflag], 1, 0",
+              "s_cmp_lt_i32 %[nvalid], 64", f"s_cselect_b32 %[mflag{par}], 1, 0",
               "s_cmp_gt_i32 %[tk], %[tqw]", "s_cselect_b32 %[x], 1, 0",
-              "s_or_b32 %[mflag], %[mflag], %[x]",
-              # LDS read address steps to K(t+1), V(t)
-              f"s_movk_i32 %[kstep], {KTILE}", f"s_movk_i32 %[x], {hex((-2 * KTILE) & 0xffff)}",
-              "s_cmp_eq_u32 %[krd], 2", "s_cselect_b32 %[kstep], %[x], %[kstep]",
-              "s_add_u32 %[krd], %[krd], 1", "s_cmp_eq_u32 %[krd], 3", "s_cselect_b32 %[krd], 0, %[krd]",
-              f"s_movk_i32 %[vstep], {KTILE}",
-              "s_cmp_eq_u32 %[vrd], 2", "s_cselect_b32 %[vstep], %[x], %[vstep]",
-              "s_add_u32 %[vrd], %[vrd], 1", "s_cmp_eq_u32 %[vrd], 3", "s_cselect_b32 %[vrd], 0, %[vrd]",
-              "s_cmp_eq_u32 %[mflag], 0", f"s_cbranch_scc0 .Lw64_m{tag}_%="]
-    lines += tile_block(pp, False, tag + "u")
-    lines += [f"s_branch .Lw64_td{tag}_%=", f".Lw64_m{tag}_%=:"]
-    lines += tile_block(pp, True, tag + "m")
-    lines += [f".Lw64_td{tag}_%=:",
-              "s_cmp_eq_u64 %[trig], 0", f"s_cbranch_scc1 .Lw64_nr{tag}_%=",
-              "s_cmp_eq_u32 %[mflag], 0", f"s_cbranch_scc1 .Lw64_ru{tag}_%="]
-    lines += rare_block(pc, True)
-    lines += [f"s_branch .Lw64_nr{tag}_%=", f".Lw64_ru{tag}_%=:"]
-    lines += rare_block(pc, False)
-    lines += [f".Lw64_nr{tag}_%=:",
-              # next tile of the softmax walk
-              "s_add_u32 %[x], %[t], 1", "s_cmp_lt_u32 %[x], %[n]", f"s_cbranch_scc0 .Lw64_ns{tag}_%=",
-              "s_add_u32 %[sk], %[sk], 1", "s_cmp_eq_u32 %[sk], %[tpf]",
-              "s_cselect_b32 %[sk], 0, %[sk]", "s_addc_u32 %[sf], %[sf], 0",
-              f".Lw64_ns{tag}_%=:",
-              "s_add_u32 %[t], %[t], 1"]
+              f"s_or_b32 %[mflag{par}], %[mflag{par}], %[x]"]
     return lines
+
+
+def read_step(kind):
+    """LDS read addresses from tile t's ring slot to the next one (placed after the last read of
+    tile t from that ring has issued)."""
+    rd, step, base, n = (("krd", "kstep", KADDR, 8) if kind == "K" else ("vrd", "vstep", VADDR, 4))
+    return ([f"s_movk_i32 %[{step}], {KTILE}", f"s_movk_i32 %[x], {hex((-2 * KTILE) & 0xffff)}",
+             f"s_cmp_eq_u32 %[{rd}], 2", f"s_cselect_b32 %[{step}], %[x], %[{step}]",
+             f"s_add_u32 %[{rd}], %[{rd}], 1", f"s_cmp_eq_u32 %[{rd}], 3", f"s_cselect_b32 %[{rd}], 0, %[{rd}]"]
+            + [f"v_add_u32 v{base + i}, %[{step}], v{base + i}" for i in range(n)])
+
+
+def iteration(pp, par, tag):
+    """Iteration t < n of parity par (P buffer pp read by PV(t-1), P(t) written into 1 - pp).
+    The masked tile block and the rescale are out of line (see out_of_line)."""
+    return [# loads of iteration t-2 (K(t), V^T(t-1)) in; every wave is done with iteration t-1's slots
+            "s_waitcnt vmcnt(8)", "s_barrier",
+            f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc0 .Lw64_m{tag}_%="] + \
+        tile_block(pp, par, False) + \
+        [f".Lw64_td{tag}_%=:",
+         "s_cmp_eq_u64 %[trig], 0", f"s_cbranch_scc0 .Lw64_r{tag}_%=",
+         f"v_add_f32 v{L}, v{L}, v{TMP}", f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}",
+         f".Lw64_nr{tag}_%=:",
+         "s_add_u32 %[t], %[t], 1"]
+
+
+def out_of_line(pp, par, tag):
+    pc = 1 - pp
+    return ([f".Lw64_m{tag}_%=:"] + tile_block(pp, par, True) + [f"s_branch .Lw64_td{tag}_%=",
+            f".Lw64_r{tag}_%=:", f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc1 .Lw64_ru{tag}_%="]
+            + rare_block(pc, True) + [f"s_branch .Lw64_nr{tag}_%=", f".Lw64_ru{tag}_%=:"]
+            + rare_block(pc, False) + [f"s_branch .Lw64_nr{tag}_%="])
 
 
 def loop_program():
-    """The whole tile loop: iterations t = 0 .. n-1 (two per pass, P buffer parity fixed),
-    then the last PV.  m0 is saved and restored."""
+    """The whole tile loop: iterations t = 0 .. n-1 (two per pass: P buffer and set-up parity
+    fixed), then the last PV.  m0 is saved and restored."""
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
-    lines += [".Lw64_loop_%=:"] + iteration(1, "a")
+    lines += walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1)
+    lines += [".Lw64_loop_%=:"] + iteration(1, 0, "a")
     lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc0 .Lw64_end_%="]
-    lines += iteration(0, "b")
+    lines += iteration(0, 1, "b")
     lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc1 .Lw64_loop_%=",
-              ".Lw64_end_%=:"] + wait_loads("z") + ["s_barrier",
+              ".Lw64_end_%=:", "s_waitcnt vmcnt(0)", "s_barrier",
               "s_bitcmp1_b32 %[n], 0", "s_cbranch_scc0 .Lw64_pv1_%="]
     lines += pv_only_block(0) + ["s_branch .Lw64_fin_%=", ".Lw64_pv1_%=:"] + pv_only_block(1)
+    lines += ["s_branch .Lw64_fin_%="] + out_of_line(1, 0, "a") + out_of_line(0, 1, "b")
     lines += [".Lw64_fin_%=:", "s_mov_b32 m0, %[m0save]"]
     return lines
 

@@ -10,7 +10,8 @@
 // (two 32-row blocks qb) every fragment feeds two MFMAs.  The state then needs
 //   O^T 128 + Q^T 64 (AGPRs) and S^T 64 + P^T 2 x 32 + fragments 48 (VGPRs),
 // which fits one wave per SIMD only.  The softmax of tile t is interleaved with the MFMAs of
-// the same wave (P V of tile t-1), so the wave overlaps its own VALU and matrix work.  That
+// the same wave (QK of its key block 1, P V of tile t-1), so the wave overlaps its own VALU and
+// matrix work; scalar set-up and tile loads sit in the remaining issue slots.  That
 // needs an instruction order and a register assignment the compiler does not produce, so the
 // whole tile loop (tile walk, global->LDS loads, waits, barriers, the 64 MFMAs and 32 fragment
 // reads of a tile, the softmax, masks and the rare rescale) is one generated asm program
@@ -26,8 +27,9 @@
 // (vmcnt) two iterations after issue, before that iteration's barrier.
 //
 // Softmax: base 2 with the lazy-max rule of the other kernel: exponentials at the running max
-// m; only when a lane's tile sum of the bf16-rounded P leaves [0, 256] (first tile, NaN, or a
-// score far above m) is the row max taken and O, l rescaled.  Masks (ragged last tile of a
+// m; only when a lane's tile sum of P leaves [0, 256] (first tile, NaN, or a score far above
+// m) is the row max taken and O, l rescaled.  The row sums l add the fp32 exponentials (the
+// masked tiles: the bf16 values kept by the masks).  Masks (ragged last tile of a
 // frame, block-causal own frames) are applied to the packed P words by AND with per-lane masks.
 #include "common.h"
 #include "attn_tiles.h"
@@ -156,7 +158,8 @@ void attn_w64_kernel(const AttnArgs a) {
   };
 
   // Prologue: V^T slot 2 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
-  // slot 1, V(0) into slot 0.
+  // slot 1 (K(0) again when n = 1: the loop counts twelve loads in flight at its start), V(0)
+  // into slot 0.
 #pragma unroll
   for (int i = 0; i < V_BYTES / (256 * 16); ++i)
     reinterpret_cast<uint4*>(ldsV + 2 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
@@ -164,10 +167,8 @@ void attn_w64_kernel(const AttnArgs a) {
   const TileCursor c0 = cursor_at(t_begin);
   TileCursor kc = c0;
   fill_k(kc, 0);
-  if (n > 1) {
-    advance(kc);
-    fill_k(kc, 1);
-  }
+  if (n > 1) advance(kc);
+  fill_k(kc, 1);
   fill_v(c0, 0);
 
   // The tile loop (generated asm, see gen_attn_w64.py).  Its state lives in the registers
@@ -197,40 +198,43 @@ void attn_w64_kernel(const AttnArgs a) {
   i32x16 frg2;
   i32x12 tmp;
   f32x2 mrun, lrun;
-  f32x4 tsum;
+  i32x8 tsum;
   i32x16 rmask;
   i32x2 cmask;
   // scalar state: cursors (frame, tile in frame) of the last K and V^T tiles loaded and of the
   // tile t, iteration t, ring offsets, read-slot indices, loads in flight
   int kf = kc.f, kk = kc.k, vf = c0.f, vk = c0.k, sf = c0.f, sk = c0.k, t = 0;
-  int krd = 0, vrd = 2, kl = K_BYTES, vl = 0, nlprev = (n > 1 ? 2 : 1) * LD;
+  int krd = 0, vrd = 2, kl = K_BYTES, vl = 0;
   const uint64_t kblk64 = (uint64_t)(uintptr_t)kblk, vblk64 = (uint64_t)(uintptr_t)vblk;
+  const uint32_t kblo = (uint32_t)kblk64, kbhi = (uint32_t)(kblk64 >> 32);
+  const uint32_t vblo = (uint32_t)vblk64, vbhi = (uint32_t)(vblk64 >> 32);
   const int slotb = (int)slot_bytes, tpf = a.tiles_per_frame, nshared = a.nshared, Ntok = a.N;
   const int mk = (int)((uint32_t)(uintptr_t)ldsK + wave * LD * 1024);
   const int mv = (int)((uint32_t)(uintptr_t)ldsV + wave * LD * 1024);
   const float sl = a.scale_log2;
   const int ones = 0x3F803F80;                // bf16 (1, 1)
   unsigned long long trig;
-  int x, y, nvalid, tk, kstep, vstep, nl, mflag, m0save, stmp;
+  int x, y, nvalid, tk, kstep, vstep, dk0, dk1, dv0, dv1, mflag0, mflag1, m0save, stmp;
   asm volatile(SDV2_W64_LOOP
                : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
                  "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),
                  "={v[128:159]}"(frg), "={v[160:175]}"(frg2), "+{v[176:183]}"(kaddr),
                  "+{v[184:187]}"(vaddr), "={v[188:199]}"(tmp), "={v[200:201]}"(mrun),
-                 "={v[202:205]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),
+                 "={v[248:255]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),
                  "={v[228:229]}"(lrun),
                  [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk), [sf] "+s"(sf),
                  [sk] "+s"(sk), [t] "+s"(t), [krd] "+s"(krd), [vrd] "+s"(vrd), [kl] "+s"(kl),
-                 [vl] "+s"(vl), [nlprev] "+s"(nlprev),
+                 [vl] "+s"(vl),
                  [trig] "=&s"(trig), [x] "=&s"(x), [y] "=&s"(y), [nvalid] "=&s"(nvalid),
-                 [tk] "=&s"(tk), [kstep] "=&s"(kstep), [vstep] "=&s"(vstep), [nl] "=&s"(nl),
-                 [mflag] "=&s"(mflag), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
+                 [tk] "=&s"(tk), [kstep] "=&s"(kstep), [vstep] "=&s"(vstep), [dk0] "=&s"(dk0),
+                 [dk1] "=&s"(dk1), [dv0] "=&s"(dv0), [dv1] "=&s"(dv1), [mflag1] "=&s"(mflag1),
+                 [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
                : "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec),
                  "{v[230:233]}"(koffv), "{v[234:237]}"(voffv), "{v238}"(slot_lane),
                  [n] "s"(n), [tpf] "s"(tpf), [nshared] "s"(nshared), [N] "s"(Ntok),
-                 [tqw] "s"(tq_wave), [kblk] "s"(kblk64), [vblk] "s"(vblk64), [slotb] "s"(slotb),
+                 [tqw] "s"(tq_wave), [kblo] "s"(kblo), [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb),
                  [mk] "s"(mk), [mv] "s"(mv), [sl] "s"(sl), [ones] "s"(ones)
-               : "vcc", "scc", "memory");
+               : "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91");
   (void)frg;
   (void)frg2;
   (void)tmp;
