@@ -59,6 +59,7 @@ TMP, M, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 206, 222, 224, 225, 227, 228
 TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
+GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
 
 
 def o_reg(db, qb):
@@ -141,7 +142,7 @@ def mfma_pair(r, slot, pp):
 
 def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
     """Groups of 4 values: 4 FMAs, 4 exponentials, 2 packs into P words, 4 adds into the four
-    tile sums of the row block.  Unmasked, the sums add the fp32 exponentials; masked, every P
+    tile sums of the row block (the row block's first group sets them).  Unmasked, the sums add the fp32 exponentials; masked, every P
     word is ANDed with its ragged-tile mask and the row block's causal mask and the sums add
     the two bf16 halves of the masked words, so masked keys add nothing.  (Row sums by dot2
     would be shorter, but gfx950 holds a dot2 back until the MFMA in flight has finished.)
@@ -174,7 +175,10 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                             ops.append(f"v_lshlrev_b32 {t[2 * wi]}, 16, {w}")
                             ops.append(f"v_and_b32 {t[2 * wi + 1]}, 0xffff0000, {w}")
                     for j in range(4):
-                        ops.append(f"v_add_f32 {sums(qb, j)}, {sums(qb, j)}, {t[j]}")
+                        if kb == 0 and half == 0 and w0 == 0:      # first group of the row block
+                            ops.append(f"v_mov_b32 {sums(qb, j)}, {t[j]}")
+                        else:
+                            ops.append(f"v_add_f32 {sums(qb, j)}, {sums(qb, j)}, {t[j]}")
     return ops
 
 
@@ -197,23 +201,47 @@ def mask_setup():
     return lines
 
 
-def stream(reads, pp, valu, dma=None, valu_from=0, extra=None):
+def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
     """Reads KA ahead of their MFMAs; VALU ops spread evenly over the MFMAs from index
     valu_from on.  dma maps a read index i to (m0 setup, tile load): the setup follows the MFMA
     pair of read i and the load the LDS read issued after it, so the tile loads of a wave are
     spread over the tile instead of queueing behind the other waves' loads at the texture unit.
-    extra maps a read index to instructions placed after its MFMA pair (scalar bookkeeping,
-    each list self-contained in its use of SCC)."""
+    extra: (first gap, units) chunks of scalar bookkeeping, placed in order and one chunk after
+    the other; a unit (a few instructions, closed in its use of SCC) goes into the gap after an
+    MFMA, from the chunk's first gap on, into the first gap with room for it (at most GAP_CAP
+    instructions besides the MFMA), so the wave can issue it while the matrix core works."""
     dma = dma or {}
-    extra = extra or {}
     lines = []
     for i in range(min(KA, len(reads))):
         lines.append(read_instr(reads[i], i % RING))
     issued = min(KA, len(reads))
     n_mfma = 2 * len(reads)
+    fixed = [0] * n_mfma                         # read, wait and load instructions after MFMA g
+    for i in range(len(reads)):
+        fixed[2 * i + 1] += 1 + (i + KA < len(reads)) + 2 * (i in dma)
+    # VALU ops in order over the gaps from valu_from on, levelling VALU + fixed per gap
     per = [0] * n_mfma
-    for i in range(len(valu)):
-        per[valu_from + i * (n_mfma - valu_from) // len(valu)] += 1
+    region = range(valu_from, n_mfma)
+    level = (len(valu) + sum(fixed[g] for g in region)) / len(region)
+    vi, done, goal = 0, 0, 0.0
+    for g in region:
+        goal += level
+        while vi < len(valu) and done + fixed[g] + per[g] + 1 <= goal + 0.5:
+            per[g] += 1
+            vi += 1
+        done += fixed[g] + per[g]
+    per[n_mfma - 1] += len(valu) - vi
+    load = [per[g] + fixed[g] for g in range(n_mfma)]
+    placed = [[] for _ in range(n_mfma)]
+    g = 0
+    for first, units in extra:
+        # chunks one after another: they share the scratch SGPRs x and y
+        g = max(g, first)
+        for u in units:
+            while g < n_mfma - 1 and load[g] + len(u) > GAP_CAP:
+                g += 1
+            placed[g] += u
+            load[g] += len(u)
     vi = 0
     for i, r in enumerate(reads):
         lines.append(f"s_waitcnt lgkmcnt({min(issued - (i + 1), 15)})")
@@ -222,7 +250,7 @@ def stream(reads, pp, valu, dma=None, valu_from=0, extra=None):
             for _ in range(per[2 * i + j]):
                 lines.append(valu[vi])
                 vi += 1
-        lines += extra.get(i, [])
+            lines += placed[2 * i + j]
         if i in dma:
             lines.append(dma[i][0])
         if i + KA < len(reads):
@@ -243,11 +271,10 @@ def tile_block(pp, par, masked):
     some lane's tile sum left [0, 256] or is not finite)."""
     pc = 1 - pp
     lines = mask_setup() if masked else []
-    extra = {2: load_setup("K", 1 - par, 3)[:8], 3: load_setup("K", 1 - par, 3)[8:],
-             4: load_setup("V", 1 - par, 2)[:8], 5: load_setup("V", 1 - par, 2)[8:],
-             6: walk_setup(1 - par, True),
-             7: [f"v_mov_b32 v{TS + i}, 0" for i in range(8)],
-             8: read_step("K"), 24: read_step("V")}
+    # first gaps: the K read address step after the last K read of the tile has issued (read
+    # 15, issued after MFMA 15), the V^T one after read 31 (issued after MFMA 47)
+    extra = [(0, load_setup("K", 1 - par, 3)), (0, load_setup("V", 1 - par, 2)),
+             (0, walk_setup(1 - par, True)), (16, read_step("K")), (48, read_step("V"))]
     lines += stream(k_reads() + v_reads(), pp, softmax_ops(pc, masked), tile_loads(par), SM_FROM, extra)
     lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
               f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
@@ -304,7 +331,6 @@ def rare_block(pc, masked):
             lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
         # P of the tile at the new m, and its sums
         ss = [f"v{140 + i}" for i in range(4)]
-        lines += [f"v_mov_b32 {x}, 0" for x in ss]
         lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: mm, sums=lambda _q, i: ss[i])
         lines += [f"v_add_f32 v{L + qb}, v{L + qb}, {x}" for x in ss]
     return lines
@@ -405,50 +431,52 @@ def load_setup(kind, par, ahead):
     """Set-up of the loads of K (t + ahead) or V^T (t + ahead) for the iteration of parity par:
     the cursor advances when that tile exists (otherwise the loads repeat the last tile, a valid
     address, into the free slot, so every iteration issues eight loads and one vmcnt serves
-    all), the ring slot advances, and the global base and LDS destination are set."""
+    all), the ring slot advances, and the global base and LDS destination are set.  Returned
+    as units (instruction lists closed in their use of SCC)."""
     f, k, lo, mbase, colb, blo, bhi, d, base = (
         ("kf", "kk", "kl", "mk", 14, "kblo", "kbhi", f"dk{par}", BASE[par][0]) if kind == "K"
         else ("vf", "vk", "vl", "mv", 7, "vblo", "vbhi", f"dv{par}", BASE[par][1]))
-    return [f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0",
-            f"s_add_u32 %[{k}], %[{k}], %[y]", f"s_cmp_eq_u32 %[{k}], %[tpf]",
-            f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0",
-            f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]",
+    return [[f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0"],
+            [f"s_add_u32 %[{k}], %[{k}], %[y]"],
+            [f"s_cmp_eq_u32 %[{k}], %[tpf]", f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0"],
+            [f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]"],
             # tile offset in the (layer, head) block: slot * slot bytes + tile (16 KB of K rows or
             # 128 B of V^T columns)
-            "s_mul_i32 %[x], %[x], %[slotb]",
-            f"s_lshl_b32 %[y], %[{k}], {colb}",
-            "s_add_u32 %[x], %[x], %[y]",
-            f"s_add_u32 s{base}, %[{blo}], %[x]", f"s_addc_u32 s{base + 1}, %[{bhi}], 0",
-            f"s_add_u32 %[{lo}], %[{lo}], {KTILE}", f"s_cmp_eq_u32 %[{lo}], {3 * KTILE}",
-            f"s_cselect_b32 %[{lo}], 0, %[{lo}]",
-            f"s_add_u32 %[{d}], %[{mbase}], %[{lo}]"]
+            [f"s_lshl_b32 %[y], %[{k}], {colb}"],
+            ["s_mul_i32 %[x], %[x], %[slotb]"],
+            ["s_add_u32 %[x], %[x], %[y]"],
+            [f"s_add_u32 s{base}, %[{blo}], %[x]", f"s_addc_u32 s{base + 1}, %[{bhi}], 0"],
+            [f"s_add_u32 %[{lo}], %[{lo}], {KTILE}"],
+            [f"s_cmp_eq_u32 %[{lo}], {3 * KTILE}", f"s_cselect_b32 %[{lo}], 0, %[{lo}]"],
+            [f"s_add_u32 %[{d}], %[{mbase}], %[{lo}]"]]
 
 
 def walk_setup(par, advance):
     """Tile t+1 of the softmax walk (tile 0 when advance is False): cursor, valid keys, own frame
-    index tk, and mflag of parity par (1: ragged or partly causal, take the masked block)."""
-    lines = []
+    index tk, and mflag of parity par (1: ragged or partly causal, take the masked block).
+    Returned as units."""
+    units = []
     if advance:
-        lines += ["s_add_u32 %[x], %[t], 1", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0",
-                  "s_add_u32 %[sk], %[sk], %[y]", "s_cmp_eq_u32 %[sk], %[tpf]",
-                  "s_cselect_b32 %[sk], 0, %[sk]", "s_addc_u32 %[sf], %[sf], 0"]
-    lines += ["s_lshl_b32 %[x], %[sk], 6", "s_sub_i32 %[nvalid], %[N], %[x]",
-              "s_min_i32 %[nvalid], %[nvalid], 64",
-              "s_sub_i32 %[tk], %[sf], %[nshared]",
-              "s_cmp_lt_i32 %[nvalid], 64", f"s_cselect_b32 %[mflag{par}], 1, 0",
-              "s_cmp_gt_i32 %[tk], %[tqw]", "s_cselect_b32 %[x], 1, 0",
-              f"s_or_b32 %[mflag{par}], %[mflag{par}], %[x]"]
-    return lines
+        units += [["s_add_u32 %[x], %[t], 1", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0"],
+                  ["s_add_u32 %[sk], %[sk], %[y]"],
+                  ["s_cmp_eq_u32 %[sk], %[tpf]", "s_cselect_b32 %[sk], 0, %[sk]", "s_addc_u32 %[sf], %[sf], 0"]]
+    units += [["s_lshl_b32 %[x], %[sk], 6"], ["s_sub_i32 %[nvalid], %[N], %[x]"],
+              ["s_min_i32 %[nvalid], %[nvalid], 64"],
+              ["s_sub_i32 %[tk], %[sf], %[nshared]"],
+              ["s_cmp_lt_i32 %[nvalid], 64", f"s_cselect_b32 %[mflag{par}], 1, 0"],
+              ["s_cmp_gt_i32 %[tk], %[tqw]", "s_cselect_b32 %[x], 1, 0"],
+              [f"s_or_b32 %[mflag{par}], %[mflag{par}], %[x]"]]
+    return units
 
 
 def read_step(kind):
-    """LDS read addresses from tile t's ring slot to the next one (placed after the last read of
-    tile t from that ring has issued)."""
+    """LDS read addresses from tile t's ring slot to the next one, as units (placed after the
+    last read of tile t from that ring has issued)."""
     rd, step, base, n = (("krd", "kstep", KADDR, 8) if kind == "K" else ("vrd", "vstep", VADDR, 4))
-    return ([f"s_movk_i32 %[{step}], {KTILE}", f"s_movk_i32 %[x], {hex((-2 * KTILE) & 0xffff)}",
-             f"s_cmp_eq_u32 %[{rd}], 2", f"s_cselect_b32 %[{step}], %[x], %[{step}]",
-             f"s_add_u32 %[{rd}], %[{rd}], 1", f"s_cmp_eq_u32 %[{rd}], 3", f"s_cselect_b32 %[{rd}], 0, %[{rd}]"]
-            + [f"v_add_u32 v{base + i}, %[{step}], v{base + i}" for i in range(n)])
+    return ([[f"s_movk_i32 %[{step}], {KTILE}"], [f"s_movk_i32 %[x], {hex((-2 * KTILE) & 0xffff)}"],
+             [f"s_cmp_eq_u32 %[{rd}], 2", f"s_cselect_b32 %[{step}], %[x], %[{step}]"],
+             [f"s_add_u32 %[{rd}], %[{rd}], 1"], [f"s_cmp_eq_u32 %[{rd}], 3", f"s_cselect_b32 %[{rd}], 0, %[{rd}]"]]
+            + [[f"v_add_u32 v{base + i}, %[{step}], v{base + i}"] for i in range(n)])
 
 
 def iteration(pp, par, tag):
@@ -477,7 +505,7 @@ def loop_program():
     """The whole tile loop: iterations t = 0 .. n-1 (two per pass: P buffer and set-up parity
     fixed), then the last PV.  m0 is saved and restored."""
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
-    lines += walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1)
+    lines += sum(walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1), [])
     lines += [".Lw64_loop_%=:"] + iteration(1, 0, "a")
     lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc0 .Lw64_end_%="]
     lines += iteration(0, 1, "b")
