@@ -34,9 +34,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+ATTN_SOURCES = ("k_attention.hip", "k_attention_w64.hip", "attn_w64_asm.h", "attn_tiles.h")
+
+
 def attn_source_hash() -> str:
-    p = ROOT / "rolling_kv_causal_amd" / "csrc" / "k_attention.hip"
-    return hashlib.sha256(p.read_bytes()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of the attention kernels' sources (in this order)."""
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        h.update((ROOT / "rolling_kv_causal_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
 
 
 def visible_keys(c, t):
@@ -209,8 +215,8 @@ def load_traffic(workload: str):
     if not p.exists():
         return None
     fields = dict(ln.split(":", 1) for ln in p.read_text().splitlines()
-                  if ln.startswith(("bytes_per_call:", "k_attention_sha256_16:")))
-    if fields.get("k_attention_sha256_16", "").strip() != attn_source_hash():
+                  if ln.startswith(("bytes_per_call:", "attn_sources_sha256_16:")))
+    if fields.get("attn_sources_sha256_16", "").strip() != attn_source_hash():
         return None
     return int(fields["bytes_per_call"].strip())
 
@@ -308,8 +314,10 @@ def main():
                    "sink_threshold": c.sink_threshold, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "sdv2_chunk_attention (attn_bf16_kernel%s + combine_kernel)"
-                               % ("<128, e4m3 cache>" if c.kv_fp8 else ""),
+                     "kernel": "sdv2_chunk_attention (%s + combine_kernel)"
+                               % ("attn_bf16_kernel<128, e4m3 cache>" if c.kv_fp8 else
+                                  "attn_w64_kernel" if c.dtype == "bf16" and c.head_dim == 128 else
+                                  "attn_bf16_kernel"),
                      "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3)},
         "chunk_attention_calls_per_s": round(c.num_layers / (ms * 1e-3), 1),
         "latent_frames_per_s": round(c.chunk_frames / (ms * 1e-3), 2),

@@ -83,7 +83,7 @@ struct AttnArgs {
   void* out;               // [nbatch][T*N][H][D]
   const void* kv;
   int64_t k_layer_off, v_layer_off, slot_stride, head_stride;
-  float* part_o;           // [nsplit][nbatch][H][T*N][D] fp32 (split-KV only)
+  uint16_t* part_o;        // [nsplit][nbatch][H][T*N][D] bf16 O/l of the split (split-KV only)
   float2* part_ml;         // [nsplit][nbatch][H][T*N] (m in log2 units, l)
   int N, Npad, H, nbatch;  // N: tokens per frame
   int T;                   // frames per chunk (block-causal inside the chunk)
@@ -98,7 +98,7 @@ struct AttnArgs {
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const uint16_t* part_o;
   const float2* part_ml;
   void* out;
   int N, H, nbatch, nsplit;  // N: query rows per (element, head)

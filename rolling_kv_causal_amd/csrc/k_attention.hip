@@ -433,19 +433,23 @@ void attn_bf16_kernel(const AttnArgs a) {
       }
   } else {
     const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + qrow;
-    float* po = a.part_o + prow * D + 4 * g;
+    uint16_t* po = a.part_o + prow * D + 4 * g;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-        *(float4*)(po + 32 * i + 8 * a4) =
-            make_float4(o[i][4 * a4] * inv, o[i][4 * a4 + 1] * inv, o[i][4 * a4 + 2] * inv,
-                        o[i][4 * a4 + 3] * inv);
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 w2;
+        w2.x = pack_bf16x2(o[i][4 * a4] * inv, o[i][4 * a4 + 1] * inv);
+        w2.y = pack_bf16x2(o[i][4 * a4 + 2] * inv, o[i][4 * a4 + 3] * inv);
+        *(uint2*)(po + 32 * i + 8 * a4) = w2;
+      }
     if (g == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
   }
 }
 
-// Merge split-KV partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - max m).
+// Merge split-KV partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - max m).  The
+// partial O_s (already divided by l_s) are bf16: the merged row is rounded to bf16 anyway, and
+// half the bytes halve the partial traffic of the attention epilogue and of this kernel.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   constexpr int TPR = D / 4;                        // threads per output row
@@ -460,7 +464,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   for (int s = 0; s < a.nsplit; ++s) {
     const float2 ml = a.part_ml[s * rows + row];
     const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
-    const float4 v = *(const float4*)(a.part_o + (s * rows + row) * D + d0);
+    const uint2 p = *(const uint2*)(a.part_o + (s * rows + row) * D + d0);
+    const float4 v = make_float4(__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u),
+                                 __uint_as_float(p.y << 16), __uint_as_float(p.y & 0xffff0000u));
     W += wgt;
     acc.x = fmaf(wgt, v.x, acc.x);
     acc.y = fmaf(wgt, v.y, acc.y);

@@ -269,14 +269,16 @@ void attn_w64_kernel(const AttnArgs a) {
         }
     } else {
       const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + row[qb];
-      float* po = a.part_o + prow * D + 4 * g;
+      uint16_t* po = a.part_o + prow * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const int i0 = 16 * qb + 4 * a4;
-          *(float4*)(po + 32 * db + 8 * a4) =
-              make_float4(ov(db, i0) * inv, ov(db, i0 + 1) * inv, ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
+          uint2 w2;
+          w2.x = pack_bf16x2(ov(db, i0) * inv, ov(db, i0 + 1) * inv);
+          w2.y = pack_bf16x2(ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
+          *(uint2*)(po + 32 * db + 8 * a4) = w2;
         }
       if (g == 0) a.part_ml[prow] = make_float2(mrun[qb], l_tot);
     }

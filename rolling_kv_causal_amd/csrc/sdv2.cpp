@@ -101,13 +101,17 @@ sdv2_layout make_layout(const sdv2_config& c) {
 }
 
 // Split-KV count for nbatch elements.  The grid runs in rounds of kSlots workgroups (256 CUs of
-// MI355X, one 8-wave workgroup each); a split count costs rounds x tiles-per-split tile steps
-// plus the fp32 partial results it writes and the combine reads back.  The constants are
-// measured on MI355X: about 1.2 us per 64-key tile step of a 256-row workgroup and ~5 TB/s for
-// the partial traffic.
+// MI355X, one workgroup each); a split count costs rounds x (tiles per split x one 64-key tile
+// step + the workgroup's prologue and epilogue) plus the bf16 partial results it writes and the
+// combine reads back.  The constants are measured on MI355X with the 64-row kernel: about
+// 1.6 us per tile step of a 256-row workgroup with every CU busy, 8 us of prologue/epilogue per
+// round and ~5 TB/s for the partial traffic.  A round that leaves CUs idle runs at a higher
+// clock (the chip is power-bound): its tile step is shorter by kClockGain x the idle fraction
+// (1.45 us measured at 3/4 occupancy).
 constexpr int kSlots = 256;
 constexpr int kMaxSplit = 16;
-constexpr double kTileUs = 1.2, kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
+constexpr double kTileUs = 1.6, kRoundUs = 8.0, kClockGain = 0.38;
+constexpr double kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 // total_tiles: key tiles of the longest query tile; min_tiles: of the shortest (block-causal
 // chunks end the walk at a query tile's last own frame), which bounds the split count so that
 // every split has at least one tile.
@@ -119,10 +123,12 @@ int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_til
   int best = 1;
   double best_cost = 1e300;
   for (int ns = 1; ns <= kMaxSplit && ns <= min_tiles; ++ns) {
-    const int64_t rounds = (base * ns + kSlots - 1) / kSlots;
+    const int64_t wgs = base * ns, full = wgs / kSlots, part = wgs % kSlots;
     const int64_t per = (total_tiles + ns - 1) / ns;
-    double cost = (double)(rounds * per) * kTileUs;
-    if (ns > 1) cost += (double)ns * rows * (2.0 * (c.head_dim * 4 + 8)) / kPartialBytesPerUs + kCombineUs;
+    double cost = (double)full * ((double)per * kTileUs + kRoundUs);
+    if (part)
+      cost += (double)per * kTileUs * (1.0 - kClockGain * (1.0 - (double)part / kSlots)) + kRoundUs;
+    if (ns > 1) cost += (double)ns * rows * (2.0 * (c.head_dim * 2 + 8)) / kPartialBytesPerUs + kCombineUs;
     if (cost < best_cost * 0.98) {   // prefer fewer splits unless clearly cheaper
       best_cost = cost;
       best = ns;
@@ -162,7 +168,7 @@ int64_t workspace_bytes(const sdv2_config& c) {
       const int ns = choose_nsplit(c, nb, (shared + c.chunk_frames) * tpf, (shared + 1) * tpf);
       if (ns < 2) continue;
       const int64_t rows = (int64_t)ns * nb * c.num_heads * c.chunk_frames * N;
-      const int64_t bytes = align_up(rows * c.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
+      const int64_t bytes = align_up(rows * c.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
       if (bytes > best) best = bytes;
     }
   return best;
@@ -486,10 +492,10 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
   if (a.nsplit > 1) {
-    const int64_t need = align_up(rows * cfg.head_dim * 4, kAlign) + align_up(rows * 8, kAlign);
+    const int64_t need = align_up(rows * cfg.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
     if (need > c->ws_bytes) return fail(SDV2_ENOSPC, "workspace too small for %d splits", a.nsplit);
-    a.part_o = (float*)c->ws;
-    a.part_ml = (float2*)(c->ws + align_up(rows * cfg.head_dim * 4, kAlign));
+    a.part_o = (uint16_t*)c->ws;
+    a.part_ml = (float2*)(c->ws + align_up(rows * cfg.head_dim * 2, kAlign));
   }
   SDV2_HIP(launch_attention(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
   if (a.nsplit > 1) {
