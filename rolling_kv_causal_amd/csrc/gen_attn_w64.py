@@ -59,6 +59,7 @@ TMP, M, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 206, 222, 224, 225, 227, 228
 TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
+WAIT_EVERY = 2                                   # one LDS wait per this many fragment reads
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
 
 
@@ -118,12 +119,14 @@ def v_reads():
     return [("V", db, ks) for ks in range(4) for db in range(4)]
 
 
-def read_instr(r, slot):
+def read_instr(r, slot, ph):
+    """LDS read of fragment r in iteration phase ph (t mod NSLOT): K(t) sits in ring slot
+    ph, V^T(t-1) in slot ph - 1; the slot is the instruction's offset."""
     if r[0] == "K":
         _, kb, kd = r
-        return f"ds_read_b128 {frag(slot)}, v{KADDR + kd} offset:{kb * 8192}"
+        return f"ds_read_b128 {frag(slot)}, v{KADDR + kd} offset:{(ph % NSLOT) * KTILE + kb * 8192}"
     _, db, ks = r
-    return f"ds_read_b128 {frag(slot)}, v{VADDR + ks} offset:{db * 4096}"
+    return f"ds_read_b128 {frag(slot)}, v{VADDR + ks} offset:{((ph - 1) % NSLOT) * KTILE + db * 4096}"
 
 
 def mfma_pair(r, slot, pp):
@@ -201,7 +204,7 @@ def mask_setup():
     return lines
 
 
-def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
+def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
     """Reads KA ahead of their MFMAs; VALU ops spread evenly over the MFMAs from index
     valu_from on.  dma maps a read index i to (m0 setup, tile load): the setup follows the MFMA
     pair of read i and the load the LDS read issued after it, so the tile loads of a wave are
@@ -213,12 +216,12 @@ def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
     dma = dma or {}
     lines = []
     for i in range(min(KA, len(reads))):
-        lines.append(read_instr(reads[i], i % RING))
+        lines.append(read_instr(reads[i], i % RING, ph))
     issued = min(KA, len(reads))
     n_mfma = 2 * len(reads)
     fixed = [0] * n_mfma                         # read, wait and load instructions after MFMA g
     for i in range(len(reads)):
-        fixed[2 * i + 1] += 1 + (i + KA < len(reads)) + 2 * (i in dma)
+        fixed[2 * i + 1] += ((i + 1) % WAIT_EVERY == 0) + (i + KA < len(reads)) + 2 * (i in dma)
     # VALU ops in order over the gaps from valu_from on, levelling VALU + fixed per gap
     per = [0] * n_mfma
     region = range(valu_from, n_mfma)
@@ -244,7 +247,8 @@ def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
             load[g] += len(u)
     vi = 0
     for i, r in enumerate(reads):
-        lines.append(f"s_waitcnt lgkmcnt({min(issued - (i + 1), 15)})")
+        if i % WAIT_EVERY == 0:                  # reads i .. i + WAIT_EVERY - 1 in
+            lines.append(f"s_waitcnt lgkmcnt({min(max(issued - (i + WAIT_EVERY), 0), 15)})")
         for j, m in enumerate(mfma_pair(r, i % RING, pp)):
             lines.append(m)
             for _ in range(per[2 * i + j]):
@@ -254,7 +258,7 @@ def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
         if i in dma:
             lines.append(dma[i][0])
         if i + KA < len(reads):
-            lines.append(read_instr(reads[i + KA], (i + KA) % RING))
+            lines.append(read_instr(reads[i + KA], (i + KA) % RING, ph))
             issued += 1
         elif i in dma:
             lines.append("s_nop 0")
@@ -265,17 +269,18 @@ def stream(reads, pp, valu, dma=None, valu_from=0, extra=()):
     return lines
 
 
-def tile_block(pp, par, masked):
-    """QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this iteration's tile
-    loads (parity par) and the next iteration's scalar set-up, then the lazy test (trig != 0:
-    some lane's tile sum left [0, 256] or is not finite)."""
+def tile_block(ph, masked):
+    """Iteration phase ph (t mod NSLOT; parity par = ph mod 2, P buffer pp = 1 - par):
+    QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this iteration's tile loads
+    (bases of parity par) and the next iteration's scalar set-up, then the lazy test
+    (trig != 0: some lane's tile sum left [0, 256] or is not finite)."""
+    par = ph % 2
+    pp = 1 - par
     pc = 1 - pp
     lines = mask_setup() if masked else []
-    # first gaps: the K read address step after the last K read of the tile has issued (read
-    # 15, issued after MFMA 15), the V^T one after read 31 (issued after MFMA 47)
     extra = [(0, load_setup("K", 1 - par, 3)), (0, load_setup("V", 1 - par, 2)),
-             (0, walk_setup(1 - par, True)), (16, read_step("K")), (48, read_step("V"))]
-    lines += stream(k_reads() + v_reads(), pp, softmax_ops(pc, masked), tile_loads(par), SM_FROM, extra)
+             (0, walk_setup(1 - par, True))]
+    lines += stream(k_reads() + v_reads(), pp, ph, softmax_ops(pc, masked), tile_loads(ph), SM_FROM, extra)
     lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
               f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
               f"v_add_f32 v{TMP + 2}, v{TS + 2}, v{TS + 3}",
@@ -345,8 +350,9 @@ def init_block():
     return lines
 
 
-def pv_only_block(pp):
-    return stream(v_reads(), pp, []) + ["s_nop 11"]
+def pv_only_block(ph):
+    """The last PV, as the PV of an iteration of phase ph would run it."""
+    return stream(v_reads(), 1 - ph % 2, ph, []) + ["s_nop 11"]
 
 
 def check_hazards(lines):
@@ -410,32 +416,35 @@ def check_hazards(lines):
 
 KOFF, VOFF, SLOTL = 230, 234, 238
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
+NSLOT = 4                                        # ring slots of K and of V^T tiles
 
 
 BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
 
 
-def tile_loads(par):
+def tile_loads(ph):
     """Read index -> (m0 setup, load) of this wave's four 1 KB K loads (after reads 1, 5, 9, 13)
-    and four V^T loads (after reads 17, 21, 25, 29); m0 holds the LDS destination, the SGPR
-    pair of parity par the global tile base and v[230:237] the lane offsets."""
+    and four V^T loads (after reads 17, 21, 25, 29) in iteration phase ph: K(t+2) into ring
+    slot ph + 2, V^T(t+1) into slot ph + 1; m0 holds the LDS destination, the SGPR pair of
+    parity ph mod 2 the global tile base and v[230:237] the lane offsets."""
+    par = ph % 2
     d = {}
-    for first, m0reg, base, v0 in ((1, f"dk{par}", BASE[par][0], KOFF), (17, f"dv{par}", BASE[par][1], VOFF)):
+    for first, mbase, slot, base, v0 in ((1, "mk", (ph + 2) % NSLOT, BASE[par][0], KOFF),
+                                         (17, "mv", (ph + 1) % NSLOT, BASE[par][1], VOFF)):
         for i in range(4):
-            setup = f"s_mov_b32 m0, %[{m0reg}]" if i == 0 else "s_add_u32 m0, m0, 1024"
+            setup = f"s_add_u32 m0, %[{mbase}], {slot * KTILE}" if i == 0 else "s_add_u32 m0, m0, 1024"
             d[first + 4 * i] = (setup, f"global_load_lds_dwordx4 v{v0 + i}, s[{base}:{base + 1}]")
     return d
 
 
 def load_setup(kind, par, ahead):
-    """Set-up of the loads of K (t + ahead) or V^T (t + ahead) for the iteration of parity par:
-    the cursor advances when that tile exists (otherwise the loads repeat the last tile, a valid
-    address, into the free slot, so every iteration issues eight loads and one vmcnt serves
-    all), the ring slot advances, and the global base and LDS destination are set.  Returned
-    as units (instruction lists closed in their use of SCC)."""
-    f, k, lo, mbase, colb, blo, bhi, d, base = (
-        ("kf", "kk", "kl", "mk", 14, "kblo", "kbhi", f"dk{par}", BASE[par][0]) if kind == "K"
-        else ("vf", "vk", "vl", "mv", 7, "vblo", "vbhi", f"dv{par}", BASE[par][1]))
+    """Global base of the loads of K (t + ahead) or V^T (t + ahead) for the iteration of parity
+    par: the cursor advances when that tile exists (otherwise the loads repeat the last tile,
+    a valid address, into the free slot, so every iteration issues eight loads and one vmcnt
+    serves all).  Returned as units (instruction lists closed in their use of SCC)."""
+    f, k, colb, blo, bhi, base = (
+        ("kf", "kk", 14, "kblo", "kbhi", BASE[par][0]) if kind == "K"
+        else ("vf", "vk", 7, "vblo", "vbhi", BASE[par][1]))
     return [[f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0"],
             [f"s_add_u32 %[{k}], %[{k}], %[y]"],
             [f"s_cmp_eq_u32 %[{k}], %[tpf]", f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0"],
@@ -445,10 +454,7 @@ def load_setup(kind, par, ahead):
             [f"s_lshl_b32 %[y], %[{k}], {colb}"],
             ["s_mul_i32 %[x], %[x], %[slotb]"],
             ["s_add_u32 %[x], %[x], %[y]"],
-            [f"s_add_u32 s{base}, %[{blo}], %[x]", f"s_addc_u32 s{base + 1}, %[{bhi}], 0"],
-            [f"s_add_u32 %[{lo}], %[{lo}], {KTILE}"],
-            [f"s_cmp_eq_u32 %[{lo}], {3 * KTILE}", f"s_cselect_b32 %[{lo}], 0, %[{lo}]"],
-            [f"s_add_u32 %[{d}], %[{mbase}], %[{lo}]"]]
+            [f"s_add_u32 s{base}, %[{blo}], %[x]", f"s_addc_u32 s{base + 1}, %[{bhi}], 0"]]
 
 
 def walk_setup(par, advance):
@@ -469,23 +475,14 @@ def walk_setup(par, advance):
     return units
 
 
-def read_step(kind):
-    """LDS read addresses from tile t's ring slot to the next one, as units (placed after the
-    last read of tile t from that ring has issued)."""
-    rd, step, base, n = (("krd", "kstep", KADDR, 8) if kind == "K" else ("vrd", "vstep", VADDR, 4))
-    return ([[f"s_movk_i32 %[{step}], {KTILE}"], [f"s_movk_i32 %[x], {hex((-2 * KTILE) & 0xffff)}"],
-             [f"s_cmp_eq_u32 %[{rd}], 2", f"s_cselect_b32 %[{step}], %[x], %[{step}]"],
-             [f"s_add_u32 %[{rd}], %[{rd}], 1"], [f"s_cmp_eq_u32 %[{rd}], 3", f"s_cselect_b32 %[{rd}], 0, %[{rd}]"]]
-            + [[f"v_add_u32 v{base + i}, %[{step}], v{base + i}"] for i in range(n)])
-
-
-def iteration(pp, par, tag):
-    """Iteration t < n of parity par (P buffer pp read by PV(t-1), P(t) written into 1 - pp).
-    The masked tile block and the rescale are out of line (see out_of_line)."""
+def iteration(ph):
+    """Iteration t < n of phase ph = t mod NSLOT (P buffer pp = 1 - ph mod 2 read by PV(t-1),
+    P(t) written into the other).  The masked tile block and the rescale are out of line."""
+    par, tag = ph % 2, "abcd"[ph]
     return [# loads of iteration t-2 (K(t), V^T(t-1)) in; every wave is done with iteration t-1's slots
             "s_waitcnt vmcnt(8)", "s_barrier",
             f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc0 .Lw64_m{tag}_%="] + \
-        tile_block(pp, par, False) + \
+        tile_block(ph, False) + \
         [f".Lw64_td{tag}_%=:",
          "s_cmp_eq_u64 %[trig], 0", f"s_cbranch_scc0 .Lw64_r{tag}_%=",
          f"v_add_f32 v{L}, v{L}, v{TMP}", f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}",
@@ -493,27 +490,36 @@ def iteration(pp, par, tag):
          "s_add_u32 %[t], %[t], 1"]
 
 
-def out_of_line(pp, par, tag):
-    pc = 1 - pp
-    return ([f".Lw64_m{tag}_%=:"] + tile_block(pp, par, True) + [f"s_branch .Lw64_td{tag}_%=",
+def out_of_line(ph):
+    par, tag = ph % 2, "abcd"[ph]
+    pc = par                                     # P buffer written by iteration phase ph
+    return ([f".Lw64_m{tag}_%=:"] + tile_block(ph, True) + [f"s_branch .Lw64_td{tag}_%=",
             f".Lw64_r{tag}_%=:", f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc1 .Lw64_ru{tag}_%="]
             + rare_block(pc, True) + [f"s_branch .Lw64_nr{tag}_%=", f".Lw64_ru{tag}_%=:"]
             + rare_block(pc, False) + [f"s_branch .Lw64_nr{tag}_%="])
 
 
 def loop_program():
-    """The whole tile loop: iterations t = 0 .. n-1 (two per pass: P buffer and set-up parity
-    fixed), then the last PV.  m0 is saved and restored."""
+    """The whole tile loop: iterations t = 0 .. n-1 (NSLOT per pass, so that ring slots, P
+    buffer and set-up parity are fixed in each copy), then the last PV.  m0 is saved and
+    restored."""
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
     lines += sum(walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1), [])
-    lines += [".Lw64_loop_%=:"] + iteration(1, 0, "a")
-    lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc0 .Lw64_end_%="]
-    lines += iteration(0, 1, "b")
+    lines += [".Lw64_loop_%=:"]
+    for ph in range(NSLOT):
+        lines += iteration(ph)
+        if ph < NSLOT - 1:
+            lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc0 .Lw64_end_%="]
     lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc1 .Lw64_loop_%=",
               ".Lw64_end_%=:", "s_waitcnt vmcnt(0)", "s_barrier",
-              "s_bitcmp1_b32 %[n], 0", "s_cbranch_scc0 .Lw64_pv1_%="]
-    lines += pv_only_block(0) + ["s_branch .Lw64_fin_%=", ".Lw64_pv1_%=:"] + pv_only_block(1)
-    lines += ["s_branch .Lw64_fin_%="] + out_of_line(1, 0, "a") + out_of_line(0, 1, "b")
+              f"s_and_b32 %[x], %[n], {NSLOT - 1}"]
+    for ph in range(1, NSLOT):
+        lines += [f"s_cmp_eq_u32 %[x], {ph}", f"s_cbranch_scc1 .Lw64_pv{ph}_%="]
+    lines += pv_only_block(0) + ["s_branch .Lw64_fin_%="]
+    for ph in range(1, NSLOT):
+        lines += [f".Lw64_pv{ph}_%=:"] + pv_only_block(ph) + ["s_branch .Lw64_fin_%="]
+    for ph in range(NSLOT):
+        lines += out_of_line(ph)
     lines += [".Lw64_fin_%=:", "s_mov_b32 m0, %[m0save]"]
     return lines
 

@@ -21,10 +21,11 @@
 //
 // Per tile t (iteration t = 0..n-1, n tiles in the split):
 //   QK(t): S^T = K(t) Q^T;  PV(t-1): O^T += V^T(t-1) P^T(t-1);  softmax(t): P^T(t) from S^T
-// with P(-1) = 0 over a zeroed V^T slot, then a last P V-only step.  LDS rings of three K and
-// three V^T tiles: iteration t loads K(t+2) and V(t+1) into the slots of K(t-1) and V(t-2)
-// after the barrier that follows everyone's reads of them; a wave waits for its own loads
-// (vmcnt) two iterations after issue, before that iteration's barrier.
+// with P(-1) = 0 over a zeroed V^T slot, then a last P V-only step.  LDS rings of four K and
+// four V^T tiles (tile t in slot t mod 4, so the generated loop has one copy per slot and
+// every LDS address is a register plus an immediate): iteration t loads K(t+2) and V(t+1)
+// into the slots of K(t-2) and V(t-3), which every wave has finished reading; a wave waits for
+// its own loads (vmcnt) two iterations after issue, before that iteration's barrier.
 //
 // Softmax: base 2 with the lazy-max rule of the other kernel: exponentials at the running max
 // m; only when a lane's tile sum of P leaves [0, 256] (first tile, NaN, or a score far above
@@ -53,7 +54,7 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) |
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_w64_kernel(const AttnArgs a) {
   constexpr int D = 128, KRB = 256, VRB = 128;
-  constexpr int K_BYTES = kTileKeys * KRB, V_BYTES = D * VRB, NBUF = 3;
+  constexpr int K_BYTES = kTileKeys * KRB, V_BYTES = D * VRB, NBUF = 4;
   constexpr int LD = K_BYTES / 1024 / 4;      // 1 KB loads per wave per tile (K; the same for V^T)
   __shared__ __attribute__((aligned(1024))) char lds[NBUF * (K_BYTES + V_BYTES)];
   char* const ldsK = lds;
@@ -157,12 +158,12 @@ void attn_w64_kernel(const AttnArgs a) {
                                        (lds_void*)(ldsV + slot * V_BYTES + (wave * LD + i) * 1024), 16, 0, 0);
   };
 
-  // Prologue: V^T slot 2 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
+  // Prologue: V^T slot 3 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
   // slot 1 (K(0) again when n = 1: the loop counts twelve loads in flight at its start), V(0)
   // into slot 0.
 #pragma unroll
   for (int i = 0; i < V_BYTES / (256 * 16); ++i)
-    reinterpret_cast<uint4*>(ldsV + 2 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(ldsV + 3 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const TileCursor c0 = cursor_at(t_begin);
   TileCursor kc = c0;
@@ -174,7 +175,7 @@ void attn_w64_kernel(const AttnArgs a) {
   // The tile loop (generated asm, see gen_attn_w64.py).  Its state lives in the registers
   // named by the operands below; the compiler sees one statement.
   i32x8 kaddr;                                // LDS addresses of K fragments per k step (slot 0)
-  i32x4 vaddr;                                // LDS addresses of V^T fragments per key step (slot 2)
+  i32x4 vaddr;                                // LDS addresses of V^T fragments per key step (slot 0)
   i32x4 lanec;                                // 8g, frame of the row per qb, (lane ^ 32) * 4
   i32x4 koffv, voffv;
   {
@@ -182,7 +183,7 @@ void attn_w64_kernel(const AttnArgs a) {
 #pragma unroll
     for (int kd = 0; kd < 8; ++kd) kaddr[kd] = (int)(kb + lds_chunk<KRB>(r, 2 * kd + g));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) vaddr[ks] = (int)(vb + 2 * V_BYTES + lds_chunk<VRB>(r, 2 * ks + g));
+    for (int ks = 0; ks < 4; ++ks) vaddr[ks] = (int)(vb + lds_chunk<VRB>(r, 2 * ks + g));
     lanec[0] = 8 * g;
     lanec[1] = tq[0];
     lanec[2] = tq[1];
@@ -202,9 +203,8 @@ void attn_w64_kernel(const AttnArgs a) {
   i32x16 rmask;
   i32x2 cmask;
   // scalar state: cursors (frame, tile in frame) of the last K and V^T tiles loaded and of the
-  // tile t, iteration t, ring offsets, read-slot indices, loads in flight
+  // tile t, iteration t
   int kf = kc.f, kk = kc.k, vf = c0.f, vk = c0.k, sf = c0.f, sk = c0.k, t = 0;
-  int krd = 0, vrd = 2, kl = K_BYTES, vl = 0;
   const uint64_t kblk64 = (uint64_t)(uintptr_t)kblk, vblk64 = (uint64_t)(uintptr_t)vblk;
   const uint32_t kblo = (uint32_t)kblk64, kbhi = (uint32_t)(kblk64 >> 32);
   const uint32_t vblo = (uint32_t)vblk64, vbhi = (uint32_t)(vblk64 >> 32);
@@ -212,9 +212,8 @@ void attn_w64_kernel(const AttnArgs a) {
   const int mk = (int)((uint32_t)(uintptr_t)ldsK + wave * LD * 1024);
   const int mv = (int)((uint32_t)(uintptr_t)ldsV + wave * LD * 1024);
   const float sl = a.scale_log2;
-  const int ones = 0x3F803F80;                // bf16 (1, 1)
   unsigned long long trig;
-  int x, y, nvalid, tk, kstep, vstep, dk0, dk1, dv0, dv1, mflag0, mflag1, m0save, stmp;
+  int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp;
   asm volatile(SDV2_W64_LOOP
                : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
                  "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),
@@ -223,17 +222,15 @@ void attn_w64_kernel(const AttnArgs a) {
                  "={v[248:255]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),
                  "={v[228:229]}"(lrun),
                  [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk), [sf] "+s"(sf),
-                 [sk] "+s"(sk), [t] "+s"(t), [krd] "+s"(krd), [vrd] "+s"(vrd), [kl] "+s"(kl),
-                 [vl] "+s"(vl),
+                 [sk] "+s"(sk), [t] "+s"(t),
                  [trig] "=&s"(trig), [x] "=&s"(x), [y] "=&s"(y), [nvalid] "=&s"(nvalid),
-                 [tk] "=&s"(tk), [kstep] "=&s"(kstep), [vstep] "=&s"(vstep), [dk0] "=&s"(dk0),
-                 [dk1] "=&s"(dk1), [dv0] "=&s"(dv0), [dv1] "=&s"(dv1), [mflag1] "=&s"(mflag1),
+                 [tk] "=&s"(tk), [mflag1] "=&s"(mflag1),
                  [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
                : "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec),
                  "{v[230:233]}"(koffv), "{v[234:237]}"(voffv), "{v238}"(slot_lane),
                  [n] "s"(n), [tpf] "s"(tpf), [nshared] "s"(nshared), [N] "s"(Ntok),
                  [tqw] "s"(tq_wave), [kblo] "s"(kblo), [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb),
-                 [mk] "s"(mk), [mv] "s"(mv), [sl] "s"(sl), [ones] "s"(ones)
+                 [mk] "s"(mk), [mv] "s"(mv), [sl] "s"(sl)
                : "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91");
   (void)frg;
   (void)frg2;
