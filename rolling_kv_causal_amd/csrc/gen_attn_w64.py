@@ -60,6 +60,7 @@ TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
 WAIT_EVERY = 2                                   # one LDS wait per this many fragment reads
+NEXT_GAP = ["<next gap>"]                        # unit marker: continue the chunk after the next MFMA
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
 
 
@@ -241,6 +242,9 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
         # chunks one after another: they share the scratch SGPRs x and y
         g = max(g, first)
         for u in units:
+            if u == NEXT_GAP:                    # the rest of the chunk goes after the next MFMA
+                g = min(g + 1, n_mfma - 1)
+                continue
             while g < n_mfma - 1 and load[g] + len(u) > GAP_CAP:
                 g += 1
             placed[g] += u
@@ -290,8 +294,7 @@ def tile_block(ph, masked):
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP}",
               "s_mov_b64 %[trig], vcc",
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP + 1}",
-              "s_or_b64 %[trig], %[trig], vcc",
-              "s_nop 11"]
+              "s_or_b64 %[trig], %[trig], vcc"]
     return lines
 
 
@@ -448,7 +451,8 @@ def load_setup(kind, par, ahead):
     return [[f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0"],
             [f"s_add_u32 %[{k}], %[{k}], %[y]"],
             [f"s_cmp_eq_u32 %[{k}], %[tpf]", f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0"],
-            [f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]"],
+            [f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]"], NEXT_GAP,     # its SGPR result is read
+            # about 20 cycles later at the earliest: the wait overlaps the next MFMA
             # tile offset in the (layer, head) block: slot * slot bytes + tile (16 KB of K rows or
             # 128 B of V^T columns)
             [f"s_lshl_b32 %[y], %[{k}], {colb}"],
@@ -504,7 +508,8 @@ def loop_program():
     buffer and set-up parity are fixed in each copy), then the last PV.  m0 is saved and
     restored."""
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
-    lines += sum(walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1), [])
+    lines += sum((u for u in walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1)
+                  if u != NEXT_GAP), [])
     lines += [".Lw64_loop_%=:"]
     for ph in range(NSLOT):
         lines += iteration(ph)

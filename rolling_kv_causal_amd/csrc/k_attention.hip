@@ -452,36 +452,38 @@ void attn_bf16_kernel(const AttnArgs a) {
 // half the bytes halve the partial traffic of the attention epilogue and of this kernel.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  constexpr int TPR = D / 4;                        // threads per output row
+  constexpr int TPR = D / 8;                        // threads per output row, 8 values each
   const int64_t rows = (int64_t)a.nbatch * a.H * a.N;
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
-  const int d0 = (threadIdx.x % TPR) * 4;
+  const int d0 = (threadIdx.x % TPR) * 8;
   float M = -INFINITY;
   for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[s * rows + row].x);
-  float W = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < a.nsplit; ++s) {
     const float2 ml = a.part_ml[s * rows + row];
     const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
-    const uint2 p = *(const uint2*)(a.part_o + (s * rows + row) * D + d0);
-    const float4 v = make_float4(__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u),
-                                 __uint_as_float(p.y << 16), __uint_as_float(p.y & 0xffff0000u));
+    const uint4 p = *(const uint4*)(a.part_o + (s * rows + row) * D + d0);
+    const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
     W += wgt;
-    acc.x = fmaf(wgt, v.x, acc.x);
-    acc.y = fmaf(wgt, v.y, acc.y);
-    acc.z = fmaf(wgt, v.z, acc.z);
-    acc.w = fmaf(wgt, v.w, acc.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(wgt, __uint_as_float(pw[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(wgt, __uint_as_float(pw[i] & 0xffff0000u), acc[2 * i + 1]);
+    }
   }
   const float inv = 1.f / W;
   const int n = (int)(row % a.N);
   const int eh = (int)(row / a.N);
   const int head = eh % a.H, elem = eh / a.H;
   uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * a.N + n) * a.H + head) * D + d0;
-  uint2 w2;
-  w2.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-  w2.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *(uint2*)op = w2;
+  uint4 w4;
+  w4.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w4.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w4.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  w4.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *(uint4*)op = w4;
 }
 
 // fp32: one query row per lane, 32-key tiles through LDS, online softmax per row.
@@ -588,7 +590,7 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t
 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s) {
   const int64_t rows = (int64_t)a.nbatch * a.H * a.N;
-  const int rows_per_block = 256 / (head_dim / 4);
+  const int rows_per_block = 256 / (head_dim / 8);
   const int grid = (int)((rows + rows_per_block - 1) / rows_per_block);
   if (head_dim == 128)
     hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, s, a);
