@@ -56,6 +56,14 @@ def decode(cfg, x: np.ndarray) -> np.ndarray:
     return np.asarray(x, np.float32).astype(np.float64)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 values -> the nearest bf16 values (via float32, then round half to even on the
+    16 dropped bits), as float64.  Finite inputs only."""
+    b = np.asarray(x, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
 def schedule(cfg, s: int) -> dict:
     """Chunks in flight at step s (element order), the chunk committed at its end, f_new."""
     B, M, T = cfg.stream_batch, cfg.num_chunks, cfg.chunk_frames
@@ -135,10 +143,13 @@ class OracleStream:
         return [e for e in self.sinks if e is not None] + list(self.window)
 
     # ---- attention of one element ---------------------------------------------------------
-    def attend(self, layer: int, elem: int, q, k, v, rows=None, heads=None) -> np.ndarray:
+    def attend(self, layer: int, elem: int, q, k, v, rows=None, heads=None, rotated="exact") -> np.ndarray:
         """Output rows of element `elem` at the current step: float64 [len(rows), len(heads), d].
 
-        q, k, v are that element's fresh storage arrays [T'N, H, d] (pre-RoPE).
+        q, k, v are that element's fresh storage arrays [T'N, H, d] (pre-RoPE).  rotated="bf16"
+        rounds the rotated queries and keys to bf16 before the product, as a bf16 path stores
+        them (reading R13: q_rot and the cached keys are bf16 tensors); the default keeps them
+        exact.
         """
         cfg = self.cfg
         N, T = cfg.tokens, cfg.chunk_frames
@@ -161,6 +172,8 @@ class OracleStream:
             v_parts.append(own[1])
             key_frame.append(np.full(N, g))
         K_all = np.concatenate(k_parts)                            # [L, H, d]
+        if rotated == "bf16" and cfg.dtype == "bf16" and not self.kv_fp8:
+            K_all = round_bf16(K_all)
         V_all = np.concatenate(v_parts)
         key_frame = np.concatenate(key_frame)
 
@@ -168,6 +181,8 @@ class OracleStream:
         gh, gw = rope.token_grid(cfg.grid_h, cfg.grid_w)
         phi = rope.angles(cfg, (q_frame - self.base).astype(np.float64), gh[rows % N], gw[rows % N])
         Q_rot = rope.rotate_pairs(qd[rows], phi[:, None, :])       # [R, H, d]
+        if rotated == "bf16" and cfg.dtype == "bf16":
+            Q_rot = round_bf16(Q_rot)
         mask = key_frame[None, :] <= q_frame[:, None]              # block-causal own chunk
 
         out = np.empty((len(rows), len(heads), cfg.head_dim))

@@ -132,7 +132,7 @@ class Harness:
         assert self.refresh_applied[self.step_no] == n_ref, (self.step_no, self.refresh_applied[self.step_no], n_ref)
         return dec
 
-    def check_outputs(self, rows=None, heads=None):
+    def check_outputs(self, rows=None, heads=None, rotated="exact"):
         """Compare the current step's outputs of every element on the checked layers."""
         cfg = self.cfg
         plan = self.st.plan
@@ -140,7 +140,7 @@ class Harness:
         for layer in self.layers:
             for b in range(len(plan["chunks"])):
                 q, k, v = self.np_inputs[(layer, b)]
-                ref = self.st.attend(layer, b, q, k, v, rows=rows, heads=heads)
+                ref = self.st.attend(layer, b, q, k, v, rows=rows, heads=heads, rotated=rotated)
                 got = self.run.out[layer, b]
                 if rows is not None:
                     got = got[torch.as_tensor(rows, device="cuda")]

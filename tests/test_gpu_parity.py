@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import Harness, log, sample_rows
+from gpu_helpers import Harness, assert_close, host64, log, sample_rows
 from oracle import motion as omotion
 from rolling_kv_causal_amd import sdv2
 from synth import configs, inputs
@@ -42,6 +42,49 @@ def test_tiny_fp32_full_stream():
     h = _stream(cfg, cfg.num_steps)
     assert h.st.refresh_log == [(8, 8)]
     assert len(h.decisions) == cfg.num_chunks - cfg.sink_frames
+
+
+def _keys_times_8(steps):
+    """inputs.qkv with the keys of the chunks entering at `steps` scaled by 8 (exact in bf16)."""
+    orig = inputs.qkv
+
+    def qkv(cfg, step, layer, elem):
+        q, k, v = orig(cfg, step, layer, elem)
+        if step in steps:
+            assert k.dtype == np.uint16
+            f = (k.astype(np.uint32) << 16).view(np.float32) * np.float32(8.0)
+            k = (f.view(np.uint32) >> 16).astype(np.uint16)
+        return q, k, v
+    return qkv
+
+
+@pytest.mark.parametrize("grid", [(5, 13), (8, 16)], ids=["ragged-tiles", "full-tiles"])
+def test_score_jump_rescales_mid_walk(monkeypatch, grid):
+    # The keys of two committed frames are scaled by 8, so their scores rise far above the
+    # running maximum of the tiles walked before them: the lazy rescale (row maximum, O and l
+    # scaled, P recomputed) runs at tiles in the middle of the walk, in the masked variant too
+    # when the tiles are ragged (65 tokens per frame), not only at the first tile.
+    # Scores 8x larger also make the bf16 rounding of the rotated q and k (R13) 8x larger in
+    # the scores, which the tolerance does not cover, so the oracle rounds them as the path
+    # stores them; what is left to differ is the kernel's own arithmetic.  The attention is
+    # then peaked, outputs reach |V| (up to about 4), and the bf16 bars apply relative to the
+    # largest output magnitude of the element (bf16 carries relative precision).
+    monkeypatch.setattr(inputs, "qkv", _keys_times_8({2, 5}))
+    cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
+                 grid_h=grid[0], grid_w=grid[1], num_heads=2, sink_frames=1, window_frames=4,
+                 stream_batch=2, num_chunks=10, softmax_scale=128 ** -0.5)
+    h = Harness(cfg, [0])
+    worst = 0.0
+    for s in range(cfg.num_steps):
+        h.step(s, full=True)
+        for b in range(len(h.st.plan["chunks"])):
+            q, k, v = h.np_inputs[(0, b)]
+            ref = h.st.attend(0, b, q, k, v, rotated="bf16")
+            got = host64(h.run.out[0, b])
+            scale = max(1.0, float(np.abs(ref).max()))
+            worst = max(worst, assert_close(cfg, got, ref, f"out step {s} elem {b}", scale) / scale)
+        h.finish_step()
+    log(f"score jump {grid}: worst max-abs relative to max |out| {worst:.3g}")
 
 
 @pytest.mark.parametrize("kw", [

@@ -158,3 +158,14 @@ def test_pinned_and_rebased_sinks_part_at_the_first_refresh():
     _, b = brute.run_oracle(cfg.with_(rope_pin_sinks=True))
     differ = sorted(k[0] for k in a if not np.allclose(a[k], b[k], atol=1e-9))
     assert differ and differ[0] == 3
+
+
+def test_round_bf16_pins():
+    # exact values stay; ties (half a bf16 quantum, 2^-8 at 1.0) go to the even neighbour;
+    # anything above a tie goes up; the float32 step keeps the sign and handles tiny values
+    from oracle.stream import round_bf16
+    q = 2.0 ** -7                                     # bf16 quantum in [1, 2)
+    x = np.array([1.0, 1.0 + q, 1.0 + q / 2, 1.0 + 3 * q / 2, 1.0 + q / 2 + 2.0 ** -20,
+                  -3.0 - q / 2, 2.0 ** -130, 65280.0 + 128.0])
+    want = np.array([1.0, 1.0 + q, 1.0, 1.0 + 2 * q, 1.0 + q, -3.0, 2.0 ** -130, 65536.0])
+    np.testing.assert_array_equal(round_bf16(x), want)
