@@ -136,7 +136,7 @@ struct SinkArgs {
 // ---- launchers (defined in the .hip files) --------------------------------------------------
 hipError_t launch_rope_append(const AppendArgs& a, int head_dim, int kv, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s);
-hipError_t launch_attention_w64(const AttnArgs& a, hipStream_t s);   // bf16 cache, head_dim 128
+hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s);   // bf16 or e4m3 cache, head_dim 128
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_rebase(const RebaseArgs& a, int head_dim, int kv, hipStream_t s);
 hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s);

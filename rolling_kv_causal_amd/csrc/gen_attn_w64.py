@@ -391,6 +391,11 @@ def check_hazards(lines):
             for v in range(dlo, dlo + 4):
                 if "v" + str(v) in last_mfma_read:
                     assert idx - last_mfma_read["v" + str(v)] >= 12, (l, idx - last_mfma_read["v" + str(v)])
+        if op.startswith("v_") and not op.startswith("v_mfma") and len(l.split()) > 1:
+            dst = l.split()[1].rstrip(",")
+            for v in ([dst] if not dst.startswith("v[") else [f"v{x}" for x in range(int(dst[2:].split(":")[0]), int(dst[:-1].split(":")[1]) + 1)]):
+                if v in last_mfma_read:
+                    assert idx - last_mfma_read[v] >= 12, (l, idx - last_mfma_read[v], "VALU overwrites an MFMA operand")
         if op.startswith("v_") or op.startswith("ds_"):
             toks = l.replace(",", " ").split()[2:] if not op.startswith("ds_") else l.replace(",", " ").split()[1:]
             for tok in toks:
@@ -423,21 +428,59 @@ NSLOT = 4                                        # ring slots of K and of V^T ti
 
 
 BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
+F8 = False                                       # program for the e4m3 cache (set by main)
+STAGE = 16384                                    # e4m3 staging slot: K tile (8 KB), then V^T tile (8 KB)
+SK, SV = 202, 203                                # e4m3: this lane's staging read addresses (K, V^T)
+WK, WV = 240, 244                                # e4m3: widened-chunk write addresses (lo, hi per load)
 
 
 def tile_loads(ph):
-    """Read index -> (m0 setup, load) of this wave's four 1 KB K loads (after reads 1, 5, 9, 13)
-    and four V^T loads (after reads 17, 21, 25, 29) in iteration phase ph: K(t+2) into ring
-    slot ph + 2, V^T(t+1) into slot ph + 1; m0 holds the LDS destination, the SGPR pair of
-    parity ph mod 2 the global tile base and v[230:237] the lane offsets."""
+    """Read index -> (m0 setup, load) of this wave's tile loads in iteration phase ph: bf16,
+    four 1 KB K loads (after reads 1, 5, 9, 13) into ring slot ph + 2 and four V^T loads (after
+    reads 17, 21, 25, 29) into slot ph + 1; e4m3, two of each (after reads 1, 9 and 17, 25)
+    into staging slot ph mod 2.  m0 holds the LDS destination, the SGPR pair of parity ph mod 2
+    the global tile base and v[230:237] the lane offsets."""
     par = ph % 2
     d = {}
-    for first, mbase, slot, base, v0 in ((1, "mk", (ph + 2) % NSLOT, BASE[par][0], KOFF),
-                                         (17, "mv", (ph + 1) % NSLOT, BASE[par][1], VOFF)):
-        for i in range(4):
-            setup = f"s_add_u32 m0, %[{mbase}], {slot * KTILE}" if i == 0 else "s_add_u32 m0, m0, 1024"
-            d[first + 4 * i] = (setup, f"global_load_lds_dwordx4 v{v0 + i}, s[{base}:{base + 1}]")
+    if F8:
+        kinds = ((1, "ms", (ph % 2) * STAGE, BASE[par][0], KOFF), (17, "ms", (ph % 2) * STAGE + STAGE // 2, BASE[par][1], VOFF))
+        n, step = 2, 8
+    else:
+        kinds = ((1, "mk", ((ph + 2) % NSLOT) * KTILE, BASE[par][0], KOFF),
+                 (17, "mv", ((ph + 1) % NSLOT) * KTILE, BASE[par][1], VOFF))
+        n, step = 4, 4
+    for first, mbase, off, base, v0 in kinds:
+        for i in range(n):
+            setup = f"s_add_u32 m0, %[{mbase}], {off}" if i == 0 else "s_add_u32 m0, m0, 1024"
+            d[first + step * i] = (setup, f"global_load_lds_dwordx4 v{v0 + i}, s[{base}:{base + 1}]")
     return d
+
+
+def widen_block(ph, k=True):
+    """e4m3, top of iteration phase ph: this wave's staged bytes of K(t) and V^T(t-1) (staging
+    slot ph mod 2, loaded two iterations ago) widened to bf16 into ring slots ph and ph - 1.
+    A staged 16-byte chunk c = 2p + h of a row holds, in the cache's byte order, elements
+    32p + 8h + [0, 8) and 32p + 16 + 8h + [0, 8): the bf16 chunks 4p + h (lo) and 4p + 2 + h
+    (hi), whose addresses are in v[240:247]."""
+    stage = (ph % 2) * STAGE
+    parts = ([("K", i) for i in range(2)] if k else []) + [("V", i) for i in range(2)]
+    lines = []
+    for j, (kind, i) in enumerate(parts):
+        addr, off = (SK, stage + i * 1024) if kind == "K" else (SV, stage + i * 1024)
+        lines.append(f"ds_read_b128 v[{128 + 4 * j}:{131 + 4 * j}], v{addr} offset:{off}")
+    lines.append("s_waitcnt lgkmcnt(0)")
+    for j in range(len(parts)):
+        for dw in range(4):
+            for sel in range(2):
+                o = f"v{144 + 8 * j + 2 * dw + sel}"
+                lines.append(f"v_cvt_scalef32_pk_bf16_fp8 {o}, v{128 + 4 * j + dw}, 1.0" + (" op_sel:[1,0,0]" if sel else ""))
+    for j, (kind, i) in enumerate(parts):
+        wbase, slot = (WK, ph % NSLOT) if kind == "K" else (WV, (ph - 1) % NSLOT)
+        for half in range(2):
+            lines.append(f"ds_write_b128 v{wbase + 2 * i + half}, v[{144 + 8 * j + 4 * half}:{147 + 8 * j + 4 * half}] "
+                         f"offset:{slot * KTILE}")
+    lines.append("s_waitcnt lgkmcnt(0)")
+    return lines
 
 
 def load_setup(kind, par, ahead):
@@ -446,15 +489,15 @@ def load_setup(kind, par, ahead):
     a valid address, into the free slot, so every iteration issues eight loads and one vmcnt
     serves all).  Returned as units (instruction lists closed in their use of SCC)."""
     f, k, colb, blo, bhi, base = (
-        ("kf", "kk", 14, "kblo", "kbhi", BASE[par][0]) if kind == "K"
-        else ("vf", "vk", 7, "vblo", "vbhi", BASE[par][1]))
+        ("kf", "kk", 13 if F8 else 14, "kblo", "kbhi", BASE[par][0]) if kind == "K"
+        else ("vf", "vk", 6 if F8 else 7, "vblo", "vbhi", BASE[par][1]))
     return [[f"s_add_u32 %[x], %[t], {ahead}", "s_cmp_lt_u32 %[x], %[n]", "s_cselect_b32 %[y], 1, 0"],
             [f"s_add_u32 %[{k}], %[{k}], %[y]"],
             [f"s_cmp_eq_u32 %[{k}], %[tpf]", f"s_cselect_b32 %[{k}], 0, %[{k}]", f"s_addc_u32 %[{f}], %[{f}], 0"],
             [f"v_readlane_b32 %[x], v{SLOTL}, %[{f}]"], NEXT_GAP,     # its SGPR result is read
             # about 20 cycles later at the earliest: the wait overlaps the next MFMA
-            # tile offset in the (layer, head) block: slot * slot bytes + tile (16 KB of K rows or
-            # 128 B of V^T columns)
+            # tile offset in the (layer, head) block: slot * slot bytes + tile (64 K rows or 64 V^T
+            # columns of 2 bytes, or 1 byte in e4m3)
             [f"s_lshl_b32 %[y], %[{k}], {colb}"],
             ["s_mul_i32 %[x], %[x], %[slotb]"],
             ["s_add_u32 %[x], %[x], %[y]"],
@@ -483,8 +526,9 @@ def iteration(ph):
     """Iteration t < n of phase ph = t mod NSLOT (P buffer pp = 1 - ph mod 2 read by PV(t-1),
     P(t) written into the other).  The masked tile block and the rescale are out of line."""
     par, tag = ph % 2, "abcd"[ph]
-    return [# loads of iteration t-2 (K(t), V^T(t-1)) in; every wave is done with iteration t-1's slots
-            "s_waitcnt vmcnt(8)", "s_barrier",
+    return [# loads of iteration t-2 (K(t), V^T(t-1)) in (e4m3: staged, widened by this wave);
+            # every wave is done with iteration t-1's slots
+            f"s_waitcnt vmcnt({4 if F8 else 8})"] + (widen_block(ph) if F8 else []) + ["s_barrier",
             f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc0 .Lw64_m{tag}_%="] + \
         tile_block(ph, False) + \
         [f".Lw64_td{tag}_%=:",
@@ -516,13 +560,13 @@ def loop_program():
         if ph < NSLOT - 1:
             lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc0 .Lw64_end_%="]
     lines += ["s_cmp_lt_u32 %[t], %[n]", "s_cbranch_scc1 .Lw64_loop_%=",
-              ".Lw64_end_%=:", "s_waitcnt vmcnt(0)", "s_barrier",
-              f"s_and_b32 %[x], %[n], {NSLOT - 1}"]
+              ".Lw64_end_%=:", "s_waitcnt vmcnt(0)", f"s_and_b32 %[x], %[n], {NSLOT - 1}"]
     for ph in range(1, NSLOT):
         lines += [f"s_cmp_eq_u32 %[x], {ph}", f"s_cbranch_scc1 .Lw64_pv{ph}_%="]
-    lines += pv_only_block(0) + ["s_branch .Lw64_fin_%="]
-    for ph in range(1, NSLOT):
-        lines += [f".Lw64_pv{ph}_%=:"] + pv_only_block(ph) + ["s_branch .Lw64_fin_%="]
+    for ph in range(NSLOT):
+        # e4m3: V^T(n-1) widened first
+        lines += ([f".Lw64_pv{ph}_%=:"] if ph else []) + (widen_block(ph, k=False) if F8 else []) + \
+            ["s_barrier"] + pv_only_block(ph) + ["s_branch .Lw64_fin_%="]
     for ph in range(NSLOT):
         lines += out_of_line(ph)
     lines += [".Lw64_fin_%=:", "s_mov_b32 m0, %[m0save]"]
@@ -538,7 +582,11 @@ def emit(name, lines):
 def main():
     out = ["// Generated by gen_attn_w64.py; do not edit.  The tile loop of the 64-row attention",
            "// kernel as one asm program (register plan, blocks and hazard rules in the generator).", ""]
+    global F8
     out.append(emit("SDV2_W64_LOOP", loop_program()))
+    F8 = True
+    out.append(emit("SDV2_W64_LOOP_FP8", loop_program()))
+    F8 = False
     sys.stdout.write("\n".join(out))
 
 

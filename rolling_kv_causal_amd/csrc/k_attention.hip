@@ -569,7 +569,7 @@ static bool use_w64() {
 }
 
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s) {
-  if (kv == kKvBF16 && head_dim == 128 && use_w64()) return launch_attention_w64(a, s);
+  if ((kv == kKvBF16 || kv == kKvFP8) && head_dim == 128 && use_w64()) return launch_attention_w64(a, kv, s);
   if (kv != kKvF32) {
     const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
     if (kv == kKvFP8)

@@ -51,12 +51,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate: vmcnt(n), lgkmcnt and expcnt at their maxima
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// F8: e4m3 cache.  Each wave loads its 2 KB share of a K and of a V^T tile (e4m3) into a
+// staging slot (two slots of 16 KB, by iteration parity) and, at the top of the iteration that
+// publishes the tile, widens exactly those bytes to bf16 into the ring slot (exact conversion);
+// the rest of the loop is the bf16 one.
+template <bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_w64_kernel(const AttnArgs a) {
-  constexpr int D = 128, KRB = 256, VRB = 128;
+  constexpr int D = 128, KRB = 256, VRB = 128, EB = F8 ? 1 : 2;   // EB: cache bytes per element
   constexpr int K_BYTES = kTileKeys * KRB, V_BYTES = D * VRB, NBUF = 4;
-  constexpr int LD = K_BYTES / 1024 / 4;      // 1 KB loads per wave per tile (K; the same for V^T)
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * (K_BYTES + V_BYTES)];
+  constexpr int STAGE = F8 ? 2 * kTileKeys * D : 0;              // e4m3 K + V^T tile bytes
+  constexpr int LD = K_BYTES * EB / 2 / 1024 / 4;                 // 1 KB loads per wave per tile (K; the same for V^T)
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF * (K_BYTES + V_BYTES) + 2 * STAGE];
+  char* const ldsS = lds + NBUF * (K_BYTES + V_BYTES);            // e4m3 staging slots
   char* const ldsK = lds;
   char* const ldsV = lds + NBUF * K_BYTES;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -109,13 +116,13 @@ void attn_w64_kernel(const AttnArgs a) {
   const int64_t head_off = (int64_t)head * a.head_stride;
   const int own_i = min(max(lane - a.nshared, 0), a.T - 1);
   const int slot_lane = lane < a.nshared ? a.slots[lane] : a.own_slot[elem * a.T + own_i];
-  const char* const kblk = kvb + (a.k_layer_off + head_off) * 2;
-  const char* const vblk = kvb + (a.v_layer_off + head_off) * 2;
-  const int64_t slot_bytes = a.slot_stride * 2;
+  const char* const kblk = kvb + (a.k_layer_off + head_off) * EB;
+  const char* const vblk = kvb + (a.v_layer_off + head_off) * EB;
+  const int64_t slot_bytes = a.slot_stride * EB;
   auto frame_at = [&](TileCursor& c) {
     const int slot = __builtin_amdgcn_readlane(slot_lane, c.f & 63);
-    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * 2);
-    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * 2);
+    c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * EB);
+    c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * EB);
   };
   auto cursor_at = [&](int tile) -> TileCursor {
     TileCursor c;
@@ -130,47 +137,70 @@ void attn_w64_kernel(const AttnArgs a) {
       ++c.f;
       frame_at(c);
     } else {
-      c.kp += kTileKeys * D * 2;
-      c.vp += kTileKeys * 2;
+      c.kp += kTileKeys * D * EB;
+      c.vp += kTileKeys * EB;
     }
   };
 
-  // Global->LDS loads: wave w fills 1 KB pieces w*LD .. w*LD+LD-1 of each tile.
+  // Global->LDS loads.  bf16: wave w fills 1 KB pieces w*LD .. w*LD+LD-1 of each ring tile.
+  // e4m3: wave w loads K rows 16w + 8i + lane / 8 (chunk lane % 8) and V^T rows 32w + 16i +
+  // lane / 4 (chunk lane % 4), i = 0, 1, in lane order into its 2 KB of the staging slot.
   uint32_t koff[LD], voff[LD];
+  int kr8[LD], vr8[LD];
 #pragma unroll
   for (int i = 0; i < LD; ++i) {
     int Rr, c;
-    lds_chunk_inv<KRB>((wave * LD + i) * 64 + lane, Rr, c);
-    koff[i] = (uint32_t)(perm_key(Rr) * KRB + c * 16);
-    lds_chunk_inv<VRB>((wave * LD + i) * 64 + lane, Rr, c);
-    voff[i] = (uint32_t)(Rr * a.Npad * 2 + c * 16);
+    if constexpr (F8) {
+      kr8[i] = 16 * wave + 8 * i + (lane >> 3);
+      koff[i] = (uint32_t)(perm_key(kr8[i]) * D + (lane & 7) * 16);
+      vr8[i] = 32 * wave + 16 * i + (lane >> 2);
+      voff[i] = (uint32_t)(vr8[i] * a.Npad + (lane & 3) * 16);
+    } else {
+      lds_chunk_inv<KRB>((wave * LD + i) * 64 + lane, Rr, c);
+      koff[i] = (uint32_t)(perm_key(Rr) * KRB + c * 16);
+      lds_chunk_inv<VRB>((wave * LD + i) * 64 + lane, Rr, c);
+      voff[i] = (uint32_t)(Rr * a.Npad * 2 + c * 16);
+    }
   }
   auto fill_k = [&](const TileCursor& c, int slot) {
 #pragma unroll
     for (int i = 0; i < LD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(c.kp + koff[i]),
-                                       (lds_void*)(ldsK + slot * K_BYTES + (wave * LD + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(c.kp + koff[i]),
+          (lds_void*)(F8 ? ldsS + slot * STAGE + wave * 2048 + i * 1024 : ldsK + slot * K_BYTES + (wave * LD + i) * 1024),
+          16, 0, 0);
   };
   auto fill_v = [&](const TileCursor& c, int slot) {
 #pragma unroll
     for (int i = 0; i < LD; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(c.vp + voff[i]),
-                                       (lds_void*)(ldsV + slot * V_BYTES + (wave * LD + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(c.vp + voff[i]),
+          (lds_void*)(F8 ? ldsS + slot * STAGE + STAGE / 2 + wave * 2048 + i * 1024
+                         : ldsV + slot * V_BYTES + (wave * LD + i) * 1024),
+          16, 0, 0);
   };
 
   // Prologue: V^T slot 3 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
-  // slot 1 (K(0) again when n = 1: the loop counts twelve loads in flight at its start), V(0)
-  // into slot 0.
+  // slot 1 (K(0) again when n = 1: the loop counts the loads in flight at its start), V(0)
+  // into slot 0.  e4m3: the V^T half of staging slot 0 is zeroed instead (the top of iteration
+  // 0 widens it into V^T slot 3); K(0) goes to staging slot 0, K(1) and V(0) to slot 1, as if
+  // loaded by iterations -2 and -1.
+  if constexpr (F8) {
 #pragma unroll
-  for (int i = 0; i < V_BYTES / (256 * 16); ++i)
-    reinterpret_cast<uint4*>(ldsV + 3 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < STAGE / 2 / (256 * 16); ++i)
+      reinterpret_cast<uint4*>(ldsS + STAGE / 2)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V_BYTES / (256 * 16); ++i)
+      reinterpret_cast<uint4*>(ldsV + 3 * V_BYTES)[tid + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   __syncthreads();
   const TileCursor c0 = cursor_at(t_begin);
   TileCursor kc = c0;
   fill_k(kc, 0);
   if (n > 1) advance(kc);
   fill_k(kc, 1);
-  fill_v(c0, 0);
+  fill_v(c0, F8 ? 1 : 0);
 
   // The tile loop (generated asm, see gen_attn_w64.py).  Its state lives in the registers
   // named by the operands below; the compiler sees one statement.
@@ -214,24 +244,50 @@ void attn_w64_kernel(const AttnArgs a) {
   const float sl = a.scale_log2;
   unsigned long long trig;
   int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp;
-  asm volatile(SDV2_W64_LOOP
-               : "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),
-                 "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),
-                 "={v[128:159]}"(frg), "={v[160:175]}"(frg2), "+{v[176:183]}"(kaddr),
-                 "+{v[184:187]}"(vaddr), "={v[188:199]}"(tmp), "={v[200:201]}"(mrun),
-                 "={v[248:255]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),
-                 "={v[228:229]}"(lrun),
-                 [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk), [sf] "+s"(sf),
-                 [sk] "+s"(sk), [t] "+s"(t),
-                 [trig] "=&s"(trig), [x] "=&s"(x), [y] "=&s"(y), [nvalid] "=&s"(nvalid),
-                 [tk] "=&s"(tk), [mflag1] "=&s"(mflag1),
-                 [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
-               : "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec),
-                 "{v[230:233]}"(koffv), "{v[234:237]}"(voffv), "{v238}"(slot_lane),
-                 [n] "s"(n), [tpf] "s"(tpf), [nshared] "s"(nshared), [N] "s"(Ntok),
-                 [tqw] "s"(tq_wave), [kblo] "s"(kblo), [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb),
-                 [mk] "s"(mk), [mv] "s"(mv), [sl] "s"(sl)
-               : "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91");
+#define SDV2_W64_OUTPUTS                                                                      \
+  "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),                  \
+      "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),               \
+      "={v[128:159]}"(frg), "={v[160:175]}"(frg2), "+{v[176:183]}"(kaddr),                      \
+      "+{v[184:187]}"(vaddr), "={v[188:199]}"(tmp), "={v[200:201]}"(mrun),                      \
+      "={v[248:255]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),                    \
+      "={v[228:229]}"(lrun), [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk),        \
+      [sf] "+s"(sf), [sk] "+s"(sk), [t] "+s"(t), [trig] "=&s"(trig), [x] "=&s"(x),              \
+      [y] "=&s"(y), [nvalid] "=&s"(nvalid), [tk] "=&s"(tk), [mflag1] "=&s"(mflag1),             \
+      [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
+#define SDV2_W64_INPUTS                                                                       \
+  "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec), "{v[230:233]}"(koffv),        \
+      "{v[234:237]}"(voffv), "{v238}"(slot_lane), [n] "s"(n), [tpf] "s"(tpf),                   \
+      [nshared] "s"(nshared), [N] "s"(Ntok), [tqw] "s"(tq_wave), [kblo] "s"(kblo),              \
+      [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb), [sl] "s"(sl)
+#define SDV2_W64_CLOBBERS "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91"
+  if constexpr (F8) {
+    // e4m3 widening addresses: this lane's staged 16 bytes of each load (K, V^T) and the two
+    // bf16 chunks each widens into (ring slot 0; the program adds the slot)
+    const int ms = (int)((uint32_t)(uintptr_t)ldsS + wave * 2048);
+    const int sk_addr = ms + lane * 16, sv_addr = ms + STAGE / 2 + lane * 16;
+    i32x4 wk, wv;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int kc8 = lane & 7, vc8 = lane & 3;
+      wk[2 * i] = (int)((uint32_t)(uintptr_t)ldsK + lds_chunk<KRB>(kr8[i], 4 * (kc8 >> 1) + (kc8 & 1)));
+      wk[2 * i + 1] = (int)((uint32_t)(uintptr_t)ldsK + lds_chunk<KRB>(kr8[i], 4 * (kc8 >> 1) + 2 + (kc8 & 1)));
+      wv[2 * i] = (int)((uint32_t)(uintptr_t)ldsV + lds_chunk<VRB>(vr8[i], 4 * (vc8 >> 1) + (vc8 & 1)));
+      wv[2 * i + 1] = (int)((uint32_t)(uintptr_t)ldsV + lds_chunk<VRB>(vr8[i], 4 * (vc8 >> 1) + 2 + (vc8 & 1)));
+    }
+    asm volatile(SDV2_W64_LOOP_FP8
+                 : SDV2_W64_OUTPUTS
+                 : SDV2_W64_INPUTS, [ms] "s"(ms), "{v202}"(sk_addr), "{v203}"(sv_addr), "{v[240:243]}"(wk),
+                   "{v[244:247]}"(wv)
+                 : SDV2_W64_CLOBBERS);
+  } else {
+    asm volatile(SDV2_W64_LOOP
+                 : SDV2_W64_OUTPUTS
+                 : SDV2_W64_INPUTS, [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_CLOBBERS);
+  }
+#undef SDV2_W64_OUTPUTS
+#undef SDV2_W64_INPUTS
+#undef SDV2_W64_CLOBBERS
   (void)frg;
   (void)frg2;
   (void)tmp;
@@ -282,9 +338,12 @@ void attn_w64_kernel(const AttnArgs a) {
   }
 }
 
-hipError_t launch_attention_w64(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s) {
   const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
-  hipLaunchKernelGGL(attn_w64_kernel, dim3(grid), dim3(256), 0, s, a);
+  if (kv == kKvFP8)
+    hipLaunchKernelGGL(attn_w64_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_w64_kernel<false>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
