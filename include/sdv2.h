@@ -170,9 +170,9 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
  * Q_rot = d_q_rot as rotated by sdv2_cache_append; inside the own chunk a query of frame t sees
  * the keys of frames 0..t (block-causal).  d_out: [nbatch][T'N][H][d], written.  The
  * workspace given at create time is used for split-KV partial results (calls on one cache
- * must not overlap in time).  With a bf16 cache and head_dim 128 the 64-query-row kernel runs;
- * the environment variable SDV2_ATTN_KERNEL=pingpong (read once per process) selects the
- * 32-row kernel, whose results agree up to fp32 summation order. */
+ * must not overlap in time).  With a bf16 or e4m3 cache and head_dim 128 the 64-query-row
+ * kernel runs; the environment variable SDV2_ATTN_KERNEL=pingpong (read once per process)
+ * selects the 32-row kernel, whose results agree up to fp32 summation order. */
 int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream);
 
