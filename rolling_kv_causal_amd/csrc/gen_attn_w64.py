@@ -11,19 +11,24 @@ and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete
 16th), the softmax of the tile's S: exp2(S*scale_log2 - m) rounded to bf16 P^T words for the
 next tile's PV, with per-lane tile sums.
 
-Iteration t (every state register is an asm operand, so the compiler never moves them):
-  wait for the loads of iteration t-2, barrier; branch on mflag(t) to the masked variant
-  tile block: QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this wave's eight
-    1 KB tile loads (K(t+2), V^T(t+1)) spread over the stream, and, in the free issue slots of
-    the QK part, the scalar set-up of iteration t+1 (load cursors, bases and ring slots, the
-    walk cursor and mflag of tile t+1, LDS read address steps); then the lazy test
-    (trig != 0: some lane's tile sum left [0, 256] or is not finite)
+Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
+moves them; the loop is generated once per phase, so the ring slots of K(t) (ph) and V^T(t-1)
+(ph - 1) are immediate offsets of the fragment reads):
+  wait for the loads of iteration t-2 (e4m3: widen this wave's staged share of K(t), V^T(t-1)
+    into the bf16 ring), barrier; branch on mflag(t) to the masked variant
+  tile block: QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this wave's tile
+    loads (K(t+2), V^T(t+1); bf16 eight of 1 KB into the ring, e4m3 four into the staging
+    slot of parity ph mod 2) spread over the stream, and, in the free issue slots of the QK
+    part, the scalar set-up of iteration t+1 (load cursors and global bases, the walk cursor
+    and mflag of tile t+1); then the lazy test (trig != 0: some lane's tile sum left [0, 256]
+    or is not finite)
   trig == 0: l += tile sums; otherwise (out of line) the rescale: masked row max, m, alpha,
     O and l scaled, P of the tile recomputed into buffer 1-pp, l += its sums
-After the loop the last PV.  Set-up values alternate between two register sets by iteration
-parity, so the loads of iteration t read one set while the stream writes the other.  The
-masked variant ANDs every P word with a ragged-tile mask (keys >= nvalid) and a per-row-block
-causal mask (own frame tk after the row's frame), both computed at the block start.
+After the loop the last PV (e4m3: after widening V^T(n-1)).  Set-up values alternate between
+two register sets by iteration parity, so the loads of iteration t read one set while the
+stream writes the other.  The masked variant ANDs every P word with a ragged-tile mask (keys
+>= nvalid) and a per-row-block causal mask (own frame tk after the row's frame), both computed
+at the block start.
 
 Register plan (per lane):
   a[0:127]    O^T  o[db][qb] at a[(2db+qb)*16 .. +15]
@@ -37,17 +42,19 @@ Register plan (per lane):
   v[206:221]  ragged masks of the 16 P words of a row block;  v[222:223] causal mask per qb
   v[224] 8g;  v[225:226] frame of the lane's row per qb;  v[227] (lane ^ 32) * 4
   v[228:229]  l per qb;  v[230:237] K and V^T lane offsets of the tile loads;  v238 frame slots
+  v[202:203], v[240:247]  e4m3: staging read and widened-chunk write addresses
   v[248:255]  tile sums, four per qb
   s[84:91]    global bases of the K and V^T tile loads, two sets by iteration parity
 
 Hazards kept by construction (gfx950, counted in issued instructions): an MFMA result is read
 by no VALU or MFMA A/B operand within 12 instructions (checked below; the rare block starts
 with 16 wait states); VALU-written P words are read by MFMAs of the next tile only; an
-exponential's result is read at least one instruction later; a fragment slot is refilled at
-least 12 instructions after the last MFMA that reads it (an MFMA may read its A operand after
-issue, so 8 reads in flight use a ring of 12 slots); an LDS DMA load does not directly follow
-a write of m0; same-accumulator MFMAs chain back to back (allowed); VOP3 forms read at most one
-SGPR.  Measured on gfx950 and avoided: a dot2 (v_dot2_f32_bf16) waits for the MFMA in flight
+exponential's result is read at least one instruction later; a register an MFMA reads is not
+overwritten by an LDS read or a VALU op within 12 instructions (an MFMA may read its A operand
+after issue, so 8 reads in flight use a ring of 12 slots); an LDS DMA load does not directly
+follow a write of m0; same-accumulator MFMAs chain back to back (allowed); VOP3 forms read at
+most one SGPR; a VALU-written SGPR (readlane) is read by the scalar unit only after the next
+MFMA (measured: the wave stalls about 20 cycles otherwise).  Measured on gfx950 and avoided: a dot2 (v_dot2_f32_bf16) waits for the MFMA in flight
 to finish, and its result is not interlocked for a non-dot2 reader (3 wait states needed).
 """
 import sys
