@@ -98,10 +98,15 @@ def test_score_jump_rescales_mid_walk(monkeypatch, grid):
     dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=12, grid_w=25,
          num_heads=4, sink_frames=3, window_frames=2, stream_batch=1, num_chunks=9, embed_dim=16,
          sink_threshold=0.2, embed_kind="iid", softmax_scale=128 ** -0.5),
-], ids=["bf16-ragged-B3-refresh", "bf16-d64-S0", "fp32-d128-W1-B4", "bf16-sinks-iid"])
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=11, grid_w=13,
+         num_heads=2, sink_frames=1, window_frames=2, stream_batch=2, num_chunks=8,
+         softmax_scale=128 ** -0.5),
+], ids=["bf16-ragged-B3-refresh", "bf16-d64-S0", "fp32-d128-W1-B4", "bf16-sinks-iid", "bf16-3-tiles-per-frame"])
 def test_small_ragged_streams(kw):
     # token counts that are not multiples of the 64-key tile or the 128-row query tile,
-    # degenerate windows (W = 1, S = 0), B up to 4, and several layers
+    # degenerate windows (W = 1, S = 0), B up to 4, and several layers; 143 tokens give three
+    # key tiles per frame, so the key walks have 3, 6 and 9 tiles (every phase of the 64-row
+    # kernel's four-slot ring ends a walk)
     cfg = _small(**kw)
     _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
 
