@@ -67,6 +67,7 @@ TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
 WAIT_EVERY = 2                                   # one LDS wait per this many fragment reads
+READ_START = 2                                   # fragment reads issued before the first MFMA
 NEXT_GAP = ["<next gap>"]                        # unit marker: continue the chunk after the next MFMA
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
 
@@ -213,7 +214,8 @@ def mask_setup():
 
 
 def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
-    """Reads KA ahead of their MFMAs; VALU ops spread evenly over the MFMAs from index
+    """Reads KA ahead of their MFMAs (after a ramp: READ_START reads before the first MFMA, then
+    two per MFMA pair until KA are in flight); VALU ops spread evenly over the MFMAs from index
     valu_from on.  dma maps a read index i to (m0 setup, tile load): the setup follows the MFMA
     pair of read i and the load the LDS read issued after it, so the tile loads of a wave are
     spread over the tile instead of queueing behind the other waves' loads at the texture unit.
@@ -223,13 +225,24 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
     instructions besides the MFMA), so the wave can issue it while the matrix core works."""
     dma = dma or {}
     lines = []
-    for i in range(min(KA, len(reads))):
+    # reads issued after the MFMA pair of read i: KA ahead in the steady state; the stream starts
+    # with READ_START reads and catches up by one extra read per pair, so the four waves leaving
+    # the barrier together do not queue 32 reads at the LDS at once
+    first = min(READ_START, len(reads))
+    after = []
+    nr = first
+    for i in range(len(reads)):
+        upto = min(len(reads), i + KA + 1, nr + 2)
+        after.append(list(range(nr, upto)))
+        nr = upto
+    assert nr == len(reads)
+    for i in range(first):
         lines.append(read_instr(reads[i], i % RING, ph))
-    issued = min(KA, len(reads))
+    issued = first
     n_mfma = 2 * len(reads)
     fixed = [0] * n_mfma                         # read, wait and load instructions after MFMA g
     for i in range(len(reads)):
-        fixed[2 * i + 1] += ((i + 1) % WAIT_EVERY == 0) + (i + KA < len(reads)) + 2 * (i in dma)
+        fixed[2 * i + 1] += ((i + 1) % WAIT_EVERY == 0) + len(after[i]) + 2 * (i in dma)
     # VALU ops in order over the gaps from valu_from on, levelling VALU + fixed per gap
     per = [0] * n_mfma
     region = range(valu_from, n_mfma)
@@ -268,10 +281,10 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
             lines += placed[2 * i + j]
         if i in dma:
             lines.append(dma[i][0])
-        if i + KA < len(reads):
-            lines.append(read_instr(reads[i + KA], (i + KA) % RING, ph))
+        for j in after[i]:
+            lines.append(read_instr(reads[j], j % RING, ph))
             issued += 1
-        elif i in dma:
+        if i in dma and not after[i]:
             lines.append("s_nop 0")
         if i in dma:
             lines.append(dma[i][1])
