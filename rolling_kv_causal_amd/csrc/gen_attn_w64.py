@@ -95,6 +95,11 @@ def s_elem(kb, qb, v):
     return f"v{(kb * 2 + qb) * 16 + v}"
 
 
+def cb_reg(qb):
+    b = CB + 16 * qb
+    return f"v[{b}:{b + 15}]"
+
+
 def p_base(buf):
     return 64 if buf == 0 else 96
 
@@ -143,7 +148,7 @@ def mfma_pair(r, slot, pp):
     if r[0] == "K":
         _, kb, kd = r
         for qb in range(2):
-            c = "0" if kd == 0 else s_reg(kb, qb)
+            c = s_reg(kb, qb) if kd else (cb_reg(qb) if NEGM else "0")
             out.append(f"v_mfma_f32_32x32x16_bf16 {s_reg(kb, qb)}, {frag(slot)}, {q_reg(qb, kd)}, {c}")
     else:
         _, db, ks = r
@@ -158,7 +163,9 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
     word is ANDed with its ragged-tile mask and the row block's causal mask and the sums add
     the two bf16 halves of the masked words, so masked keys add nothing.  (Row sums by dot2
     would be shorter, but gfx950 holds a dot2 back until the MFMA in flight has finished.)
-    mreg(qb): register holding m; sums(qb, i): the four tile-sum accumulators."""
+    mreg(qb): register holding m (bf16: the shift of S, given only when recomputing); sums(qb,
+    i): the four tile-sum accumulators."""
+    shifted = mreg is not None
     mreg = mreg or (lambda qb: f"v{M + qb}")
     sums = sums or (lambda qb, i: f"v{TS + 4 * qb + i}")
     ops = []
@@ -171,18 +178,31 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                     t = [f"v{TMP + (gi % 3) * 4 + j}" for j in range(4)]
                     gi += 1
                     vs = [half * 8 + 2 * w0 + j for j in range(4)]
-                    for j in range(4):
-                        ops.append(f"v_fma_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, %[sl], -{mreg(qb)}")
-                    for j in range(4):
-                        ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
+                    if not NEGM:
+                        for j in range(4):
+                            ops.append(f"v_fma_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, %[sl], -{mreg(qb)}")
+                        for j in range(4):
+                            ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
+                    elif shifted:
+                        for j in range(4):
+                            ops.append(f"v_sub_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, {mreg(qb)}")
+                        for j in range(4):
+                            ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
+                    else:                  # S already holds s * scale_log2 - m
+                        for j in range(4):
+                            ops.append(f"v_exp_f32 {t[j]}, {s_elem(kb, qb, vs[j])}")
                     words = [p_word(pc, qb, ks, w0), p_word(pc, qb, ks, w0 + 1)]
                     ops.append(f"v_cvt_pk_bf16_f32 {words[0]}, {t[0]}, {t[1]}")
                     ops.append(f"v_cvt_pk_bf16_f32 {words[1]}, {t[2]}, {t[3]}")
                     if masked:
                         for wi, w in enumerate(words):
                             j = ks * 4 + w0 + wi
-                            ops.append(f"v_and_b32 {w}, {w}, v{RMASK + j}")
-                            ops.append(f"v_and_b32 {w}, {w}, v{CMASK + qb}")
+                            if NEGM:
+                                ops.append(f"v_accvgpr_read_b32 v{MT}, a{MKA + 16 * qb + j}")
+                                ops.append(f"v_and_b32 {w}, {w}, v{MT}")
+                            else:
+                                ops.append(f"v_and_b32 {w}, {w}, v{RMASK + j}")
+                                ops.append(f"v_and_b32 {w}, {w}, v{CMASK + qb}")
                         for wi, w in enumerate(words):
                             ops.append(f"v_lshlrev_b32 {t[2 * wi]}, 16, {w}")
                             ops.append(f"v_and_b32 {t[2 * wi + 1]}, 0xffff0000, {w}")
@@ -196,7 +216,29 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
 
 def mask_setup():
     """Ragged masks: low half of word j valid iff 8g + key(j) < nvalid, high half iff
-    8g + key(j) + 1 < nvalid.  Causal mask of qb: all ones iff tk <= frame of the row."""
+    8g + key(j) + 1 < nvalid.  Causal mask of qb: all ones iff tk <= frame of the row.
+    bf16: the product of both per (qb, word) into a[192 + 16 qb + j]."""
+    if NEGM:
+        g8, tq0, tq1 = (f"v{TMP + 5}", f"v{TMP + 6}", f"v{TMP + 7}")
+        lines = [f"v_accvgpr_read_b32 {g8}, a{LANEA}", f"v_accvgpr_read_b32 {tq0}, a{LANEA + 1}",
+                 f"v_accvgpr_read_b32 {tq1}, a{LANEA + 2}",
+                 f"v_mov_b32 v{TMP + 2}, 0xffff", f"v_mov_b32 v{TMP + 3}, 0xffff0000", f"v_mov_b32 v{TMP + 4}, -1"]
+        for qb in range(2):
+            lines += [f"v_cmp_le_i32 vcc, %[tk], v{TMP + 6 + qb}",
+                      f"v_cndmask_b32 v{TMP + 8 + qb}, 0, v{TMP + 4}, vcc"]
+        for j in range(16):
+            c = word_key(j)
+            lines += [f"s_sub_i32 %[stmp], %[nvalid], {c}",
+                      f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
+                      f"v_cndmask_b32 v{TMP}, 0, v{TMP + 2}, vcc",
+                      f"s_sub_i32 %[stmp], %[nvalid], {c + 1}",
+                      f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
+                      f"v_cndmask_b32 v{TMP + 1}, 0, v{TMP + 3}, vcc",
+                      f"v_or_b32 v{TMP + 10}, v{TMP}, v{TMP + 1}"]
+            for qb in range(2):
+                lines += [f"v_and_b32 v{TMP + 11}, v{TMP + 10}, v{TMP + 8 + qb}",
+                          f"v_accvgpr_write_b32 a{MKA + 16 * qb + j}, v{TMP + 11}"]
+        return lines
     lines = [f"v_mov_b32 v{TMP + 2}, 0xffff", f"v_mov_b32 v{TMP + 3}, 0xffff0000", f"v_mov_b32 v{TMP + 4}, -1"]
     for j in range(16):
         c = word_key(j)
@@ -302,8 +344,8 @@ def tile_block(ph, masked):
     pp = 1 - par
     pc = 1 - pp
     lines = mask_setup() if masked else []
-    extra = [(0, load_setup("K", 1 - par, 3)), (0, load_setup("V", 1 - par, 2)),
-             (0, walk_setup(1 - par, True))]
+    extra = [(0, v_setup(1 - par)), (0, cursor_shift()), (0, k_setup(1 - par, 3)),
+             (0, walk_setup(1 - par, False))]
     lines += stream(k_reads() + v_reads(), pp, ph, softmax_ops(pc, masked), tile_loads(ph), SM_FROM, extra)
     lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
               f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
@@ -315,10 +357,71 @@ def tile_block(ph, masked):
               "s_mov_b64 %[trig], vcc",
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP + 1}",
               "s_or_b64 %[trig], %[trig], vcc"]
+    if NEGM:
+        # a row that has no maximum yet (m = -inf) scores against m = 0: rescale it
+        lines.append("s_or_b64 %[trig], %[trig], %[ninf]")
+    return lines
+
+
+def rare_block_negm(pc, masked):
+    """bf16 rescale of the tile: S = s * scale_log2 - mc, mc = m if finite, else 0.  New row
+    maximum m' = max(m, max over valid keys of S + mc); O, l scaled by 2^(m - m'); the tile's
+    P recomputed as 2^(S - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of the row
+    block set to -mc'; ninf: lanes whose row still has m = -inf."""
+    mx, y, mn, al, mcn, t0, t1, ninf = (f"v{x}" for x in range(128, 136))
+    mc, dd, bp = "v144", "v145", "v146"
+    lines = ["s_nop 15", f"v_mov_b32 {ninf}, {NEG_INF}", f"v_accvgpr_read_b32 {bp}, a{LANEA + 3}"]
+    for qb in range(2):
+        lines.append(f"v_mov_b32 {mx}, {NEG_INF}")
+        for j in range(16):
+            kb, v = j >> 3, ((j >> 2) & 1) * 8 + 2 * (j & 3)
+            lo, hi = s_elem(kb, qb, v), s_elem(kb, qb, v + 1)
+            if masked:
+                lines += [f"v_accvgpr_read_b32 {t0}, a{MKA + 16 * qb + j}",
+                          f"v_and_b32 {t1}, 0xffff, {t0}",
+                          f"v_cmp_ne_u32 vcc, 0, {t1}",
+                          f"v_cndmask_b32 {t1}, {ninf}, {lo}, vcc",
+                          f"v_max_f32 {mx}, {mx}, {t1}",
+                          f"v_cmp_lt_u32 vcc, 0xffff, {t0}",
+                          f"v_cndmask_b32 {t1}, {ninf}, {hi}, vcc",
+                          f"v_max_f32 {mx}, {mx}, {t1}"]
+            else:
+                lines.append(f"v_max3_f32 {mx}, {mx}, {lo}, {hi}")
+        lines += [f"ds_bpermute_b32 {y}, {bp}, {mx}",
+                  "s_waitcnt lgkmcnt(0)",
+                  f"v_max_f32 {mx}, {mx}, {y}",
+                  f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + qb}",
+                  f"v_cndmask_b32_e64 {mc}, v{M + qb}, 0, vcc",       # mc: m, 0 while m = -inf
+                  f"v_add_f32 {t0}, {mx}, {mc}",
+                  f"v_max_f32 {mn}, v{M + qb}, {t0}",                 # m'
+                  f"v_sub_f32 {t0}, v{M + qb}, {mn}",
+                  f"v_exp_f32 {al}, {t0}",
+                  f"v_cmp_eq_f32 vcc, {NEG_INF}, {mn}",
+                  f"v_cndmask_b32_e64 {al}, {al}, 1.0, vcc",          # alpha = 1 if m' = -inf
+                  f"v_cndmask_b32_e64 {mcn}, {mn}, 0, vcc",           # mc'
+                  f"v_sub_f32 {dd}, {mcn}, {mc}",
+                  f"v_mov_b32 v{M + qb}, {mn}",
+                  f"v_mul_f32 v{L + qb}, v{L + qb}, {al}"]
+        vals = [(db, v) for db in range(4) for v in range(16)]
+        for k in range(0, 64, 4):
+            grp = vals[k:k + 4]
+            tmps = [f"v{136 + i}" for i in range(4)]   # v136..v139
+            lines += [f"v_accvgpr_read_b32 {tmps[i]}, {o_elem(db, qb, v)}" for i, (db, v) in enumerate(grp)]
+            lines += [f"v_mul_f32 {tmps[i]}, {tmps[i]}, {al}" for i in range(4)]
+            lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
+        ss = [f"v{140 + i}" for i in range(4)]
+        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: dd, sums=lambda _q, i: ss[i])
+        lines += [f"v_add_f32 v{L + qb}, v{L + qb}, {x}" for x in ss]
+        lines.append(f"v_mul_f32 {t0}, -1.0, {mcn}")
+        lines += [f"v_mov_b32 v{CB + 16 * qb + i}, {t0}" for i in range(16)]
+    lines += [f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M}", "s_mov_b64 %[ninf], vcc",
+              f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + 1}", "s_or_b64 %[ninf], %[ninf], vcc"]
     return lines
 
 
 def rare_block(pc, masked):
+    if NEGM:
+        return rare_block_negm(pc, masked)
     mx, y, mn, al, mm, t0, t1, ninf = (f"v{x}" for x in range(128, 136))
     lines = ["s_nop 15", f"v_mov_b32 {ninf}, {NEG_INF}"]
     for qb in range(2):
@@ -369,7 +472,12 @@ def init_block():
     lines = [f"v_accvgpr_write_b32 a{i}, 0" for i in range(128)]
     lines += [f"v_mov_b32 v{i}, 0" for i in range(128)]
     lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
-    lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
+    if NEGM:
+        # mc = 0 while m = -inf: the -m blocks start at zero and every row is flagged
+        lines += [f"v_mov_b32 v{i}, 0" for i in list(range(CB, CB + 32)) + list(range(TS, TS + 8)) + [L, L + 1]]
+        lines.append("s_mov_b64 %[ninf], -1")
+    else:
+        lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
     return lines
 
 
@@ -387,6 +495,7 @@ def check_hazards(lines):
     last_exp = {}
     last_mfma_read = {}
     last_dot = {}
+    last_valu = {}
     last_m0 = -100
     for idx, l in enumerate(lines):
         op = l.split()[0] if l.split() else ""
@@ -395,6 +504,12 @@ def check_hazards(lines):
         if op.startswith("global_load_lds"):
             assert idx - last_m0 >= 2, (l, "m0 written by the previous instruction")
         if op.startswith("v_mfma"):
+            for opnd in l.replace(",", " ").split()[2:5]:
+                if opnd.startswith("v["):
+                    lo_, hi_ = (int(x) for x in opnd[2:-1].split(":"))
+                    for v in range(lo_, hi_ + 1):
+                        if f"v{v}" in last_valu:
+                            assert idx - last_valu[f"v{v}"] >= 4, (l, idx - last_valu[f"v{v}"], "MFMA reads a fresh VALU result")
             dst = l.split()[1].rstrip(",")
             lo = int(dst[2:].split(":")[0])
             for v in range(lo, lo + 16):
@@ -426,6 +541,8 @@ def check_hazards(lines):
                     assert idx - last_exp[tok] >= 2, (l, idx - last_exp[tok])
             if op == "v_exp_f32":
                 last_exp[l.split()[1].rstrip(",")] = idx
+            if op.startswith("v_") and not op.startswith(("v_cmp", "v_readlane", "v_readfirstlane", "v_accvgpr_write")):
+                last_valu[l.split()[1].rstrip(",")] = idx
             if op == "v_dot2_f32_bf16":
                 last_dot[l.split()[1].rstrip(",")] = idx
             else:
@@ -439,16 +556,33 @@ def check_hazards(lines):
             last_exp = {k: v - n for k, v in last_exp.items()}
             last_mfma_read = {k: v - n for k, v in last_mfma_read.items()}
             last_dot = {k: v - n for k, v in last_dot.items()}
+            last_valu = {k: v - n for k, v in last_valu.items()}
             last_m0 -= n
 
 
 KOFF, VOFF, SLOTL = 230, 234, 238
+CB = 202                                         # bf16: -m blocks, v[202:217] (qb 0) and v[218:233]
+MT = 245                                         # bf16: mask word read from its AGPR
+MKA, LANEA = 192, 224                            # bf16: mask words a[192 + 16 qb + j]; 8g, tq, bperm at a[224:227]
+
+
+def set_mode(f8):
+    """Register plan of the program: e4m3 keeps the fused scale-and-subtract softmax and its
+    masks in VGPRs; bf16 (NEGM) takes Q pre-scaled and the -m blocks as the first QK
+    accumulator, with the masks and lane constants in AGPRs."""
+    global F8, NEGM, L, KOFF, VOFF, SLOTL
+    F8, NEGM = f8, not f8
+    if f8:
+        L, KOFF, VOFF, SLOTL = 228, 230, 234, 238
+    else:
+        L, KOFF, VOFF, SLOTL = 234, 236, 240, 244
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
 NSLOT = 4                                        # ring slots of K and of V^T tiles
 
 
 BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
-F8 = False                                       # program for the e4m3 cache (set by main)
+F8 = False                                       # program for the e4m3 cache (set by set_mode)
+NEGM = True                                      # S = Q' K^T - m in the MFMA (set by set_mode)
 STAGE = 16384                                    # e4m3 staging slot: K tile (8 KB), then V^T tile (8 KB)
 SK, SV = 202, 203                                # e4m3: this lane's staging read addresses (K, V^T)
 WK, WV = 240, 244                                # e4m3: widened-chunk write addresses (lo, hi per load)
@@ -501,6 +635,34 @@ def widen_block(ph, k=True):
                          f"offset:{slot * KTILE}")
     lines.append("s_waitcnt lgkmcnt(0)")
     return lines
+
+
+def k_setup(par, ahead):
+    """Global base of the loads of K (t + ahead) for the iteration of parity par, as
+    load_setup does it, and besides it ov, the V^T offset of the same tile (its V^T base one
+    iteration later: V^T runs one tile behind K).  Units."""
+    units = load_setup("K", par, ahead)
+    i = units.index(NEXT_GAP)
+    return units[:i + 1] + [[f"s_lshl_b32 %[y], %[kk], {6 if F8 else 7}"],
+                            ["s_mul_i32 %[x], %[x], %[slotb]"],
+                            ["s_add_u32 %[ov], %[x], %[y]"],
+                            [f"s_lshl_b32 %[y], %[kk], {13 if F8 else 14}"],
+                            ["s_add_u32 %[x], %[x], %[y]"],
+                            units[-1]]
+
+
+def v_setup(par):
+    """Global base of the V^T loads of the next iteration of parity par: V^T (t + 2) is the K
+    tile of the previous iteration's k_setup, whose V^T offset is ov."""
+    b = BASE[par][1]
+    return [[f"s_add_u32 s{b}, %[vblo], %[ov]", f"s_addc_u32 s{b + 1}, %[vbhi], 0"]]
+
+
+def cursor_shift():
+    """The walk cursor of tile t+1 is the K cursor of two iterations before (held in vk, vf
+    for one iteration): sk, sf <- vk, vf <- kk, kf, before k_setup advances kk, kf."""
+    return [["s_mov_b32 %[sk], %[vk]"], ["s_mov_b32 %[sf], %[vf]"],
+            ["s_mov_b32 %[vk], %[kk]"], ["s_mov_b32 %[vf], %[kf]"]]
 
 
 def load_setup(kind, par, ahead):
@@ -571,9 +733,16 @@ def loop_program():
     """The whole tile loop: iterations t = 0 .. n-1 (NSLOT per pass, so that ring slots, P
     buffer and set-up parity are fixed in each copy), then the last PV.  m0 is saved and
     restored."""
+    set_mode(F8)
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
-    lines += sum((u for u in walk_setup(0, False) + load_setup("K", 0, 2) + load_setup("V", 0, 1)
-                  if u != NEXT_GAP), [])
+    # V^T base of tile 1 from the K cursor (tile 1), then vk, vf <- kk, kf and K advances to tile 2
+    b = BASE[0][1]
+    v1 = [f"v_readlane_b32 %[x], v{SLOTL}, %[kf]", "s_mul_i32 %[x], %[x], %[slotb]",
+          f"s_lshl_b32 %[y], %[kk], {6 if F8 else 7}", "s_add_u32 %[x], %[x], %[y]",
+          f"s_add_u32 s{b}, %[vblo], %[x]", f"s_addc_u32 s{b + 1}, %[vbhi], 0"]
+    lines += sum((u for u in walk_setup(0, False) if u != NEXT_GAP), []) + v1 + \
+        ["s_mov_b32 %[vk], %[kk]", "s_mov_b32 %[vf], %[kf]"] + \
+        sum((u for u in k_setup(0, 2) if u != NEXT_GAP), [])
     lines += [".Lw64_loop_%=:"]
     for ph in range(NSLOT):
         lines += iteration(ph)
@@ -602,11 +771,11 @@ def emit(name, lines):
 def main():
     out = ["// Generated by gen_attn_w64.py; do not edit.  The tile loop of the 64-row attention",
            "// kernel as one asm program (register plan, blocks and hazard rules in the generator).", ""]
-    global F8
+    set_mode(False)
     out.append(emit("SDV2_W64_LOOP", loop_program()))
-    F8 = True
+    set_mode(True)
     out.append(emit("SDV2_W64_LOOP_FP8", loop_program()))
-    F8 = False
+    set_mode(False)
     sys.stdout.write("\n".join(out))
 
 

@@ -92,6 +92,8 @@ void attn_w64_kernel(const AttnArgs a) {
   const int tq_wave = wrow / a.N;             // lowest frame of the wave's rows
 
   // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb].
+  // bf16 cache: Q scaled by scale * log2(e) and rounded to bf16 again, so the QK MFMA yields
+  // the exponent's argument directly (its accumulator starts at -m).
   i32x32 q0, q1;
   {
     const uint16_t* qb0 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[0] ? row[0] : 0)) * a.H + head) * D + 8 * g;
@@ -102,6 +104,18 @@ void attn_w64_kernel(const AttnArgs a) {
       const uint4 y = valid[1] ? *(const uint4*)(qb1 + 16 * kd) : make_uint4(0, 0, 0, 0);
       q0[4 * kd] = x.x; q0[4 * kd + 1] = x.y; q0[4 * kd + 2] = x.z; q0[4 * kd + 3] = x.w;
       q1[4 * kd] = y.x; q1[4 * kd + 1] = y.y; q1[4 * kd + 2] = y.z; q1[4 * kd + 3] = y.w;
+    }
+    if constexpr (!F8) {
+      const float sl = a.scale_log2;
+      auto scaled = [sl](int w) {
+        const uint32_t u = (uint32_t)w;
+        return (int)pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * sl, bf16_bits_to_f32(u >> 16) * sl);
+      };
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        q0[i] = scaled(q0[i]);
+        q1[i] = scaled(q1[i]);
+      }
     }
   }
 
@@ -243,20 +257,23 @@ void attn_w64_kernel(const AttnArgs a) {
   const int mv = (int)((uint32_t)(uintptr_t)ldsV + wave * LD * 1024);
   const float sl = a.scale_log2;
   unsigned long long trig;
-  int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp;
+  int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp, ov;
+  // Register plan (both programs): O^T a[0:127], Q^T a[128:191], S^T v[0:63], P^T v[64:127],
+  // fragment ring v[128:175], LDS addresses v[176:187], temporaries v[188:199], m v[200:201],
+  // tile sums v[248:255].  The e4m3 program keeps its masks and lane constants in VGPRs; the
+  // bf16 program holds the -m blocks in v[202:233], l in v[234:235], the load offsets and frame
+  // slots in v[236:244], a mask temporary in v245, and its masks and lane constants in AGPRs.
 #define SDV2_W64_OUTPUTS                                                                      \
   "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),                  \
       "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),               \
       "={v[128:159]}"(frg), "={v[160:175]}"(frg2), "+{v[176:183]}"(kaddr),                      \
       "+{v[184:187]}"(vaddr), "={v[188:199]}"(tmp), "={v[200:201]}"(mrun),                      \
-      "={v[248:255]}"(tsum), "={v[206:221]}"(rmask), "={v[222:223]}"(cmask),                    \
-      "={v[228:229]}"(lrun), [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk),        \
+      "={v[248:255]}"(tsum), [kf] "+s"(kf), [kk] "+s"(kk), [vf] "+s"(vf), [vk] "+s"(vk),        \
       [sf] "+s"(sf), [sk] "+s"(sk), [t] "+s"(t), [trig] "=&s"(trig), [x] "=&s"(x),              \
       [y] "=&s"(y), [nvalid] "=&s"(nvalid), [tk] "=&s"(tk), [mflag1] "=&s"(mflag1),             \
-      [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp)
+      [mflag0] "=&s"(mflag0), [m0save] "=&s"(m0save), [stmp] "=&s"(stmp), [ov] "=&s"(ov)
 #define SDV2_W64_INPUTS                                                                       \
-  "{a[128:159]}"(q0), "{a[160:191]}"(q1), "{v[224:227]}"(lanec), "{v[230:233]}"(koffv),        \
-      "{v[234:237]}"(voffv), "{v238}"(slot_lane), [n] "s"(n), [tpf] "s"(tpf),                   \
+  "{a[128:159]}"(q0), "{a[160:191]}"(q1), [n] "s"(n), [tpf] "s"(tpf),                           \
       [nshared] "s"(nshared), [N] "s"(Ntok), [tqw] "s"(tq_wave), [kblo] "s"(kblo),              \
       [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb), [sl] "s"(sl)
 #define SDV2_W64_CLOBBERS "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91"
@@ -275,15 +292,23 @@ void attn_w64_kernel(const AttnArgs a) {
       wv[2 * i + 1] = (int)((uint32_t)(uintptr_t)ldsV + lds_chunk<VRB>(vr8[i], 4 * (vc8 >> 1) + 2 + (vc8 & 1)));
     }
     asm volatile(SDV2_W64_LOOP_FP8
-                 : SDV2_W64_OUTPUTS
-                 : SDV2_W64_INPUTS, [ms] "s"(ms), "{v202}"(sk_addr), "{v203}"(sv_addr), "{v[240:243]}"(wk),
+                 : SDV2_W64_OUTPUTS, "={v[206:221]}"(rmask), "={v[222:223]}"(cmask), "={v[228:229]}"(lrun)
+                 : SDV2_W64_INPUTS, "{v[224:227]}"(lanec), "{v[230:233]}"(koffv), "{v[234:237]}"(voffv),
+                   "{v238}"(slot_lane), [ms] "s"(ms), "{v202}"(sk_addr), "{v203}"(sv_addr), "{v[240:243]}"(wk),
                    "{v[244:247]}"(wv)
                  : SDV2_W64_CLOBBERS);
   } else {
+    i32x32 negm, amask;
+    unsigned long long ninf;
     asm volatile(SDV2_W64_LOOP
-                 : SDV2_W64_OUTPUTS
-                 : SDV2_W64_INPUTS, [mk] "s"(mk), [mv] "s"(mv)
-                 : SDV2_W64_CLOBBERS);
+                 : SDV2_W64_OUTPUTS, "={v[202:233]}"(negm), "={v[234:235]}"(lrun), "={a[192:223]}"(amask),
+                   [ninf] "=&s"(ninf)
+                 : SDV2_W64_INPUTS, "{a[224:227]}"(lanec), "{v[236:239]}"(koffv), "{v[240:243]}"(voffv),
+                   "{v244}"(slot_lane), [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_CLOBBERS, "v245");   // v245: mask word temporary
+    (void)negm;
+    (void)amask;
+    (void)ninf;
   }
 #undef SDV2_W64_OUTPUTS
 #undef SDV2_W64_INPUTS

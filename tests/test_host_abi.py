@@ -206,3 +206,49 @@ def test_generated_attention_asm_is_current():
     csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
     out = subprocess.run([sys.executable, "gen_attn_w64.py"], cwd=csrc, capture_output=True, text=True, check=True)
     assert out.stdout == (csrc / "attn_w64_asm.h").read_text()
+
+
+def _asm_register_set(spec):
+    """Registers named by one constraint or clobber string: v12, a[0:31], s84 ..."""
+    import re
+    m = re.match(r"^([vas])\[(\d+):(\d+)\]$", spec)
+    if m:
+        return {f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    return {spec} if re.match(r"^[vas]\d+$", spec) else set()
+
+
+def test_generated_asm_writes_only_declared_registers():
+    # every register the tile-loop programs write is an output or a clobber of the asm statement
+    # that runs them (an undeclared write corrupts whatever the compiler keeps there)
+    import importlib.util
+    import pathlib
+    import re
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    src = (csrc / "k_attention_w64.hip").read_text()
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_test", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+
+    def macro(name):
+        i = src.index(f"#define {name}")
+        return src[i:src.index("\n#define", i + 1)] if "\n#define" in src[i + 1:] else src[i:]
+
+    shared = macro("SDV2_W64_OUTPUTS") + macro("SDV2_W64_CLOBBERS")
+    for prog_name, f8 in (("SDV2_W64_LOOP_FP8", True), ("SDV2_W64_LOOP\n", False)):
+        i = src.index(f"asm volatile({prog_name}")
+        stmt = src[i:src.index(");", i)]
+        declared = set()
+        for text in (shared, stmt):
+            for c in re.findall(r'"[=+]&?\{([^}]*)\}"', text):
+                declared |= _asm_register_set(c)
+            for c in re.findall(r'"([vas]\d+)"', text):
+                declared |= _asm_register_set(c)
+        gen.F8 = f8
+        written = set()
+        for line in gen.loop_program():
+            t = line.replace(",", " ").split()
+            if not t or t[0].startswith(".") or t[0] in ("s_waitcnt", "s_nop", "s_barrier", "s_branch") or \
+                    t[0].startswith(("s_cbranch", "s_cmp", "global_load", "ds_write", "v_cmp_")):
+                continue
+            written |= _asm_register_set(t[1])
+        assert not written - declared, (prog_name.strip(), sorted(written - declared))
