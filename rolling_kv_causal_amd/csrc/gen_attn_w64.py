@@ -95,6 +95,16 @@ def s_elem(kb, qb, v):
     return f"v{(kb * 2 + qb) * 16 + v}"
 
 
+def rowsum_mfma(pp, qb, ks):
+    """bf16: l += row sums of P^T[qb][ks] (16 keys) on the matrix core.  Read as the B operand
+    of a 16x16x32 MFMA, lane (g, r) of the P^T quad is column r mod 16 and k-block 2g + r / 16;
+    the selector (ones at lanes 0 and 32 for output row 0, 17 and 49 for row 1) sums row r < 16
+    into output row 0 and row r >= 16 into output row 1 of column r mod 16: lane j < 16 holds
+    l(row j) in its first and l(row j + 16) in its second accumulator register."""
+    b = TS + 4 * qb
+    return f"v_mfma_f32_16x16x32_bf16 v[{b}:{b + 3}], a[{SEL}:{SEL + 3}], {p_reg(pp, qb, ks)}, v[{b}:{b + 3}]"
+
+
 def cb_reg(qb):
     b = CB + 16 * qb
     return f"v[{b}:{b + 15}]"
@@ -204,8 +214,15 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                                 ops.append(f"v_and_b32 {w}, {w}, v{RMASK + j}")
                                 ops.append(f"v_and_b32 {w}, {w}, v{CMASK + qb}")
                         for wi, w in enumerate(words):
+                            if NEGM:
+                                break
                             ops.append(f"v_lshlrev_b32 {t[2 * wi]}, 16, {w}")
                             ops.append(f"v_and_b32 {t[2 * wi + 1]}, 0xffff0000, {w}")
+                    if NEGM:
+                        if not shifted:        # the lazy test of the tile: OR of its P words
+                            ops.append(f"v_or_b32 v{ACC}, {words[0]}, {words[1]}" if gi == 1 else
+                                       f"v_or3_b32 v{ACC}, v{ACC}, {words[0]}, {words[1]}")
+                        continue
                     for j in range(4):
                         if kb == 0 and half == 0 and w0 == 0:      # first group of the row block
                             ops.append(f"v_mov_b32 {sums(qb, j)}, {t[j]}")
@@ -346,6 +363,24 @@ def tile_block(ph, masked):
     lines = mask_setup() if masked else []
     extra = [(0, v_setup(1 - par)), (0, cursor_shift()), (0, k_setup(1 - par, 3)),
              (0, walk_setup(1 - par, False))]
+    valu = softmax_ops(pc, masked)
+    if NEGM:
+        # l += row sums of P(t-1) (buffer pp, complete), one MFMA after every other group
+        sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)]
+        out, gcount = [], 0
+        for op in valu:
+            out.append(op)
+            if op.startswith(("v_or_b32", "v_or3_b32")) and f"v{ACC}" in op:
+                gcount += 1
+                if gcount % 2 == 1 and sums:
+                    out.append(sums.pop(0))
+        valu = out + sums
+        lines += stream(k_reads() + v_reads(), pp, ph, valu, tile_loads(ph), SM_FROM, extra)
+        # lazy test: some P word >= 2 (a score 9 above m, or not finite), or a row without m
+        return lines + [f"v_and_b32 v{TMP}, 0x40004000, v{ACC}",
+                        f"v_cmp_ne_u32 vcc, 0, v{TMP}",
+                        "s_mov_b64 %[trig], vcc",
+                        "s_or_b64 %[trig], %[trig], %[ninf]"]
     lines += stream(k_reads() + v_reads(), pp, ph, softmax_ops(pc, masked), tile_loads(ph), SM_FROM, extra)
     lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
               f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
@@ -357,9 +392,6 @@ def tile_block(ph, masked):
               "s_mov_b64 %[trig], vcc",
               f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP + 1}",
               "s_or_b64 %[trig], %[trig], vcc"]
-    if NEGM:
-        # a row that has no maximum yet (m = -inf) scores against m = 0: rescale it
-        lines.append("s_or_b64 %[trig], %[trig], %[ninf]")
     return lines
 
 
@@ -393,6 +425,7 @@ def rare_block_negm(pc, masked):
                   f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + qb}",
                   f"v_cndmask_b32_e64 {mc}, v{M + qb}, 0, vcc",       # mc: m, 0 while m = -inf
                   f"v_add_f32 {t0}, {mx}, {mc}",
+                  f"v_add_f32 {t0}, {hex(0x41000000)}, {t0}",                  # + BIAS (8.0)
                   f"v_max_f32 {mn}, v{M + qb}, {t0}",                 # m'
                   f"v_sub_f32 {t0}, v{M + qb}, {mn}",
                   f"v_exp_f32 {al}, {t0}",
@@ -401,7 +434,12 @@ def rare_block_negm(pc, masked):
                   f"v_cndmask_b32_e64 {mcn}, {mn}, 0, vcc",           # mc'
                   f"v_sub_f32 {dd}, {mcn}, {mc}",
                   f"v_mov_b32 v{M + qb}, {mn}",
-                  f"v_mul_f32 v{L + qb}, v{L + qb}, {al}"]
+                  # l of row j (< 16) sits in lane j, register 0; of row j + 16 in lane j, register 1
+                  f"v_mul_f32 v{TS + 4 * qb}, v{TS + 4 * qb}, {al}",
+                  f"v_xor_b32 {t1}, 0xc0, {bp}",                       # (lane ^ 16) * 4
+                  f"ds_bpermute_b32 {y}, {t1}, {al}",
+                  "s_waitcnt lgkmcnt(0)",
+                  f"v_mul_f32 v{TS + 4 * qb + 1}, v{TS + 4 * qb + 1}, {y}"]
         vals = [(db, v) for db in range(4) for v in range(16)]
         for k in range(0, 64, 4):
             grp = vals[k:k + 4]
@@ -409,10 +447,8 @@ def rare_block_negm(pc, masked):
             lines += [f"v_accvgpr_read_b32 {tmps[i]}, {o_elem(db, qb, v)}" for i, (db, v) in enumerate(grp)]
             lines += [f"v_mul_f32 {tmps[i]}, {tmps[i]}, {al}" for i in range(4)]
             lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
-        ss = [f"v{140 + i}" for i in range(4)]
-        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: dd, sums=lambda _q, i: ss[i])
-        lines += [f"v_add_f32 v{L + qb}, v{L + qb}, {x}" for x in ss]
-        lines.append(f"v_mul_f32 {t0}, -1.0, {mcn}")
+        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: dd)
+        lines.append(f"v_sub_f32 {t0}, {hex(0xc1000000)}, {mcn}")                  # -(mc' + BIAS)
         lines += [f"v_mov_b32 v{CB + 16 * qb + i}, {t0}" for i in range(16)]
     lines += [f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M}", "s_mov_b64 %[ninf], vcc",
               f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + 1}", "s_or_b64 %[ninf], %[ninf], vcc"]
@@ -473,8 +509,9 @@ def init_block():
     lines += [f"v_mov_b32 v{i}, 0" for i in range(128)]
     lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
     if NEGM:
-        # mc = 0 while m = -inf: the -m blocks start at zero and every row is flagged
-        lines += [f"v_mov_b32 v{i}, 0" for i in list(range(CB, CB + 32)) + list(range(TS, TS + 8)) + [L, L + 1]]
+        # mc = 0 while m = -inf: the -m blocks start at -BIAS and every row is flagged
+        lines += [f"v_mov_b32 v{i}, {hex(0xc1000000)}" for i in range(CB, CB + 32)]
+        lines += [f"v_mov_b32 v{i}, 0" for i in range(TS, TS + 8)]
         lines.append("s_mov_b64 %[ninf], -1")
     else:
         lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
@@ -483,7 +520,9 @@ def init_block():
 
 def pv_only_block(ph):
     """The last PV, as the PV of an iteration of phase ph would run it."""
-    return stream(v_reads(), 1 - ph % 2, ph, []) + ["s_nop 11"]
+    pp = 1 - ph % 2
+    sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)] if NEGM else []
+    return stream(v_reads(), pp, ph, sums) + ["s_nop 11"]
 
 
 def check_hazards(lines):
@@ -564,6 +603,9 @@ KOFF, VOFF, SLOTL = 230, 234, 238
 CB = 202                                         # bf16: -m blocks, v[202:217] (qb 0) and v[218:233]
 MT = 245                                         # bf16: mask word read from its AGPR
 MKA, LANEA = 192, 224                            # bf16: mask words a[192 + 16 qb + j]; 8g, tq, bperm at a[224:227]
+SEL = 228                                        # bf16: row-sum selector a[228:231] (A operand)
+ACC = 246                                        # bf16: OR of the tile's P words (lazy test)
+BIAS = 8                                         # bf16: P = 2^(s * scale_log2 - m - BIAS)
 
 
 def set_mode(f8):
@@ -715,7 +757,7 @@ def iteration(ph):
         tile_block(ph, False) + \
         [f".Lw64_td{tag}_%=:",
          "s_cmp_eq_u64 %[trig], 0", f"s_cbranch_scc0 .Lw64_r{tag}_%=",
-         f"v_add_f32 v{L}, v{L}, v{TMP}", f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}",
+         *([] if NEGM else [f"v_add_f32 v{L}, v{L}, v{TMP}", f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}"]),
          f".Lw64_nr{tag}_%=:",
          "s_add_u32 %[t], %[t], 1"]
 

@@ -261,8 +261,9 @@ void attn_w64_kernel(const AttnArgs a) {
   // Register plan (both programs): O^T a[0:127], Q^T a[128:191], S^T v[0:63], P^T v[64:127],
   // fragment ring v[128:175], LDS addresses v[176:187], temporaries v[188:199], m v[200:201],
   // tile sums v[248:255].  The e4m3 program keeps its masks and lane constants in VGPRs; the
-  // bf16 program holds the -m blocks in v[202:233], l in v[234:235], the load offsets and frame
-  // slots in v[236:244], a mask temporary in v245, and its masks and lane constants in AGPRs.
+  // bf16 program holds the -m blocks in v[202:233], the load offsets and frame slots in
+  // v[236:244], a mask temporary in v245, the OR of a tile's P words in v246, its l accumulators
+  // (row sums on the matrix core) in v[248:255], and masks and lane constants in AGPRs.
 #define SDV2_W64_OUTPUTS                                                                      \
   "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),                  \
       "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),               \
@@ -300,15 +301,26 @@ void attn_w64_kernel(const AttnArgs a) {
   } else {
     i32x32 negm, amask;
     unsigned long long ninf;
+    // row-sum selector: bf16 ones at lanes 0 and 32 (output row 0) and 17 and 49 (row 1)
+    i32x4 sel;
+    const int one2 = (lane == 0 || lane == 17 || lane == 32 || lane == 49) ? 0x3F803F80 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sel[i] = one2;
     asm volatile(SDV2_W64_LOOP
-                 : SDV2_W64_OUTPUTS, "={v[202:233]}"(negm), "={v[234:235]}"(lrun), "={a[192:223]}"(amask),
-                   [ninf] "=&s"(ninf)
-                 : SDV2_W64_INPUTS, "{a[224:227]}"(lanec), "{v[236:239]}"(koffv), "{v[240:243]}"(voffv),
-                   "{v244}"(slot_lane), [mk] "s"(mk), [mv] "s"(mv)
-                 : SDV2_W64_CLOBBERS, "v245");   // v245: mask word temporary
+                 : SDV2_W64_OUTPUTS, "={v[202:233]}"(negm), "={a[192:223]}"(amask), [ninf] "=&s"(ninf)
+                 : SDV2_W64_INPUTS, "{a[224:227]}"(lanec), "{a[228:231]}"(sel), "{v[236:239]}"(koffv),
+                   "{v[240:243]}"(voffv), "{v244}"(slot_lane), [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_CLOBBERS, "v245", "v246");   // mask word temporary, OR of the P words
     (void)negm;
     (void)amask;
     (void)ninf;
+    // l of row j < 16 sits in lane j, register 4 qb; of row j + 16 in lane j, register 4 qb + 1
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float x0 = __shfl(__int_as_float(tsum[4 * qb]), r & 15);
+      const float x1 = __shfl(__int_as_float(tsum[4 * qb + 1]), r & 15);
+      lrun[qb] = r < 16 ? x0 : x1;
+    }
   }
 #undef SDV2_W64_OUTPUTS
 #undef SDV2_W64_INPUTS
@@ -329,7 +341,7 @@ void attn_w64_kernel(const AttnArgs a) {
   // O^T[d = 32 db + 8 (v / 4) + 4 g + v % 4][row r of block qb].
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    const float l_tot = F8 ? lrun[qb] + __shfl_xor(lrun[qb], 32) : lrun[qb];
     if (!valid[qb]) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     auto ov = [&](int db, int i) { return db == 0 ? o0[i] : db == 1 ? o1[i] : db == 2 ? o2[i] : o3[i]; };
