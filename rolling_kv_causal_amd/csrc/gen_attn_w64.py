@@ -395,6 +395,9 @@ def tile_block(ph, masked):
     return lines
 
 
+RARE_ID = [0]                                    # unique labels of the rare blocks
+
+
 def rare_block_negm(pc, masked):
     """bf16 rescale of the tile: S = s * scale_log2 - mc, mc = m if finite, else 0.  New row
     maximum m' = max(m, max over valid keys of S + mc); O, l scaled by 2^(m - m'); the tile's
@@ -424,6 +427,7 @@ def rare_block_negm(pc, masked):
                   f"v_max_f32 {mx}, {mx}, {y}",
                   f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + qb}",
                   f"v_cndmask_b32_e64 {mc}, v{M + qb}, 0, vcc",       # mc: m, 0 while m = -inf
+                  "s_cmp_eq_u64 vcc, exec",                            # no row has a maximum yet:
                   f"v_add_f32 {t0}, {mx}, {mc}",
                   f"v_add_f32 {t0}, {hex(0x41000000)}, {t0}",                  # + BIAS (8.0)
                   f"v_max_f32 {mn}, v{M + qb}, {t0}",                 # m'
@@ -434,6 +438,7 @@ def rare_block_negm(pc, masked):
                   f"v_cndmask_b32_e64 {mcn}, {mn}, 0, vcc",           # mc'
                   f"v_sub_f32 {dd}, {mcn}, {mc}",
                   f"v_mov_b32 v{M + qb}, {mn}",
+                  f"s_cbranch_scc1 .Lw64_ns{RARE_ID[0]}_%=",         # O and l are 0: no scaling
                   # l of row j (< 16) sits in lane j, register 0; of row j + 16 in lane j, register 1
                   f"v_mul_f32 v{TS + 4 * qb}, v{TS + 4 * qb}, {al}",
                   f"v_xor_b32 {t1}, 0xc0, {bp}",                       # (lane ^ 16) * 4
@@ -447,6 +452,8 @@ def rare_block_negm(pc, masked):
             lines += [f"v_accvgpr_read_b32 {tmps[i]}, {o_elem(db, qb, v)}" for i, (db, v) in enumerate(grp)]
             lines += [f"v_mul_f32 {tmps[i]}, {tmps[i]}, {al}" for i in range(4)]
             lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
+        lines.append(f".Lw64_ns{RARE_ID[0]}_%=:")
+        RARE_ID[0] += 1
         lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: dd)
         lines.append(f"v_sub_f32 {t0}, {hex(0xc1000000)}, {mcn}")                  # -(mc' + BIAS)
         lines += [f"v_mov_b32 v{CB + 16 * qb + i}, {t0}" for i in range(16)]
@@ -504,14 +511,22 @@ def rare_block(pc, masked):
 
 
 def init_block():
-    """O = 0, S = 0, P = 0 (P(-1) = 0 is read by the first PV), m = -inf, sums, masks, l = 0."""
-    lines = [f"v_accvgpr_write_b32 a{i}, 0" for i in range(128)]
-    lines += [f"v_mov_b32 v{i}, 0" for i in range(128)]
+    """O = 0 and P(-1) = 0 (read by the first PV), written sixteen registers at a time by MFMAs
+    of zero operands; m = -inf; bf16: the -m blocks -BIAS (a product of ones and -1/2 summed
+    over 16), the row-sum accumulators 0, every row flagged; e4m3: sums and l = 0."""
+    zero, ones, half = "v[128:131]", "v[132:135]", "v[136:139]"
+    lines = [f"v_mov_b32 v{128 + i}, 0" for i in range(4)]
+    lines += [f"v_mov_b32 v{132 + i}, 0x3f803f80" for i in range(4)]
+    lines += [f"v_mov_b32 v{136 + i}, 0xbf00bf00" for i in range(4)]
+    lines += [f"v_mfma_f32_32x32x16_bf16 a[{16 * i}:{16 * i + 15}], {zero}, {zero}, 0" for i in range(8)]
+    b = p_base(1)
+    lines += [f"v_mfma_f32_32x32x16_bf16 v[{b + 16 * i}:{b + 16 * i + 15}], {zero}, {zero}, 0" for i in range(2)]
     lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
     if NEGM:
         # mc = 0 while m = -inf: the -m blocks start at -BIAS and every row is flagged
-        lines += [f"v_mov_b32 v{i}, {hex(0xc1000000)}" for i in range(CB, CB + 32)]
-        lines += [f"v_mov_b32 v{i}, 0" for i in range(TS, TS + 8)]
+        assert BIAS == 8
+        lines += [f"v_mfma_f32_32x32x16_bf16 {cb_reg(qb)}, {ones}, {half}, 0" for qb in range(2)]
+        lines += [f"v_mfma_f32_16x16x32_bf16 v[{TS + 4 * qb}:{TS + 4 * qb + 3}], {zero}, {zero}, 0" for qb in range(2)]
         lines.append("s_mov_b64 %[ninf], -1")
     else:
         lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
@@ -776,6 +791,7 @@ def loop_program():
     buffer and set-up parity are fixed in each copy), then the last PV.  m0 is saved and
     restored."""
     set_mode(F8)
+    RARE_ID[0] = 0
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
     # V^T base of tile 1 from the K cursor (tile 1), then vk, vf <- kk, kf and K advances to tile 2
     b = BASE[0][1]
