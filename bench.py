@@ -315,7 +315,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "sdv2_chunk_attention (%s + combine_kernel)"
-                               % ("attn_bf16_kernel<128, e4m3 cache>" if c.kv_fp8 else
+                               % ("attn_w64_kernel<e4m3 cache>" if c.kv_fp8 and c.head_dim == 128 else
                                   "attn_w64_kernel" if c.dtype == "bf16" and c.head_dim == 128 else
                                   "attn_bf16_kernel"),
                      "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3)},

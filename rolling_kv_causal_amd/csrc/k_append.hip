@@ -50,7 +50,9 @@ __device__ __forceinline__ void rotate8_f32(const uint4& w, const float2* cs, fl
 }
 
 // KV: cache element type (kKvF32, kKvBF16, kKvFP8); q, k, v are fp32 for kKvF32, else bf16.
-template <int KV, int D>
+// TILE: tokens per workgroup, 64 (a key tile) or 32 (half of one, for grids that would leave
+// CUs idle; not for e4m3, whose V^T byte order spans a whole key tile).
+template <int KV, int D, int TILE>
 __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   constexpr bool BF16 = KV != kKvF32;
   using T = typename std::conditional<BF16, uint16_t, float>::type;   // activations
@@ -58,12 +60,12 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   constexpr int VEC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int CH = D / VEC;                // chunks per row
   constexpr int ROWS = 256 / CH;             // token rows per pass
-  constexpr int TILE = kTileKeys;
+  static_assert(TILE == kTileKeys || (TILE == kTileKeys / 2 && KV != kKvFP8), "tile");
   constexpr int VSTR = D + (BF16 ? 2 : 1);   // LDS row stride (elements): breaks bank aliasing
   __shared__ T vs[TILE * VSTR];
   __shared__ float2 tcs[kMaxTPairs];
 
-  const int tiles = (a.N + TILE - 1) / TILE;
+  const int tiles = (a.N + kTileKeys - 1) / kTileKeys * (kTileKeys / TILE);   // padding included
   const int t = blockIdx.x / tiles;                // frame of the chunk
   const int n0 = (blockIdx.x - t * tiles) * TILE, head = blockIdx.y, b = blockIdx.z;
   const int fr = b * a.T + t;                      // frame index within the call
@@ -149,10 +151,21 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
 }
 
 hipError_t launch_rope_append(const AppendArgs& a, int head_dim, int kv, hipStream_t s) {
-  const dim3 grid(a.T * ((a.N + kTileKeys - 1) / kTileKeys), a.H, a.nbatch);
-#define SDV2_APPEND(KV_, D_) hipLaunchKernelGGL((rope_append_kernel<KV_, D_>), grid, dim3(256), 0, s, a)
+  // Every workgroup loads its whole tile before storing, so one round of workgroups runs as a
+  // load phase then a store phase: a grid under two rounds of the 256 CUs takes half tiles.
+  const int tiles64 = (a.N + kTileKeys - 1) / kTileKeys;
+  const bool half = kv != kKvFP8 && (int64_t)a.T * tiles64 * a.H * a.nbatch < 2 * 256;
+  const dim3 grid(a.T * tiles64 * (half ? 2 : 1), a.H, a.nbatch);
+#define SDV2_APPEND(KV_, D_)                                                                          \
+  do {                                                                                               \
+    if (half) hipLaunchKernelGGL((rope_append_kernel<KV_, D_, kTileKeys / 2>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((rope_append_kernel<KV_, D_, kTileKeys>), grid, dim3(256), 0, s, a);     \
+  } while (0)
   if (kv == kKvFP8) {
-    if (head_dim == 128) SDV2_APPEND(kKvFP8, 128); else SDV2_APPEND(kKvFP8, 64);
+    if (head_dim == 128)
+      hipLaunchKernelGGL((rope_append_kernel<kKvFP8, 128, kTileKeys>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((rope_append_kernel<kKvFP8, 64, kTileKeys>), grid, dim3(256), 0, s, a);
   } else if (kv == kKvBF16) {
     if (head_dim == 128) SDV2_APPEND(kKvBF16, 128); else SDV2_APPEND(kKvBF16, 64);
   } else {
