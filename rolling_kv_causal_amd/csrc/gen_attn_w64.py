@@ -8,8 +8,11 @@ issues 64 MFMAs 32x32x16 bf16 fed by 32 LDS fragment reads (each read feeds both
   QK:  S^T[kb][qb] = K[kb] Q^T[qb]      16 K reads (kb-major, 8 k steps each)
   PV:  O^T[db][qb] += V^T[db] P^T[qb]   16 V^T reads (key step ks-major, d block db)
 and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete after the
-16th), the softmax of the tile's S: exp2(S*scale_log2 - m) rounded to bf16 P^T words for the
-next tile's PV, with per-lane tile sums.
+16th), the softmax of the tile's S into bf16 P^T words for the next tile's PV.  bf16 program:
+Q arrives scaled by scale_log2 and the first QK MFMA of a chain accumulates onto the -(m + BIAS)
+block, so S is already the exponent; the P words are ORed for the lazy test, and eight 16x16x32
+MFMAs add the previous tile's P row sums into l.  e4m3 program: exp2(S*scale_log2 - m) with
+fp32 per-lane tile sums.
 
 Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
 moves them; the loop is generated once per phase, so the ring slots of K(t) (ph) and V^T(t-1)
@@ -22,8 +25,9 @@ moves them; the loop is generated once per phase, so the ring slots of K(t) (ph)
     part, the scalar set-up of iteration t+1 (load cursors and global bases, the walk cursor
     and mflag of tile t+1); then the lazy test (trig != 0: some lane's tile sum left [0, 256]
     or is not finite)
-  trig == 0: l += tile sums; otherwise (out of line) the rescale: masked row max, m, alpha,
-    O and l scaled, P of the tile recomputed into buffer 1-pp, l += its sums
+  trig == 0: (e4m3) l += tile sums; otherwise (out of line) the rescale: masked row max, m,
+    alpha, O and l scaled, P of the tile recomputed into buffer 1-pp (e4m3: l += its sums;
+    bf16: the -m blocks rewritten)
 After the loop the last PV (e4m3: after widening V^T(n-1)).  Set-up values alternate between
 two register sets by iteration parity, so the loads of iteration t read one set while the
 stream writes the other.  The masked variant ANDs every P word with a ragged-tile mask (keys
@@ -39,11 +43,17 @@ Register plan (per lane):
   v[176:183]  K fragment LDS addresses per k step kd;  v[184:187] V^T addresses per key step
   v[188:199]  temporaries
   v[200:201]  m per qb (running max, log2 units)
+  v[248:255]  e4m3: tile sums, four per qb; bf16: l accumulators (16x16 MFMA layout), four per qb
+ e4m3 program:
   v[206:221]  ragged masks of the 16 P words of a row block;  v[222:223] causal mask per qb
   v[224] 8g;  v[225:226] frame of the lane's row per qb;  v[227] (lane ^ 32) * 4
   v[228:229]  l per qb;  v[230:237] K and V^T lane offsets of the tile loads;  v238 frame slots
-  v[202:203], v[240:247]  e4m3: staging read and widened-chunk write addresses
-  v[248:255]  tile sums, four per qb
+  v[202:203], v[240:247]  staging read and widened-chunk write addresses
+ bf16 program:
+  v[202:233]  -(m + BIAS) blocks per qb (first QK accumulator);  v[236:243] load offsets;
+  v244 frame slots;  v245 mask temporary;  v246 OR of the tile's P words
+  a[192:223]  mask words per (qb, word);  a[224:227] 8g, frame per qb, (lane ^ 32) * 4;
+  a[228:231]  row-sum selector
   s[84:91]    global bases of the K and V^T tile loads, two sets by iteration parity
 
 Hazards kept by construction (gfx950, counted in issued instructions): an MFMA result is read
