@@ -457,20 +457,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
   const int d0 = (threadIdx.x % TPR) * 8;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[s * rows + row].x);
-  float W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float2 ml = a.part_ml[s * rows + row];
-    const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - M);
-    const uint4 p = *(const uint4*)(a.part_o + (s * rows + row) * D + d0);
-    const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-    W += wgt;
+  // Splits in groups of eight: every load of a group is issued before any arithmetic, so the
+  // kernel pays one memory round trip per group (one in all for up to eight splits); a later
+  // group with a larger maximum rescales what the earlier ones summed.
+  constexpr int G = 8;
+  float M = -INFINITY, W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < a.nsplit; s0 += G) {
+    float2 ml[G];
+    uint4 p[G];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wgt, __uint_as_float(pw[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wgt, __uint_as_float(pw[i] & 0xffff0000u), acc[2 * i + 1]);
+    for (int j = 0; j < G; ++j) {
+      if (s0 + j < a.nsplit) {
+        ml[j] = a.part_ml[(s0 + j) * rows + row];
+        p[j] = *(const uint4*)(a.part_o + ((s0 + j) * rows + row) * D + d0);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (s0 + j < a.nsplit) Mn = fmaxf(Mn, ml[j].x);
+    if (M != Mn && M != -INFINITY) {
+      const float r = __builtin_amdgcn_exp2f(M - Mn);
+      W *= r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= r;
+    }
+    M = Mn;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (s0 + j < a.nsplit) {
+        const float wgt = ml[j].y * __builtin_amdgcn_exp2f(ml[j].x - M);
+        const uint32_t pw[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+        W += wgt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wgt, __uint_as_float(pw[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wgt, __uint_as_float(pw[i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+      }
     }
   }
   const float inv = 1.f / W;
