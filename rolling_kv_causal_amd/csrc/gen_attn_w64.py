@@ -76,7 +76,7 @@ TMP, M, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 206, 222, 224, 225, 227, 228
 TS = 248                                         # tile sums, four per row block
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
-WAIT_EVERY = 2                                   # one LDS wait per this many fragment reads
+WAIT_EVERY = 4                                   # one LDS wait per this many fragment reads
 READ_START = 2                                   # fragment reads issued before the first MFMA
 NEXT_GAP = ["<next gap>"]                        # unit marker: continue the chunk after the next MFMA
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
