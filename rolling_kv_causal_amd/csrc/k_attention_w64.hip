@@ -338,39 +338,45 @@ void attn_w64_kernel(const AttnArgs a) {
   (void)trig;
 
   // Epilogue.  Lane (g, r), element v of o[db][qb] (o_db[16 qb + v]) holds
-  // O^T[d = 32 db + 8 (v / 4) + 4 g + v % 4][row r of block qb].
+  // O^T[d = 32 db + 8 (v / 4) + 4 g + v % 4][row r of block qb].  The wave writes its 64 rows of
+  // O / l (bf16) into LDS row by row, then stores them four whole rows per instruction: stored
+  // straight from the accumulator layout, each instruction would write 8 bytes into each of
+  // 32 rows, and the L2's write transactions took about 5 us per workgroup.
+  constexpr int EP_STRIDE = D * 2 + 16;                         // bytes per LDS row (padded)
+  __syncthreads();                                              // every wave is done with the rings
+  char* const ep = lds + wave * 64 * EP_STRIDE;
+  auto oval = [&](int db, int i) { return db == 0 ? o0[i] : db == 1 ? o1[i] : db == 2 ? o2[i] : o3[i]; };
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = F8 ? lrun[qb] + __shfl_xor(lrun[qb], 32) : lrun[qb];
-    if (!valid[qb]) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    auto ov = [&](int db, int i) { return db == 0 ? o0[i] : db == 1 ? o1[i] : db == 2 ? o2[i] : o3[i]; };
-    if (a.nsplit == 1) {
-      uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * R + row[qb]) * a.H + head) * D + 4 * g;
+    char* const erow = ep + (32 * qb + r) * EP_STRIDE + 8 * g;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int i0 = 16 * qb + 4 * a4;
-          uint2 w2;
-          w2.x = pack_bf16x2(ov(db, i0) * inv, ov(db, i0 + 1) * inv);
-          w2.y = pack_bf16x2(ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
-          *(uint2*)(op + 32 * db + 8 * a4) = w2;
-        }
-    } else {
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int i0 = 16 * qb + 4 * a4;
+        uint2 w2;
+        w2.x = pack_bf16x2(oval(db, i0) * inv, oval(db, i0 + 1) * inv);
+        w2.y = pack_bf16x2(oval(db, i0 + 2) * inv, oval(db, i0 + 3) * inv);
+        *(uint2*)(erow + 2 * (32 * db + 8 * a4)) = w2;
+      }
+    if (a.nsplit > 1 && g == 0 && valid[qb]) {
       const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + row[qb];
-      uint16_t* po = a.part_o + prow * D + 4 * g;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int i0 = 16 * qb + 4 * a4;
-          uint2 w2;
-          w2.x = pack_bf16x2(ov(db, i0) * inv, ov(db, i0 + 1) * inv);
-          w2.y = pack_bf16x2(ov(db, i0 + 2) * inv, ov(db, i0 + 3) * inv);
-          *(uint2*)(po + 32 * db + 8 * a4) = w2;
-        }
-      if (g == 0) a.part_ml[prow] = make_float2(mrun[qb], l_tot);
+      a.part_ml[prow] = make_float2(mrun[qb], l_tot);
+    }
+  }
+  // lane L stores 16 bytes (8 values of d) of row 4 i + L / 16 of the wave
+  const int chunk = lane & 15;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int rl = 4 * i + (lane >> 4), grow = wrow + rl;
+    const uint4 w4 = *(const uint4*)(ep + rl * EP_STRIDE + 16 * chunk);
+    if (grow < R) {
+      uint16_t* dst = a.nsplit == 1
+          ? (uint16_t*)a.out + ((int64_t)(elem * R + grow) * a.H + head) * D
+          : a.part_o + ((((int64_t)split * a.nbatch + elem) * a.H + head) * R + grow) * D;
+      *(uint4*)(dst + 8 * chunk) = w4;
     }
   }
 }
