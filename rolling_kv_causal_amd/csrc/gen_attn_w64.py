@@ -638,11 +638,8 @@ def set_mode(f8):
     masks in VGPRs; bf16 (NEGM) takes Q pre-scaled and the -m blocks as the first QK
     accumulator, with the masks and lane constants in AGPRs."""
     global F8, NEGM, L, KOFF, VOFF, SLOTL
-    F8, NEGM = f8, not f8
-    if f8:
-        L, KOFF, VOFF, SLOTL = 228, 230, 234, 238
-    else:
-        L, KOFF, VOFF, SLOTL = 234, 236, 240, 244
+    F8, NEGM = f8, True
+    L, KOFF, VOFF, SLOTL = 234, 236, 240, 244
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
 NSLOT = 4                                        # ring slots of K and of V^T tiles
 
@@ -651,8 +648,8 @@ BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the 
 F8 = False                                       # program for the e4m3 cache (set by set_mode)
 NEGM = True                                      # S = Q' K^T - m in the MFMA (set by set_mode)
 STAGE = 16384                                    # e4m3 staging slot: K tile (8 KB), then V^T tile (8 KB)
-SK, SV = 202, 203                                # e4m3: this lane's staging read addresses (K, V^T)
-WK, WV = 240, 244                                # e4m3: widened-chunk write addresses (lo, hi per load)
+SK, SV = 234, 235                                # e4m3: this lane's staging read addresses (K, V^T)
+WKA, WVA = 232, 236                              # e4m3: widened-chunk write addresses (AGPRs; lo, hi per load)
 
 
 def tile_loads(ph):
@@ -682,13 +679,20 @@ def widen_block(ph, k=True):
     slot ph mod 2, loaded two iterations ago) widened to bf16 into ring slots ph and ph - 1.
     A staged 16-byte chunk c = 2p + h of a row holds, in the cache's byte order, elements
     32p + 8h + [0, 8) and 32p + 16 + 8h + [0, 8): the bf16 chunks 4p + h (lo) and 4p + 2 + h
-    (hi), whose addresses are in v[240:247]."""
+    (hi), whose LDS addresses wait in a[232:239]."""
     stage = (ph % 2) * STAGE
     parts = ([("K", i) for i in range(2)] if k else []) + [("V", i) for i in range(2)]
     lines = []
     for j, (kind, i) in enumerate(parts):
         addr, off = (SK, stage + i * 1024) if kind == "K" else (SV, stage + i * 1024)
         lines.append(f"ds_read_b128 v[{128 + 4 * j}:{131 + 4 * j}], v{addr} offset:{off}")
+    # the write addresses wait in AGPRs: copy this block's into the free temporaries
+    waddr = {}
+    for kind, i in parts:
+        for half in range(2):
+            src = (WKA if kind == "K" else WVA) + 2 * i + half
+            waddr[(kind, i, half)] = f"v{TMP + len(waddr)}"
+            lines.append(f"v_accvgpr_read_b32 {waddr[(kind, i, half)]}, a{src}")
     lines.append("s_waitcnt lgkmcnt(0)")
     for j in range(len(parts)):
         for dw in range(4):
@@ -696,9 +700,9 @@ def widen_block(ph, k=True):
                 o = f"v{144 + 8 * j + 2 * dw + sel}"
                 lines.append(f"v_cvt_scalef32_pk_bf16_fp8 {o}, v{128 + 4 * j + dw}, 1.0" + (" op_sel:[1,0,0]" if sel else ""))
     for j, (kind, i) in enumerate(parts):
-        wbase, slot = (WK, ph % NSLOT) if kind == "K" else (WV, (ph - 1) % NSLOT)
+        slot = ph % NSLOT if kind == "K" else (ph - 1) % NSLOT
         for half in range(2):
-            lines.append(f"ds_write_b128 v{wbase + 2 * i + half}, v[{144 + 8 * j + 4 * half}:{147 + 8 * j + 4 * half}] "
+            lines.append(f"ds_write_b128 {waddr[(kind, i, half)]}, v[{144 + 8 * j + 4 * half}:{147 + 8 * j + 4 * half}] "
                          f"offset:{slot * KTILE}")
     lines.append("s_waitcnt lgkmcnt(0)")
     return lines

@@ -92,8 +92,8 @@ void attn_w64_kernel(const AttnArgs a) {
   const int tq_wave = wrow / a.N;             // lowest frame of the wave's rows
 
   // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb].
-  // bf16 cache: Q scaled by scale * log2(e) and rounded to bf16 again, so the QK MFMA yields
-  // the exponent's argument directly (its accumulator starts at -m).
+  // Q is scaled by scale * log2(e) and rounded to bf16 again, so the QK MFMA yields the
+  // exponent's argument directly (its accumulator starts at -m).
   i32x32 q0, q1;
   {
     const uint16_t* qb0 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[0] ? row[0] : 0)) * a.H + head) * D + 8 * g;
@@ -105,7 +105,7 @@ void attn_w64_kernel(const AttnArgs a) {
       q0[4 * kd] = x.x; q0[4 * kd + 1] = x.y; q0[4 * kd + 2] = x.z; q0[4 * kd + 3] = x.w;
       q1[4 * kd] = y.x; q1[4 * kd + 1] = y.y; q1[4 * kd + 2] = y.z; q1[4 * kd + 3] = y.w;
     }
-    if constexpr (!F8) {
+    {
       const float sl = a.scale_log2;
       auto scaled = [sl](int w) {
         const uint32_t u = (uint32_t)w;
@@ -244,8 +244,6 @@ void attn_w64_kernel(const AttnArgs a) {
   i32x12 tmp;
   f32x2 mrun, lrun;
   i32x8 tsum;
-  i32x16 rmask;
-  i32x2 cmask;
   // scalar state: cursors (frame, tile in frame) of the last K and V^T tiles loaded and of the
   // tile t, iteration t
   int kf = kc.f, kk = kc.k, vf = c0.f, vk = c0.k, sf = c0.f, sk = c0.k, t = 0;
@@ -258,12 +256,12 @@ void attn_w64_kernel(const AttnArgs a) {
   const float sl = a.scale_log2;
   unsigned long long trig;
   int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp, ov;
-  // Register plan (both programs): O^T a[0:127], Q^T a[128:191], S^T v[0:63], P^T v[64:127],
-  // fragment ring v[128:175], LDS addresses v[176:187], temporaries v[188:199], m v[200:201],
-  // tile sums v[248:255].  The e4m3 program keeps its masks and lane constants in VGPRs; the
-  // bf16 program holds the -m blocks in v[202:233], the load offsets and frame slots in
-  // v[236:244], a mask temporary in v245, the OR of a tile's P words in v246, its l accumulators
-  // (row sums on the matrix core) in v[248:255], and masks and lane constants in AGPRs.
+  // Register plan: O^T a[0:127], Q^T a[128:191], mask words a[192:223], lane constants
+  // a[224:227], row-sum selector a[228:231]; S^T v[0:63], P^T v[64:127], fragment ring
+  // v[128:175], LDS addresses v[176:187], temporaries v[188:199], m v[200:201], -m blocks
+  // v[202:233], load offsets and frame slots v[236:244], a mask temporary v245, the OR of a
+  // tile's P words v246, l accumulators (row sums on the matrix core) v[248:255].  e4m3 only:
+  // staging read addresses v[234:235], widened-chunk write addresses a[232:239].
 #define SDV2_W64_OUTPUTS                                                                      \
   "={a[0:31]}"(o0), "={a[32:63]}"(o1), "={a[64:95]}"(o2), "={a[96:127]}"(o3),                  \
       "={v[0:31]}"(s0), "={v[32:63]}"(s1), "={v[64:95]}"(p0), "={v[96:127]}"(p1),               \
@@ -278,6 +276,19 @@ void attn_w64_kernel(const AttnArgs a) {
       [nshared] "s"(nshared), [N] "s"(Ntok), [tqw] "s"(tq_wave), [kblo] "s"(kblo),              \
       [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb), [sl] "s"(sl)
 #define SDV2_W64_CLOBBERS "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91"
+  i32x32 negm, amask;
+  unsigned long long ninf;
+  // row-sum selector: bf16 ones at lanes 0 and 32 (output row 0) and 17 and 49 (row 1)
+  i32x4 sel;
+  {
+    const int one2 = (lane == 0 || lane == 17 || lane == 32 || lane == 49) ? 0x3F803F80 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sel[i] = one2;
+  }
+#define SDV2_W64_NEGM_OUTPUTS "={v[202:233]}"(negm), "={a[192:223]}"(amask), [ninf] "=&s"(ninf)
+#define SDV2_W64_PLAN_INPUTS                                                                  \
+  "{a[224:227]}"(lanec), "{a[228:231]}"(sel), "{v[236:239]}"(koffv), "{v[240:243]}"(voffv),    \
+      "{v244}"(slot_lane)
   if constexpr (F8) {
     // e4m3 widening addresses: this lane's staged 16 bytes of each load (K, V^T) and the two
     // bf16 chunks each widens into (ring slot 0; the program adds the slot)
@@ -293,35 +304,28 @@ void attn_w64_kernel(const AttnArgs a) {
       wv[2 * i + 1] = (int)((uint32_t)(uintptr_t)ldsV + lds_chunk<VRB>(vr8[i], 4 * (vc8 >> 1) + 2 + (vc8 & 1)));
     }
     asm volatile(SDV2_W64_LOOP_FP8
-                 : SDV2_W64_OUTPUTS, "={v[206:221]}"(rmask), "={v[222:223]}"(cmask), "={v[228:229]}"(lrun)
-                 : SDV2_W64_INPUTS, "{v[224:227]}"(lanec), "{v[230:233]}"(koffv), "{v[234:237]}"(voffv),
-                   "{v238}"(slot_lane), [ms] "s"(ms), "{v202}"(sk_addr), "{v203}"(sv_addr), "{v[240:243]}"(wk),
-                   "{v[244:247]}"(wv)
-                 : SDV2_W64_CLOBBERS);
-  } else {
-    i32x32 negm, amask;
-    unsigned long long ninf;
-    // row-sum selector: bf16 ones at lanes 0 and 32 (output row 0) and 17 and 49 (row 1)
-    i32x4 sel;
-    const int one2 = (lane == 0 || lane == 17 || lane == 32 || lane == 49) ? 0x3F803F80 : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sel[i] = one2;
-    asm volatile(SDV2_W64_LOOP
-                 : SDV2_W64_OUTPUTS, "={v[202:233]}"(negm), "={a[192:223]}"(amask), [ninf] "=&s"(ninf)
-                 : SDV2_W64_INPUTS, "{a[224:227]}"(lanec), "{a[228:231]}"(sel), "{v[236:239]}"(koffv),
-                   "{v[240:243]}"(voffv), "{v244}"(slot_lane), [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_OUTPUTS, SDV2_W64_NEGM_OUTPUTS
+                 : SDV2_W64_INPUTS, SDV2_W64_PLAN_INPUTS, [ms] "s"(ms), "{v234}"(sk_addr), "{v235}"(sv_addr),
+                   "{a[232:235]}"(wk), "{a[236:239]}"(wv)
                  : SDV2_W64_CLOBBERS, "v245", "v246");   // mask word temporary, OR of the P words
-    (void)negm;
-    (void)amask;
-    (void)ninf;
-    // l of row j < 16 sits in lane j, register 4 qb; of row j + 16 in lane j, register 4 qb + 1
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float x0 = __shfl(__int_as_float(tsum[4 * qb]), r & 15);
-      const float x1 = __shfl(__int_as_float(tsum[4 * qb + 1]), r & 15);
-      lrun[qb] = r < 16 ? x0 : x1;
-    }
+  } else {
+    asm volatile(SDV2_W64_LOOP
+                 : SDV2_W64_OUTPUTS, SDV2_W64_NEGM_OUTPUTS
+                 : SDV2_W64_INPUTS, SDV2_W64_PLAN_INPUTS, [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_CLOBBERS, "v245", "v246");   // mask word temporary, OR of the P words
   }
+  (void)negm;
+  (void)amask;
+  (void)ninf;
+  // l of row j < 16 sits in lane j, register 4 qb; of row j + 16 in lane j, register 4 qb + 1
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float x0 = __shfl(__int_as_float(tsum[4 * qb]), r & 15);
+    const float x1 = __shfl(__int_as_float(tsum[4 * qb + 1]), r & 15);
+    lrun[qb] = r < 16 ? x0 : x1;
+  }
+#undef SDV2_W64_NEGM_OUTPUTS
+#undef SDV2_W64_PLAN_INPUTS
 #undef SDV2_W64_OUTPUTS
 #undef SDV2_W64_INPUTS
 #undef SDV2_W64_CLOBBERS
@@ -333,8 +337,6 @@ void attn_w64_kernel(const AttnArgs a) {
   (void)p0;
   (void)p1;
   (void)tsum;
-  (void)rmask;
-  (void)cmask;
   (void)trig;
 
   // Epilogue.  Lane (g, r), element v of o[db][qb] (o_db[16 qb + v]) holds
@@ -348,7 +350,7 @@ void attn_w64_kernel(const AttnArgs a) {
   auto oval = [&](int db, int i) { return db == 0 ? o0[i] : db == 1 ? o1[i] : db == 2 ? o2[i] : o3[i]; };
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = F8 ? lrun[qb] + __shfl_xor(lrun[qb], 32) : lrun[qb];
+    const float l_tot = lrun[qb];
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* const erow = ep + (32 * qb + r) * EP_STRIDE + 8 * g;
 #pragma unroll

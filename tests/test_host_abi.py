@@ -230,10 +230,16 @@ def test_generated_asm_writes_only_declared_registers():
     spec.loader.exec_module(gen)
 
     def macro(name):
-        i = src.index(f"#define {name}")
-        return src[i:src.index("\n#define", i + 1)] if "\n#define" in src[i + 1:] else src[i:]
+        # the #define line and its backslash-continued lines
+        lines = src[src.index(f"#define {name}"):].split("\n")
+        out = []
+        for line in lines:
+            out.append(line)
+            if not line.rstrip().endswith("\\"):
+                break
+        return "\n".join(out)
 
-    shared = macro("SDV2_W64_OUTPUTS") + macro("SDV2_W64_CLOBBERS")
+    shared = "".join(macro(m) for m in re.findall(r"#define (SDV2_W64_\w*(?:OUTPUTS|CLOBBERS))\b", src))
     for prog_name, f8 in (("SDV2_W64_LOOP_FP8", True), ("SDV2_W64_LOOP\n", False)):
         i = src.index(f"asm volatile({prog_name}")
         stmt = src[i:src.index(");", i)]
