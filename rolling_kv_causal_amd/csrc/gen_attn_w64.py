@@ -8,11 +8,11 @@ issues 64 MFMAs 32x32x16 bf16 fed by 32 LDS fragment reads (each read feeds both
   QK:  S^T[kb][qb] = K[kb] Q^T[qb]      16 K reads (kb-major, 8 k steps each)
   PV:  O^T[db][qb] += V^T[db] P^T[qb]   16 V^T reads (key step ks-major, d block db)
 and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete after the
-16th), the softmax of the tile's S into bf16 P^T words for the next tile's PV.  bf16 program:
-Q arrives scaled by scale_log2 and the first QK MFMA of a chain accumulates onto the -(m + BIAS)
-block, so S is already the exponent; the P words are ORed for the lazy test, and eight 16x16x32
-MFMAs add the previous tile's P row sums into l.  e4m3 program: exp2(S*scale_log2 - m) with
-fp32 per-lane tile sums.
+16th), the softmax of the tile's S into bf16 P^T words for the next tile's PV: Q arrives
+scaled by scale_log2 and the first QK MFMA of a chain accumulates onto the -(m + BIAS) block, so
+S is already the exponent; the P words are ORed for the lazy test, and eight 16x16x32 MFMAs add
+the previous tile's P row sums into l.  The e4m3 program differs only in its loads (staged,
+then widened to bf16 at the top of the iteration).
 
 Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
 moves them; the loop is generated once per phase, so the ring slots of K(t) (ph) and V^T(t-1)
@@ -23,16 +23,16 @@ moves them; the loop is generated once per phase, so the ring slots of K(t) (ph)
     loads (K(t+2), V^T(t+1); bf16 eight of 1 KB into the ring, e4m3 four into the staging
     slot of parity ph mod 2) spread over the stream, and, in the free issue slots of the QK
     part, the scalar set-up of iteration t+1 (load cursors and global bases, the walk cursor
-    and mflag of tile t+1); then the lazy test (trig != 0: some lane's tile sum left [0, 256]
-    or is not finite)
-  trig == 0: (e4m3) l += tile sums; otherwise (out of line) the rescale: masked row max, m,
-    alpha, O and l scaled, P of the tile recomputed into buffer 1-pp (e4m3: l += its sums;
-    bf16: the -m blocks rewritten)
+    and mflag of tile t+1); then the lazy test (trig != 0: some P word of the tile is >= 2 or
+    not finite, or some row has no maximum yet)
+  trig != 0 (out of line): the rescale: masked row max, m, alpha, O and l scaled (not while
+    no row of the block has a maximum), P of the tile recomputed into buffer 1-pp, the -m
+    blocks rewritten
 After the loop the last PV (e4m3: after widening V^T(n-1)).  Set-up values alternate between
 two register sets by iteration parity, so the loads of iteration t read one set while the
-stream writes the other.  The masked variant ANDs every P word with a ragged-tile mask (keys
->= nvalid) and a per-row-block causal mask (own frame tk after the row's frame), both computed
-at the block start.
+stream writes the other.  The masked variant ANDs every P word with its mask word: the
+ragged-tile mask (keys >= nvalid) times the row block's causal mask (own frame tk after the
+row's frame), computed at the block start into AGPRs.
 
 Register plan (per lane):
   a[0:127]    O^T  o[db][qb] at a[(2db+qb)*16 .. +15]
@@ -43,17 +43,13 @@ Register plan (per lane):
   v[176:183]  K fragment LDS addresses per k step kd;  v[184:187] V^T addresses per key step
   v[188:199]  temporaries
   v[200:201]  m per qb (running max, log2 units)
-  v[248:255]  e4m3: tile sums, four per qb; bf16: l accumulators (16x16 MFMA layout), four per qb
- e4m3 program:
-  v[206:221]  ragged masks of the 16 P words of a row block;  v[222:223] causal mask per qb
-  v[224] 8g;  v[225:226] frame of the lane's row per qb;  v[227] (lane ^ 32) * 4
-  v[228:229]  l per qb;  v[230:237] K and V^T lane offsets of the tile loads;  v238 frame slots
-  v[202:203], v[240:247]  staging read and widened-chunk write addresses
- bf16 program:
-  v[202:233]  -(m + BIAS) blocks per qb (first QK accumulator);  v[236:243] load offsets;
-  v244 frame slots;  v245 mask temporary;  v246 OR of the tile's P words
-  a[192:223]  mask words per (qb, word);  a[224:227] 8g, frame per qb, (lane ^ 32) * 4;
+  v[202:233]  -(m + BIAS) blocks per qb (first QK accumulator)
+  v[236:243]  K and V^T lane offsets of the tile loads;  v244 frame slots
+  v245        mask temporary;  v246 OR of the tile's P words
+  v[248:255]  l accumulators (16x16 MFMA layout), four per qb
+  a[192:223]  mask words per (qb, word);  a[224:227] 8g, frame per qb, (lane ^ 32) * 4
   a[228:231]  row-sum selector
+  e4m3 only:  v[234:235] staging read addresses; a[232:239] widened-chunk write addresses
   s[84:91]    global bases of the K and V^T tile loads, two sets by iteration parity
 
 Hazards kept by construction (gfx950, counted in issued instructions): an MFMA result is read
@@ -72,8 +68,8 @@ import sys
 KA = 8                                           # fragment reads in flight
 RING = 12                                        # fragment slots: a slot is refilled 4 reads after its last use
 FR, KADDR, VADDR = 128, 176, 184
-TMP, M, RMASK, CMASK, G8, TQ, BPERM, L = 188, 200, 206, 222, 224, 225, 227, 228
-TS = 248                                         # tile sums, four per row block
+TMP, M = 188, 200
+TS = 248                                         # l accumulators, four per row block (16x16 MFMA layout)
 NEG_INF = "0xff800000"
 SM_FROM = 20                                     # first MFMA followed by softmax VALU ops
 WAIT_EVERY = 4                                   # one LDS wait per this many fragment reads
@@ -168,7 +164,7 @@ def mfma_pair(r, slot, pp):
     if r[0] == "K":
         _, kb, kd = r
         for qb in range(2):
-            c = s_reg(kb, qb) if kd else (cb_reg(qb) if NEGM else "0")
+            c = s_reg(kb, qb) if kd else cb_reg(qb)
             out.append(f"v_mfma_f32_32x32x16_bf16 {s_reg(kb, qb)}, {frag(slot)}, {q_reg(qb, kd)}, {c}")
     else:
         _, db, ks = r
@@ -177,17 +173,13 @@ def mfma_pair(r, slot, pp):
     return out
 
 
-def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
-    """Groups of 4 values: 4 FMAs, 4 exponentials, 2 packs into P words, 4 adds into the four
-    tile sums of the row block (the row block's first group sets them).  Unmasked, the sums add the fp32 exponentials; masked, every P
-    word is ANDed with its ragged-tile mask and the row block's causal mask and the sums add
-    the two bf16 halves of the masked words, so masked keys add nothing.  (Row sums by dot2
-    would be shorter, but gfx950 holds a dot2 back until the MFMA in flight has finished.)
-    mreg(qb): register holding m (bf16: the shift of S, given only when recomputing); sums(qb,
-    i): the four tile-sum accumulators."""
+def softmax_ops(pc, masked, qbs=(0, 1), mreg=None):
+    """Groups of 4 values of S (already s * scale_log2 - m - BIAS): 4 exponentials, 2 packs into
+    P words and, in the tile's stream, an OR of the words into the lazy-test accumulator.  Masked,
+    every P word is ANDed with its mask word (ragged tile and causal), so masked keys weigh and
+    sum to nothing.  mreg(qb): given only when the rescale recomputes P, the register holding
+    the shift subtracted from S first.  (The row sums run on the matrix core.)"""
     shifted = mreg is not None
-    mreg = mreg or (lambda qb: f"v{M + qb}")
-    sums = sums or (lambda qb, i: f"v{TS + 4 * qb + i}")
     ops = []
     gi = 0
     for kb in range(2):
@@ -198,12 +190,7 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                     t = [f"v{TMP + (gi % 3) * 4 + j}" for j in range(4)]
                     gi += 1
                     vs = [half * 8 + 2 * w0 + j for j in range(4)]
-                    if not NEGM:
-                        for j in range(4):
-                            ops.append(f"v_fma_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, %[sl], -{mreg(qb)}")
-                        for j in range(4):
-                            ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
-                    elif shifted:
+                    if shifted:
                         for j in range(4):
                             ops.append(f"v_sub_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, {mreg(qb)}")
                         for j in range(4):
@@ -217,68 +204,37 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None, sums=None):
                     if masked:
                         for wi, w in enumerate(words):
                             j = ks * 4 + w0 + wi
-                            if NEGM:
-                                ops.append(f"v_accvgpr_read_b32 v{MT}, a{MKA + 16 * qb + j}")
-                                ops.append(f"v_and_b32 {w}, {w}, v{MT}")
-                            else:
-                                ops.append(f"v_and_b32 {w}, {w}, v{RMASK + j}")
-                                ops.append(f"v_and_b32 {w}, {w}, v{CMASK + qb}")
-                        for wi, w in enumerate(words):
-                            if NEGM:
-                                break
-                            ops.append(f"v_lshlrev_b32 {t[2 * wi]}, 16, {w}")
-                            ops.append(f"v_and_b32 {t[2 * wi + 1]}, 0xffff0000, {w}")
-                    if NEGM:
-                        if not shifted:        # the lazy test of the tile: OR of its P words
-                            ops.append(f"v_or_b32 v{ACC}, {words[0]}, {words[1]}" if gi == 1 else
-                                       f"v_or3_b32 v{ACC}, v{ACC}, {words[0]}, {words[1]}")
-                        continue
-                    for j in range(4):
-                        if kb == 0 and half == 0 and w0 == 0:      # first group of the row block
-                            ops.append(f"v_mov_b32 {sums(qb, j)}, {t[j]}")
-                        else:
-                            ops.append(f"v_add_f32 {sums(qb, j)}, {sums(qb, j)}, {t[j]}")
+                            ops.append(f"v_accvgpr_read_b32 v{MT}, a{MKA + 16 * qb + j}")
+                            ops.append(f"v_and_b32 {w}, {w}, v{MT}")
+                    if not shifted:            # the lazy test of the tile: OR of its P words
+                        ops.append(f"v_or_b32 v{ACC}, {words[0]}, {words[1]}" if gi == 1 else
+                                   f"v_or3_b32 v{ACC}, v{ACC}, {words[0]}, {words[1]}")
     return ops
 
 
 def mask_setup():
     """Ragged masks: low half of word j valid iff 8g + key(j) < nvalid, high half iff
     8g + key(j) + 1 < nvalid.  Causal mask of qb: all ones iff tk <= frame of the row.
-    bf16: the product of both per (qb, word) into a[192 + 16 qb + j]."""
-    if NEGM:
-        g8, tq0, tq1 = (f"v{TMP + 5}", f"v{TMP + 6}", f"v{TMP + 7}")
-        lines = [f"v_accvgpr_read_b32 {g8}, a{LANEA}", f"v_accvgpr_read_b32 {tq0}, a{LANEA + 1}",
-                 f"v_accvgpr_read_b32 {tq1}, a{LANEA + 2}",
-                 f"v_mov_b32 v{TMP + 2}, 0xffff", f"v_mov_b32 v{TMP + 3}, 0xffff0000", f"v_mov_b32 v{TMP + 4}, -1"]
-        for qb in range(2):
-            lines += [f"v_cmp_le_i32 vcc, %[tk], v{TMP + 6 + qb}",
-                      f"v_cndmask_b32 v{TMP + 8 + qb}, 0, v{TMP + 4}, vcc"]
-        for j in range(16):
-            c = word_key(j)
-            lines += [f"s_sub_i32 %[stmp], %[nvalid], {c}",
-                      f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
-                      f"v_cndmask_b32 v{TMP}, 0, v{TMP + 2}, vcc",
-                      f"s_sub_i32 %[stmp], %[nvalid], {c + 1}",
-                      f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
-                      f"v_cndmask_b32 v{TMP + 1}, 0, v{TMP + 3}, vcc",
-                      f"v_or_b32 v{TMP + 10}, v{TMP}, v{TMP + 1}"]
-            for qb in range(2):
-                lines += [f"v_and_b32 v{TMP + 11}, v{TMP + 10}, v{TMP + 8 + qb}",
-                          f"v_accvgpr_write_b32 a{MKA + 16 * qb + j}, v{TMP + 11}"]
-        return lines
-    lines = [f"v_mov_b32 v{TMP + 2}, 0xffff", f"v_mov_b32 v{TMP + 3}, 0xffff0000", f"v_mov_b32 v{TMP + 4}, -1"]
+    The product of both per (qb, word) goes to a[192 + 16 qb + j]."""
+    g8, tq0, tq1 = (f"v{TMP + 5}", f"v{TMP + 6}", f"v{TMP + 7}")
+    lines = [f"v_accvgpr_read_b32 {g8}, a{LANEA}", f"v_accvgpr_read_b32 {tq0}, a{LANEA + 1}",
+             f"v_accvgpr_read_b32 {tq1}, a{LANEA + 2}",
+             f"v_mov_b32 v{TMP + 2}, 0xffff", f"v_mov_b32 v{TMP + 3}, 0xffff0000", f"v_mov_b32 v{TMP + 4}, -1"]
+    for qb in range(2):
+        lines += [f"v_cmp_le_i32 vcc, %[tk], v{TMP + 6 + qb}",
+                  f"v_cndmask_b32 v{TMP + 8 + qb}, 0, v{TMP + 4}, vcc"]
     for j in range(16):
         c = word_key(j)
         lines += [f"s_sub_i32 %[stmp], %[nvalid], {c}",
-                  f"v_cmp_gt_i32 vcc, %[stmp], v{G8}",
+                  f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
                   f"v_cndmask_b32 v{TMP}, 0, v{TMP + 2}, vcc",
                   f"s_sub_i32 %[stmp], %[nvalid], {c + 1}",
-                  f"v_cmp_gt_i32 vcc, %[stmp], v{G8}",
+                  f"v_cmp_gt_i32 vcc, %[stmp], {g8}",
                   f"v_cndmask_b32 v{TMP + 1}, 0, v{TMP + 3}, vcc",
-                  f"v_or_b32 v{RMASK + j}, v{TMP}, v{TMP + 1}"]
-    for qb in range(2):
-        lines += [f"v_cmp_le_i32 vcc, %[tk], v{TQ + qb}",
-                  f"v_cndmask_b32 v{CMASK + qb}, 0, v{TMP + 4}, vcc"]
+                  f"v_or_b32 v{TMP + 10}, v{TMP}, v{TMP + 1}"]
+        for qb in range(2):
+            lines += [f"v_and_b32 v{TMP + 11}, v{TMP + 10}, v{TMP + 8 + qb}",
+                      f"v_accvgpr_write_b32 a{MKA + 16 * qb + j}, v{TMP + 11}"]
     return lines
 
 
@@ -366,7 +322,7 @@ def tile_block(ph, masked):
     """Iteration phase ph (t mod NSLOT; parity par = ph mod 2, P buffer pp = 1 - par):
     QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this iteration's tile loads
     (bases of parity par) and the next iteration's scalar set-up, then the lazy test
-    (trig != 0: some lane's tile sum left [0, 256] or is not finite)."""
+    (trig != 0: some P word of the tile is >= 2 or not finite, or a row has no maximum yet)."""
     par = ph % 2
     pp = 1 - par
     pc = 1 - pp
@@ -374,41 +330,28 @@ def tile_block(ph, masked):
     extra = [(0, v_setup(1 - par)), (0, cursor_shift()), (0, k_setup(1 - par, 3)),
              (0, walk_setup(1 - par, False))]
     valu = softmax_ops(pc, masked)
-    if NEGM:
-        # l += row sums of P(t-1) (buffer pp, complete), one MFMA after every other group
-        sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)]
-        out, gcount = [], 0
-        for op in valu:
-            out.append(op)
-            if op.startswith(("v_or_b32", "v_or3_b32")) and f"v{ACC}" in op:
-                gcount += 1
-                if gcount % 2 == 1 and sums:
-                    out.append(sums.pop(0))
-        valu = out + sums
-        lines += stream(k_reads() + v_reads(), pp, ph, valu, tile_loads(ph), SM_FROM, extra)
-        # lazy test: some P word >= 2 (a score 9 above m, or not finite), or a row without m
-        return lines + [f"v_and_b32 v{TMP}, 0x40004000, v{ACC}",
-                        f"v_cmp_ne_u32 vcc, 0, v{TMP}",
-                        "s_mov_b64 %[trig], vcc",
-                        "s_or_b64 %[trig], %[trig], %[ninf]"]
-    lines += stream(k_reads() + v_reads(), pp, ph, softmax_ops(pc, masked), tile_loads(ph), SM_FROM, extra)
-    lines += [f"v_add_f32 v{TMP}, v{TS}, v{TS + 1}",
-              f"v_add_f32 v{TMP + 1}, v{TS + 4}, v{TS + 5}",
-              f"v_add_f32 v{TMP + 2}, v{TS + 2}, v{TS + 3}",
-              f"v_add_f32 v{TMP + 3}, v{TS + 6}, v{TS + 7}",
-              f"v_add_f32 v{TMP}, v{TMP}, v{TMP + 2}",
-              f"v_add_f32 v{TMP + 1}, v{TMP + 1}, v{TMP + 3}",
-              f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP}",
-              "s_mov_b64 %[trig], vcc",
-              f"v_cmp_nge_f32 vcc, 0x43800000, v{TMP + 1}",
-              "s_or_b64 %[trig], %[trig], vcc"]
-    return lines
+    # l += row sums of P(t-1) (buffer pp, complete), one MFMA after every other group
+    sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)]
+    out, gcount = [], 0
+    for op in valu:
+        out.append(op)
+        if op.startswith(("v_or_b32", "v_or3_b32")) and f"v{ACC}" in op:
+            gcount += 1
+            if gcount % 2 == 1 and sums:
+                out.append(sums.pop(0))
+    valu = out + sums
+    lines += stream(k_reads() + v_reads(), pp, ph, valu, tile_loads(ph), SM_FROM, extra)
+    # lazy test: some P word >= 2 (a score 9 above m, or not finite), or a row without m
+    return lines + [f"v_and_b32 v{TMP}, 0x40004000, v{ACC}",
+                    f"v_cmp_ne_u32 vcc, 0, v{TMP}",
+                    "s_mov_b64 %[trig], vcc",
+                    "s_or_b64 %[trig], %[trig], %[ninf]"]
 
 
 RARE_ID = [0]                                    # unique labels of the rare blocks
 
 
-def rare_block_negm(pc, masked):
+def rare_block(pc, masked):
     """bf16 rescale of the tile: S = s * scale_log2 - mc, mc = m if finite, else 0.  New row
     maximum m' = max(m, max over valid keys of S + mc); O, l scaled by 2^(m - m'); the tile's
     P recomputed as 2^(S - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of the row
@@ -472,58 +415,10 @@ def rare_block_negm(pc, masked):
     return lines
 
 
-def rare_block(pc, masked):
-    if NEGM:
-        return rare_block_negm(pc, masked)
-    mx, y, mn, al, mm, t0, t1, ninf = (f"v{x}" for x in range(128, 136))
-    lines = ["s_nop 15", f"v_mov_b32 {ninf}, {NEG_INF}"]
-    for qb in range(2):
-        lines.append(f"v_mov_b32 {mx}, {NEG_INF}")
-        for j in range(16):
-            kb, v = j >> 3, ((j >> 2) & 1) * 8 + 2 * (j & 3)
-            lo, hi = s_elem(kb, qb, v), s_elem(kb, qb, v + 1)
-            if masked:
-                lines += [f"v_and_b32 {t0}, v{RMASK + j}, v{CMASK + qb}",
-                          f"v_and_b32 {t1}, 0xffff, {t0}",
-                          f"v_cmp_ne_u32 vcc, 0, {t1}",
-                          f"v_cndmask_b32 {t1}, {ninf}, {lo}, vcc",
-                          f"v_max_f32 {mx}, {mx}, {t1}",
-                          f"v_cmp_lt_u32 vcc, 0xffff, {t0}",
-                          f"v_cndmask_b32 {t1}, {ninf}, {hi}, vcc",
-                          f"v_max_f32 {mx}, {mx}, {t1}"]
-            else:
-                lines.append(f"v_max3_f32 {mx}, {mx}, {lo}, {hi}")
-        lines += [f"ds_bpermute_b32 {y}, v{BPERM}, {mx}",
-                  "s_waitcnt lgkmcnt(0)",
-                  f"v_max_f32 {mx}, {mx}, {y}",
-                  f"v_mul_f32 {t0}, %[sl], {mx}",
-                  f"v_max_f32 {mn}, v{M + qb}, {t0}",                 # m_new
-                  f"v_sub_f32 {t0}, v{M + qb}, {mn}",
-                  f"v_exp_f32 {al}, {t0}",
-                  f"v_cmp_eq_f32 vcc, {NEG_INF}, {mn}",
-                  f"v_cndmask_b32_e64 {al}, {al}, 1.0, vcc",          # alpha = 1 if m_new = -inf
-                  f"v_cndmask_b32_e64 {mm}, {mn}, 0, vcc",            # m used for P: 0 if -inf
-                  f"v_mov_b32 v{M + qb}, {mn}",
-                  f"v_mul_f32 v{L + qb}, v{L + qb}, {al}"]
-        # O^T of this row block *= alpha, four values at a time
-        vals = [(db, v) for db in range(4) for v in range(16)]
-        for k in range(0, 64, 4):
-            grp = vals[k:k + 4]
-            tmps = [f"v{136 + i}" for i in range(4)]   # v136..v139
-            lines += [f"v_accvgpr_read_b32 {tmps[i]}, {o_elem(db, qb, v)}" for i, (db, v) in enumerate(grp)]
-            lines += [f"v_mul_f32 {tmps[i]}, {tmps[i]}, {al}" for i in range(4)]
-            lines += [f"v_accvgpr_write_b32 {o_elem(db, qb, v)}, {tmps[i]}" for i, (db, v) in enumerate(grp)]
-        # P of the tile at the new m, and its sums
-        ss = [f"v{140 + i}" for i in range(4)]
-        lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: mm, sums=lambda _q, i: ss[i])
-        lines += [f"v_add_f32 v{L + qb}, v{L + qb}, {x}" for x in ss]
-    return lines
-
-
 def init_block():
     """O = 0 and P(-1) = 0 (read by the first PV), written sixteen registers at a time by MFMAs
-    of zero operands; m = -inf; bf16: the -m blocks -BIAS (a product of ones and -1/2 summed
-    over 16), the row-sum accumulators 0, every row flagged; e4m3: sums and l = 0."""
+    of zero operands; m = -inf; the -m blocks -BIAS (a product of ones and -1/2 summed
+    over 16), the row-sum accumulators 0, every row flagged."""
     zero, ones, half = "v[128:131]", "v[132:135]", "v[136:139]"
     lines = [f"v_mov_b32 v{128 + i}, 0" for i in range(4)]
     lines += [f"v_mov_b32 v{132 + i}, 0x3f803f80" for i in range(4)]
@@ -532,21 +427,18 @@ def init_block():
     b = p_base(1)
     lines += [f"v_mfma_f32_32x32x16_bf16 v[{b + 16 * i}:{b + 16 * i + 15}], {zero}, {zero}, 0" for i in range(2)]
     lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
-    if NEGM:
-        # mc = 0 while m = -inf: the -m blocks start at -BIAS and every row is flagged
-        assert BIAS == 8
-        lines += [f"v_mfma_f32_32x32x16_bf16 {cb_reg(qb)}, {ones}, {half}, 0" for qb in range(2)]
-        lines += [f"v_mfma_f32_16x16x32_bf16 v[{TS + 4 * qb}:{TS + 4 * qb + 3}], {zero}, {zero}, 0" for qb in range(2)]
-        lines.append("s_mov_b64 %[ninf], -1")
-    else:
-        lines += [f"v_mov_b32 v{i}, 0" for i in list(range(RMASK, CMASK + 2)) + list(range(TS, TS + 8)) + [L, L + 1]]
+    # mc = 0 while m = -inf: the -m blocks start at -BIAS and every row is flagged
+    assert BIAS == 8
+    lines += [f"v_mfma_f32_32x32x16_bf16 {cb_reg(qb)}, {ones}, {half}, 0" for qb in range(2)]
+    lines += [f"v_mfma_f32_16x16x32_bf16 v[{TS + 4 * qb}:{TS + 4 * qb + 3}], {zero}, {zero}, 0" for qb in range(2)]
+    lines.append("s_mov_b64 %[ninf], -1")
     return lines
 
 
 def pv_only_block(ph):
     """The last PV, as the PV of an iteration of phase ph would run it."""
     pp = 1 - ph % 2
-    sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)] if NEGM else []
+    sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)]
     return stream(v_reads(), pp, ph, sums) + ["s_nop 11"]
 
 
@@ -624,29 +516,27 @@ def check_hazards(lines):
             last_m0 -= n
 
 
-KOFF, VOFF, SLOTL = 230, 234, 238
-CB = 202                                         # bf16: -m blocks, v[202:217] (qb 0) and v[218:233]
-MT = 245                                         # bf16: mask word read from its AGPR
-MKA, LANEA = 192, 224                            # bf16: mask words a[192 + 16 qb + j]; 8g, tq, bperm at a[224:227]
-SEL = 228                                        # bf16: row-sum selector a[228:231] (A operand)
-ACC = 246                                        # bf16: OR of the tile's P words (lazy test)
-BIAS = 8                                         # bf16: P = 2^(s * scale_log2 - m - BIAS)
+KOFF, VOFF, SLOTL = 236, 240, 244                # lane offsets of the K and V^T tile loads, frame slots
+CB = 202                                         # -(m + BIAS) blocks, v[202:217] (qb 0) and v[218:233]
+MT = 245                                         # mask word read from its AGPR
+MKA, LANEA = 192, 224                            # mask words a[192 + 16 qb + j]; 8g, tq, bperm at a[224:227]
+SEL = 228                                        # row-sum selector a[228:231] (A operand)
+ACC = 246                                        # OR of the tile's P words (lazy test)
+BIAS = 8                                         # P = 2^(s * scale_log2 - m - BIAS)
 
 
 def set_mode(f8):
-    """Register plan of the program: e4m3 keeps the fused scale-and-subtract softmax and its
-    masks in VGPRs; bf16 (NEGM) takes Q pre-scaled and the -m blocks as the first QK
-    accumulator, with the masks and lane constants in AGPRs."""
-    global F8, NEGM, L, KOFF, VOFF, SLOTL
-    F8, NEGM = f8, True
-    L, KOFF, VOFF, SLOTL = 234, 236, 240, 244
+    """Program for the e4m3 cache (staged loads widened to bf16) or the bf16 cache."""
+    global F8
+    F8 = f8
+
+
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
 NSLOT = 4                                        # ring slots of K and of V^T tiles
 
 
 BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
 F8 = False                                       # program for the e4m3 cache (set by set_mode)
-NEGM = True                                      # S = Q' K^T - m in the MFMA (set by set_mode)
 STAGE = 16384                                    # e4m3 staging slot: K tile (8 KB), then V^T tile (8 KB)
 SK, SV = 234, 235                                # e4m3: this lane's staging read addresses (K, V^T)
 WKA, WVA = 232, 236                              # e4m3: widened-chunk write addresses (AGPRs; lo, hi per load)
@@ -786,7 +676,6 @@ def iteration(ph):
         tile_block(ph, False) + \
         [f".Lw64_td{tag}_%=:",
          "s_cmp_eq_u64 %[trig], 0", f"s_cbranch_scc0 .Lw64_r{tag}_%=",
-         *([] if NEGM else [f"v_add_f32 v{L}, v{L}, v{TMP}", f"v_add_f32 v{L + 1}, v{L + 1}, v{TMP + 1}"]),
          f".Lw64_nr{tag}_%=:",
          "s_add_u32 %[t], %[t], 1"]
 
