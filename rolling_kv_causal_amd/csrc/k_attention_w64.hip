@@ -100,22 +100,12 @@ void attn_w64_kernel(const AttnArgs a) {
     const uint16_t* qb1 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[1] ? row[1] : 0)) * a.H + head) * D + 8 * g;
 #pragma unroll
     for (int kd = 0; kd < 8; ++kd) {
-      const uint4 x = valid[0] ? *(const uint4*)(qb0 + 16 * kd) : make_uint4(0, 0, 0, 0);
-      const uint4 y = valid[1] ? *(const uint4*)(qb1 + 16 * kd) : make_uint4(0, 0, 0, 0);
+      // unconditional (an invalid row reads row 0 of the element and is zeroed below): a
+      // conditional load compiles to a branch that waits for it
+      const uint4 x = *(const uint4*)(qb0 + 16 * kd);
+      const uint4 y = *(const uint4*)(qb1 + 16 * kd);
       q0[4 * kd] = x.x; q0[4 * kd + 1] = x.y; q0[4 * kd + 2] = x.z; q0[4 * kd + 3] = x.w;
       q1[4 * kd] = y.x; q1[4 * kd + 1] = y.y; q1[4 * kd + 2] = y.z; q1[4 * kd + 3] = y.w;
-    }
-    {
-      const float sl = a.scale_log2;
-      auto scaled = [sl](int w) {
-        const uint32_t u = (uint32_t)w;
-        return (int)pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * sl, bf16_bits_to_f32(u >> 16) * sl);
-      };
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        q0[i] = scaled(q0[i]);
-        q1[i] = scaled(q1[i]);
-      }
     }
   }
 
@@ -133,8 +123,13 @@ void attn_w64_kernel(const AttnArgs a) {
   const char* const kblk = kvb + (a.k_layer_off + head_off) * EB;
   const char* const vblk = kvb + (a.v_layer_off + head_off) * EB;
   const int64_t slot_bytes = a.slot_stride * EB;
+  // frame f's ring slot, f uniform: a scalar load, so the first tiles' loads do not wait for
+  // slot_lane (a vector load)
+  auto slot_of = [&](int f) -> int {
+    return f < a.nshared ? a.slots[f] : a.own_slot[elem * a.T + min(max(f - a.nshared, 0), a.T - 1)];
+  };
   auto frame_at = [&](TileCursor& c) {
-    const int slot = __builtin_amdgcn_readlane(slot_lane, c.f & 63);
+    const int slot = slot_of(c.f);
     c.kp = kblk + slot * slot_bytes + (int64_t)c.k * (kTileKeys * D * EB);
     c.vp = vblk + slot * slot_bytes + c.k * (kTileKeys * EB);
   };
@@ -215,6 +210,23 @@ void attn_w64_kernel(const AttnArgs a) {
   if (n > 1) advance(kc);
   fill_k(kc, 1);
   fill_v(c0, F8 ? 1 : 0);
+
+  // Q scaled once its loads (issued before the first tiles' loads, and not waited for until
+  // here) arrive.
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const float sl = a.scale_log2;
+    auto scaled = [sl](int w) {
+      const uint32_t u = (uint32_t)w;
+      return (int)pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * sl, bf16_bits_to_f32(u >> 16) * sl);
+    };
+    const int keep0 = valid[0] ? -1 : 0, keep1 = valid[1] ? -1 : 0;   // masks, not branches
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      q0[i] = scaled(q0[i]) & keep0;
+      q1[i] = scaled(q1[i]) & keep1;
+    }
+  }
 
   // The tile loop (generated asm, see gen_attn_w64.py).  Its state lives in the registers
   // named by the operands below; the compiler sees one statement.
