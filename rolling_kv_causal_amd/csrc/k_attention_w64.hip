@@ -27,11 +27,13 @@
 // into the slots of K(t-2) and V(t-3), which every wave has finished reading; a wave waits for
 // its own loads (vmcnt) two iterations after issue, before that iteration's barrier.
 //
-// Softmax: base 2 with the lazy-max rule of the other kernel: exponentials at the running max
-// m; only when a lane's tile sum of P leaves [0, 256] (first tile, NaN, or a score far above
-// m) is the row max taken and O, l rescaled.  The row sums l add the fp32 exponentials (the
-// masked tiles: the bf16 values kept by the masks).  Masks (ragged last tile of a
-// frame, block-causal own frames) are applied to the packed P words by AND with per-lane masks.
+// Softmax: base 2 with a lazy running maximum m per row.  Q is staged scaled by
+// scale * log2(e) (rounded to bf16 again) and the first QK MFMA of each chain accumulates onto
+// a block holding -(m + 8), so the MFMA result is the exponent itself: P = 2^(s c - m - 8), the
+// factor 2^-8 cancelling between O and l.  Only when some P word of a tile reaches 2 (a score
+// 9 above m, a NaN or an infinity), or a row has no maximum yet, is the row maximum taken and
+// O, l rescaled.  The row sums l are MFMAs over P with a selector operand.  Masks (ragged last
+// tile of a frame, block-causal own frames) are applied to the packed P words by AND.
 #include "common.h"
 #include "attn_tiles.h"
 #include "attn_w64_asm.h"
