@@ -172,7 +172,10 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
  * workspace given at create time is used for split-KV partial results (calls on one cache
  * must not overlap in time).  With a bf16 or e4m3 cache and head_dim 128 the 64-query-row
  * kernel runs; the environment variable SDV2_ATTN_KERNEL=pingpong (read once per process)
- * selects the 32-row kernel, whose results agree up to fp32 summation order. */
+ * selects the 32-row kernel, whose results agree up to fp32 summation order.  The split-KV
+ * count follows a cost model; SDV2_NSPLIT=n (read at create and at each call; clamped to
+ * [1, 16] and to the shortest walk) forces it, for tests and tuning: the cache must be created
+ * with the variable set, so that the workspace covers the forced count. */
 int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream);
 

@@ -4,9 +4,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -117,6 +119,10 @@ constexpr double kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 // every split has at least one tile.
 int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_tiles) {
   if (c.dtype == SDV2_F32) return 1;
+  if (const char* e = std::getenv("SDV2_NSPLIT")) {   // forced count (tests, tuning)
+    const int v = std::atoi(e);
+    if (v > 0) return std::max(1, std::min({v, kMaxSplit, min_tiles}));
+  }
   const int64_t R = (int64_t)c.chunk_frames * c.grid_h * c.grid_w;   // query rows per element
   const int64_t base = (int64_t)nbatch * c.num_heads * ((R + kQTile - 1) / kQTile);
   const int64_t rows = (int64_t)nbatch * c.num_heads * R;

@@ -111,6 +111,20 @@ def test_small_ragged_streams(kw):
     _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
 
 
+def test_split_without_visible_keys_for_some_rows(monkeypatch):
+    # Four splits forced over a T' = 2 chunk of 81 tokens (two tiles per frame) with one sink
+    # and a window of one: at steady state the walk of the query tile is 8 tiles, and the last
+    # split holds only own frame 1, which the rows of own frame 0 may not see.  Those rows keep
+    # no maximum through that split (they go through the rescale every tile and end with l = 0
+    # and m = -inf), and the combine must give that split no weight.
+    monkeypatch.setenv("SDV2_NSPLIT", "4")
+    cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, chunk_frames=2,
+                 grid_h=9, grid_w=9, num_heads=2, sink_frames=1, window_frames=1, stream_batch=2,
+                 num_chunks=7, softmax_scale=128 ** -0.5)
+    assert sdv2.sdv2_cache_size(sdv2.config_of(cfg))[2] > 0     # the forced splits are in effect
+    _stream(cfg, cfg.num_steps)
+
+
 @pytest.mark.parametrize("kw", [
     dict(dtype="fp32", chunk_frames=2, grid_h=5, grid_w=7, num_heads=2, sink_frames=1, window_frames=3,
          stream_batch=2, rope_refresh_period=5, num_chunks=8, num_layers=2),

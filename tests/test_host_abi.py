@@ -258,3 +258,24 @@ def test_generated_asm_writes_only_declared_registers():
                 continue
             written |= _asm_register_set(t[1])
         assert not written - declared, (prog_name.strip(), sorted(written - declared))
+
+
+def test_forced_split_count_sizes_the_workspace(monkeypatch):
+    # SDV2_NSPLIT forces the split-KV count: a small bf16 stream whose cost model keeps one
+    # split (no workspace) needs partials for four when forced, clamped to the shortest walk
+    from synth import configs
+    c = configs.TINY_FP32.with_(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
+                                chunk_frames=2, grid_h=9, grid_w=9, num_heads=2, sink_frames=1,
+                                window_frames=1, stream_batch=2, rope_refresh_period=0, sink_threshold=None,
+                                embed_dim=0, embed_kind=None)
+    cfg = sdv2.config_of(c)
+    monkeypatch.delenv("SDV2_NSPLIT", raising=False)
+    ws_model = sdv2.sdv2_cache_size(cfg)[2]
+    monkeypatch.setenv("SDV2_NSPLIT", "4")
+    ws4 = sdv2.sdv2_cache_size(cfg)[2]
+    monkeypatch.setenv("SDV2_NSPLIT", "64")
+    ws_big = sdv2.sdv2_cache_size(cfg)[2]
+    rows = 2 * 2 * 2 * 81                       # elements x heads x T' x tokens, per split
+    assert ws_model == 0
+    assert ws4 >= 4 * rows * (128 * 2 + 8)
+    assert ws4 <= ws_big <= 16 * rows * (128 * 2 + 8) + 4096
