@@ -279,3 +279,18 @@ def test_forced_split_count_sizes_the_workspace(monkeypatch):
     assert ws_model == 0
     assert ws4 >= 4 * rows * (128 * 2 + 8)
     assert ws4 <= ws_big <= 16 * rows * (128 * 2 + 8) + 4096
+
+
+def test_generator_hazard_check_rejects_an_early_softmax():
+    # the generator's hazard check is live: starting the exponentials at the 17th MFMA reads
+    # S^T of key block 0 fewer than 12 instructions after the MFMA that writes it
+    import importlib.util
+    import pathlib
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_hz", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    gen.emit("X", gen.loop_program())          # the committed schedule passes
+    gen.SM_FROM = 17
+    with pytest.raises(AssertionError):
+        gen.emit("X", gen.loop_program())
