@@ -352,10 +352,11 @@ RARE_ID = [0]                                    # unique labels of the rare blo
 
 
 def rare_block(pc, masked):
-    """bf16 rescale of the tile: S = s * scale_log2 - mc, mc = m if finite, else 0.  New row
-    maximum m' = max(m, max over valid keys of S + mc); O, l scaled by 2^(m - m'); the tile's
-    P recomputed as 2^(S - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of the row
-    block set to -mc'; ninf: lanes whose row still has m = -inf."""
+    """Rescale of the tile: S = s * scale_log2 - mc - BIAS, mc = m if finite, else 0.  New row
+    maximum m' = max(m, max over valid keys of S + mc + BIAS); O, l scaled by 2^(m - m') (not
+    while no row of the block has a maximum: both are zero then); the tile's P recomputed as
+    2^(S - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of the row block set to
+    -(mc' + BIAS); ninf: lanes whose row still has m = -inf."""
     mx, y, mn, al, mcn, t0, t1, ninf = (f"v{x}" for x in range(128, 136))
     mc, dd, bp = "v144", "v145", "v146"
     lines = ["s_nop 15", f"v_mov_b32 {ninf}, {NEG_INF}", f"v_accvgpr_read_b32 {bp}, a{LANEA + 3}"]
@@ -547,7 +548,7 @@ def tile_loads(ph):
     four 1 KB K loads (after reads 1, 5, 9, 13) into ring slot ph + 2 and four V^T loads (after
     reads 17, 21, 25, 29) into slot ph + 1; e4m3, two of each (after reads 1, 9 and 17, 25)
     into staging slot ph mod 2.  m0 holds the LDS destination, the SGPR pair of parity ph mod 2
-    the global tile base and v[230:237] the lane offsets."""
+    the global tile base and v[236:243] the lane offsets."""
     par = ph % 2
     d = {}
     if F8:

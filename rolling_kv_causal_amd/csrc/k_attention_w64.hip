@@ -258,8 +258,8 @@ void attn_w64_kernel(const AttnArgs a) {
   i32x12 tmp;
   f32x2 mrun, lrun;
   i32x8 tsum;
-  // scalar state: cursors (frame, tile in frame) of the last K and V^T tiles loaded and of the
-  // tile t, iteration t
+  // scalar state: cursors (frame, tile in frame): kf, kk of the last K tile set up, vf, vk the
+  // same one iteration earlier, sf, sk of the walk's tile t; iteration t
   int kf = kc.f, kk = kc.k, vf = c0.f, vk = c0.k, sf = c0.f, sk = c0.k, t = 0;
   const uint64_t kblk64 = (uint64_t)(uintptr_t)kblk, vblk64 = (uint64_t)(uintptr_t)vblk;
   const uint32_t kblo = (uint32_t)kblk64, kbhi = (uint32_t)(kblk64 >> 32);
@@ -350,7 +350,6 @@ void attn_w64_kernel(const AttnArgs a) {
   (void)s1;
   (void)p0;
   (void)p1;
-  (void)tsum;
   (void)trig;
 
   // Epilogue.  Lane (g, r), element v of o[db][qb] (o_db[16 qb + v]) holds
