@@ -264,10 +264,20 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
     for i in range(first):
         lines.append(read_instr(reads[i], i % RING, ph))
     issued = first
+    # LDS waits: before the MFMA pair of read i when read i is not yet covered; a wait covers
+    # reads up to i + WAIT_EVERY - 1, but not those issued after the previous pair (during the
+    # ramp they would stall the wave), and at least read i.  waits[i] = lgkmcnt operand.
+    waits, done, n_issued = {}, 0, first
+    for i in range(len(reads)):
+        if i >= done:
+            recent = len(after[i - 1]) if i else 0
+            done = max(i + 1, min(i + WAIT_EVERY, n_issued - recent))
+            waits[i] = min(n_issued - done, 15)
+        n_issued += len(after[i])
     n_mfma = 2 * len(reads)
     fixed = [0] * n_mfma                         # read, wait and load instructions after MFMA g
     for i in range(len(reads)):
-        fixed[2 * i + 1] += ((i + 1) % WAIT_EVERY == 0) + len(after[i]) + 2 * (i in dma)
+        fixed[2 * i + 1] += (i + 1 in waits) + len(after[i]) + 2 * (i in dma)
     # VALU ops in order over the gaps from valu_from on, levelling VALU + fixed per gap
     per = [0] * n_mfma
     region = range(valu_from, n_mfma)
@@ -296,8 +306,8 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
             load[g] += len(u)
     vi = 0
     for i, r in enumerate(reads):
-        if i % WAIT_EVERY == 0:                  # reads i .. i + WAIT_EVERY - 1 in
-            lines.append(f"s_waitcnt lgkmcnt({min(max(issued - (i + WAIT_EVERY), 0), 15)})")
+        if i in waits:
+            lines.append(f"s_waitcnt lgkmcnt({waits[i]})")
         for j, m in enumerate(mfma_pair(r, i % RING, pp)):
             lines.append(m)
             for _ in range(per[2 * i + j]):
@@ -453,6 +463,7 @@ def check_hazards(lines):
     last_mfma_read = {}
     last_dot = {}
     last_valu = {}
+    pending = []                                 # destination registers of LDS ops in flight
     last_m0 = -100
     for idx, l in enumerate(lines):
         op = l.split()[0] if l.split() else ""
@@ -460,6 +471,33 @@ def check_hazards(lines):
             last_m0 = idx
         if op.startswith("global_load_lds"):
             assert idx - last_m0 >= 2, (l, "m0 written by the previous instruction")
+        if op == "s_waitcnt" and "lgkmcnt(" in l:
+            n = int(l.split("lgkmcnt(")[1].split(")")[0])
+            pending = pending[max(len(pending) - n, 0):]
+        if op.startswith(("v_", "ds_")) and pending:
+            srcs = l.replace(",", " ").split()[2:] if not op.startswith("ds_") else l.replace(",", " ").split()[1:]
+            if op.startswith("ds_read") or op == "ds_bpermute_b32":
+                srcs = l.replace(",", " ").split()[2:]
+            for tok in srcs:
+                tok = tok.lstrip("-")
+                regs = set()
+                if tok.startswith("v[") and ":" in tok:
+                    lo_, hi_ = (int(x) for x in tok[2:].rstrip("]").split(":"))
+                    regs = {f"v{x}" for x in range(lo_, hi_ + 1)}
+                elif tok.startswith("v") and tok[1:].isdigit():
+                    regs = {tok}
+                for d in pending:
+                    assert not (regs & d), (l, "reads an LDS result before its lgkmcnt wait")
+        if op.startswith("ds_"):
+            d = set()
+            if op.startswith("ds_read") or op == "ds_bpermute_b32":
+                dst = l.split()[1].rstrip(",")
+                if dst.startswith("v["):
+                    lo_, hi_ = (int(x) for x in dst[2:-1].split(":"))
+                    d = {f"v{x}" for x in range(lo_, hi_ + 1)}
+                else:
+                    d = {dst}
+            pending.append(d)
         if op.startswith("v_mfma"):
             for opnd in l.replace(",", " ").split()[2:5]:
                 if opnd.startswith("v["):
