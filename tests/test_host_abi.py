@@ -294,3 +294,20 @@ def test_generator_hazard_check_rejects_an_early_softmax():
     gen.SM_FROM = 17
     with pytest.raises(AssertionError):
         gen.emit("X", gen.loop_program())
+
+
+def test_generator_hazard_check_rejects_a_missing_lds_wait():
+    # dropping the second LDS wait of the first tile stream leaves an MFMA reading a fragment
+    # whose ds_read may still be in flight: the check must reject the program
+    import importlib.util
+    import pathlib
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_lds", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    lines = [l for l in gen.loop_program() if not l.startswith(".L")]
+    gen.check_hazards(lines)
+    first_read = next(i for i, l in enumerate(lines) if l.startswith("ds_read_b128"))
+    waits = [i for i, l in enumerate(lines) if i > first_read and l.startswith("s_waitcnt lgkmcnt")]
+    with pytest.raises(AssertionError):
+        gen.check_hazards(lines[:waits[1]] + lines[waits[1] + 1:])
