@@ -12,7 +12,8 @@ Sources and readings:
 * Sink frames + rolling window ([NEWS] algorithm item 1: the earliest frames' KV stay as sink
   tokens, the rest of the cache rolls; [REPO] core components: ring-buffer KV cache with
   sliding-window attention).  Keys of a chunk: every present sink, the last <= W committed
-  non-sink frames, and the chunk's own frames (block-causal inside the chunk).
+  non-sink frames, and the chunk's own frames (block-causal inside the chunk).  The window is
+  kept as a list here; ring_slot() states where a ring of W + T' slots places each frame.
 * Stream batch ([NEWS] system item 1, [WT] "可擴展的pipeline編排": B chunks at different noise
   levels in one call, one finished frame per call; [REPO] quick example: denoise returns
   nothing while the pipeline fills).  At step s the in-flight chunks are
@@ -76,9 +77,18 @@ def schedule(cfg, s: int) -> dict:
 
 
 def ring_slot(cfg, frame: int) -> int:
-    """Cache slot of a committed frame: sinks are slots [0, S); frame f >= S lives at S + f mod W."""
-    S, W = cfg.sink_frames, cfg.window_frames
-    return frame if frame < S else S + frame % W
+    """Cache slot of a frame once its chunk is appended: sinks are slots [0, S); frame f >= S
+    lives in ring slot S + f mod (W + T').
+
+    Reading ([REPO] core components: a ring-buffer KV cache with sliding-window attention;
+    [NEWS] algorithm item 1): the step appends the new chunk's K/V into the ring while the
+    chunk still attends the W committed frames before it, so the ring holds W + T' frames -
+    the window plus the chunk being written - and a frame's slot is its index modulo that
+    length.  The T' slots of chunk c hold frames c*T' - W - T' .. c*T' - W - 1, which left the
+    window when chunk c - 1 was committed, so writing chunk c into its final slots disturbs no
+    attended frame."""
+    S, W, T = cfg.sink_frames, cfg.window_frames, cfg.chunk_frames
+    return frame if frame < S else S + frame % (W + T)
 
 
 @dataclass

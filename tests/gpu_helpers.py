@@ -150,7 +150,8 @@ class Harness:
         return worst
 
     def check_cache(self, layers=None):
-        """Slot table bit-exact, V bytes bit-exact, K_rot within tolerance, for cached frames."""
+        """Slot table bit-exact (frame and label per slot, each window frame in the slot the
+        oracle's ring_slot() gives it), V bytes bit-exact, K_rot within tolerance."""
         cfg = self.cfg
         N = cfg.tokens
         r = len(self.st.refresh_log)
@@ -158,7 +159,7 @@ class Harness:
         base, committed, refreshes = cache.state()
         assert base == self.st.base and refreshes == r
         entries = [(j, e) for j, e in enumerate(self.st.sinks) if e is not None]
-        entries += [(lib_slot(cfg, e.frame), e) for e in self.st.window]
+        entries += [(ost.ring_slot(cfg, e.frame), e) for e in self.st.window]
         # every other sink / ring slot is empty, or holds a frame of the staged (not yet
         # committed) chunk written there by this step's append
         held = {slot for slot, _ in entries}
@@ -166,7 +167,7 @@ class Harness:
         for slot in range(cfg.sink_frames + cfg.window_frames + T):
             if slot not in held:
                 f = cache.slot_info(slot)[0]
-                assert f == -1 or (committed * T <= f < (committed + 1) * T and slot == lib_slot(cfg, f)), \
+                assert f == -1 or (committed * T <= f < (committed + 1) * T and slot == ost.ring_slot(cfg, f)), \
                     (slot, f, committed)
         if self.st.kv_fp8:
             return self._check_cache_fp8(entries, r, layers)
@@ -206,14 +207,6 @@ class Harness:
                 assert np.array_equal(v_codes, ofp8.encode(e.kv[layer][1])), f"V bytes slot {slot}"
             if Npad > N:
                 assert torch.count_nonzero(Kg[:, :, N:, :]) == 0 and torch.count_nonzero(Vg[:, :, :, N:]) == 0
-
-
-def lib_slot(cfg, frame):
-    """Physical slot of a committed frame in the library's cache layout (sdv2.h): sink slot f for
-    f < S, else ring slot S + f mod (W + T').  The pages' ring has W slots; the library keeps T'
-    spare ones so the chunk being finished can be written in place."""
-    S, W = cfg.sink_frames, cfg.window_frames
-    return frame if frame < S else S + frame % (W + cfg.chunk_frames)
 
 
 def sample_rows(N, n=40, seed=0):

@@ -30,24 +30,36 @@ def test_schedule_fill_steady_drain():
     assert [ost.schedule(cfg2, s)["newest_frame"] for s in range(4)] == [1, 3, 5, 5]
 
 
-@pytest.mark.parametrize("S,W", [(1, 8), (2, 6), (1, 4), (0, 3), (3, 1)])
-def test_ring_slots_hold_exactly_the_window(S, W):
-    # Commit frames one by one into both the oracle's chronological window and a ring indexed by
-    # ring_slot(): after every commit the ring's window slots hold exactly the window's frames.
-    cfg = tiny(sink_frames=S, window_frames=W)
+@pytest.mark.parametrize("S,W,T", [(1, 8, 1), (2, 6, 1), (1, 4, 1), (0, 3, 1), (3, 1, 1),
+                                   (1, 8, 2), (2, 3, 3), (0, 2, 4), (3, 1, 2), (1, 5, 8)])
+def test_ring_slots_hold_exactly_the_window(S, W, T):
+    # Stream chunks of T frames through the oracle's chronological window (the last W committed
+    # non-sink frames) and place every frame in a ring by ring_slot():
+    #  - sinks keep slots [0, S); every other frame lands in [S, S + W + T);
+    #  - after every commit the ring slots of the window frames are distinct and the slot of
+    #    each window frame still holds it (nothing later overwrote it);
+    #  - the T slots the next chunk is written to hold no window frame, so appending that chunk
+    #    in place leaves every frame it attends intact.
+    cfg = tiny(sink_frames=S, window_frames=W, chunk_frames=T, num_chunks=6 * (W + T) + S + 3)
+    st = ost.OracleStream(cfg, layers=[])
     ring = {}
-    window = []
-    for f in range(5 * W + S + 3):
-        slot = ost.ring_slot(cfg, f)
-        if f < S:
-            assert slot == f
-        else:
-            assert S <= slot < S + W
-            window.append(f)
-            window = window[-W:]
-        ring[slot] = f
-        assert sorted(ring[j] for j in range(S, S + W) if j in ring) == sorted(window)
-        assert [ring[j] for j in range(min(S, f + 1))] == list(range(min(S, f + 1)))
+    for s_ in range(cfg.num_chunks):
+        st.begin_step(s_)
+        c = st.plan["chunks"][0]
+        window = [e.frame for e in st.window]
+        nxt = [ost.ring_slot(cfg, c * T + t) for t in range(T)]
+        # the chunk's own slots do not hold a frame the chunk attends
+        assert not set(nxt) & {ost.ring_slot(cfg, f) for f in window}
+        for t, slot in enumerate(nxt):
+            f = c * T + t
+            assert slot == f if f < S else S <= slot < S + W + T
+            ring[slot] = f                        # the append writes the frame to its final slot
+        st.end_step({}, None)
+        window = [e.frame for e in st.window]
+        slots = [ost.ring_slot(cfg, f) for f in window]
+        assert len(set(slots)) == len(slots)
+        assert all(ring[ost.ring_slot(cfg, f)] == f for f in window)
+        assert [ring[j] for j in range(S) if j in ring] == [e.frame for e in st.sinks if e is not None]
 
 
 def test_ring_order_attention_equals_chronological():
@@ -59,8 +71,11 @@ def test_ring_order_attention_equals_chronological():
     want = st.attend(0, 0, q, k, v)
     entries = sorted(st.cached_entries(), key=lambda e: ost.ring_slot(cfg, e.frame))
     assert [e.frame for e in st.window] == [7, 8, 9, 10]
-    assert [ost.ring_slot(cfg, e.frame) for e in entries] == [0, 1, 2, 3, 4]
-    assert [e.frame for e in entries] == [0, 8, 9, 10, 7]
+    # a ring of W + T' = 5 slots after the sink: frame f in slot 1 + f mod 5; slot 2 is the
+    # one the chunk of frame 11 is written to
+    assert [ost.ring_slot(cfg, e.frame) for e in entries] == [0, 1, 3, 4, 5]
+    assert [e.frame for e in entries] == [0, 10, 7, 8, 9]
+    assert ost.ring_slot(cfg, 11) == 2
     ks = [rope.rope_frame(cfg, e.kv[0][0], e.label) for e in entries]
     vs = [e.kv[0][1] for e in entries]
     ks.append(rope.rope_frame(cfg, brute.to_f64(cfg, k), 11))
