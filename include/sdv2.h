@@ -63,7 +63,10 @@ enum {
                             rounded to nearest even, saturated at +-448; fp32 accumulation */
 };
 
-/* Library limits (validated by sdv2_config_validate). */
+/* Library limits (validated by sdv2_config_validate).  Besides these: one slot of the cache
+ * (slot_stride * elem_bytes) must be under 2 GiB and one layer's K block (slots * slot_stride *
+ * elem_bytes) under 4 GiB, since the attention kernel forms offsets inside a block in 32 bits;
+ * and N = grid_h * grid_w <= 2^20. */
 enum {
   SDV2_MAX_SLOTS_SHARED = 64, /* S + W + T' */
   SDV2_MAX_BATCH = 8,         /* B, and B * T' */

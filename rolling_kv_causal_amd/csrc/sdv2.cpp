@@ -86,6 +86,17 @@ int validate(const sdv2_config* c) {
   if (c->rope_pin_sinks != 0 && c->rope_pin_sinks != 1) return fail(SDV2_EINVAL, "rope_pin_sinks must be 0 or 1");
   if (tau_on(*c) && (c->embed_dim < 1 || c->sink_frames < 1))
     return fail(SDV2_EINVAL, "sink refresh needs embed_dim >= 1 and sink_frames >= 1");
+  // The attention tile loop forms a tile's byte offset inside a layer's K (or V) block as
+  // slot * slot_bytes + tile offset in 32-bit scalar arithmetic, with slot_bytes a signed int.
+  const int64_t N = (int64_t)c->grid_h * c->grid_w;
+  const int64_t eb = c->dtype == SDV2_F32 ? 4 : c->dtype == SDV2_BF16 ? 2 : 1;
+  const int64_t slot_bytes = (int64_t)c->num_heads * ((N + kTileKeys - 1) / kTileKeys * kTileKeys) * c->head_dim * eb;
+  const int64_t slots = c->sink_frames + c->window_frames + (int64_t)c->stream_batch * c->chunk_frames;
+  if (slot_bytes >= (int64_t)1 << 31)
+    return fail(SDV2_EINVAL, "one cache slot (%lld bytes) must be under 2 GiB", (long long)slot_bytes);
+  if (slots * slot_bytes >= (int64_t)1 << 32)
+    return fail(SDV2_EINVAL, "a layer's K block (%lld slots x %lld bytes) must be under 4 GiB",
+                (long long)slots, (long long)slot_bytes);
   return SDV2_OK;
 }
 

@@ -311,3 +311,20 @@ def test_generator_hazard_check_rejects_a_missing_lds_wait():
     waits = [i for i, l in enumerate(lines) if i > first_read and l.startswith("s_waitcnt lgkmcnt")]
     with pytest.raises(AssertionError):
         gen.check_hazards(lines[:waits[1]] + lines[waits[1] + 1:])
+
+
+def test_layer_blocks_over_the_32_bit_offset_range_are_rejected():
+    # The attention tile loop forms offsets inside a layer's K or V block in 32 bits: a layer
+    # block of 4 GiB or more, or a slot of 2 GiB or more, is refused at validation.
+    big = sdv2.config_of(configs.WAN14B_40LAYER_B4.with_(grid_h=128, grid_w=128, sink_frames=16,
+                                                         window_frames=40, stream_batch=8,
+                                                         sink_threshold=None, embed_dim=0))
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_config_validate(big)
+    assert e.value.code == sdv2.SDV2_EINVAL and "4 GiB" in str(e.value)
+    slot = sdv2.config_of(configs.WAN13B_1LAYER.with_(grid_h=1024, grid_w=1024, num_heads=8))
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_config_validate(slot)
+    assert "2 GiB" in str(e.value)
+    # the largest workload is far inside: 13 slots x 10.5 MB
+    sdv2.sdv2_config_validate(sdv2.config_of(configs.WAN14B_40LAYER_B4))
