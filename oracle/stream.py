@@ -47,7 +47,7 @@ import numpy as np
 from . import fp8 as ofp8
 from . import rope
 from .attention import attention
-from .sink import decide
+from .sink import decide, similarity_terms
 
 
 def decode(cfg, x: np.ndarray) -> np.ndarray:
@@ -226,11 +226,12 @@ class OracleStream:
                     self.window.pop(0)
         decision = None
         if cfg.sink_threshold is not None and entry.frame >= S and S > 0:
+            terms = similarity_terms(h, self.sink_embed)
             j, alpha, replace = decide(h, self.sink_embed, cfg.sink_threshold)
             if replace:
                 self.sinks[j] = copy.deepcopy(entry)
                 self.sink_embed[j] = h
             decision = {"step": self.step, "chunk": c0, "frame": entry.frame, "slot": j,
-                        "alpha": alpha, "replaced": replace}
+                        "alpha": alpha, "replaced": replace, "terms": terms}
             self.sink_log.append(decision)
         return decision

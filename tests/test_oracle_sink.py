@@ -100,3 +100,17 @@ def test_chunk_of_two_frames_decides_on_its_last_frame():
     for s in range(2, cfg.num_steps):
         np.testing.assert_allclose(outs[(s, 0, 0)], brute.history_output(cfg, s, 0, 0, sink_frames=[3]),
                                    atol=1e-12)
+
+
+def test_similarity_terms_on_hand_computed_vectors():
+    # h = (3, 4, 0), e0 = (4, 3, 0), e1 = (0, 0, 2), e2 = 0: h.h = 25, e.e = 25, 4, 0;
+    # h.e = 24, 0, 0; alpha = 24/25, 0 (orthogonal), 0 (zero norm).
+    h = np.array([3.0, 4.0, 0.0])
+    t = sink.similarity_terms(h, [np.array([4.0, 3.0, 0.0]), np.array([0.0, 0.0, 2.0]), np.zeros(3)])
+    assert t["hh"] == 25.0
+    assert t["ee"] == [25.0, 4.0, 0.0]
+    assert t["he"] == [24.0, 0.0, 0.0]
+    assert t["alphas"] == [24.0 / 25.0, 0.0, 0.0]
+    # a negative dot product: e = (-3, -4, 0) is antiparallel, alpha = -1 exactly
+    t2 = sink.similarity_terms(h, [np.array([-3.0, -4.0, 0.0])])
+    assert t2["he"] == [-25.0] and t2["alphas"] == [-1.0]
