@@ -6,31 +6,23 @@
 // [REPO] core components: ring-buffer KV cache with sliding-window attention); the walkthrough
 // ([WT] SLO-aware batching scheduler) names FlashAttention as the exact tiled evaluation of it.
 //
-// bf16 path (split-KV, flash-style):
-//  * workgroup = 4 waves x 32 query rows of one (element, head); grid = heads x splits x
-//    elements x query tiles, remapped so that the workgroups sharing one head's K/V run on one
-//    XCD (one L2);
-//  * K tile [64 keys][d] and V^T tile [d][64 keys] (V is stored transposed in the cache) are
-//    staged through LDS, double-buffered: the next tile's global loads are in flight while
-//    the current tile is consumed;
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K as the A operand from LDS, Q^T as the B
-//    operand held in registers for the whole kernel).  K rows are placed in LDS with bits 2
-//    and 3 of the key index swapped so that the accumulator layout of S^T is already the B
-//    operand layout of the P V product: every lane holds 8 consecutive keys of one query per
-//    16-key step, so P never leaves registers;
-//  * online softmax in base 2: one row max per 64-key tile (within the lane, then one lane
-//    swap across the two 32-lane halves), exponentials by v_exp_f32, row sums kept per lane
-//    and merged once at the end;
-//  * O^T += V^T P^T with the same MFMA (V^T rows from LDS as the A operand);
-//  * with several splits each workgroup writes (O/l, m, l) in fp32 and a combine kernel merges
-//    them by log-sum-exp weights; with one split the output is normalised and written in bf16.
-// fp32 path: a plain per-query-row kernel in fp32 (no reduced-precision matrix instructions).
+// Kernels here (the head_dim-128 bf16 and e4m3 cache kernel is in k_attention_w64.hip):
+//  * attn_bf16_kernel, bf16 cache with head_dim 64 (split-KV, flash-style): workgroup = 8 waves
+//    x 32 query rows of one (element, head); grid = heads x splits x elements x query tiles,
+//    remapped so that the workgroups sharing one head's K/V run on one XCD (one L2).  K tile
+//    [64 keys][d] and V^T tile [d][64 keys] (V is stored transposed in the cache) are staged
+//    through LDS, double-buffered.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K as the A
+//    operand from LDS, Q^T as the B operand held in registers); K rows sit in LDS with bits 2
+//    and 3 of the key index swapped so that the S^T accumulator layout is already the B
+//    operand layout of O^T += V^T P^T, and P never leaves registers.  Online softmax in base 2.
+//  * combine_kernel: merges the split-KV partials (bf16 O/l of each split, fp32 m and l) by
+//    log-sum-exp weights into the bf16 output.
+//  * attn_f32_kernel, fp32 cache: a plain per-query-row kernel in fp32 (no reduced-precision
+//    matrix instructions).
 #include "common.h"
 #include "attn_tiles.h"
 
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 namespace sdv2 {
 
@@ -44,15 +36,12 @@ namespace sdv2 {
 // LDS rings of two K and two V^T tiles: K(m+1) and V(m) stream in during phases 2m and 2m+1
 // (direct global->LDS loads issued by all waves at the start of phase 2m, awaited before the
 // barrier that ends phase 2m+1), into slots whose previous tiles were last read in phase 2m-1.
-// KV = kKvBF16: bf16 cache; kKvFP8: e4m3 cache (head_dim 128).  The e4m3 tiles land in a
-// staging area (each wave 1 KB of K and 1 KB of V^T, the bytes it loaded itself); once its
-// loads are in, the wave widens exactly those bytes to bf16 into the ring slots, so every
-// element is converted once per workgroup and the MFMA phase is the bf16 one.
-template <int D, int KV>
+// bf16 cache.  The 64-row kernel (k_attention_w64.hip) serves head_dim 128; this kernel serves
+// head_dim 64.
+template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
-  constexpr bool F8 = KV == kKvFP8;
-  constexpr int EB = F8 ? 1 : 2;              // bytes per cache element in HBM
+  constexpr int EB = 2;                       // bytes per cache element in HBM
   constexpr int KD = D / 16;                  // 16-wide k steps over d (QK)
   constexpr int DB = D / 32;                  // 32-row d blocks of O^T (PV)
   constexpr int KRB = D * 2;                  // bytes per K row in LDS (bf16)
@@ -64,25 +53,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   constexpr int KLD = KG_BYTES / 1024 / NW;   // 1 KB wave loads per wave per K tile
   constexpr int VLD = KLD;
   static_assert(KLD >= 1 && (D == 64 || D == 128), "head_dim 64 or 128");
-  static_assert(!F8 || (D == 128 && KLD == 1), "e4m3 cache: head_dim 128");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * K_BYTES + 2 * V_BYTES + (F8 ? 2 * KG_BYTES : 0)];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * K_BYTES + 2 * V_BYTES];
   char* const ldsK = lds;
   char* const ldsV = lds + 2 * K_BYTES;
-  char* const ldsS = lds + 2 * K_BYTES + 2 * V_BYTES;   // e4m3 staging: K, then V^T
-  // 16 e4m3 bytes -> the bf16 values of bytes 0-7 (lo) and 8-15 (hi), exactly
-#define SDV2_WIDEN(w_, lo_, hi_)                                                               \
-  do {                                                                                         \
-    const bf16x2 a0_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).x, 1.f, false);     \
-    const bf16x2 a1_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).x, 1.f, true);      \
-    const bf16x2 a2_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).y, 1.f, false);     \
-    const bf16x2 a3_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).y, 1.f, true);      \
-    const bf16x2 b0_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).z, 1.f, false);     \
-    const bf16x2 b1_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).z, 1.f, true);      \
-    const bf16x2 b2_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).w, 1.f, false);     \
-    const bf16x2 b3_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)(w_).w, 1.f, true);      \
-    lo_ = bf16x8{a0_.x, a0_.y, a1_.x, a1_.y, a2_.x, a2_.y, a3_.x, a3_.y};                      \
-    hi_ = bf16x8{b0_.x, b0_.y, b1_.x, b1_.y, b2_.x, b2_.y, b3_.x, b3_.y};                      \
-  } while (0)
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -157,38 +130,24 @@ void attn_bf16_kernel(const AttnArgs a) {
     }
   };
 
-  // Per-lane byte offsets of the tile fills (loop invariant).  bf16: LDS row R of a K tile
-  // holds key perm_key(R), its chunks placed by lds_chunk.  e4m3 (one 1 KB load per tile
-  // each): lane (row kr8, chunk kc8) of K, lane (row vr8, chunk vc8) of V^T, in lane order
-  // in the staging area.
-  const int kr8 = wave * 8 + (lane >> 3), kc8 = lane & 7;     // 8 rows of 128 bytes per wave
-  const int vr8 = wave * 16 + (lane >> 2), vc8 = lane & 3;    // 16 rows of 64 bytes per wave
+  // Per-lane byte offsets of the tile fills (loop invariant): LDS row R of a K tile holds key
+  // perm_key(R), its chunks placed by lds_chunk.
   uint32_t koff[KLD], voff[VLD];
 #pragma unroll
   for (int i = 0; i < KLD; ++i) {
     int R, c;
-    if constexpr (F8) {
-      R = kr8;
-      c = kc8;
-    } else {
-      lds_chunk_inv<KRB>((wave * KLD + i) * 64 + lane, R, c);
-    }
+    lds_chunk_inv<KRB>((wave * KLD + i) * 64 + lane, R, c);
     koff[i] = (uint32_t)(perm_key(R) * D * EB + c * 16);
   }
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
     int R, c;
-    if constexpr (F8) {
-      R = vr8;
-      c = vc8;
-    } else {
-      lds_chunk_inv<VRB>((wave * VLD + i) * 64 + lane, R, c);
-    }
+    lds_chunk_inv<VRB>((wave * VLD + i) * 64 + lane, R, c);
     voff[i] = (uint32_t)(R * a.Npad * EB + c * 16);
   }
-  char* const kdst = F8 ? ldsS : ldsK;
-  char* const vdst = F8 ? ldsS + KG_BYTES : ldsV;
-  constexpr int KDST = F8 ? 0 : K_BYTES, VDST = F8 ? 0 : V_BYTES;   // per ring slot
+  char* const kdst = ldsK;
+  char* const vdst = ldsV;
+  constexpr int KDST = K_BYTES, VDST = V_BYTES;   // per ring slot
   auto fill_k = [&](const TileCursor& c, int buf) {
     const char* src = c.kp;
 #pragma unroll
@@ -202,31 +161,6 @@ void attn_bf16_kernel(const AttnArgs a) {
     for (int i = 0; i < VLD; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(src + voff[i]),
                                        (lds_void*)(vdst + buf * VDST + (wave * VLD + i) * 1024), 16, 0, 0);
-  };
-  // e4m3: after this wave's loads are in, widen its staged bytes into ring slots kslot / vslot
-  // (-1: none).  An e4m3 chunk c = 2p + h of a row holds, in the cache's byte order, elements
-  // 32p + 8h + [0, 8) and 32p + 16 + 8h + [0, 8): bf16 chunks 4p + h and 4p + 2 + h.
-  auto widen_staged = [&](int kslot, int vslot) {
-    if constexpr (F8) {
-      if (kslot >= 0) {
-        const uint4 w = *(const uint4*)(ldsS + wave * 1024 + lane * 16);
-        bf16x8 lo, hi;
-        SDV2_WIDEN(w, lo, hi);
-        char* const kt = ldsK + kslot * K_BYTES;
-        const int p = kc8 >> 1, h = kc8 & 1;
-        *(bf16x8*)(kt + lds_chunk<KRB>(kr8, 4 * p + h)) = lo;
-        *(bf16x8*)(kt + lds_chunk<KRB>(kr8, 4 * p + 2 + h)) = hi;
-      }
-      if (vslot >= 0) {
-        const uint4 w = *(const uint4*)(ldsS + KG_BYTES + wave * 1024 + lane * 16);
-        bf16x8 lo, hi;
-        SDV2_WIDEN(w, lo, hi);
-        char* const vt = ldsV + vslot * V_BYTES;
-        const int p = vc8 >> 1, h = vc8 & 1;
-        *(bf16x8*)(vt + lds_chunk<VRB>(vr8, 4 * p + h)) = lo;
-        *(bf16x8*)(vt + lds_chunk<VRB>(vr8, 4 * p + 2 + h)) = hi;
-      }
-    }
   };
   // Per-lane LDS read offsets (loop invariant): one 16-byte chunk per fragment.
   int kro[KD], vro[4];
@@ -357,30 +291,22 @@ void attn_bf16_kernel(const AttnArgs a) {
   TileCursor kc = cursor_at(t_begin);         // K tile of the next loads
   TileCursor vc = kc;                         // V tile of the next loads
   TileCursor sc = kc;                         // tile of this wave's next VALU phase
-  int pend_k = -1, pend_v = -1;               // ring slots of this wave's loads in flight (e4m3)
   auto loads = [&](int m) {
     if (m + 1 <= last) {
       advance(kc);
       fill_k(kc, (m + 1) & 1);
-      pend_k = (m + 1) & 1;
     }
     if (m <= last) {
       fill_v(vc, m & 1);
-      pend_v = m & 1;
       if (m + 1 <= last) advance(vc);
     }
   };
-  // wait for this wave's loads; e4m3: widen them into their slots (before the barrier)
-  auto loads_in = [&]() {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    widen_staged(pend_k, pend_v);
-    pend_k = pend_v = -1;
-  };
+  // wait for this wave's loads (before the barrier that publishes them)
+  auto loads_in = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVm0); };
 
   // prologue: K(0) resident before phase 0; group B idles through phase 0 (it issues its
   // share of the phase-0 loads there)
   fill_k(kc, 0);
-  pend_k = 0;
   // V^T slot 1 is read by M(0) (with P = 0) before V(1) arrives: make it finite
 #pragma unroll
   for (int i = 0; i < V_BYTES / (512 * 16); ++i)
@@ -413,7 +339,6 @@ void attn_bf16_kernel(const AttnArgs a) {
 #undef SDV2_FRAG
 #undef SDV2_FRAG_MFMA
 #undef SDV2_MFMA_RUN
-#undef SDV2_WIDEN
 #undef SDV2_MFMA_PHASE
 
   // lane (g, r), accumulator v of o[i] holds O^T[d = 32i + 8(v/4) + 4g + v%4][query r]
@@ -582,32 +507,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
   for (int d = 0; d < D; ++d) op[d] = o[d] * inv;
 }
 
-// bf16 cache with head_dim 128 runs the 64-row kernel (k_attention_w64.hip) unless the
-// environment sets SDV2_ATTN_KERNEL=pingpong (read once per process).
-static bool use_w64() {
-  static const bool w64 = [] {
-    const char* e = getenv("SDV2_ATTN_KERNEL");
-    return !(e && strcmp(e, "pingpong") == 0);
-  }();
-  return w64;
-}
-
+// bf16 or e4m3 cache with head_dim 128: the 64-row kernel (k_attention_w64.hip); bf16 with
+// head_dim 64: the 32-row ping-pong kernel above; fp32: the per-row kernel.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s) {
-  if ((kv == kKvBF16 || kv == kKvFP8) && head_dim == 128 && use_w64()) return launch_attention_w64(a, kv, s);
-  if (kv != kKvF32) {
+  if (kv != kKvF32 && head_dim == 128) return launch_attention_w64(a, kv, s);
+  if (kv == kKvBF16 && head_dim == 64) {
     const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
-    if (kv == kKvFP8)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, kKvFP8>), dim3(grid), dim3(512), 0, s, a);
-    else if (head_dim == 128)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, kKvBF16>), dim3(grid), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, kKvBF16>), dim3(grid), dim3(512), 0, s, a);
-  } else {
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+  } else if (kv == kKvF32) {
     const int grid = a.nbatch * a.H * ((a.T * a.N + 63) / 64);
     if (head_dim == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(64), 0, s, a);
     else
       hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(64), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;             // e4m3 needs head_dim 128 (refused at validation)
   }
   return hipGetLastError();
 }
