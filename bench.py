@@ -8,9 +8,14 @@ tensors of the workload's shapes, generated before the timed region.
 
 Prints one JSON line.  `value` is the attention work of the step (algorithmic FLOPs,
 4 * nbatch * H * N * L * d per layer with L = (S + W + 1) * N keys) divided by the step time.
-`roofline` scores the attention call (split-KV kernel + combine) against the bf16 MFMA peak
-with its average duration measured by HIP events on the library's stream.  `cpu_baseline`
+`roofline` scores the attention call (split-KV kernel + combine) against the bf16 MFMA peak;
+its duration is the time of a batch of back-to-back attention calls, by HIP events on the
+library's stream, over the calls in the batch.  `hbm_kernels` scores the HBM-bound kernels
+(append, rebase, sink copy, split combine, motion reduction) against 8 TB/s.  `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the host cores.
+
+The default workload is the largest single-GPU one: the Wan-14B-shaped 40-layer stack with a
+stream batch of 4 and the sink refresh.
 """
 from __future__ import annotations
 
@@ -65,109 +70,201 @@ def workload_numbers(c):
     return {"keys": L, "flops_per_layer": flops_layer, "attn_bytes_per_layer": qo + shared + own}
 
 
-def run_gpu(c, steps, warmup, pool=2):
+def make_inputs(c, run, pool, seed=20261203):
+    """Seeded device-resident q, k, v of the workload's shapes: pool sets per layer."""
     import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    shape = (c.stream_batch, c.chunk_rows, c.num_heads, c.head_dim)
+    return [[tuple((torch.randn(shape, generator=g, device="cuda") *
+                    (c.q_prescale if j == 0 else 1.0)).to(run.dtype) for j in range(3))
+             for _ in range(c.num_layers)] for _ in range(pool)]
 
-    from rolling_kv_causal_amd import sdv2
-    from rolling_kv_causal_amd.stream import StreamRunner
-    from synth import inputs
 
-    torch.cuda.set_device(0)
-    dev = "cuda"
-    cfg = sdv2.config_of(c)
-    big = 1 << 40                                  # an unbounded stream: steady state throughout
-    run = StreamRunner(cfg, big, c.softmax_scale)
-    dt = run.dtype
-    B, N, H, D, Lyr = c.stream_batch, c.tokens, c.num_heads, c.head_dim, c.num_layers
-    g = torch.Generator(device=dev)
-    g.manual_seed(20261203)
-    shape = (B, c.chunk_rows, H, D)
-    sets = [[tuple((torch.randn(shape, generator=g, device=dev) *
-                    (c.q_prescale if j == 0 else 1.0)).to(dt) for j in range(3))
-             for _ in range(Lyr)] for _ in range(pool)]
-    embeds = None
-    if c.embed_dim > 0:
-        embeds = torch.stack([torch.from_numpy(inputs.chunk_embedding(c, i)) for i in range(c.num_chunks)]).to(dev)
-    motion = None
-    if c.motion is not None:
-        m = c.motion
-        frames = torch.from_numpy(inputs.motion_frames(c)).to(dev)
-        dist = torch.empty(m.frames, dtype=torch.float64, device=dev)
-        mws = torch.empty(sdv2.sdv2_motion_workspace_size(2, m.elems), dtype=torch.uint8, device=dev)
-        motion = (frames, dist, mws, m)
+class Stepper:
+    """One stream of the workload over device-resident inputs; steps of the whole hot path."""
 
-    events = {}
+    def __init__(self, c, pool=2):
+        import torch
 
-    def ev_pair(name):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        events.setdefault(name, []).append((a, b))
-        return a, b
+        from rolling_kv_causal_amd.stream import StreamRunner
+        from synth import inputs
+        self.c = c
+        self.run = StreamRunner(self._cfg(c), 1 << 40, c.softmax_scale)   # unbounded: steady state
+        self.sets = make_inputs(c, self.run, pool)
+        self.embeds = None
+        if c.embed_dim > 0:
+            self.embeds = torch.stack([torch.from_numpy(inputs.chunk_embedding(c, i))
+                                       for i in range(c.num_chunks)]).cuda()
+        self.frames = None
+        if c.motion is not None:
+            self.frames = torch.from_numpy(inputs.motion_frames(c)).cuda()
+        self.stats = torch.empty(4 + 2 * c.sink_frames, dtype=torch.float64, device="cuda")
+        self.s = 0
 
-    def one_step(s, timed_parts=False):
-        first, nb, commit, newest = run.plan(s)
-        st = sets[s % pool]
-        if timed_parts:
-            a, b = ev_pair("refresh"); a.record()
+    @staticmethod
+    def _cfg(c):
+        from rolling_kv_causal_amd import sdv2
+        return sdv2.config_of(c)
+
+    def step(self, ev=None, attn_repeat=1):
+        """One step.  ev: dict of event pairs to record around the append batch, the attention
+        batch (all layers back to back, each call repeated attn_repeat times), the refresh and
+        the end-of-step chunk statistics / sink refresh.  Without ev, append and attention
+        alternate per layer as in a DiT forward."""
+        c, run = self.c, self.run
+        first, nb, commit, newest = run.plan(self.s)
+        st = self.sets[self.s % len(self.sets)]
+        mark = (lambda k, i: ev[k][i].record()) if ev else (lambda k, i: None)
+        mark("refresh", 0)
         run.cache.refresh(newest)
-        if timed_parts:
-            b.record()
-        for layer in range(Lyr):
-            q, k, v = st[layer]
-            if timed_parts:
-                a, b = ev_pair("append"); a.record()
-            run.cache.append(layer, first, nb, q[:nb], k[:nb], v[:nb])
-            if timed_parts:
-                b.record(); a, b = ev_pair("attention"); a.record()
-            run.cache.attention(layer, nb, q[:nb], run.out[layer, :nb], run.scale)
-            if timed_parts:
-                b.record()
+        mark("refresh", 1)
+        if ev:
+            mark("append", 0)
+            for layer in range(c.num_layers):
+                q, k, v = st[layer]
+                run.cache.append(layer, first, nb, q[:nb], k[:nb], v[:nb])
+            mark("append", 1)
+            mark("attention", 0)
+            for layer in range(c.num_layers):
+                for _ in range(attn_repeat):
+                    run.cache.attention(layer, nb, st[layer][0][:nb], run.out[layer, :nb], run.scale)
+            mark("attention", 1)
+        else:
+            for layer in range(c.num_layers):
+                q, k, v = st[layer]
+                run.cache.append(layer, first, nb, q[:nb], k[:nb], v[:nb])
+                run.cache.attention(layer, nb, q[:nb], run.out[layer, :nb], run.scale)
         if commit >= 0:
-            if timed_parts:
-                a, b = ev_pair("commit"); a.record()
             run.cache.commit(commit)
-            if timed_parts:
-                b.record()
-            if embeds is not None:
-                if timed_parts:
-                    a, b = ev_pair("sink_replace"); a.record()
-                last = (commit + 1) * c.chunk_frames - 1          # the chunk's last frame
-                run.cache.sink_replace(last, embeds[commit % len(embeds)], sync=False)
-                if timed_parts:
-                    b.record()
-            if motion is not None:
-                frames, dist, mws, m = motion
-                t = 1 + commit % (m.frames - 1)
-                if timed_parts:
-                    a, b = ev_pair("motion"); a.record()
-                sdv2.sdv2_motion_l2(frames[t - 1:t + 1], 2, m.elems, dist, mws)
-                if timed_parts:
-                    b.record()
+            last = (commit + 1) * c.chunk_frames - 1            # the chunk's last frame
+            e = self.embeds[commit % len(self.embeds)] if self.embeds is not None else None
+            prev = cur = None
+            if self.frames is not None:
+                t = 1 + last % (len(self.frames) - 1)
+                prev, cur = self.frames[t - 1], self.frames[t]
+            if e is not None or cur is not None:
+                mark("stats", 0)
+                run.cache.sink_replace(last, e, prev, cur, self.stats, sync=False)
+                mark("stats", 1)
+        self.s += 1
 
-    fill = c.sink_frames + c.window_frames + B + 1
-    s = 0
+
+def events(names):
+    import torch
+    return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+
+
+def run_gpu(c, steps, warmup):
+    """Whole-step time, then a pass with events around batched calls (per-kernel figures)."""
+    import torch
+    torch.cuda.set_device(0)
+    st = Stepper(c)
+    fill = c.sink_frames + c.window_frames + c.stream_batch + 1
     for _ in range(fill + warmup):
-        one_step(s)
-        s += 1
+        st.step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for _ in range(steps):
-        one_step(s)
-        s += 1
+        st.step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / steps
-    # second pass: per-call durations by HIP events on the same stream
-    for _ in range(steps):
-        one_step(s, timed_parts=True)
-        s += 1
+    # batched pass: events around the append batch and the attention batch of each step; a
+    # single-layer workload repeats its attention call so that a batch holds several calls
+    repeat = max(1, 8 // c.num_layers)
+    names = ("refresh", "append", "attention", "stats")
+    acc = {n: [] for n in names}
+    npass = max(3, min(10, steps // 2))
+    for _ in range(npass):
+        ev = events(names)
+        st.step(ev, attn_repeat=repeat)
+        torch.cuda.synchronize()
+        for n in names:
+            a, b = ev[n]
+            if a.query() and b.query():
+                try:
+                    acc[n].append(a.elapsed_time(b))
+                except RuntimeError:          # the pair was not recorded this step
+                    pass
+    med = lambda v: sorted(v)[len(v) // 2] if v else None
+    attn_ms = med(acc["attention"])
+    return {"ms_per_step": ms_step, "wall_s": wall,
+            "attention_us": attn_ms * 1e3 / (c.num_layers * repeat), "attention_calls_per_batch": c.num_layers * repeat,
+            "append_us": med(acc["append"]) * 1e3 / c.num_layers,
+            "stats_us": None if not acc["stats"] else med(acc["stats"]) * 1e3,
+            "refreshes": st.run.cache.state()[2]}
+
+
+def hbm_side_runs(c, append_us):
+    """HBM-bound kernels at the workload's shape, each scored on 8 TB/s:
+    rope_append from the batched pass; rebase and sink copy in a side stream of the same shape
+    with a refresh every frame (every cached key rebased each step) and, where the workload has
+    chunk embeddings, a threshold every cosine is below (every commit replaces a sink); the
+    motion reduction over 1025 latent frames of 16x60x104."""
+    import torch
+
+    from rolling_kv_causal_amd import sdv2
+    out = {}
+    eb = 2 if c.dtype == "bf16" else 4
+    kb = 1 if c.kv_fp8 else eb
+    tensor = c.stream_batch * c.chunk_rows * c.num_heads * c.head_dim
+    def entry(nbytes, us, note):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"bytes_per_call": int(nbytes), "us": round(us, 3), "gbs": round(gbs, 1),
+                "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "how": note}
+    # append: q, k, v read, q rotated back, k_rot and v^T written
+    out["rope_append"] = entry(3 * tensor * eb + tensor * eb + 2 * tensor * kb, append_us,
+                               "events around all layers' appends of a step, per layer")
+    side = c.with_(rope_refresh_period=1, name=c.name + "_side",
+                   sink_threshold=(2.0 if c.embed_dim > 0 else None))
+    st = Stepper(side, pool=1)
+    fill = c.sink_frames + c.window_frames + c.stream_batch + 1
+    for _ in range(fill):
+        st.step()
     torch.cuda.synchronize()
-    parts = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) * 1e3 for k, v in events.items()}
-    counts = {k: len(v) for k, v in events.items()}
-    return {"ms_per_step": ms_step, "wall_s": wall, "part_us": parts, "part_calls": counts,
-            "refreshes": run.cache.state()[2]}
+    reb, stats = [], []
+    for _ in range(5):
+        ev = events(("refresh", "append", "attention", "stats"))
+        st.step(ev)
+        torch.cuda.synchronize()
+        reb.append(ev["refresh"][0].elapsed_time(ev["refresh"][1]))
+        if c.embed_dim > 0:
+            stats.append(ev["stats"][0].elapsed_time(ev["stats"][1]))
+    N = c.tokens
+    nslots = c.sink_frames + c.window_frames
+    pairs_bytes = c.num_layers * nslots * c.num_heads * N * c.rope_dim_t * kb
+    out["rebase"] = entry(2 * pairs_bytes, sorted(reb)[2] * 1e3,
+                          "refresh with T_reset = 1: every cached key's temporal pairs turned each step")
+    if c.embed_dim > 0:
+        L = sdv2.sdv2_cache_layout(Stepper._cfg(c))
+        slot_bytes = L.slot_stride * L.elem_bytes
+        out["sink_copy"] = entry(2 * 2 * c.num_layers * slot_bytes, sorted(stats)[2] * 1e3,
+                                 "sdv2_sink_replace with every cosine below tau: statistics, decision and "
+                                 "the copy of K and V of one frame into the sink, all layers")
+    del st
+    torch.cuda.empty_cache()
+    # motion reduction over 1025 frames of the 480p latent shape
+    n = 16 * 60 * 104
+    F = 1025
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    frames = torch.randn((F, n), generator=g, device="cuda")
+    dist = torch.empty(F - 1, dtype=torch.float64, device="cuda")
+    ws = torch.empty(sdv2.sdv2_motion_workspace_size(F, n), dtype=torch.uint8, device="cuda")
+    sdv2.sdv2_motion_l2(frames, F, n, dist, ws)
+    ev = events(("m",))
+    ev["m"][0].record()
+    for _ in range(5):
+        sdv2.sdv2_motion_l2(frames, F, n, dist, ws)
+    ev["m"][1].record()
+    torch.cuda.synchronize()
+    out["motion_1025_frames"] = entry(F * n * 4, ev["m"][0].elapsed_time(ev["m"][1]) * 1e3 / 5,
+                                      "sdv2_motion_l2 over 1025 frames of 16x60x104 fp32, mean of 5 calls")
+    return out
 
 
 def cpu_baseline(c, budget_s=12.0):
@@ -208,17 +305,27 @@ def cpu_baseline(c, budget_s=12.0):
                       f"{L} keys (layer 0, element 0, steady-state step {steady}), {t_used:.1f} s"}
 
 
+def profile_fields(stem: str):
+    """key: value lines of a committed rocprofv3 summary (profiles/<stem>.md), or None when it is
+    missing or the attention sources changed since it was taken."""
+    p = ROOT / "profiles" / f"{stem}.md"
+    if not p.exists():
+        return None
+    fields = {}
+    for ln in p.read_text().splitlines():
+        if ":" in ln and not ln.startswith(("|", "#", " ", "`")) and ln.split(":", 1)[0].replace("_", "").isalnum():
+            k, v = ln.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("attn_sources_sha256_16", "") != attn_source_hash():
+        return None
+    return fields
+
+
 def load_traffic(workload: str):
     """HBM bytes per attention call (kernel + combine) from the committed rocprofv3 counter
     summary, or None when there is none or the kernel source changed since it was taken."""
-    p = ROOT / "profiles" / f"attn_traffic_{workload}.md"
-    if not p.exists():
-        return None
-    fields = dict(ln.split(":", 1) for ln in p.read_text().splitlines()
-                  if ln.startswith(("bytes_per_call:", "attn_sources_sha256_16:")))
-    if fields.get("attn_sources_sha256_16", "").strip() != attn_source_hash():
-        return None
-    return int(fields["bytes_per_call"].strip())
+    f = profile_fields(f"attn_traffic_{workload}")
+    return None if not f or "bytes_per_call" not in f else int(f["bytes_per_call"])
 
 
 def calibration_copy(nbytes=1 << 30):
@@ -258,8 +365,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="wan13b_512_1layer")
+    ap.add_argument("--workload", default="wan14b_512_40layer_b4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the HBM-bound kernels' side runs")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a 1 GiB plain copy first (scales HBM counters in rocprofv3 runs)")
     ap.add_argument("--slo-table", action="store_true",
@@ -293,13 +401,27 @@ def main():
     if args.calibration_copy:
         calibration_copy()
     g = run_gpu(c, args.steps, args.warmup)
+    log(f"bench: {g['ms_per_step']:.4f} ms/step, attention call {g['attention_us']:.2f} us")
     ms = g["ms_per_step"]
     step_flops = wn["flops_per_layer"] * c.num_layers
     value = step_flops / (ms * 1e-3) / 1e12
-    attn_us = g["part_us"]["attention"]
+    attn_us = g["attention_us"]
     achieved = wn["flops_per_layer"] / (attn_us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if c.dtype == "bf16" else PEAK_FP32_TFLOPS
+    prof = profile_fields(f"attn_trace_{c.name}")
     traffic = load_traffic(c.name)
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": "sdv2_chunk_attention (%s + combine_kernel)"
+                      % ("attn_w64_kernel<e4m3 cache>" if c.kv_fp8 and c.head_dim == 128 else
+                         "attn_w64_kernel" if c.dtype == "bf16" and c.head_dim == 128 else
+                         "attn_bf16_kernel" if c.dtype == "bf16" else "attn_f32_kernel"),
+            "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3),
+            "timing": f"HIP events on the library's stream around {g['attention_calls_per_batch']} back-to-back "
+                      "attention calls per step (median of the batched steps)"}
+    if prof:
+        roof["profile_call_us"] = prof.get("call_us")
+        roof["profile_kernel_us"] = prof.get("kernel_us")
     out = {
         "metric": "sink+rolling-KV chunk attention TFLOP/s & HBM GB/s, % of roofline, 1 GPU",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -312,20 +434,24 @@ def main():
                    "rope_refresh_period": c.rope_refresh_period, "rope_pin_sinks": c.rope_pin_sinks,
                    "kv_cache": "e4m3" if c.kv_fp8 else c.dtype,
                    "sink_threshold": c.sink_threshold, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "sdv2_chunk_attention (%s + combine_kernel)"
-                               % ("attn_w64_kernel<e4m3 cache>" if c.kv_fp8 and c.head_dim == 128 else
-                                  "attn_w64_kernel" if c.dtype == "bf16" and c.head_dim == 128 else
-                                  "attn_bf16_kernel"),
-                     "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3)},
+        "roofline": roof,
         "chunk_attention_calls_per_s": round(c.num_layers / (ms * 1e-3), 1),
         "latent_frames_per_s": round(c.chunk_frames / (ms * 1e-3), 2),
         "attention_hbm_gbs": round(wn["attn_bytes_per_layer"] / (attn_us * 1e-6) / 1e9, 1),
-        "per_call_us": {k: round(v, 3) for k, v in g["part_us"].items()},
-        "calls_per_step": {k: round(v / args.steps, 3) for k, v in g["part_calls"].items()},
+        "append_us_per_layer": round(g["append_us"], 3),
+        "stats_sink_us_per_step": None if g["stats_us"] is None else round(g["stats_us"], 3),
         "wall_s_timed": round(g["wall_s"], 4),
     }
+    if not args.no_hbm:
+        log("bench: HBM-bound kernels at the workload's shape")
+        hbm = hbm_side_runs(c, g["append_us"])
+        if prof and prof.get("combine_us") and prof.get("combine_bytes"):
+            us, nb = float(prof["combine_us"]), float(prof["combine_bytes"])
+            hbm["combine"] = {"bytes_per_call": int(nb), "us": us, "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                              "how": f"rocprofv3 kernel trace, profiles/attn_trace_{c.name}.md "
+                                     f"({prof.get('nsplit')} split partials read, output written)"}
+        out["hbm_kernels"] = hbm
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline(c)

@@ -173,9 +173,7 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
  * Q_rot = d_q_rot as rotated by sdv2_cache_append; inside the own chunk a query of frame t sees
  * the keys of frames 0..t (block-causal).  d_out: [nbatch][T'N][H][d], written.  The
  * workspace given at create time is used for split-KV partial results (calls on one cache
- * must not overlap in time).  With a bf16 or e4m3 cache and head_dim 128 the 64-query-row
- * kernel runs; the environment variable SDV2_ATTN_KERNEL=pingpong (read once per process)
- * selects the 32-row kernel, whose results agree up to fp32 summation order.  The split-KV
+ * must not overlap in time).  The split-KV
  * count follows a cost model; SDV2_NSPLIT=n (read at create and at each call; clamped to
  * [1, 16] and to the shortest walk) forces it, for tests and tuning: the cache must be created
  * with the variable set, so that the workspace covers the forced count. */
@@ -189,19 +187,33 @@ int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const
  * `stream`. */
 int sdv2_cache_commit(sdv2_cache* cache, int64_t chunk, void* stream);
 
-/* Adaptive sink refresh after a commit ([WT] adaptive sink and RoPE refresh).  `frame` is the
- * last frame of the committed chunk.  d_embed: fp32 [embed_dim] chunk embedding h (device).
- * Every frame of the chunk below S became a sink and gets h as its embedding.  Then, if
- * frame >= S and tau is on: alpha_j = cos(h, e_j) for j < S (fp64; 0 if a norm is 0), j* =
- * argmin (lowest j on ties); if alpha_j* < tau frame `frame`'s K/V are copied into sink j* for
- * all layers and e_j* = h.  The decision is taken on the device.  If h_slot is
- * non-NULL the call synchronises `stream` and returns j* if replaced, else -1 (h_alpha, may be
- * NULL: alpha_j*); with h_slot NULL nothing synchronises and sdv2_cache_slot_info reports the
- * sink slots as unknown (-2) from then on. */
-int sdv2_sink_replace(sdv2_cache* cache, int64_t frame, const float* d_embed, int32_t* h_slot,
-                      double* h_alpha, void* stream);
+/* Chunk statistics and adaptive sink refresh after a commit, one fused statistics launch
+ * ([WT] adaptive sink and RoPE refresh; [WT] motion-aware noise scheduler and [NEWS] algorithm
+ * item 2: the distance between consecutive latent frames drives the noise rate).  `frame` is the
+ * last frame of the committed chunk.
+ *  - d_embed: fp32 [embed_dim] chunk embedding h (device); required when embed_dim >= 1, NULL
+ *    otherwise.  Every frame of the chunk below S became a sink and gets h as its embedding.
+ *  - d_prev_latent, d_cur_latent: fp32 [latent_elems] latent frames x_{t-1}, x_t (device), both
+ *    or neither (NULL: no motion term).
+ *  - One launch reduces, in fp64 and a fixed order, sum_i (x_t[i] - x_{t-1}[i])^2 and h.h,
+ *    e_j.e_j, h.e_j for the S sinks; a one-block launch then forms the statistics and the
+ *    decision: if frame >= S and tau is on, alpha_j = cos(h, e_j) (0 if a norm is 0), j* = argmin
+ *    (lowest j on ties), and if alpha_j* < tau frame `frame`'s K/V are copied into sink j* for
+ *    all layers and e_j* = h.  A sink stored by this call has e_j = h in the decision.
+ *  - d_stats (device, may be NULL): fp64 [4 + 2S] = { sum (dx)^2, sqrt(sum (dx)^2 /
+ *    latent_elems), h.h, e_0.e_0 .. e_{S-1}.e_{S-1}, h.e_0 .. h.e_{S-1}, alpha_j* }, NaN for a
+ *    term not computed (no latents, no embedding, no decision).  8-byte aligned.
+ * The decision stays on the device.  If h_slot is non-NULL and a decision is taken the call
+ * synchronises `stream` and returns j* if replaced, else -1 (h_alpha, may be NULL: alpha_j*);
+ * with h_slot NULL nothing synchronises and sdv2_cache_slot_info reports the sink slots as
+ * unknown (-2) from then on.  With no embedding, no latents and d_stats NULL nothing is launched
+ * (the call only closes the step). */
+int sdv2_sink_replace(sdv2_cache* cache, int64_t frame, const float* d_embed,
+                      const float* d_prev_latent, const float* d_cur_latent, int64_t latent_elems,
+                      double* d_stats, int32_t* h_slot, double* h_alpha, void* stream);
 
-/* Motion estimate ([NEWS] algorithm item 2; [WT] motion-aware noise scheduler): for t = 1 ..
+/* Batched motion estimate over a stored series ([NEWS] algorithm item 2; [WT] motion-aware
+ * noise scheduler; the per-step form is the motion term of sdv2_sink_replace): for t = 1 ..
  * nframes-1, d_dist[t-1] = sqrt(sum_i (x_t[i] - x_{t-1}[i])^2 / elems_per_frame), summed in fp64
  * in a fixed order.  d_frames: fp32 [nframes][elems_per_frame]; d_dist: fp64 [nframes-1];
  * d_workspace: at least sdv2_motion_workspace_size() bytes.  Stateless. */
@@ -252,6 +264,12 @@ int sdv2_cache_state(const sdv2_cache* cache, int64_t* rope_base, int64_t* commi
  * frame, the last frame of the newest chunk (-1 past the end).  Host only. */
 int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int64_t* first_chunk,
                    int32_t* nbatch, int64_t* commit_chunk, int64_t* newest_frame);
+
+/* Fault injection for tests of the error paths: the nth HIP runtime call or kernel launch the
+ * library makes from now on (0 = the next one) is not issued and its entry point returns
+ * SDV2_EHIP, as a failing launch would; nth < 0 disarms.  Process-wide; fires once.  An entry
+ * point whose first launch fails this way has launched nothing and changed no state. */
+int sdv2_debug_fail_hip_call(int32_t nth);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* sdv2_last_error(void);

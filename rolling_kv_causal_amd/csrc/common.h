@@ -6,12 +6,12 @@
 
 namespace sdv2 {
 
-constexpr int kMaxShared = 64;   // S + W
+constexpr int kMaxShared = 64;   // S + W + T'
 constexpr int kMaxBatch = 8;     // B
 constexpr int kMaxSinks = 16;    // S
 constexpr int kMaxTPairs = 32;   // temporal RoPE pairs
 constexpr int kTileKeys = 64;    // key tile; tokens are padded to a multiple of it
-constexpr int kQTile = 256;      // query rows per attention workgroup (8 waves x 32)
+constexpr int kQTile = 256;      // query rows per attention workgroup (4 waves x 64, or 8 x 32 at d = 64)
 constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -123,14 +123,41 @@ struct CopyArgs {
   int L;
 };
 
+// Fused chunk statistics ([NEWS] algorithm item 2 and [WT] motion-aware noise scheduler: the
+// distance between consecutive latent frames; [WT] adaptive sink and RoPE refresh: cosine
+// similarity of the chunk embedding against the sinks).  Pass 1, many blocks: per block the
+// fp64 partial sums of sum (cur - prev)^2 over a range of latent elements and of h.h, e_j.e_j,
+// h.e_j over a range of embedding elements.  Pass 2, one block: the partials summed in block
+// order, the statistics, the replacement decision and the embedding stores.
+constexpr int kStatsQ = 2 + 2 * kMaxSinks;   // per block: motion, h.h, e_j.e_j, h.e_j
+constexpr int kStatsMaxBlocks = 256;
+constexpr int kStatsLatPerBlock = 8192;      // latent elements per block (at least)
+constexpr int kStatsEmbPerBlock = 1024;      // embedding elements per block (at least)
+
+struct StatsArgs {
+  const float* prev;       // [n_lat] previous latent frame (n_lat = 0: no motion term)
+  const float* cur;        // [n_lat] newest latent frame
+  int64_t n_lat;
+  int64_t lat_per_block;   // multiple of 4
+  const float* h;          // [D] chunk embedding (D = 0: no similarity terms)
+  const float* embeds;     // [S][D] sink embeddings
+  int S, D, emb_per_block;
+  double* part;            // [gridDim.x][kStatsQ] partial sums
+};
+
 struct SinkArgs {
-  const float* h;          // [D] new chunk embedding
+  const double* part;      // [blocks][kStatsQ] from the stats pass
+  int blocks;
+  int64_t n_lat;
+  const float* h;          // [D] chunk embedding
   float* embeds;           // [S][D] sink embeddings
+  int S, D;
+  int store_lo, store_hi;  // sinks [store_lo, store_hi) take h as their embedding (chunk frames below S)
+  int decide;              // 1: take the replacement decision (frame >= S, tau on)
+  double tau;
   int32_t* decision;       // [0] = replaced slot or -1
   double* alpha;           // [0] = alpha of the least similar sink
-  int S, D;
-  int store_slot;          // >= 0: store h as that sink's embedding, no decision
-  double tau;
+  double* stats;           // [4 + 2S] caller's statistics, or nullptr
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------------------------
@@ -140,6 +167,7 @@ hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s);   // 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_rebase(const RebaseArgs& a, int head_dim, int kv, hipStream_t s);
 hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s);
+hipError_t launch_chunk_stats(const StatsArgs& a, int blocks, hipStream_t s);
 hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s);
 hipError_t launch_motion(const float* frames, int nframes, int64_t elems, double* dist,
                          double* partials, int parts, hipStream_t s);

@@ -1,5 +1,6 @@
-// Cache maintenance kernels: slot copies (commit, sink replacement), RoPE rebase, the sink
-// similarity decision and the per-frame motion reduction.
+// Cache maintenance kernels: the sink-replacement copy, the RoPE rebase, the fused chunk
+// statistics (motion distance and sink similarity) with the sink decision, and the batched
+// motion reduction.
 #include "common.h"
 
 #include <math.h>
@@ -7,9 +8,10 @@
 namespace sdv2 {
 
 // ---- slot copy: K and V of one slot into another, every layer --------------------------------
-// Commit ([NEWS] algorithm item 1, [REPO] ring-buffer KV cache): the finished element's staged
-// frame enters slot S + f mod W (or sink slot f).  Sink replacement ([WT] adaptive sink and RoPE
-// refresh): the committed frame enters the chosen sink slot, read from the device decision.
+// Sink replacement ([WT] adaptive sink and RoPE refresh): the committed frame's K and V (in its
+// ring slot) enter the chosen sink slot, read from the device decision; nothing is copied when
+// the decision is -1.  (The commit itself moves no data: the append wrote element 0's frames to
+// the ring slots they keep.)
 __global__ __launch_bounds__(256) void copy_slots_kernel(const CopyArgs a) {
   int dst = a.dst_slot;
   if (a.dst_from != nullptr) {
@@ -93,66 +95,133 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// ---- sink decision ------------------------------------------------------------------------------
-// [WT] adaptive sink and RoPE refresh: cosine similarity of the new chunk embedding against each
-// sink's embedding, in fp64 with a fixed reduction order; the least similar sink (lowest index on
-// ties; similarity 0 when a norm is 0) is replaced when its similarity is below tau.  One block.
-__global__ __launch_bounds__(256) void sink_decide_kernel(const SinkArgs a) {
-  __shared__ double red[4][1 + 2 * kMaxSinks];
-  __shared__ int dec;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (a.store_slot >= 0) {
-    for (int i = tid; i < a.D; i += 256) a.embeds[(int64_t)a.store_slot * a.D + i] = a.h[i];
-    if (tid == 0) {
-      a.decision[0] = -1;
-      a.alpha[0] = 1.0;
-    }
-    return;
-  }
-  double hh = 0.0, ee[kMaxSinks], he[kMaxSinks];
+// ---- fused chunk statistics, pass 1 -----------------------------------------------------------
+// Per block: sum (cur - prev)^2 over latent elements [b*lpb, (b+1)*lpb) and h.h, e_j.e_j, h.e_j
+// over embedding elements [b*epb, (b+1)*epb), all in fp64, reduced in a fixed order (lane
+// strides, a butterfly inside each wave, then the four waves in order).
+template <bool VEC4>
+__global__ __launch_bounds__(256) void chunk_stats_kernel(const StatsArgs a) {
+  __shared__ double red[4][kStatsQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  double mo = 0.0, hh = 0.0, ee[kMaxSinks], he[kMaxSinks];
 #pragma unroll
   for (int j = 0; j < kMaxSinks; ++j) { ee[j] = 0.0; he[j] = 0.0; }
-  for (int i = tid; i < a.D; i += 256) {
-    const double x = a.h[i];
-    hh = fma(x, x, hh);
-#pragma unroll
-    for (int j = 0; j < kMaxSinks; ++j)
-      if (j < a.S) {
-        const double e = a.embeds[(int64_t)j * a.D + i];
-        ee[j] = fma(e, e, ee[j]);
-        he[j] = fma(x, e, he[j]);
+  if (a.n_lat > 0) {
+    const int64_t lo = (int64_t)b * a.lat_per_block;
+    const int64_t hi = lo + a.lat_per_block < a.n_lat ? lo + a.lat_per_block : a.n_lat;
+    if constexpr (VEC4) {
+#pragma unroll 2
+      for (int64_t i = lo + 4 * tid; i < hi; i += 4 * 256) {
+        const float4 x = *(const float4*)(a.cur + i), y = *(const float4*)(a.prev + i);
+        const double d0 = (double)x.x - (double)y.x, d1 = (double)x.y - (double)y.y;
+        const double d2 = (double)x.z - (double)y.z, d3 = (double)x.w - (double)y.w;
+        mo = fma(d0, d0, mo);
+        mo = fma(d1, d1, mo);
+        mo = fma(d2, d2, mo);
+        mo = fma(d3, d3, mo);
       }
+    } else {
+      for (int64_t i = lo + tid; i < hi; i += 256) {
+        const double d = (double)a.cur[i] - (double)a.prev[i];
+        mo = fma(d, d, mo);
+      }
+    }
   }
+  if (a.D > 0) {
+    const int lo = b * a.emb_per_block;
+    const int hi = lo + a.emb_per_block < a.D ? lo + a.emb_per_block : a.D;
+#pragma unroll 4
+    for (int i = lo + tid; i < hi; i += 256) {
+      const double x = a.h[i];
+      hh = fma(x, x, hh);
+#pragma unroll
+      for (int j = 0; j < kMaxSinks; ++j)
+        if (j < a.S) {
+          const double e = a.embeds[(int64_t)j * a.D + i];
+          ee[j] = fma(e, e, ee[j]);
+          he[j] = fma(x, e, he[j]);
+        }
+    }
+  }
+  mo = wave_sum(mo);
   hh = wave_sum(hh);
 #pragma unroll
   for (int j = 0; j < kMaxSinks; ++j)
     if (j < a.S) { ee[j] = wave_sum(ee[j]); he[j] = wave_sum(he[j]); }
   if (lane == 0) {
-    red[wave][0] = hh;
+    red[wave][0] = mo;
+    red[wave][1] = hh;
 #pragma unroll
     for (int j = 0; j < kMaxSinks; ++j)
-      if (j < a.S) { red[wave][1 + j] = ee[j]; red[wave][1 + kMaxSinks + j] = he[j]; }
+      if (j < a.S) { red[wave][2 + j] = ee[j]; red[wave][2 + kMaxSinks + j] = he[j]; }
+  }
+  __syncthreads();
+  const int q = tid;   // quantity: 0 motion, 1 h.h, 2 + j e_j.e_j, 2 + kMaxSinks + j h.e_j
+  const bool used = q < 2 || (q >= 2 && q < 2 + a.S) || (q >= 2 + kMaxSinks && q < 2 + kMaxSinks + a.S);
+  if (q < kStatsQ && used)
+    a.part[(int64_t)b * kStatsQ + q] = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
+}
+
+hipError_t launch_chunk_stats(const StatsArgs& a, int blocks, hipStream_t s) {
+  const bool vec4 = a.n_lat > 0 && (a.n_lat % 4 == 0) && (((uintptr_t)a.prev | (uintptr_t)a.cur) & 15) == 0;
+  if (vec4)
+    hipLaunchKernelGGL(chunk_stats_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(chunk_stats_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- fused chunk statistics, pass 2: statistics, sink decision, embedding stores ---------------
+// [WT] adaptive sink and RoPE refresh: cosine similarity of the new chunk embedding against each
+// sink's embedding; the least similar sink (lowest index on ties; similarity 0 when a norm is 0)
+// is replaced when its similarity is below tau.  A sink stored by this call (a chunk frame below
+// S) has h as its embedding.  One block.
+__global__ __launch_bounds__(256) void sink_decide_kernel(const SinkArgs a) {
+  __shared__ double tot[kStatsQ];
+  __shared__ int dec;
+  const int tid = threadIdx.x;
+  if (tid < kStatsQ) {
+    double sum = 0.0;
+    for (int b = 0; b < a.blocks; ++b) sum += a.part[(int64_t)b * kStatsQ + tid];
+    tot[tid] = sum;
   }
   __syncthreads();
   if (tid == 0) {
-    const double h2 = ((red[0][0] + red[1][0]) + red[2][0]) + red[3][0];
+    const double nan = __builtin_nan("");
+    const double h2 = tot[1];
     int best = -1;
-    double best_alpha = 0.0;
-    for (int j = 0; j < a.S; ++j) {
-      const double e2 = ((red[0][1 + j] + red[1][1 + j]) + red[2][1 + j]) + red[3][1 + j];
-      const double he2 = ((red[0][1 + kMaxSinks + j] + red[1][1 + kMaxSinks + j]) +
-                          red[2][1 + kMaxSinks + j]) + red[3][1 + kMaxSinks + j];
-      const double al = (h2 == 0.0 || e2 == 0.0) ? 0.0 : he2 / (sqrt(h2) * sqrt(e2));
-      if (best < 0 || al < best_alpha) { best = j; best_alpha = al; }
+    double best_alpha = 1.0;
+    if (a.decide) {
+      for (int j = 0; j < a.S; ++j) {
+        const bool stored = j >= a.store_lo && j < a.store_hi;
+        const double e2 = stored ? h2 : tot[2 + j], he2 = stored ? h2 : tot[2 + kMaxSinks + j];
+        const double al = (h2 == 0.0 || e2 == 0.0) ? 0.0 : he2 / (sqrt(h2) * sqrt(e2));
+        if (best < 0 || al < best_alpha) { best = j; best_alpha = al; }
+      }
     }
-    const int d = best_alpha < a.tau ? best : -1;
+    const int d = (a.decide && best_alpha < a.tau) ? best : -1;
     a.decision[0] = d;
     a.alpha[0] = best_alpha;
     dec = d;
+    if (a.stats) {
+      a.stats[0] = a.n_lat > 0 ? tot[0] : nan;
+      a.stats[1] = a.n_lat > 0 ? sqrt(tot[0] / (double)a.n_lat) : nan;
+      a.stats[2] = a.D > 0 ? h2 : nan;
+      for (int j = 0; j < a.S; ++j) {
+        const bool stored = j >= a.store_lo && j < a.store_hi;
+        a.stats[3 + j] = a.D > 0 ? (stored ? h2 : tot[2 + j]) : nan;
+        a.stats[3 + a.S + j] = a.D > 0 ? (stored ? h2 : tot[2 + kMaxSinks + j]) : nan;
+      }
+      a.stats[3 + 2 * a.S] = a.decide ? best_alpha : nan;
+    }
   }
   __syncthreads();
-  if (dec >= 0)
-    for (int i = tid; i < a.D; i += 256) a.embeds[(int64_t)dec * a.D + i] = a.h[i];
+  if (a.D > 0 && (a.store_hi > a.store_lo || dec >= 0))
+    for (int i = tid; i < a.D; i += 256) {
+      const float x = a.h[i];
+      for (int j = a.store_lo; j < a.store_hi; ++j) a.embeds[(int64_t)j * a.D + i] = x;
+      if (dec >= 0) a.embeds[(int64_t)dec * a.D + i] = x;
+    }
 }
 
 hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s) {

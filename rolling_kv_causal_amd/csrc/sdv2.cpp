@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -39,8 +40,19 @@ int ok() {
   return SDV2_OK;
 }
 
+// Fault injection (sdv2_debug_fail_hip_call): calls left before the one that fails, -1 = off.
+std::atomic<int> g_fail_hip{-1};
+
+bool injected_failure() {
+  int v = g_fail_hip.load();
+  while (v >= 0)
+    if (g_fail_hip.compare_exchange_weak(v, v - 1)) return v == 0;
+  return false;
+}
+
 #define SDV2_HIP(call)                                                                         \
   do {                                                                                         \
+    if (injected_failure()) return fail(SDV2_EHIP, "%s: injected failure", #call);            \
     hipError_t e_ = (call);                                                                    \
     if (e_ != hipSuccess) return fail(SDV2_EHIP, "%s: %s", #call, hipGetErrorString(e_));      \
   } while (0)
@@ -155,7 +167,7 @@ int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_til
 }
 
 struct MetaLayout {
-  int64_t tab_h, tab_w, embeds, decision, alpha, total;
+  int64_t tab_h, tab_w, embeds, decision, alpha, stats_part, total;
 };
 
 MetaLayout meta_layout(const sdv2_config& c) {
@@ -171,6 +183,8 @@ MetaLayout meta_layout(const sdv2_config& c) {
   off = align_up(off + 16, kAlign);
   m.alpha = off;
   off = align_up(off + 16, kAlign);
+  m.stats_part = off;                  // partial sums of the fused chunk-statistics pass
+  off = align_up(off + (int64_t)kStatsMaxBlocks * kStatsQ * 8, kAlign);
   m.total = off;
   return m;
 }
@@ -259,6 +273,58 @@ int shared_slots(const sdv2_cache* c, int* out) {
   for (int s = 0; s < R; ++s)
     if (c->slot_written[s]) out[n++] = s;
   return n;
+}
+
+// One attention call; split-KV partial results go to ws (ws_bytes long).
+int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q_rot, void* d_out,
+                   float scale, void* stream, char* ws, int64_t ws_bytes, const char* ws_name) {
+  const sdv2_config& cfg = c->cfg;
+  if (c->state != kStep) return fail(SDV2_ESTATE, "attention outside a step or after the commit");
+  if (layer < 0 || layer >= cfg.num_layers) return fail(SDV2_EINVAL, "layer %d out of range", layer);
+  if (!c->appended[layer]) return fail(SDV2_ESTATE, "layer %d not appended this step", layer);
+  if (nbatch != c->step_nbatch) return fail(SDV2_EINVAL, "nbatch %d differs from the append's %d", nbatch, c->step_nbatch);
+  if (!d_q_rot || !d_out) return fail(SDV2_EINVAL, "q_rot and out must not be NULL");
+  if (((uintptr_t)d_q_rot | (uintptr_t)d_out) & 15) return fail(SDV2_EINVAL, "q_rot and out must be 16-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SDV2_EINVAL, "scale must be finite and > 0");
+
+  AttnArgs a{};
+  a.q = d_q_rot;
+  a.out = d_out;
+  a.kv = c->kv;
+  a.k_layer_off = layer * c->lay.layer_stride;
+  a.v_layer_off = a.k_layer_off + c->lay.slots * c->lay.slot_stride;
+  a.slot_stride = c->lay.slot_stride;
+  a.head_stride = c->lay.head_stride;
+  a.N = (int)c->N;
+  a.Npad = (int)c->lay.tokens_padded;
+  a.H = cfg.num_heads;
+  a.nbatch = nbatch;
+  a.nshared = shared_slots(c, a.slots);
+  const int Tc = cfg.chunk_frames;
+  a.T = Tc;
+  for (int b = 0; b < nbatch; ++b)
+    for (int t = 0; t < Tc; ++t) a.own_slot[b * Tc + t] = chunk_slot(cfg, c->step_first, b, t);
+  a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
+  a.total_tiles = (a.nshared + Tc) * a.tiles_per_frame;
+  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
+  a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
+  if (a.nsplit > 1) {
+    const int64_t need = align_up(rows * cfg.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
+    if (need > ws_bytes)
+      return fail(SDV2_ENOSPC, "%s of %lld bytes is too small for %d splits (%lld bytes)", ws_name,
+                  (long long)ws_bytes, a.nsplit, (long long)need);
+    a.part_o = (uint16_t*)ws;
+    a.part_ml = (float2*)(ws + align_up(rows * cfg.head_dim * 2, kAlign));
+  }
+  SDV2_HIP(launch_attention(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
+  if (a.nsplit > 1) {
+    CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.nsplit};
+    SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));
+  }
+  return ok();
 }
 
 }  // namespace
@@ -475,51 +541,7 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
 int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream) {
   if (int rc = check_cache(c)) return rc;
-  const sdv2_config& cfg = c->cfg;
-  if (c->state != kStep) return fail(SDV2_ESTATE, "attention outside a step or after the commit");
-  if (layer < 0 || layer >= cfg.num_layers) return fail(SDV2_EINVAL, "layer %d out of range", layer);
-  if (!c->appended[layer]) return fail(SDV2_ESTATE, "layer %d not appended this step", layer);
-  if (nbatch != c->step_nbatch) return fail(SDV2_EINVAL, "nbatch %d differs from the append's %d", nbatch, c->step_nbatch);
-  if (!d_q_rot || !d_out) return fail(SDV2_EINVAL, "q_rot and out must not be NULL");
-  if (((uintptr_t)d_q_rot | (uintptr_t)d_out) & 15) return fail(SDV2_EINVAL, "q_rot and out must be 16-byte aligned");
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SDV2_EINVAL, "scale must be finite and > 0");
-
-  AttnArgs a{};
-  a.q = d_q_rot;
-  a.out = d_out;
-  a.kv = c->kv;
-  a.k_layer_off = layer * c->lay.layer_stride;
-  a.v_layer_off = a.k_layer_off + c->lay.slots * c->lay.slot_stride;
-  a.slot_stride = c->lay.slot_stride;
-  a.head_stride = c->lay.head_stride;
-  a.N = (int)c->N;
-  a.Npad = (int)c->lay.tokens_padded;
-  a.H = cfg.num_heads;
-  a.nbatch = nbatch;
-  a.nshared = shared_slots(c, a.slots);
-  const int Tc = cfg.chunk_frames;
-  a.T = Tc;
-  for (int b = 0; b < nbatch; ++b)
-    for (int t = 0; t < Tc; ++t) a.own_slot[b * Tc + t] = chunk_slot(cfg, c->step_first, b, t);
-  a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
-  a.total_tiles = (a.nshared + Tc) * a.tiles_per_frame;
-  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
-  a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
-  a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
-  if (a.nsplit > 1) {
-    const int64_t need = align_up(rows * cfg.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
-    if (need > c->ws_bytes) return fail(SDV2_ENOSPC, "workspace too small for %d splits", a.nsplit);
-    a.part_o = (uint16_t*)c->ws;
-    a.part_ml = (float2*)(c->ws + align_up(rows * cfg.head_dim * 2, kAlign));
-  }
-  SDV2_HIP(launch_attention(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
-  if (a.nsplit > 1) {
-    CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.nsplit};
-    SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));
-  }
-  return ok();
+  return attention_call(c, layer, nbatch, d_q_rot, d_out, scale, stream, c->ws, c->ws_bytes, "workspace");
 }
 
 int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {
@@ -549,34 +571,71 @@ int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {
   return ok();
 }
 
-int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_t* h_slot,
+int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, const float* d_prev_latent,
+                      const float* d_cur_latent, int64_t latent_elems, double* d_stats, int32_t* h_slot,
                       double* h_alpha, void* stream) {
   if (int rc = check_cache(c)) return rc;
   const sdv2_config& cfg = c->cfg;
   if (c->state != kCommitted) return fail(SDV2_ESTATE, "sink_replace must follow a commit");
   if (frame != c->last_commit_frame) return fail(SDV2_ESTATE, "frame %lld is not the committed frame %lld",
                                                   (long long)frame, (long long)c->last_commit_frame);
-  if (cfg.embed_dim < 1) return fail(SDV2_EINVAL, "the cache has no chunk embeddings (embed_dim 0)");
-  if (!d_embed) return fail(SDV2_EINVAL, "d_embed must not be NULL");
-  const int S = cfg.sink_frames;
-  hipStream_t s = (hipStream_t)stream;
-  SinkArgs a{};
-  a.h = d_embed;
-  a.embeds = (float*)(c->meta_base + c->meta.embeds);
-  a.decision = (int32_t*)(c->meta_base + c->meta.decision);
-  a.alpha = (double*)(c->meta_base + c->meta.alpha);
-  a.S = S;
-  a.D = cfg.embed_dim;
-  a.tau = cfg.sink_threshold;
-  const bool decide = frame >= S && tau_on(cfg);
+  if (cfg.embed_dim < 1 && d_embed) return fail(SDV2_EINVAL, "the cache has no chunk embeddings (embed_dim 0)");
+  if (cfg.embed_dim >= 1 && !d_embed) return fail(SDV2_EINVAL, "d_embed must not be NULL (embed_dim %d)", cfg.embed_dim);
+  if ((d_prev_latent == nullptr) != (d_cur_latent == nullptr))
+    return fail(SDV2_EINVAL, "give both latent frames or neither");
+  const bool motion = d_cur_latent != nullptr;
+  if (motion && latent_elems < 1) return fail(SDV2_EINVAL, "latent_elems must be >= 1");
+  if (motion && latent_elems > ((int64_t)1 << 40)) return fail(SDV2_EINVAL, "latent_elems too large");
+  if (motion && (((uintptr_t)d_prev_latent | (uintptr_t)d_cur_latent) & 3))
+    return fail(SDV2_EINVAL, "latent frames must be 4-byte aligned");
+  if ((uintptr_t)d_embed & 3) return fail(SDV2_EINVAL, "d_embed must be 4-byte aligned");
+  if ((uintptr_t)d_stats & 7) return fail(SDV2_EINVAL, "d_stats must be 8-byte aligned");
+  const int S = cfg.sink_frames, D = d_embed ? cfg.embed_dim : 0;
+  const int64_t n_lat = motion ? latent_elems : 0;
   // the chunk's frames below S became sinks: h is their embedding
-  for (int64_t f = frame - cfg.chunk_frames + 1; f <= frame && f < S; ++f) {
-    a.store_slot = (int)f;
+  const int64_t first = frame - cfg.chunk_frames + 1;
+  const int store_lo = (int)std::min<int64_t>(first, S), store_hi = (int)std::min<int64_t>(frame + 1, S);
+  const bool decide = frame >= S && tau_on(cfg);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* decision = (int32_t*)(c->meta_base + c->meta.decision);
+  double* alpha_dev = (double*)(c->meta_base + c->meta.alpha);
+  if (D > 0 || motion || d_stats) {
+    // pass 1: enough blocks for both reductions, each block at least 8192 latent or 1024
+    // embedding elements (a fixed split for a given size, so results repeat bit for bit)
+    int64_t blocks = std::max<int64_t>({1, (n_lat + kStatsLatPerBlock - 1) / kStatsLatPerBlock,
+                                        ((int64_t)D + kStatsEmbPerBlock - 1) / kStatsEmbPerBlock});
+    blocks = std::min<int64_t>(blocks, kStatsMaxBlocks);
+    StatsArgs st{};
+    st.prev = d_prev_latent;
+    st.cur = d_cur_latent;
+    st.n_lat = n_lat;
+    st.lat_per_block = align_up((n_lat + blocks - 1) / blocks, 4);
+    st.h = d_embed;
+    st.embeds = (const float*)(c->meta_base + c->meta.embeds);
+    st.S = D > 0 ? S : 0;
+    st.D = D;
+    st.emb_per_block = (int)((D + blocks - 1) / blocks);
+    st.part = (double*)(c->meta_base + c->meta.stats_part);
+    SDV2_HIP(launch_chunk_stats(st, (int)blocks, s));
+    // pass 2: statistics, decision, embedding stores
+    SinkArgs a{};
+    a.part = st.part;
+    a.blocks = (int)blocks;
+    a.n_lat = n_lat;
+    a.h = d_embed;
+    a.embeds = (float*)(c->meta_base + c->meta.embeds);
+    a.S = S;                           // the statistics hold 4 + 2S values
+    a.D = D;
+    a.store_lo = D > 0 ? store_lo : 0;
+    a.store_hi = D > 0 ? store_hi : 0;
+    a.decide = decide ? 1 : 0;
+    a.tau = cfg.sink_threshold;
+    a.decision = decision;
+    a.alpha = alpha_dev;
+    a.stats = d_stats;
     SDV2_HIP(launch_sink_decide(a, s));
   }
   if (decide) {
-    a.store_slot = -1;
-    SDV2_HIP(launch_sink_decide(a, s));
     CopyArgs cp{};
     cp.kv = c->kv;
     cp.layer_stride_bytes = c->lay.layer_stride * c->lay.elem_bytes;
@@ -584,15 +643,15 @@ int sdv2_sink_replace(sdv2_cache* c, int64_t frame, const float* d_embed, int32_
     cp.slot_bytes = c->lay.slot_stride * c->lay.elem_bytes;
     cp.src_slot = home_slot(cfg, frame);
     cp.dst_slot = -1;
-    cp.dst_from = a.decision;
+    cp.dst_from = decision;
     cp.L = cfg.num_layers;
     SDV2_HIP(launch_copy_slots(cp, s));
   }
   int32_t slot = -1;
   double alpha = 1.0;
   if (decide && h_slot) {
-    SDV2_HIP(hipMemcpyAsync(&slot, a.decision, sizeof(slot), hipMemcpyDeviceToHost, s));
-    SDV2_HIP(hipMemcpyAsync(&alpha, a.alpha, sizeof(alpha), hipMemcpyDeviceToHost, s));
+    SDV2_HIP(hipMemcpyAsync(&slot, decision, sizeof(slot), hipMemcpyDeviceToHost, s));
+    SDV2_HIP(hipMemcpyAsync(&alpha, alpha_dev, sizeof(alpha), hipMemcpyDeviceToHost, s));
     SDV2_HIP(hipStreamSynchronize(s));
     if (slot >= 0) {
       c->slot_frame[slot] = frame;
@@ -734,6 +793,11 @@ int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int
   if (nbatch) *nbatch = (int32_t)nb;
   if (commit_chunk) *commit_chunk = (c0 >= 0 && c0 < num_chunks) ? c0 : -1;
   if (newest_frame) *newest_frame = nb > 0 ? (hi + 1) * cfg->chunk_frames - 1 : -1;
+  return ok();
+}
+
+int sdv2_debug_fail_hip_call(int32_t nth) {
+  g_fail_hip.store(nth < 0 ? -1 : nth);
   return ok();
 }
 

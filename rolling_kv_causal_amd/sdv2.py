@@ -56,7 +56,7 @@ _PROTOS = {
     "sdv2_cache_append": [_P, _I32, _I64, _I32, _P, _P, _P, _P],
     "sdv2_chunk_attention": [_P, _I32, _I32, _P, _P, _F, _P],
     "sdv2_cache_commit": [_P, _I64, _P],
-    "sdv2_sink_replace": [_P, _I64, _P, ctypes.POINTER(_I32), ctypes.POINTER(_D), _P],
+    "sdv2_sink_replace": [_P, _I64, _P, _P, _P, _I64, _P, ctypes.POINTER(_I32), ctypes.POINTER(_D), _P],
     "sdv2_motion_workspace_size": [_I32, _I64, ctypes.POINTER(_SZ)],
     "sdv2_motion_l2": [_P, _I32, _I64, _P, _P, _SZ, _P],
     "sdv2_noise_schedule": [_P, _I32, _D, _I32, _D, _D, _D, _D, _P],
@@ -64,6 +64,7 @@ _PROTOS = {
     "sdv2_slo_select": [_D, _D, _D, _D, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     "sdv2_cache_slot_info": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)],
     "sdv2_cache_state": [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "sdv2_debug_fail_hip_call": [_I32],
     "sdv2_plan_step": [ctypes.POINTER(Config), _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                        ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
 }
@@ -176,11 +177,15 @@ def sdv2_cache_commit(handle, chunk: int, stream=None) -> None:
     _call("sdv2_cache_commit", handle, chunk, _stream(stream))
 
 
-def sdv2_sink_replace(handle, frame: int, embed, sync: bool = True, stream=None):
-    """Returns (slot or -1, alpha) when sync, else None (the decision stays on the device)."""
+def sdv2_sink_replace(handle, frame: int, embed=None, prev_latent=None, cur_latent=None, stats=None,
+                      sync: bool = True, stream=None):
+    """Fused chunk statistics + sink refresh.  Returns (slot or -1, alpha) when sync, else None
+    (the decision stays on the device).  stats: fp64 device tensor of 4 + 2S values, or None."""
     slot, alpha = _I32(), _D()
-    _call("sdv2_sink_replace", handle, frame, _ptr(embed), ctypes.byref(slot) if sync else None,
-          ctypes.byref(alpha) if sync else None, _stream(stream))
+    n = 0 if cur_latent is None else cur_latent.numel()
+    _call("sdv2_sink_replace", handle, frame, _ptr(embed), _ptr(prev_latent), _ptr(cur_latent), n,
+          _ptr(stats), ctypes.byref(slot) if sync else None, ctypes.byref(alpha) if sync else None,
+          _stream(stream))
     return (slot.value, alpha.value) if sync else None
 
 
@@ -238,6 +243,10 @@ def sdv2_plan_step(cfg: Config, num_chunks: int, step: int) -> tuple[int, int, i
     _call("sdv2_plan_step", ctypes.byref(cfg), num_chunks, step, ctypes.byref(f), ctypes.byref(n),
           ctypes.byref(c), ctypes.byref(nf))
     return f.value, n.value, c.value, nf.value
+
+
+def sdv2_debug_fail_hip_call(nth: int) -> None:
+    _call("sdv2_debug_fail_hip_call", nth)
 
 
 def sdv2_last_error() -> str:
@@ -301,8 +310,9 @@ class Cache:
     def commit(self, chunk, stream=None):
         sdv2_cache_commit(self.handle, chunk, stream)
 
-    def sink_replace(self, frame, embed, sync=True, stream=None):
-        return sdv2_sink_replace(self.handle, frame, embed, sync, stream)
+    def sink_replace(self, frame, embed=None, prev_latent=None, cur_latent=None, stats=None, sync=True,
+                     stream=None):
+        return sdv2_sink_replace(self.handle, frame, embed, prev_latent, cur_latent, stats, sync, stream)
 
     def slot_info(self, slot):
         return sdv2_cache_slot_info(self.handle, slot)

@@ -34,9 +34,11 @@ class StreamRunner:
         return sdv2.sdv2_plan_step(self.cfg, self.num_chunks, step)
 
     def step(self, s: int, qkv: Callable[[int, int, int], tuple], embed: Optional[Callable] = None,
-             sink_sync: bool = True) -> dict:
+             latents: Optional[Callable] = None, stats=None, sink_sync: bool = True) -> dict:
         """Run step s.  qkv(s, layer, nbatch) -> (q, k, v) device tensors [nbatch][T'N][H][d]
-        (q is rotated in place).  embed(chunk) -> fp32 device embedding or None."""
+        (q is rotated in place).  embed(chunk) -> fp32 device embedding or None.
+        latents(frame) -> (previous, newest) fp32 device latent frames or None.  stats: fp64
+        device tensor of 4 + 2S values receiving the chunk statistics, or None."""
         first, nb, commit, newest = self.plan(s)
         info = {"first": first, "nbatch": nb, "commit": commit, "refreshed": 0, "sink": None}
         if nb == 0:
@@ -48,9 +50,10 @@ class StreamRunner:
             self.cache.attention(layer, nb, q, self.out[layer, :nb], self.scale)
         if commit >= 0:
             self.cache.commit(commit)
-            if embed is not None and self.cfg.embed_dim > 0:
-                e = embed(commit)
-                if e is not None:
-                    last = (commit + 1) * self.cfg.chunk_frames - 1   # the chunk's last frame
-                    info["sink"] = self.cache.sink_replace(last, e, sync=sink_sync)
+            last = (commit + 1) * self.cfg.chunk_frames - 1   # the chunk's last frame
+            e = embed(commit) if (embed is not None and self.cfg.embed_dim > 0) else None
+            lat = latents(last) if latents is not None else None
+            if e is not None or lat is not None or stats is not None:
+                prev, cur = lat if lat is not None else (None, None)
+                info["sink"] = self.cache.sink_replace(last, e, prev, cur, stats, sync=sink_sync)
         return info

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 from oracle import fp8 as ofp8
+from oracle import motion as omotion
 from oracle import rope as orope
 from oracle import stream as ost
 from rolling_kv_causal_amd import sdv2
@@ -69,7 +70,7 @@ class Harness:
     every step (so the oracle knows every cached frame) and for all elements at checked steps;
     other (layer, element) pairs get device-side random inputs."""
 
-    def __init__(self, cfg, layers, num_chunks=None, seed=1234):
+    def __init__(self, cfg, layers, num_chunks=None, seed=1234, motion_cfg=None):
         self.cfg = cfg
         self.layers = list(layers)
         self.M = cfg.num_chunks if num_chunks is None else num_chunks
@@ -82,6 +83,14 @@ class Harness:
         self.refresh_applied = {}
         self.decisions = {}
         self.step_no = -1
+        # fused chunk statistics: fp64 [4 + 2S] per commit; the motion term from the workload's
+        # latent series (frame f against f - 1) where it has one
+        self.stats = torch.full((4 + 2 * cfg.sink_frames,), float("nan"), dtype=torch.float64, device="cuda")
+        self.frames = None
+        if (motion_cfg or cfg).motion is not None:
+            self.frames_np = inputs.motion_frames(motion_cfg or cfg)
+            self.frames = torch.from_numpy(self.frames_np).cuda()
+        self.stats_checked = 0
 
     def _random(self, nb):
         shape = (nb, self.cfg.chunk_rows, self.cfg.num_heads, self.cfg.head_dim)
@@ -111,7 +120,11 @@ class Harness:
         emb = None
         if cfg.embed_dim > 0:
             emb = lambda c: dev(cfg, inputs.chunk_embedding(cfg, c))
-        info = self.run.step(s, qkv, embed=emb)
+        lat = None
+        if self.frames is not None:
+            lat = lambda f: ((self.frames[f - 1], self.frames[f]) if 1 <= f < len(self.frames) else None)
+        self.stats.fill_(float("nan"))
+        info = self.run.step(s, qkv, embed=emb, latents=lat, stats=self.stats)
         self.refresh_applied[s] = info["refreshed"]
         commit_kv = {layer: self.np_inputs[(layer, 0)][1:] for layer in self.layers}
         h = inputs.chunk_embedding(cfg, plan["commit"]) if (cfg.embed_dim > 0 and plan["commit"] is not None) else None
@@ -127,10 +140,38 @@ class Harness:
             want = dec["slot"] if dec["replaced"] else -1
             assert info["sink"][0] == want, f"sink decision chunk {plan['commit']}: gpu {info['sink']} oracle {dec}"
             assert abs(info["sink"][1] - dec["alpha"]) <= 1e-9, (info["sink"], dec)
+        if plan["commit"] is not None:
+            self._check_stats(plan, dec)
         # refresh events must match the oracle's
         n_ref = sum(1 for (s_, _) in self.st.refresh_log if s_ == self.step_no)
         assert self.refresh_applied[self.step_no] == n_ref, (self.step_no, self.refresh_applied[self.step_no], n_ref)
         return dec
+
+    def _check_stats(self, plan, dec):
+        """The fused statistics of this commit against oracle.motion (the newest latent frame's
+        distance) and oracle.sink (h.h, e.e, h.e, alpha of the decision), rtol 1e-12."""
+        cfg, S = self.cfg, self.cfg.sink_frames
+        st = self.stats.cpu().numpy()
+        f = (plan["commit"] + 1) * cfg.chunk_frames - 1
+        if self.frames is not None and 1 <= f < len(self.frames_np):
+            d = omotion.frame_distances(self.frames_np[f - 1:f + 1])[0]
+            n = self.frames_np[f].size
+            np.testing.assert_allclose(st[1], d, rtol=1e-12, atol=0)
+            np.testing.assert_allclose(st[0], d * d * n, rtol=1e-12, atol=0)
+            self.stats_checked += 1
+        else:
+            assert np.isnan(st[0]) and np.isnan(st[1])
+        if dec is not None:
+            t = dec["terms"]
+            np.testing.assert_allclose(st[2], t["hh"], rtol=1e-12, atol=0)
+            np.testing.assert_allclose(st[3:3 + S], t["ee"], rtol=1e-12, atol=0)
+            # h.e may cancel to near zero: its bar scales with |h| |e_j|
+            he_bar = 1e-12 * (np.abs(t["he"]) + np.sqrt(t["hh"] * np.array(t["ee"])))
+            assert np.all(np.abs(st[3 + S:3 + 2 * S] - t["he"]) <= he_bar), (st[3 + S:3 + 2 * S], t["he"])
+            assert abs(st[3 + 2 * S] - dec["alpha"]) <= 1e-12
+            self.stats_checked += 1
+        elif cfg.embed_dim == 0:
+            assert np.all(np.isnan(st[2:]))
 
     def check_outputs(self, rows=None, heads=None, rotated="exact"):
         """Compare the current step's outputs of every element on the checked layers."""
@@ -147,6 +188,8 @@ class Harness:
                 if heads is not None:
                     got = got[:, torch.as_tensor(heads, device="cuda")]
                 worst = max(worst, assert_close(cfg, host64(got), ref, f"out step {self.step_no} layer {layer} elem {b}"))
+                if rows is None and cfg.tokens >= 1024:
+                    log(f"  {cfg.name} step {self.step_no} layer {layer} elem {b}: all rows ok, worst {worst:.3g}")
         return worst
 
     def check_cache(self, layers=None):

@@ -21,14 +21,17 @@ def _small(**kw):
     return configs.TINY_FP32.with_(**base)
 
 
-def _stream(cfg, steps, layers=(0,), check=lambda s: True, rows=None, cache_check=lambda s: True):
+def _stream(cfg, steps, layers=(0,), check=lambda s: True, rows=None, cache_check=lambda s: True,
+            all_rows_at=()):
+    """Run both sides for `steps` steps; outputs checked at steps where check(s) holds (on the
+    sampled rows, or on every row and head at the steps in all_rows_at)."""
     h = Harness(cfg, layers)
     worst = 0.0
     for s in range(steps):
-        full = check(s)
+        full = check(s) or s in all_rows_at
         h.step(s, full=full)
         if full:
-            worst = max(worst, h.check_outputs(rows=rows))
+            worst = max(worst, h.check_outputs(rows=None if s in all_rows_at else rows))
         h.finish_step()
         if cache_check(s):
             h.check_cache()
@@ -216,11 +219,13 @@ def test_wan13b_30layer_t2b2_full_size():
 
 
 def test_wan13b_single_layer_full_size():
+    # sampled rows through fill, wrap and refresh; every row and head (1024 x 12) at step 33,
+    # the first steady step after the refresh
     cfg = configs.WAN13B_1LAYER
-    checked = {0, 1, 8, 9, 10, 31, 32, 33, cfg.num_steps - 1}
+    checked = {0, 1, 8, 9, 10, 31, 32, cfg.num_steps - 1}
     rows = sample_rows(cfg.tokens, n=48)
     h = _stream(cfg, cfg.num_steps, check=lambda s: s in checked, rows=rows,
-                cache_check=lambda s: s in checked)
+                cache_check=lambda s: s in checked | {33}, all_rows_at={33})
     assert h.st.refresh_log == [(32, 32)]
 
 
@@ -236,22 +241,29 @@ def test_wan13b_480p_b2_full_size_with_refresh():
     cfg = configs.WAN13B_480P_B2
     checked = {2, 10, 24, 25}
     rows = sample_rows(cfg.tokens, n=24, seed=2)
-    h = _stream(cfg, 26, layers=(0,), check=lambda s: s in checked, rows=rows,
+    h = _stream(cfg, 26, layers=(0, 29), check=lambda s: s in checked, rows=rows,
                 cache_check=lambda s: s in checked)
     assert h.st.refresh_log == [(24, 24)]
+    assert h.stats_checked == 24                # the motion term of commits 1..24 (frame 0 has none)
 
 
+@pytest.mark.timeout(900)
 def test_wan14b_40layer_b4_full_size_with_sink_refresh():
+    # layers 0 and 39 (the largest cache offsets); sampled rows and heads at step 12, every row,
+    # head and element (4 x 1024 x 40) at the last step
     cfg = configs.WAN14B_40LAYER_B4
     steps = 40
     rows = sample_rows(cfg.tokens, n=16, seed=3)
-    h = Harness(cfg, layers=(0,))
+    h = Harness(cfg, layers=(0, 39))
     replaced = kept = 0
     for s in range(steps):
         full = s in (12, steps - 1)
         h.step(s, full=full)
-        if full:
+        if s == 12:
             h.check_outputs(rows=rows, heads=np.arange(0, 40, 3))
+        elif full:
+            log(f"{cfg.name}: step {s}, all rows, heads and elements of layers 0 and 39")
+            h.check_outputs()
         dec = h.finish_step()
         if dec is not None:
             replaced += dec["replaced"]
@@ -260,6 +272,28 @@ def test_wan14b_40layer_b4_full_size_with_sink_refresh():
             h.check_cache()
     log(f"{cfg.name}: sink decisions replaced {replaced} kept {kept}")
     assert replaced >= 1 and kept >= 1
+
+
+def test_fused_chunk_stats_over_the_480p_latent_series_and_14b_embeddings():
+    # One sdv2_sink_replace per commit reduces the newest 16x60x104 latent frame against the one
+    # before it and the 5120-d chunk embedding against the sink (the 14B workload's scene
+    # generator, tau 0.95), in one statistics launch.  All 128 commits of the 129-frame series:
+    # distances and similarity terms against oracle.motion / oracle.sink at rtol 1e-12, every
+    # decision bit-exact (a tiny attention shape keeps the stream cheap).
+    c5 = configs.WAN14B_40LAYER_B4
+    cfg = _small(cfg_id=c5.cfg_id, num_chunks=128, embed_dim=c5.embed_dim, sink_threshold=c5.sink_threshold,
+                 embed_kind=c5.embed_kind, scene_change_prob=c5.scene_change_prob, scene_noise=c5.scene_noise)
+    h = Harness(cfg, [0], motion_cfg=configs.WAN13B_480P_B2)
+    replaced = kept = 0
+    for s in range(cfg.num_steps):
+        h.step(s)
+        dec = h.finish_step()
+        if dec is not None:
+            replaced += dec["replaced"]
+            kept += not dec["replaced"]
+    assert h.stats_checked == 2 * (cfg.num_chunks - 1)
+    assert replaced >= 3 and kept >= 3
+    log(f"fused stats: {h.stats_checked} checks, replaced {replaced} kept {kept}")
 
 
 def test_motion_l2_and_noise_schedule():

@@ -328,3 +328,31 @@ def test_layer_blocks_over_the_32_bit_offset_range_are_rejected():
     assert "2 GiB" in str(e.value)
     # the largest workload is far inside: 13 slots x 10.5 MB
     sdv2.sdv2_config_validate(sdv2.config_of(configs.WAN14B_40LAYER_B4))
+
+
+def test_create_with_short_buffers_is_enospc_before_any_device_work():
+    # the size checks come before any HIP call, so (aligned, never touched) stand-in addresses
+    # are enough: each buffer one byte short gives SDV2_ENOSPC and no handle
+    import ctypes
+    cfg = sdv2.config_of(configs.WAN13B_1LAYER)
+    kv, meta, ws = sdv2.sdv2_cache_size(cfg)
+    assert ws > 0
+    L = sdv2.lib()
+    fake = 1 << 20
+    for sizes in ((kv - 1, meta, ws), (kv, meta - 1, ws), (kv, meta, ws - 1)):
+        h = ctypes.c_void_p()
+        rc = L.sdv2_cache_create(ctypes.byref(cfg), fake, sizes[0], fake, sizes[1], fake, sizes[2], None,
+                                 ctypes.byref(h))
+        assert rc == sdv2.SDV2_ENOSPC and h.value is None, (sizes, rc)
+        assert "bytes" in sdv2.sdv2_last_error()
+    # misaligned buffers are EINVAL, also before any device work
+    h = ctypes.c_void_p()
+    assert L.sdv2_cache_create(ctypes.byref(cfg), fake + 16, kv, fake, meta, fake, ws, None,
+                               ctypes.byref(h)) == sdv2.SDV2_EINVAL
+
+
+def test_fault_injection_hook_arms_and_disarms():
+    # host-only: arming and disarming the injection makes no HIP call
+    sdv2.sdv2_debug_fail_hip_call(3)
+    sdv2.sdv2_debug_fail_hip_call(-1)
+    sdv2.sdv2_config_validate(sdv2.config_of(configs.TINY_FP32))
