@@ -180,6 +180,19 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
 int sdv2_chunk_attention(sdv2_cache* cache, int32_t layer, int32_t nbatch, const void* d_q_rot,
                          void* d_out, float scale, void* stream);
 
+/* Chunk attention for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the operation, arguments and
+ * kernels of sdv2_chunk_attention, with the split-KV partial results kept in a static device
+ * array of the library (SDV2_STATIC_SCRATCH_BYTES per GPU, held until the process ends) instead
+ * of the workspace given at create time.  Allocates nothing.  The split count is the one
+ * sdv2_chunk_attention uses; if its partial results exceed the array the call returns
+ * SDV2_ENOSPC and launches nothing.  The array's device address is looked up on the first call
+ * on each device.  Every call on one GPU shares that GPU's array (nothing in it needs to start
+ * at zero): calls that overlap in time on one GPU race, whatever cache they use. */
+enum { SDV2_STATIC_SCRATCH_BYTES = 96 << 20 };
+int sdv2_chunk_attention_static(sdv2_cache* cache, int32_t layer, int32_t nbatch,
+                                const void* d_q_rot, void* d_out, float scale, void* stream);
+
 /* Commit the finished chunk (element 0, which must be `chunk`) for all layers: from the next
  * step on, its T' frames' K and V (already in sink slot f if f < S, else in ring slot
  * S + f mod (W+T')) are attended, and for each of them the frame W older leaves the window.

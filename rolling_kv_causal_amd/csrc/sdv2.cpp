@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -327,6 +328,30 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
   return ok();
 }
 
+// Split-KV partials of sdv2_chunk_attention_static: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never uses the array's name as an address: its
+// device address is looked up once per device with hipGetSymbolAddress (with that device
+// current) and kept.
+constexpr int64_t kStaticScratchBytes = SDV2_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<char*> g_scratch_ptr;   // per device ordinal; nullptr until looked up
+
+int static_scratch(char** out) {
+  int dev = 0;
+  SDV2_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    SDV2_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDV2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -542,6 +567,15 @@ int sdv2_chunk_attention(sdv2_cache* c, int32_t layer, int32_t nbatch, const voi
                          void* d_out, float scale, void* stream) {
   if (int rc = check_cache(c)) return rc;
   return attention_call(c, layer, nbatch, d_q_rot, d_out, scale, stream, c->ws, c->ws_bytes, "workspace");
+}
+
+int sdv2_chunk_attention_static(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q_rot,
+                                void* d_out, float scale, void* stream) {
+  if (int rc = check_cache(c)) return rc;
+  char* ptr = nullptr;
+  if (int rc = static_scratch(&ptr)) return rc;
+  return attention_call(c, layer, nbatch, d_q_rot, d_out, scale, stream, ptr, kStaticScratchBytes,
+                        "static scratch");
 }
 
 int sdv2_cache_commit(sdv2_cache* c, int64_t chunk, void* stream) {

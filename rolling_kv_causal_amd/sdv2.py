@@ -16,6 +16,7 @@ _LIB_PATH = pathlib.Path(__file__).resolve().parent / "libsdv2.so"
 
 SDV2_OK, SDV2_EINVAL, SDV2_ESTATE, SDV2_EHIP, SDV2_ENOSPC = 0, -1, -2, -3, -4
 SDV2_F32, SDV2_BF16, SDV2_BF16_KV_FP8 = 0, 1, 2
+SDV2_STATIC_SCRATCH_BYTES = 96 << 20
 ERROR_NAMES = {SDV2_EINVAL: "EINVAL", SDV2_ESTATE: "ESTATE", SDV2_EHIP: "EHIP", SDV2_ENOSPC: "ENOSPC"}
 
 
@@ -55,6 +56,7 @@ _PROTOS = {
     "sdv2_rope_refresh": [_P, _I64, ctypes.POINTER(_I32), _P],
     "sdv2_cache_append": [_P, _I32, _I64, _I32, _P, _P, _P, _P],
     "sdv2_chunk_attention": [_P, _I32, _I32, _P, _P, _F, _P],
+    "sdv2_chunk_attention_static": [_P, _I32, _I32, _P, _P, _F, _P],
     "sdv2_cache_commit": [_P, _I64, _P],
     "sdv2_sink_replace": [_P, _I64, _P, _P, _P, _I64, _P, ctypes.POINTER(_I32), ctypes.POINTER(_D), _P],
     "sdv2_motion_workspace_size": [_I32, _I64, ctypes.POINTER(_SZ)],
@@ -171,6 +173,10 @@ def sdv2_cache_append(handle, layer: int, first_chunk: int, nbatch: int, q, k, v
 
 def sdv2_chunk_attention(handle, layer: int, nbatch: int, q_rot, out, scale: float, stream=None) -> None:
     _call("sdv2_chunk_attention", handle, layer, nbatch, _ptr(q_rot), _ptr(out), scale, _stream(stream))
+
+
+def sdv2_chunk_attention_static(handle, layer: int, nbatch: int, q_rot, out, scale: float, stream=None) -> None:
+    _call("sdv2_chunk_attention_static", handle, layer, nbatch, _ptr(q_rot), _ptr(out), scale, _stream(stream))
 
 
 def sdv2_cache_commit(handle, chunk: int, stream=None) -> None:

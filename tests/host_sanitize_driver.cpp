@@ -113,6 +113,7 @@ int main() {
   CHECK(sdv2_rope_refresh(nullptr, 0, &t, nullptr) == SDV2_EINVAL);
   CHECK(sdv2_cache_append(nullptr, 0, 0, 1, nullptr, nullptr, nullptr, nullptr) == SDV2_EINVAL);
   CHECK(sdv2_chunk_attention(nullptr, 0, 1, nullptr, nullptr, 1.f, nullptr) == SDV2_EINVAL);
+  CHECK(sdv2_chunk_attention_static(nullptr, 0, 1, nullptr, nullptr, 1.f, nullptr) == SDV2_EINVAL);
   CHECK(sdv2_cache_commit(nullptr, 0, nullptr) == SDV2_EINVAL);
   CHECK(sdv2_sink_replace(nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr) == SDV2_EINVAL);
   CHECK(sdv2_cache_destroy(nullptr) == SDV2_OK);
