@@ -185,11 +185,10 @@ def run_gpu(c, steps, warmup):
         torch.cuda.synchronize()
         for n in names:
             a, b = ev[n]
-            if a.query() and b.query():
-                try:
-                    acc[n].append(a.elapsed_time(b))
-                except RuntimeError:          # the pair was not recorded this step
-                    pass
+            try:
+                acc[n].append(a.elapsed_time(b))
+            except (RuntimeError, ValueError):    # the pair was not recorded this step
+                pass
     med = lambda v: sorted(v)[len(v) // 2] if v else None
     attn_ms = med(acc["attention"])
     return {"ms_per_step": ms_step, "wall_s": wall,

@@ -94,6 +94,8 @@ struct AttnArgs {
   int nsplit, qtiles;
   float scale_log2;        // softmax scale * log2(e)
   float scale;
+  float scale_log2_inv;    // 1 / scale_log2
+  float neg_bias;          // -8 / scale_log2: start of the 64-row kernel's -(m + 8) / scale_log2 blocks
   int slots[kMaxShared];   // cache slots of the shared frames, in attention order
 };
 
@@ -106,8 +108,9 @@ struct CombineArgs {
 
 struct RebaseArgs {
   void* kv;
-  int64_t layer_stride, slot_stride, head_stride;
+  int64_t layer_stride, slot_stride, head_stride;   // elements
   int L, H, N, pt, nslots;
+  int cpr;                 // 16-byte chunks at the start of a key row that hold every temporal pair
   int slots[kMaxShared];
   float2 cs[kMaxTPairs];   // (cos, sin) of the rebase angle per temporal pair
 };

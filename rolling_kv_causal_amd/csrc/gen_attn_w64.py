@@ -8,10 +8,11 @@ issues 64 MFMAs 32x32x16 bf16 fed by 32 LDS fragment reads (each read feeds both
   QK:  S^T[kb][qb] = K[kb] Q^T[qb]      16 K reads (kb-major, 8 k steps each)
   PV:  O^T[db][qb] += V^T[db] P^T[qb]   16 V^T reads (key step ks-major, d block db)
 and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete after the
-16th), the softmax of the tile's S into bf16 P^T words for the next tile's PV: Q arrives
-scaled by scale_log2 and the first QK MFMA of a chain accumulates onto the -(m + BIAS) block, so
-S is already the exponent; the P words are ORed for the lazy test, and eight 16x16x32 MFMAs add
-the previous tile's P row sums into l.  The e4m3 program differs only in its loads (staged,
+16th), the softmax of the tile's S into bf16 P^T words for the next tile's PV: Q^T holds the
+stored bf16 queries unchanged and the first QK MFMA of a chain accumulates onto the
+-(m + BIAS) / scale_log2 block, so scale_log2 * S (one fp32 product per score) is the exponent;
+the P words are ORed for the lazy test, and eight 16x16x32 MFMAs add the previous tile's P row
+sums into l.  The e4m3 program differs only in its loads (staged,
 then widened to bf16 at the top of the iteration).
 
 Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
@@ -43,7 +44,7 @@ Register plan (per lane):
   v[176:183]  K fragment LDS addresses per k step kd;  v[184:187] V^T addresses per key step
   v[188:199]  temporaries
   v[200:201]  m per qb (running max, log2 units)
-  v[202:233]  -(m + BIAS) blocks per qb (first QK accumulator)
+  v[202:233]  -(m + BIAS) / scale_log2 blocks per qb (first QK accumulator)
   v[236:243]  K and V^T lane offsets of the tile loads;  v244 frame slots
   v245        mask temporary;  v246 OR of the tile's P words
   v[248:255]  l accumulators (16x16 MFMA layout), four per qb
@@ -174,11 +175,12 @@ def mfma_pair(r, slot, pp):
 
 
 def softmax_ops(pc, masked, qbs=(0, 1), mreg=None):
-    """Groups of 4 values of S (already s * scale_log2 - m - BIAS): 4 exponentials, 2 packs into
-    P words and, in the tile's stream, an OR of the words into the lazy-test accumulator.  Masked,
-    every P word is ANDed with its mask word (ragged tile and causal), so masked keys weigh and
-    sum to nothing.  mreg(qb): given only when the rescale recomputes P, the register holding
-    the shift subtracted from S first.  (The row sums run on the matrix core.)"""
+    """Groups of 4 values of S (s - (m + BIAS) / scale_log2, in the units of the stored q and
+    k): 4 products by scale_log2 in fp32, 4 exponentials, 2 packs into P words and, in the
+    tile's stream, an OR of the words into the lazy-test accumulator.  Masked, every P word is
+    ANDed with its mask word (ragged tile and causal), so masked keys weigh and sum to nothing.
+    mreg(qb): given only when the rescale recomputes P, the register holding the shift
+    subtracted after the product (one fma).  (The row sums run on the matrix core.)"""
     shifted = mreg is not None
     ops = []
     gi = 0
@@ -190,14 +192,14 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None):
                     t = [f"v{TMP + (gi % 3) * 4 + j}" for j in range(4)]
                     gi += 1
                     vs = [half * 8 + 2 * w0 + j for j in range(4)]
-                    if shifted:
+                    if shifted:            # S * scale_log2 - shift
                         for j in range(4):
-                            ops.append(f"v_sub_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, {mreg(qb)}")
+                            ops.append(f"v_fma_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, %[sl], -{mreg(qb)}")
+                    else:                  # S * scale_log2 = s * scale_log2 - m - BIAS
                         for j in range(4):
-                            ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
-                    else:                  # S already holds s * scale_log2 - m
-                        for j in range(4):
-                            ops.append(f"v_exp_f32 {t[j]}, {s_elem(kb, qb, vs[j])}")
+                            ops.append(f"v_mul_f32 {t[j]}, %[sl], {s_elem(kb, qb, vs[j])}")
+                    for j in range(4):
+                        ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
                     words = [p_word(pc, qb, ks, w0), p_word(pc, qb, ks, w0 + 1)]
                     ops.append(f"v_cvt_pk_bf16_f32 {words[0]}, {t[0]}, {t[1]}")
                     ops.append(f"v_cvt_pk_bf16_f32 {words[1]}, {t[2]}, {t[3]}")
@@ -362,11 +364,11 @@ RARE_ID = [0]                                    # unique labels of the rare blo
 
 
 def rare_block(pc, masked):
-    """Rescale of the tile: S = s * scale_log2 - mc - BIAS, mc = m if finite, else 0.  New row
-    maximum m' = max(m, max over valid keys of S + mc + BIAS); O, l scaled by 2^(m - m') (not
-    while no row of the block has a maximum: both are zero then); the tile's P recomputed as
-    2^(S - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of the row block set to
-    -(mc' + BIAS); ninf: lanes whose row still has m = -inf."""
+    """Rescale of the tile: S = s - (mc + BIAS) / scale_log2, mc = m if finite, else 0.  New row
+    maximum m' = max(m, scale_log2 * (max over valid keys of S) + mc + BIAS); O, l scaled by
+    2^(m - m') (not while no row of the block has a maximum: both are zero then); the tile's P
+    recomputed as 2^(S scale_log2 - (mc' - mc)) with mc' = m' if finite, else 0; the -m block of
+    the row block set to -(mc' + BIAS) / scale_log2; ninf: lanes whose row still has m = -inf."""
     mx, y, mn, al, mcn, t0, t1, ninf = (f"v{x}" for x in range(128, 136))
     mc, dd, bp = "v144", "v145", "v146"
     lines = ["s_nop 15", f"v_mov_b32 {ninf}, {NEG_INF}", f"v_accvgpr_read_b32 {bp}, a{LANEA + 3}"]
@@ -389,6 +391,7 @@ def rare_block(pc, masked):
         lines += [f"ds_bpermute_b32 {y}, {bp}, {mx}",
                   "s_waitcnt lgkmcnt(0)",
                   f"v_max_f32 {mx}, {mx}, {y}",
+                  f"v_mul_f32 {mx}, %[sl], {mx}",                      # scale_log2 > 0 keeps the max
                   f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + qb}",
                   f"v_cndmask_b32_e64 {mc}, v{M + qb}, 0, vcc",       # mc: m, 0 while m = -inf
                   "s_cmp_eq_u64 vcc, exec",                            # no row has a maximum yet:
@@ -420,6 +423,7 @@ def rare_block(pc, masked):
         RARE_ID[0] += 1
         lines += softmax_ops(pc, masked, qbs=(qb,), mreg=lambda _q: dd)
         lines.append(f"v_sub_f32 {t0}, {hex(0xc1000000)}, {mcn}")                  # -(mc' + BIAS)
+        lines.append(f"v_mul_f32 {t0}, %[slinv], {t0}")                            # / scale_log2
         lines += [f"v_mov_b32 v{CB + 16 * qb + i}, {t0}" for i in range(16)]
     lines += [f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M}", "s_mov_b64 %[ninf], vcc",
               f"v_cmp_eq_f32 vcc, {NEG_INF}, v{M + 1}", "s_or_b64 %[ninf], %[ninf], vcc"]
@@ -428,19 +432,16 @@ def rare_block(pc, masked):
 
 def init_block():
     """O = 0 and P(-1) = 0 (read by the first PV), written sixteen registers at a time by MFMAs
-    of zero operands; m = -inf; the -m blocks -BIAS (a product of ones and -1/2 summed
-    over 16), the row-sum accumulators 0, every row flagged."""
-    zero, ones, half = "v[128:131]", "v[132:135]", "v[136:139]"
+    of zero operands; m = -inf; the -m blocks -BIAS / scale_log2 (nbias), the row-sum
+    accumulators 0, every row flagged."""
+    zero = "v[128:131]"
     lines = [f"v_mov_b32 v{128 + i}, 0" for i in range(4)]
-    lines += [f"v_mov_b32 v{132 + i}, 0x3f803f80" for i in range(4)]
-    lines += [f"v_mov_b32 v{136 + i}, 0xbf00bf00" for i in range(4)]
+    # mc = 0 while m = -inf: the -m blocks start at -BIAS / scale_log2 and every row is flagged
+    lines += [f"v_mov_b32 v{CB + i}, %[nbias]" for i in range(32)]
+    lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
     lines += [f"v_mfma_f32_32x32x16_bf16 a[{16 * i}:{16 * i + 15}], {zero}, {zero}, 0" for i in range(8)]
     b = p_base(1)
     lines += [f"v_mfma_f32_32x32x16_bf16 v[{b + 16 * i}:{b + 16 * i + 15}], {zero}, {zero}, 0" for i in range(2)]
-    lines += [f"v_mov_b32 v{M}, {NEG_INF}", f"v_mov_b32 v{M + 1}, {NEG_INF}"]
-    # mc = 0 while m = -inf: the -m blocks start at -BIAS and every row is flagged
-    assert BIAS == 8
-    lines += [f"v_mfma_f32_32x32x16_bf16 {cb_reg(qb)}, {ones}, {half}, 0" for qb in range(2)]
     lines += [f"v_mfma_f32_16x16x32_bf16 v[{TS + 4 * qb}:{TS + 4 * qb + 3}], {zero}, {zero}, 0" for qb in range(2)]
     lines.append("s_mov_b64 %[ninf], -1")
     return lines
@@ -556,7 +557,7 @@ def check_hazards(lines):
 
 
 KOFF, VOFF, SLOTL = 236, 240, 244                # lane offsets of the K and V^T tile loads, frame slots
-CB = 202                                         # -(m + BIAS) blocks, v[202:217] (qb 0) and v[218:233]
+CB = 202                                         # -(m + BIAS) / scale_log2 blocks, v[202:217] (qb 0) and v[218:233]
 MT = 245                                         # mask word read from its AGPR
 MKA, LANEA = 192, 224                            # mask words a[192 + 16 qb + j]; 8g, tq, bperm at a[224:227]
 SEL = 228                                        # row-sum selector a[228:231] (A operand)

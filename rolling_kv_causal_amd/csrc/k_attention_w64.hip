@@ -27,10 +27,10 @@
 // into the slots of K(t-2) and V(t-3), which every wave has finished reading; a wave waits for
 // its own loads (vmcnt) two iterations after issue, before that iteration's barrier.
 //
-// Softmax: base 2 with a lazy running maximum m per row.  Q is staged scaled by
-// scale * log2(e) (rounded to bf16 again) and the first QK MFMA of each chain accumulates onto
-// a block holding -(m + 8), so the MFMA result is the exponent itself: P = 2^(s c - m - 8), the
-// factor 2^-8 cancelling between O and l.  Only when some P word of a tile reaches 2 (a score
+// Softmax: base 2 with a lazy running maximum m per row.  Q is staged as stored (bf16) and the
+// first QK MFMA of each chain accumulates onto a block holding -(m + 8) / c, c = scale *
+// log2(e), so one fp32 product by c turns the MFMA result into the exponent: P = 2^(s c - m -
+// 8), the factor 2^-8 cancelling between O and l.  Only when some P word of a tile reaches 2 (a score
 // 9 above m, a NaN or an infinity), or a row has no maximum yet, is the row maximum taken and
 // O, l rescaled.  The row sums l are MFMAs over P with a selector operand.  Masks (ragged last
 // tile of a frame, block-causal own frames) are applied to the packed P words by AND.
@@ -93,9 +93,8 @@ void attn_w64_kernel(const AttnArgs a) {
   }
   const int tq_wave = wrow / a.N;             // lowest frame of the wave's rows
 
-  // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb].
-  // Q is scaled by scale * log2(e) and rounded to bf16 again, so the QK MFMA yields the
-  // exponent's argument directly (its accumulator starts at -m).
+  // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb],
+  // the stored bf16 values unchanged (the softmax scale is applied to each score in fp32).
   i32x32 q0, q1;
   {
     const uint16_t* qb0 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[0] ? row[0] : 0)) * a.H + head) * D + 8 * g;
@@ -213,20 +212,15 @@ void attn_w64_kernel(const AttnArgs a) {
   fill_k(kc, 1);
   fill_v(c0, F8 ? 1 : 0);
 
-  // Q scaled once its loads (issued before the first tiles' loads, and not waited for until
-  // here) arrive.
+  // Rows past the end read row 0 of the element (unconditional loads, issued before the first
+  // tiles' loads and not waited for until here) and are zeroed.
   __builtin_amdgcn_sched_barrier(0);
   {
-    const float sl = a.scale_log2;
-    auto scaled = [sl](int w) {
-      const uint32_t u = (uint32_t)w;
-      return (int)pack_bf16x2(bf16_bits_to_f32(u & 0xffffu) * sl, bf16_bits_to_f32(u >> 16) * sl);
-    };
     const int keep0 = valid[0] ? -1 : 0, keep1 = valid[1] ? -1 : 0;   // masks, not branches
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      q0[i] = scaled(q0[i]) & keep0;
-      q1[i] = scaled(q1[i]) & keep1;
+      q0[i] &= keep0;
+      q1[i] &= keep1;
     }
   }
 
@@ -267,7 +261,11 @@ void attn_w64_kernel(const AttnArgs a) {
   const int slotb = (int)slot_bytes, tpf = a.tiles_per_frame, nshared = a.nshared, Ntok = a.N;
   const int mk = (int)((uint32_t)(uintptr_t)ldsK + wave * LD * 1024);
   const int mv = (int)((uint32_t)(uintptr_t)ldsV + wave * LD * 1024);
-  const float sl = a.scale_log2;
+  // softmax scale in log2 units, its inverse, and the bias blocks' start -8 / scale_log2: kernel
+  // arguments made wave-uniform, so the "s" operands below are scalar registers (a value the
+  // compiler computes in a VGPR can be handed to an "s" operand as that VGPR)
+  auto uniform = [](float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); };
+  const float sl = uniform(a.scale_log2), slinv = uniform(a.scale_log2_inv), nbias = uniform(a.neg_bias);
   unsigned long long trig;
   int x, y, nvalid, tk, mflag0, mflag1, m0save, stmp, ov;
   // Register plan: O^T a[0:127], Q^T a[128:191], mask words a[192:223], lane constants
@@ -288,7 +286,8 @@ void attn_w64_kernel(const AttnArgs a) {
 #define SDV2_W64_INPUTS                                                                       \
   "{a[128:159]}"(q0), "{a[160:191]}"(q1), [n] "s"(n), [tpf] "s"(tpf),                           \
       [nshared] "s"(nshared), [N] "s"(Ntok), [tqw] "s"(tq_wave), [kblo] "s"(kblo),              \
-      [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb), [sl] "s"(sl)
+      [kbhi] "s"(kbhi), [vblo] "s"(vblo), [vbhi] "s"(vbhi), [slotb] "s"(slotb), [sl] "s"(sl),   \
+      [slinv] "s"(slinv), [nbias] "s"(nbias)
 #define SDV2_W64_CLOBBERS "vcc", "scc", "memory", "s84", "s85", "s86", "s87", "s88", "s89", "s90", "s91"
   i32x32 negm, amask;
   unsigned long long ninf;

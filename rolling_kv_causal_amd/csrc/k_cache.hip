@@ -39,44 +39,87 @@ hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s) {
 // [WT] adaptive sink and RoPE refresh: the RoPE phase is reset once the frame index passes the
 // threshold; rotating every cached key by -delta on the temporal pairs (queries are rotated at
 // the new base by the append) keeps every score unchanged.
+// Work item = one 16-byte chunk of a key row among the first a.cpr chunks, which hold every
+// temporal pair (the rest of the chunk is written back unchanged); consecutive threads take
+// consecutive chunks of a row, then the next row; each thread has four chunks in flight.
 template <int KV>
-__global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) {
-  __shared__ float2 cs[kMaxTPairs];
-  if ((int)threadIdx.x < a.pt) cs[threadIdx.x] = a.cs[threadIdx.x];
-  __syncthreads();
-  const int si = blockIdx.y / a.L, layer = blockIdx.y % a.L;
-  const int64_t slot = a.slots[si];
-  const int64_t npairs = (int64_t)a.H * a.N * a.pt;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < npairs;
-       i += (int64_t)gridDim.x * 256) {
-    const int p = (int)(i % a.pt);
-    const int64_t rowi = i / a.pt;
-    const int n = (int)(rowi % a.N), h = (int)(rowi / a.N);
-    // dims 2p, 2p+1 stay adjacent in the e4m3 order (fp8_pos keeps bits 0-2)
-    const int dpos = KV == kKvFP8 ? fp8_pos(2 * p) : 2 * p;
-    const int64_t off = layer * a.layer_stride + slot * a.slot_stride + h * a.head_stride +
-                        (int64_t)n * D + dpos;
-    const float c = cs[p].x, sn = cs[p].y;
-    if constexpr (KV == kKvFP8) {
-      uint16_t* ptr = (uint16_t*)((uint8_t*)a.kv + off);
-      const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)*ptr, false);
-      *ptr = (uint16_t)(pack_fp8x4(v.x * c - v.y * sn, v.x * sn + v.y * c, 0.f, 0.f) & 0xffffu);
-    } else if constexpr (KV == kKvBF16) {
-      uint32_t* ptr = (uint32_t*)((uint16_t*)a.kv + off);
-      const uint32_t w = *ptr;
-      const float x = bf16_bits_to_f32(w & 0xffffu), y = bf16_bits_to_f32(w >> 16);
-      *ptr = pack_bf16x2(x * c - y * sn, x * sn + y * c);
-    } else {
-      float2* ptr = (float2*)((float*)a.kv + off);
-      const float2 v = *ptr;
-      *ptr = make_float2(v.x * c - v.y * sn, v.x * sn + v.y * c);
+__device__ __forceinline__ void rebase_chunk(uint4& w, int c, const float2* cs, int pt) {
+  if constexpr (KV == kKvBF16) {
+    uint32_t* u = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = 4 * c + j;
+      if (p < pt) {
+        const float x = bf16_bits_to_f32(u[j] & 0xffffu), y = bf16_bits_to_f32(u[j] >> 16);
+        u[j] = pack_bf16x2(x * cs[p].x - y * cs[p].y, x * cs[p].y + y * cs[p].x);
+      }
+    }
+  } else if constexpr (KV == kKvF32) {
+    float* f = reinterpret_cast<float*>(&w);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = 2 * c + j;
+      if (p < pt) {
+        const float x = f[2 * j], y = f[2 * j + 1];
+        f[2 * j] = x * cs[p].x - y * cs[p].y;
+        f[2 * j + 1] = x * cs[p].y + y * cs[p].x;
+      }
+    }
+  } else {
+    // e4m3: the byte pair at positions 16c + 2k holds dims fp8_pos(16c + 2k) and the next one
+    // (fp8_pos keeps bits 0-2), i.e. pair fp8_pos(16c + 2k) / 2
+    uint32_t* u = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int p = fp8_pos(16 * c + 2 * k) >> 1;
+      if (p < pt) {
+        const uint32_t word = u[k >> 1];
+        const int half = (k & 1) * 16;
+        const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)(word >> half), false);
+        const uint32_t r = pack_fp8x4(v.x * cs[p].x - v.y * cs[p].y, v.x * cs[p].y + v.y * cs[p].x, 0.f, 0.f) & 0xffffu;
+        u[k >> 1] = (word & ~(0xffffu << half)) | (r << half);
+      }
     }
   }
 }
 
+template <int KV>
+__global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) {
+  constexpr int EB = KV == kKvF32 ? 4 : KV == kKvBF16 ? 2 : 1;
+  constexpr int U = 4;                             // chunks in flight per thread
+  __shared__ float2 cs[kMaxTPairs];
+  if ((int)threadIdx.x < a.pt) cs[threadIdx.x] = a.cs[threadIdx.x];
+  __syncthreads();
+  const int si = blockIdx.y / a.L, layer = blockIdx.y % a.L;
+  char* const base = (char*)a.kv + (layer * a.layer_stride + (int64_t)a.slots[si] * a.slot_stride) * EB;
+  const int64_t nwork = (int64_t)a.H * a.N * a.cpr;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i0 < nwork; i0 += (int64_t)gridDim.x * 256 * U) {
+    uint4 w[U];
+    uint4* ptr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * 256;
+      ptr[u] = nullptr;
+      if (i < nwork) {
+        const int c = (int)(i % a.cpr);
+        const int64_t row = i / a.cpr;
+        const int n = (int)(row % a.N), h = (int)(row / a.N);
+        ptr[u] = (uint4*)(base + ((int64_t)h * a.head_stride + (int64_t)n * D) * EB + 16 * c);
+        w[u] = *ptr[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ptr[u]) {
+        rebase_chunk<KV>(w[u], (int)((i0 + u * 256) % a.cpr), cs, a.pt);
+        *ptr[u] = w[u];
+      }
+  }
+}
+
 hipError_t launch_rebase(const RebaseArgs& a, int head_dim, int kv, hipStream_t s) {
-  const int64_t npairs = (int64_t)a.H * a.N * a.pt;
-  int gx = (int)((npairs + 256 * 4 - 1) / (256 * 4));
+  const int64_t nwork = (int64_t)a.H * a.N * a.cpr;
+  int gx = (int)((nwork + 256 * 4 - 1) / (256 * 4));
   gx = gx < 1 ? 1 : gx > 1024 ? 1024 : gx;
   const dim3 grid(gx, a.nslots * a.L);
   if (kv == kKvFP8)

@@ -311,6 +311,8 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
   a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2_inv = 1.0f / a.scale_log2;
+  a.neg_bias = -8.0f / a.scale_log2;
   const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
   if (a.nsplit > 1) {
     const int64_t need = align_up(rows * cfg.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
@@ -468,6 +470,13 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
       a.N = (int)c->N;
       a.pt = cfg.rope_dim_t / 2;
       a.nslots = ns;
+      // 16-byte chunks of a key row that hold the temporal dims 0 .. 2 pt - 1 (e4m3: at their
+      // permuted byte positions)
+      const int per_chunk = 16 / (int)c->lay.elem_bytes;
+      int last = 2 * a.pt - 1;
+      if (cfg.dtype == SDV2_BF16_KV_FP8)
+        for (int d = 0; d < 2 * a.pt; ++d) last = std::max(last, fp8_pos(d));
+      a.cpr = last / per_chunk + 1;
       for (int i = 0; i < ns; ++i) a.slots[i] = slots[i];
       const double delta = (double)(count * T);
       for (int i = 0; i < a.pt; ++i) {

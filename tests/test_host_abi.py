@@ -356,3 +356,57 @@ def test_fault_injection_hook_arms_and_disarms():
     sdv2.sdv2_debug_fail_hip_call(3)
     sdv2.sdv2_debug_fail_hip_call(-1)
     sdv2.sdv2_config_validate(sdv2.config_of(configs.TINY_FP32))
+
+
+def test_asm_program_scalar_operands_are_sgprs(tmp_path):
+    # Every named operand of the generated tile-loop program is scalar ("s").  The compiler may
+    # satisfy an "s" operand whose value it computed in a VGPR with that VGPR, which the program
+    # then reads while it overwrites the register for its own state (a scale computed in the
+    # kernel once landed in an S^T register).  Compile the kernel to gfx950 assembly and check
+    # that every %[name] of every program line was substituted with an SGPR.
+    import re
+    import subprocess
+    csrc = pathlib.Path(__file__).resolve().parents[1] / "rolling_kv_causal_amd" / "csrc"
+    out = tmp_path / "w64.s"
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only",
+                        "-S", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-I", str(csrc.parents[1] / "include"), "-I", str(csrc),
+                        str(csrc / "k_attention_w64.hip"), "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    header = (csrc / "attn_w64_asm.h").read_text()
+    programs = {}
+    for name, body in re.findall(r"#define (SDV2_W64_LOOP\w*) \\\n(.*?)(?:\n\n|\Z)", header, re.S):
+        programs[name] = [ln for ln in re.findall(r'"(.*?)\\n\\t"', body)]
+    assert set(programs) == {"SDV2_W64_LOOP", "SDV2_W64_LOOP_FP8"}
+    asm = out.read_text()
+    blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", asm, re.S)
+    blocks = [[ln.strip() for ln in b.splitlines() if ln.strip() and not ln.strip().startswith(";")] for b in blocks]
+    blocks = [b for b in blocks if len(b) > 1000]
+    assert len(blocks) == 2, [len(b) for b in blocks]
+
+    def pattern(tmpl):
+        parts = re.split(r"(%\[\w+\]|%=)", tmpl.strip())
+        rx, names = "", []
+        for part in parts:
+            if part == "%=":
+                rx += r"\d+"
+            elif part.startswith("%["):
+                rx += r"(\S+?)"
+                names.append(part[2:-1])
+            else:
+                rx += re.escape(part).replace(r"\ ", r"\s+")
+        return re.compile(rx + r"$"), names
+
+    checked = 0
+    for prog in programs.values():
+        blk = next(b for b in blocks if len(b) == len(prog))
+        for tmpl, line in zip(prog, blk):
+            if "%[" not in tmpl:
+                continue
+            rx, names = pattern(tmpl)
+            m = rx.match(line)
+            assert m, (tmpl, line)
+            for name, reg in zip(names, m.groups()):
+                assert re.fullmatch(r"s\d+|s\[\d+:\d+\]", reg), f"%[{name}] is {reg} in: {line}"
+                checked += 1
+    assert checked > 1000
