@@ -763,8 +763,68 @@ def loop_program():
     return lines
 
 
+def basic_blocks(lines):
+    """Split a program into basic blocks: (label or None, instructions, successor labels).  A
+    block ends at a label or after a branch; s_branch has only its target as successor, a
+    conditional branch its target and the next block, any other end the next block."""
+    blocks, cur, lab = [], [], None
+    for l in lines + [".Lprogram_end:"]:
+        if l.startswith(".L"):
+            if cur or lab is not None:
+                blocks.append([lab, cur])
+            lab, cur = l.rstrip(":"), []
+            continue
+        cur.append(l)
+        if l.split()[0].startswith(("s_branch", "s_cbranch")):
+            blocks.append([lab, cur])
+            lab, cur = None, []
+    out = []
+    for i, (lab, ins) in enumerate(blocks):
+        succ = []
+        last = ins[-1].split() if ins else [""]
+        nxt = blocks[i + 1][0] if i + 1 < len(blocks) else None
+        if last[0].startswith(("s_branch", "s_cbranch")):
+            succ.append(last[-1])
+        if not last[0].startswith("s_branch") and i + 1 < len(blocks):
+            if nxt is None:                      # an unlabelled block after a conditional branch
+                nxt = blocks[i + 1][0] = f".Lfall{i + 1}"
+            succ.append(nxt)
+        out.append((lab if lab is not None else f".Lentry{i}", ins, succ))
+    # an unlabelled block reached by fall-through got its name above
+    return [(blocks[i][0] or lab, ins, succ) for i, (lab, ins, succ) in enumerate(out)]
+
+
+def check_paths(lines, history=64, depth=3):
+    """check_hazards along the control flow: for every chain of up to `depth` basic blocks
+    linked by a branch or a fall-through, the last `history` instructions of the chain's first
+    blocks followed by the whole last block."""
+    blocks = basic_blocks(lines)
+    by_label = {lab: (ins, succ) for lab, ins, succ in blocks}
+    preds = {lab: [] for lab, _, _ in blocks}
+    for lab, _, succ in blocks:
+        for t in succ:
+            if t in preds:
+                preds[t].append(lab)
+    checked = set()
+
+    def walk(lab, tail, d):
+        key = (lab, d, tuple(tail[-history:]))
+        if key in checked:
+            return
+        checked.add(key)
+        check_hazards(tail[-history:] + by_label[lab][0])
+        if d < depth:
+            for s in by_label[lab][1]:
+                if s in by_label:
+                    walk(s, (tail + by_label[lab][0])[-history:], d + 1)
+
+    for lab, ins, _ in blocks:
+        walk(lab, [], 1)
+
+
 def emit(name, lines):
     check_hazards([l for l in lines if not l.startswith(".L")])
+    check_paths(lines)
     body = " \\\n".join(f'  "{l}\\n\\t"' for l in lines)
     return f"#define {name} \\\n{body}\n"
 

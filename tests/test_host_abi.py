@@ -410,3 +410,29 @@ def test_asm_program_scalar_operands_are_sgprs(tmp_path):
                 assert re.fullmatch(r"s\d+|s\[\d+:\d+\]", reg), f"%[{name}] is {reg} in: {line}"
                 checked += 1
     assert checked > 1000
+
+
+def test_generator_path_check_follows_branches():
+    # An exponential at a branch target reads an MFMA result two instructions after the MFMA
+    # along the branch; in text order 20 instructions separate them, so only the check that
+    # follows branches (check_paths) rejects the program.
+    import importlib.util
+    import pathlib
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_paths", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    prog = (["v_mfma_f32_32x32x16_bf16 v[0:15], v[128:131], a[0:3], v[0:15]", "s_cbranch_scc0 .Lx"]
+            + ["v_mov_b32 v200, 0"] * 20 + ["s_branch .Ly", ".Lx:", "v_exp_f32 v190, v3", ".Ly:", "s_nop 0"])
+    gen.check_hazards([l for l in prog if not l.startswith(".L")])          # text order: passes
+    with pytest.raises(AssertionError):
+        gen.check_paths(prog)
+    # with 12 instructions between them on the branch path as well, both checks pass
+    ok = (["v_mfma_f32_32x32x16_bf16 v[0:15], v[128:131], a[0:3], v[0:15]"] + ["v_mov_b32 v201, 0"] * 12
+          + ["s_cbranch_scc0 .Lx"] + ["v_mov_b32 v200, 0"] * 20 + ["s_branch .Ly", ".Lx:", "v_exp_f32 v190, v3",
+                                                                   ".Ly:", "s_nop 0"])
+    gen.check_paths(ok)
+    # the committed programs pass along every path
+    for f8 in (False, True):
+        gen.set_mode(f8)
+        gen.check_paths(gen.loop_program())
