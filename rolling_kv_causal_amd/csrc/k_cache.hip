@@ -274,43 +274,69 @@ hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s) {
 
 // ---- motion: d_t = sqrt(sum (x_t - x_{t-1})^2 / n), fp64 ----------------------------------
 // [NEWS] algorithm item 2 / [WT] motion-aware noise scheduler: the distance between consecutive
-// latent frames.  Pass 1: each block sums one 16384-element part of one frame pair; pass 2 adds
-// the parts of a frame in order - a fixed reduction order, so results are run-to-run identical.
-constexpr int kMotionChunk = 16384;
+// latent frames.  Pass 1: a block walks kMotionRun consecutive frame pairs of one part of
+// kMotionChunk elements, keeping the previous frame's values in registers, so every frame is
+// read once; per pair it sums (x_t - x_{t-1})^2 in fp64 (lane strides, a butterfly in each
+// wave, the four waves in order).  Pass 2 adds the parts of a frame in order.  A fixed
+// reduction order: results are run-to-run identical.
+constexpr int kMotionChunk = 4096;   // elements of a part: 16 per thread
+constexpr int kMotionRun = 32;       // frame pairs per block
 
 int motion_parts(int64_t elems) { return (int)((elems + kMotionChunk - 1) / kMotionChunk); }
 
 template <bool VEC4>
-__global__ __launch_bounds__(256) void motion_partial_kernel(const float* x, int64_t n,
+__global__ __launch_bounds__(256) void motion_partial_kernel(const float* x, int64_t n, int F,
                                                              double* partials, int parts) {
-  __shared__ double red[4];
-  const int t = blockIdx.y + 1, p = blockIdx.x;
-  const float* cur = x + (int64_t)t * n;
-  const float* prev = cur - n;
+  constexpr int E = kMotionChunk / 256;            // elements per thread
+  __shared__ double red[4][kMotionRun];
+  const int p = blockIdx.x, t0 = blockIdx.y * kMotionRun;   // pairs (t0 + i, t0 + i + 1)
+  const int pairs = F - t0 < kMotionRun ? F - t0 : kMotionRun;
   const int64_t lo = (int64_t)p * kMotionChunk;
-  const int64_t hi = lo + kMotionChunk < n ? lo + kMotionChunk : n;
-  double acc = 0.0;
-  if constexpr (VEC4) {
-    for (int64_t i = lo + 4 * threadIdx.x; i < hi; i += 4 * 256) {
-      const float4 a = *(const float4*)(cur + i), b = *(const float4*)(prev + i);
-      const double d0 = (double)a.x - (double)b.x, d1 = (double)a.y - (double)b.y;
-      const double d2 = (double)a.z - (double)b.z, d3 = (double)a.w - (double)b.w;
-      acc = fma(d0, d0, acc);
-      acc = fma(d1, d1, acc);
-      acc = fma(d2, d2, acc);
-      acc = fma(d3, d3, acc);
+  float prev[E], cur[E];
+  auto load = [&](int t, float* v) {
+    const float* f = x + (int64_t)t * n + lo;
+    if constexpr (VEC4) {                          // n % 4 == 0 and 16-byte aligned frames
+#pragma unroll
+      for (int j = 0; j < E / 4; ++j) {
+        const int64_t i = 4 * (threadIdx.x + 256 * j);
+        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lo + i < n) w = *(const float4*)(f + i);
+        v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int64_t i = threadIdx.x + 256 * j;
+        v[j] = lo + i < n ? f[i] : 0.f;
+      }
     }
-  } else {
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-      const double d = (double)cur[i] - (double)prev[i];
-      acc = fma(d, d, acc);
+  };
+  load(t0, prev);
+  double acc[kMotionRun];
+#pragma unroll
+  for (int k = 0; k < kMotionRun; ++k) {
+    acc[k] = 0.0;
+    if (k < pairs) {
+      load(t0 + k + 1, cur);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const double d = (double)cur[j] - (double)prev[j];
+        acc[k] = fma(d, d, acc[k]);
+        prev[j] = cur[j];
+      }
     }
   }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < kMotionRun; ++k) {
+    const double v = wave_sum(acc[k]);
+    if (lane == 0) red[wave][k] = v;
+  }
   __syncthreads();
-  if (threadIdx.x == 0)
-    partials[(int64_t)(t - 1) * parts + p] = ((red[0] + red[1]) + red[2]) + red[3];
+  if ((int)threadIdx.x < pairs) {
+    const int k = threadIdx.x;
+    partials[(int64_t)(t0 + k) * parts + p] = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+  }
 }
 
 __global__ __launch_bounds__(256) void motion_final_kernel(const double* partials, int parts,
@@ -326,12 +352,11 @@ hipError_t launch_motion(const float* frames, int nframes, int64_t elems, double
                          double* partials, int parts, hipStream_t s) {
   const int F = nframes - 1;
   const bool vec4 = (elems % 4 == 0) && (((uintptr_t)frames & 15) == 0);
+  const dim3 grid(parts, (F + kMotionRun - 1) / kMotionRun);
   if (vec4)
-    hipLaunchKernelGGL(motion_partial_kernel<true>, dim3(parts, F), dim3(256), 0, s, frames, elems,
-                       partials, parts);
+    hipLaunchKernelGGL(motion_partial_kernel<true>, grid, dim3(256), 0, s, frames, elems, F, partials, parts);
   else
-    hipLaunchKernelGGL(motion_partial_kernel<false>, dim3(parts, F), dim3(256), 0, s, frames,
-                       elems, partials, parts);
+    hipLaunchKernelGGL(motion_partial_kernel<false>, grid, dim3(256), 0, s, frames, elems, F, partials, parts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(motion_final_kernel, dim3((F + 255) / 256), dim3(256), 0, s, partials, parts,

@@ -153,7 +153,7 @@ def test_noise_schedule_matches_oracle():
 
 
 def test_motion_workspace_size_and_errors():
-    assert sdv2.sdv2_motion_workspace_size(129, 99840) == 128 * 7 * 8
+    assert sdv2.sdv2_motion_workspace_size(129, 99840) == 128 * 25 * 8    # 25 parts of 4096 elements per pair
     with pytest.raises(sdv2.SDV2Error):
         sdv2.sdv2_motion_workspace_size(1, 10)
 
