@@ -284,6 +284,16 @@ int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int
  * point whose first launch fails this way has launched nothing and changed no state. */
 int sdv2_debug_fail_hip_call(int32_t nth);
 
+/* Check of the split-KV work plan sdv2_chunk_attention uses for nbatch elements with nshared
+ * cached frames present, for tests: every workgroup of the grid decodes (as the kernels decode
+ * it) to a query tile of its XCD; every key tile of every query tile is covered by exactly one
+ * workgroup; split query tiles have all their splits and partial-result indices inside the
+ * workspace sdv2_cache_size asks for.  Outputs (may be NULL): the split count of the split
+ * query tiles, their number and the workgroups that do work.  SDV2_EINVAL names the first
+ * violation.  Host only. */
+int sdv2_debug_check_plan(const sdv2_config* cfg, int32_t nbatch, int32_t nshared, int32_t* nsplit,
+                          int32_t* tail_items, int32_t* workgroups);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* sdv2_last_error(void);
 

@@ -59,6 +59,67 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return xcd * per + (xcd < rem ? xcd : rem) + bid / kNumXcd;
 }
 
+// ---- split-KV work plan ---------------------------------------------------------------------
+// Work items are query tiles of kQTile rows of one (element, head), numbered
+// item = (head * nbatch + elem) * qtiles + qtile.  XCD x owns items [first[x], first[x + 1]),
+// so the items sharing one head's K/V use one L2.  On XCD x the first whole[x] items run whole,
+// one workgroup each (output written directly); the rest, its tail items, are split into
+// nsplit key ranges, one workgroup each, whose partial results combine_kernel merges.  Tail
+// items are numbered across XCDs from tail_first[x].  Hardware sends workgroup b to XCD
+// b % kNumXcd as that XCD's (b / kNumXcd)-th workgroup, so each XCD starts its whole items
+// first; the grid holds wg_per_xcd workgroups per XCD, and those past an XCD's share exit.
+struct WorkPlan {
+  int first[kNumXcd + 1];
+  int whole[kNumXcd];
+  int tail_first[kNumXcd + 1];   // tail_first[kNumXcd] = tail items in all
+  int nsplit;                    // key ranges of a tail item (>= 2 when there are tail items)
+  int wg_per_xcd;
+};
+
+struct WorkItem {
+  int head, elem, qtile;
+  int split, nsplit;             // key range split of nsplit (0 of 1 for a whole item)
+  int tail;                      // tail item index, or -1 for a whole item
+};
+
+// Workgroup b of the plan; false for a workgroup past its XCD's share.
+__host__ __device__ __forceinline__ bool plan_item(const WorkPlan& p, int qtiles, int nbatch, int b,
+                                                   WorkItem& w) {
+  const int x = b % kNumXcd, j = b / kNumXcd;
+  int item;
+  if (j < p.whole[x]) {
+    item = p.first[x] + j;
+    w.split = 0;
+    w.nsplit = 1;
+    w.tail = -1;
+  } else {
+    const int jj = j - p.whole[x];
+    const int t = jj / p.nsplit;
+    item = p.first[x] + p.whole[x] + t;
+    if (item >= p.first[x + 1]) return false;
+    w.split = jj - t * p.nsplit;
+    w.nsplit = p.nsplit;
+    w.tail = p.tail_first[x] + t;
+  }
+  w.qtile = item % qtiles;
+  const int r = item / qtiles;
+  w.elem = r % nbatch;
+  w.head = r / nbatch;
+  return true;
+}
+
+// Tail item t -> (head, elem, qtile).
+__host__ __device__ __forceinline__ void plan_tail(const WorkPlan& p, int qtiles, int nbatch, int t,
+                                                   int& head, int& elem, int& qtile) {
+  int x = 0;
+  while (x + 1 < kNumXcd && t >= p.tail_first[x + 1]) ++x;
+  const int item = p.first[x] + p.whole[x] + (t - p.tail_first[x]);
+  qtile = item % qtiles;
+  const int r = item / qtiles;
+  elem = r % nbatch;
+  head = r / nbatch;
+}
+
 // ---- kernel argument blocks (passed by value) ----------------------------------------------
 struct AppendArgs {
   void* q;                 // [nbatch][T*N][H][D], rotated in place
@@ -83,15 +144,16 @@ struct AttnArgs {
   void* out;               // [nbatch][T*N][H][D]
   const void* kv;
   int64_t k_layer_off, v_layer_off, slot_stride, head_stride;
-  uint16_t* part_o;        // [nsplit][nbatch][H][T*N][D] bf16 O/l of the split (split-KV only)
-  float2* part_ml;         // [nsplit][nbatch][H][T*N] (m in log2 units, l)
+  uint16_t* part_o;        // [nsplit][tail items][kQTile][D] bf16 O/l of the split
+  float2* part_ml;         // [nsplit][tail items][kQTile] (m in log2 units, l)
   int N, Npad, H, nbatch;  // N: tokens per frame
   int T;                   // frames per chunk (block-causal inside the chunk)
   int nshared;             // cached frames attended (sinks + window)
   int own_slot[kMaxBatch]; // slot of own-chunk frame t of element b, index b * T + t
   int tiles_per_frame;     // Npad / kTileKeys
   int total_tiles;         // (nshared + T) * tiles_per_frame
-  int nsplit, qtiles;
+  int qtiles;
+  WorkPlan plan;
   float scale_log2;        // softmax scale * log2(e)
   float scale;
   float scale_log2_inv;    // 1 / scale_log2
@@ -103,7 +165,8 @@ struct CombineArgs {
   const uint16_t* part_o;
   const float2* part_ml;
   void* out;
-  int N, H, nbatch, nsplit;  // N: query rows per (element, head)
+  int N, H, nbatch, qtiles;  // N: query rows per (element, head)
+  WorkPlan plan;
 };
 
 struct RebaseArgs {

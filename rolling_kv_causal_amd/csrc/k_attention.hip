@@ -58,13 +58,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   char* const ldsV = lds + 2 * K_BYTES;
   typedef __attribute__((address_space(3))) void lds_void;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int qtile = w % a.qtiles;
-  int rest = w / a.qtiles;
-  const int elem = rest % a.nbatch;
-  rest /= a.nbatch;
-  const int split = rest % a.nsplit;
-  const int head = rest / a.nsplit;
+  WorkItem wi;
+  if (!plan_item(a.plan, a.qtiles, a.nbatch, blockIdx.x, wi)) return;   // past its XCD's share
+  const int qtile = wi.qtile, elem = wi.elem, head = wi.head, split = wi.split, nsplit = wi.nsplit;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,8 +89,8 @@ void attn_bf16_kernel(const AttnArgs a) {
   // so every split has a tile.
   const int tq_hi = min(a.T - 1, (qtile * kQTile + kQTile - 1) / a.N);
   const int tiles_q = (a.nshared + tq_hi + 1) * a.tiles_per_frame;
-  const int t_begin = (int)((int64_t)split * tiles_q / a.nsplit);
-  const int t_end = (int)((int64_t)(split + 1) * tiles_q / a.nsplit);
+  const int t_begin = (int)((int64_t)split * tiles_q / nsplit);
+  const int t_end = (int)((int64_t)(split + 1) * tiles_q / nsplit);
   const int ntiles = t_end - t_begin;         // >= 1
   const int last = ntiles - 1;
   const char* kvb = (const char*)a.kv;
@@ -345,7 +341,7 @@ void attn_bf16_kernel(const AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // 0: no visible key in this split
-  if (a.nsplit == 1) {
+  if (nsplit == 1) {
     uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * R + qrow) * a.H + head) * D + 4 * g;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
@@ -357,7 +353,7 @@ void attn_bf16_kernel(const AttnArgs a) {
         *(uint2*)(op + 32 * i + 8 * a4) = w2;
       }
   } else {
-    const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + qrow;
+    const int64_t prow = ((int64_t)split * a.plan.tail_first[kNumXcd] + wi.tail) * kQTile + qrow - qtile * kQTile;
     uint16_t* po = a.part_o + prow * D + 4 * g;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
@@ -374,25 +370,32 @@ void attn_bf16_kernel(const AttnArgs a) {
 
 // Merge split-KV partials: O = sum_s w_s O_s / sum_s w_s, w_s = l_s 2^(m_s - max m).  The
 // partial O_s (already divided by l_s) are bf16: the merged row is rounded to bf16 anyway, and
-// half the bytes halve the partial traffic of the attention epilogue and of this kernel.
+// half the bytes halve the partial traffic of the attention epilogue and of this kernel.  Rows
+// are those of the plan's tail items (row r of tail item t: query tile row r).
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   constexpr int TPR = D / 8;                        // threads per output row, 8 values each
-  const int64_t rows = (int64_t)a.nbatch * a.H * a.N;
+  const int ntail = a.plan.tail_first[kNumXcd], nsplit = a.plan.nsplit;
+  const int64_t rows = (int64_t)ntail * kQTile;
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
+  const int t = (int)(row / kQTile), rq = (int)(row % kQTile);
+  int head, elem, qtile;
+  plan_tail(a.plan, a.qtiles, a.nbatch, t, head, elem, qtile);
+  const int n = qtile * kQTile + rq;                // query row of the element
+  if (n >= a.N) return;
   const int d0 = (threadIdx.x % TPR) * 8;
   // Splits in groups of eight: every load of a group is issued before any arithmetic, so the
   // kernel pays one memory round trip per group (one in all for up to eight splits); a later
   // group with a larger maximum rescales what the earlier ones summed.
   constexpr int G = 8;
   float M = -INFINITY, W = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.nsplit; s0 += G) {
+  for (int s0 = 0; s0 < nsplit; s0 += G) {
     float2 ml[G];
     uint4 p[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      if (s0 + j < a.nsplit) {
+      if (s0 + j < nsplit) {
         ml[j] = a.part_ml[(s0 + j) * rows + row];
         p[j] = *(const uint4*)(a.part_o + ((s0 + j) * rows + row) * D + d0);
       }
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     float Mn = M;
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      if (s0 + j < a.nsplit) Mn = fmaxf(Mn, ml[j].x);
+      if (s0 + j < nsplit) Mn = fmaxf(Mn, ml[j].x);
     if (M != Mn && M != -INFINITY) {
       const float r = __builtin_amdgcn_exp2f(M - Mn);
       W *= r;
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     M = Mn;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      if (s0 + j < a.nsplit) {
+      if (s0 + j < nsplit) {
         const float wgt = ml[j].y * __builtin_amdgcn_exp2f(ml[j].x - M);
         const uint32_t pw[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
         W += wgt;
@@ -423,9 +426,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     }
   }
   const float inv = 1.f / W;
-  const int n = (int)(row % a.N);
-  const int eh = (int)(row / a.N);
-  const int head = eh % a.H, elem = eh / a.H;
   uint16_t* op = (uint16_t*)a.out + ((int64_t)(elem * a.N + n) * a.H + head) * D + d0;
   uint4 w4;
   w4.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t s) {
   if (kv != kKvF32 && head_dim == 128) return launch_attention_w64(a, kv, s);
   if (kv == kKvBF16 && head_dim == 64) {
-    const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
+    const int grid = kNumXcd * a.plan.wg_per_xcd;
     hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
   } else if (kv == kKvF32) {
     const int grid = a.nbatch * a.H * ((a.T * a.N + 63) / 64);
@@ -527,7 +527,7 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int kv, hipStream_t
 }
 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s) {
-  const int64_t rows = (int64_t)a.nbatch * a.H * a.N;
+  const int64_t rows = (int64_t)a.plan.tail_first[kNumXcd] * kQTile;
   const int rows_per_block = 256 / (head_dim / 8);
   const int grid = (int)((rows + rows_per_block - 1) / rows_per_block);
   if (head_dim == 128)

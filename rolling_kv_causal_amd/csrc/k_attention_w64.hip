@@ -70,13 +70,9 @@ void attn_w64_kernel(const AttnArgs a) {
   char* const ldsV = lds + NBUF * K_BYTES;
   typedef __attribute__((address_space(3))) void lds_void;
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int qtile = w % a.qtiles;
-  int rest = w / a.qtiles;
-  const int elem = rest % a.nbatch;
-  rest /= a.nbatch;
-  const int split = rest % a.nsplit;
-  const int head = rest / a.nsplit;
+  WorkItem wi;
+  if (!plan_item(a.plan, a.qtiles, a.nbatch, blockIdx.x, wi)) return;   // past its XCD's share
+  const int qtile = wi.qtile, elem = wi.elem, head = wi.head, split = wi.split, nsplit = wi.nsplit;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,8 +110,8 @@ void attn_w64_kernel(const AttnArgs a) {
   // row of the query tile sees).
   const int tq_hi = min(a.T - 1, (qtile * kQTile + kQTile - 1) / a.N);
   const int tiles_q = (a.nshared + tq_hi + 1) * a.tiles_per_frame;
-  const int t_begin = (int)((int64_t)split * tiles_q / a.nsplit);
-  const int t_end = (int)((int64_t)(split + 1) * tiles_q / a.nsplit);
+  const int t_begin = (int)((int64_t)split * tiles_q / nsplit);
+  const int t_end = (int)((int64_t)(split + 1) * tiles_q / nsplit);
   const int n = t_end - t_begin;              // >= 1
   const char* kvb = (const char*)a.kv;
   const int64_t head_off = (int64_t)head * a.head_stride;
@@ -375,8 +371,8 @@ void attn_w64_kernel(const AttnArgs a) {
         w2.y = pack_bf16x2(oval(db, i0 + 2) * inv, oval(db, i0 + 3) * inv);
         *(uint2*)(erow + 2 * (32 * db + 8 * a4)) = w2;
       }
-    if (a.nsplit > 1 && g == 0 && valid[qb]) {
-      const int64_t prow = (((int64_t)split * a.nbatch + elem) * a.H + head) * R + row[qb];
+    if (nsplit > 1 && g == 0 && valid[qb]) {
+      const int64_t prow = ((int64_t)split * a.plan.tail_first[kNumXcd] + wi.tail) * kQTile + wave * 64 + 32 * qb + r;
       a.part_ml[prow] = make_float2(mrun[qb], l_tot);
     }
   }
@@ -387,16 +383,16 @@ void attn_w64_kernel(const AttnArgs a) {
     const int rl = 4 * i + (lane >> 4), grow = wrow + rl;
     const uint4 w4 = *(const uint4*)(ep + rl * EP_STRIDE + 16 * chunk);
     if (grow < R) {
-      uint16_t* dst = a.nsplit == 1
+      uint16_t* dst = nsplit == 1
           ? (uint16_t*)a.out + ((int64_t)(elem * R + grow) * a.H + head) * D
-          : a.part_o + ((((int64_t)split * a.nbatch + elem) * a.H + head) * R + grow) * D;
+          : a.part_o + (((int64_t)split * a.plan.tail_first[kNumXcd] + wi.tail) * kQTile + grow - qtile * kQTile) * D;
       *(uint4*)(dst + 8 * chunk) = w4;
     }
   }
 }
 
 hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s) {
-  const int grid = a.H * a.nsplit * a.nbatch * a.qtiles;
+  const int grid = kNumXcd * a.plan.wg_per_xcd;
   if (kv == kKvFP8)
     hipLaunchKernelGGL(attn_w64_kernel<true>, dim3(grid), dim3(256), 0, s, a);
   else

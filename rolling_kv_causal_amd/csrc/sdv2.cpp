@@ -126,45 +126,98 @@ sdv2_layout make_layout(const sdv2_config& c) {
   return l;
 }
 
-// Split-KV count for nbatch elements.  The grid runs in rounds of kSlots workgroups (256 CUs of
-// MI355X, one workgroup each); a split count costs rounds x (tiles per split x one 64-key tile
-// step + the workgroup's prologue and epilogue) plus the bf16 partial results it writes and the
-// combine reads back.  The constants are measured on MI355X with the 64-row kernel: about
-// 1.6 us per tile step of a 256-row workgroup with every CU busy, 8 us of prologue/epilogue per
-// round and ~5 TB/s for the partial traffic.  A round that leaves CUs idle runs at a higher
-// clock (the chip is power-bound): its tile step is shorter by kClockGain x the idle fraction
-// (1.45 us measured at 3/4 occupancy).
-constexpr int kSlots = 256;
+// Split-KV work plan (WorkPlan in common.h) for nbatch elements.  Each XCD runs its items on its
+// 32 CUs, one workgroup per CU at a time, the whole items first.  A plan (whole items per XCD in
+// full rounds of 32, the rest split into k key ranges) costs, on the slowest XCD, its rounds x
+// (tiles per workgroup x one 64-key tile step + the workgroup's prologue and epilogue), plus
+// the bf16 partial results the tail items write and the combine reads back.  The constants are
+// measured on MI355X with the 64-row kernel: about 1.6 us per tile step of a 256-row workgroup
+// with every CU busy, 8 us of prologue/epilogue per round and ~5 TB/s for the partial traffic.
+// A round that leaves CUs idle runs at a higher clock (the chip is power-bound): its tile step
+// is shorter by kClockGain x the idle fraction (1.45 us measured at 3/4 occupancy).
+constexpr int kCuPerXcd = 32;
 constexpr int kMaxSplit = 16;
 constexpr double kTileUs = 1.6, kRoundUs = 8.0, kClockGain = 0.38;
 constexpr double kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
+
+// Rounds of n workgroups of `tiles` tiles each on one XCD.
+double xcd_rounds_us(int64_t n, double tiles) {
+  const int64_t full = n / kCuPerXcd, part = n % kCuPerXcd;
+  double us = (double)full * (tiles * kTileUs + kRoundUs);
+  if (part) us += tiles * kTileUs * (1.0 - kClockGain * (1.0 - (double)part / kCuPerXcd)) + kRoundUs;
+  return us;
+}
+
 // total_tiles: key tiles of the longest query tile; min_tiles: of the shortest (block-causal
 // chunks end the walk at a query tile's last own frame), which bounds the split count so that
-// every split has at least one tile.
-int choose_nsplit(const sdv2_config& c, int nbatch, int total_tiles, int min_tiles) {
-  if (c.dtype == SDV2_F32) return 1;
-  if (const char* e = std::getenv("SDV2_NSPLIT")) {   // forced count (tests, tuning)
-    const int v = std::atoi(e);
-    if (v > 0) return std::max(1, std::min({v, kMaxSplit, min_tiles}));
-  }
+// every split has at least one tile.  SDV2_NSPLIT=n (tests, tuning) splits every item n ways.
+WorkPlan make_plan(const sdv2_config& c, int nbatch, int total_tiles, int min_tiles) {
   const int64_t R = (int64_t)c.chunk_frames * c.grid_h * c.grid_w;   // query rows per element
-  const int64_t base = (int64_t)nbatch * c.num_heads * ((R + kQTile - 1) / kQTile);
-  const int64_t rows = (int64_t)nbatch * c.num_heads * R;
-  int best = 1;
-  double best_cost = 1e300;
-  for (int ns = 1; ns <= kMaxSplit && ns <= min_tiles; ++ns) {
-    const int64_t wgs = base * ns, full = wgs / kSlots, part = wgs % kSlots;
-    const int64_t per = (total_tiles + ns - 1) / ns;
-    double cost = (double)full * ((double)per * kTileUs + kRoundUs);
-    if (part)
-      cost += (double)per * kTileUs * (1.0 - kClockGain * (1.0 - (double)part / kSlots)) + kRoundUs;
-    if (ns > 1) cost += (double)ns * rows * (2.0 * (c.head_dim * 2 + 8)) / kPartialBytesPerUs + kCombineUs;
-    if (cost < best_cost * 0.98) {   // prefer fewer splits unless clearly cheaper
-      best_cost = cost;
-      best = ns;
-    }
+  const int qtiles = (int)((R + kQTile - 1) / kQTile);
+  const int items = nbatch * c.num_heads * qtiles;
+  int ix[kNumXcd];
+  WorkPlan p{};
+  for (int x = 0; x <= kNumXcd; ++x) p.first[x] = (int)((int64_t)x * items / kNumXcd);
+  for (int x = 0; x < kNumXcd; ++x) ix[x] = p.first[x + 1] - p.first[x];
+  int best_k = 1, best_rounds = 0;
+  const char* forced = std::getenv("SDV2_NSPLIT");
+  if (c.dtype != SDV2_F32 && forced && std::atoi(forced) > 0) {
+    best_k = std::max(1, std::min({std::atoi(forced), kMaxSplit, min_tiles}));
+  } else if (c.dtype != SDV2_F32) {
+    double best = 1e300;
+    // k = 1: every item whole; else whole rounds r (the first r x 32 items of each XCD) and the
+    // rest split k ways
+    for (int k = 1; k <= kMaxSplit && k <= min_tiles; ++k)
+      for (int r = 0; r * kCuPerXcd <= items; ++r) {
+        if (k == 1 && r > 0) break;
+        double slowest = 0.0;
+        int64_t tail_items = 0;
+        for (int x = 0; x < kNumXcd; ++x) {
+          const int whole = k == 1 ? ix[x] : std::min(ix[x], r * kCuPerXcd);
+          const int tail = ix[x] - whole;
+          tail_items += tail;
+          double us = 0.0;
+          if (k == 1) {
+            us = xcd_rounds_us(whole, total_tiles);
+          } else {
+            us = (double)(whole / kCuPerXcd) * (total_tiles * kTileUs + kRoundUs);
+            if (whole % kCuPerXcd) us += total_tiles * kTileUs + kRoundUs;   // (r caps whole at full rounds)
+            us += xcd_rounds_us((int64_t)tail * k, (double)total_tiles / k);
+          }
+          slowest = std::max(slowest, us);
+        }
+        if (k > 1 && tail_items == 0) continue;
+        double cost = slowest;
+        if (k > 1)
+          cost += (double)k * tail_items * kQTile * (2.0 * (c.head_dim * 2 + 8)) / kPartialBytesPerUs + kCombineUs;
+        if (cost < best * 0.98) {   // prefer fewer splits unless clearly cheaper
+          best = cost;
+          best_k = k;
+          best_rounds = r;
+        }
+      }
   }
-  return best;
+  p.nsplit = best_k;
+  int tail_total = 0;
+  for (int x = 0; x < kNumXcd; ++x) {
+    p.whole[x] = best_k == 1 ? ix[x] : std::min(ix[x], best_rounds * kCuPerXcd);
+    p.tail_first[x] = tail_total;
+    tail_total += ix[x] - p.whole[x];
+  }
+  p.tail_first[kNumXcd] = tail_total;
+  if (tail_total == 0) p.nsplit = 1;
+  p.wg_per_xcd = 0;
+  for (int x = 0; x < kNumXcd; ++x)
+    p.wg_per_xcd = std::max(p.wg_per_xcd, p.whole[x] + (ix[x] - p.whole[x]) * p.nsplit);
+  return p;
+}
+
+// Bytes of the split-KV partials of a plan.
+int64_t plan_partial_bytes(const WorkPlan& p, int head_dim, int64_t* o_bytes) {
+  const int64_t rows = (int64_t)p.nsplit * p.tail_first[kNumXcd] * kQTile;
+  const int64_t ob = align_up(rows * head_dim * 2, 256);
+  if (o_bytes) *o_bytes = ob;
+  return p.tail_first[kNumXcd] ? ob + align_up(rows * 8, 256) : 0;
 }
 
 struct MetaLayout {
@@ -197,11 +250,8 @@ int64_t workspace_bytes(const sdv2_config& c) {
   // every (nbatch, shared frames present) the stream can reach, warm-up included
   for (int nb = 1; nb <= c.stream_batch; ++nb)
     for (int shared = 0; shared <= c.sink_frames + c.window_frames; ++shared) {
-      const int ns = choose_nsplit(c, nb, (shared + c.chunk_frames) * tpf, (shared + 1) * tpf);
-      if (ns < 2) continue;
-      const int64_t rows = (int64_t)ns * nb * c.num_heads * c.chunk_frames * N;
-      const int64_t bytes = align_up(rows * c.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
-      if (bytes > best) best = bytes;
+      const WorkPlan p = make_plan(c, nb, (shared + c.chunk_frames) * tpf, (shared + 1) * tpf);
+      best = std::max(best, plan_partial_bytes(p, c.head_dim, nullptr));
     }
   return best;
 }
@@ -307,24 +357,24 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
     for (int t = 0; t < Tc; ++t) a.own_slot[b * Tc + t] = chunk_slot(cfg, c->step_first, b, t);
   a.tiles_per_frame = (int)(c->lay.tokens_padded / kTileKeys);
   a.total_tiles = (a.nshared + Tc) * a.tiles_per_frame;
-  a.nsplit = choose_nsplit(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
+  a.plan = make_plan(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
   a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.scale_log2_inv = 1.0f / a.scale_log2;
   a.neg_bias = -8.0f / a.scale_log2;
-  const int64_t rows = (int64_t)a.nsplit * nbatch * cfg.num_heads * Tc * c->N;
-  if (a.nsplit > 1) {
-    const int64_t need = align_up(rows * cfg.head_dim * 2, kAlign) + align_up(rows * 8, kAlign);
+  if (cfg.dtype != SDV2_F32 && a.plan.nsplit > 1) {
+    int64_t ob = 0;
+    const int64_t need = plan_partial_bytes(a.plan, cfg.head_dim, &ob);
     if (need > ws_bytes)
-      return fail(SDV2_ENOSPC, "%s of %lld bytes is too small for %d splits (%lld bytes)", ws_name,
-                  (long long)ws_bytes, a.nsplit, (long long)need);
+      return fail(SDV2_ENOSPC, "%s of %lld bytes is too small for %d splits of %d query tiles (%lld bytes)",
+                  ws_name, (long long)ws_bytes, a.plan.nsplit, a.plan.tail_first[kNumXcd], (long long)need);
     a.part_o = (uint16_t*)ws;
-    a.part_ml = (float2*)(ws + align_up(rows * cfg.head_dim * 2, kAlign));
+    a.part_ml = (float2*)(ws + ob);
   }
   SDV2_HIP(launch_attention(a, cfg.head_dim, cfg.dtype, (hipStream_t)stream));
-  if (a.nsplit > 1) {
-    CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.nsplit};
+  if (cfg.dtype != SDV2_F32 && a.plan.nsplit > 1) {
+    CombineArgs m{a.part_o, a.part_ml, d_out, (int)(Tc * c->N), a.H, nbatch, a.qtiles, a.plan};
     SDV2_HIP(launch_combine(m, cfg.head_dim, (hipStream_t)stream));
   }
   return ok();
@@ -836,6 +886,70 @@ int sdv2_plan_step(const sdv2_config* cfg, int64_t num_chunks, int64_t step, int
   if (nbatch) *nbatch = (int32_t)nb;
   if (commit_chunk) *commit_chunk = (c0 >= 0 && c0 < num_chunks) ? c0 : -1;
   if (newest_frame) *newest_frame = nb > 0 ? (hi + 1) * cfg->chunk_frames - 1 : -1;
+  return ok();
+}
+
+int sdv2_debug_check_plan(const sdv2_config* cfg, int32_t nbatch, int32_t nshared, int32_t* nsplit,
+                          int32_t* tail_items, int32_t* workgroups) {
+  if (int rc = validate(cfg)) return rc;
+  const sdv2_config& c = *cfg;
+  if (nbatch < 1 || nbatch > c.stream_batch) return fail(SDV2_EINVAL, "nbatch out of range");
+  if (nshared < 0 || nshared > c.sink_frames + c.window_frames) return fail(SDV2_EINVAL, "nshared out of range");
+  const int64_t N = (int64_t)c.grid_h * c.grid_w, R = c.chunk_frames * N;
+  const int tpf = (int)(align_up(N, kTileKeys) / kTileKeys);
+  const WorkPlan p = make_plan(c, nbatch, (nshared + c.chunk_frames) * tpf, (nshared + 1) * tpf);
+  const int qtiles = (int)((R + kQTile - 1) / kQTile), items = nbatch * c.num_heads * qtiles;
+  const int ntail = p.tail_first[kNumXcd];
+  if (p.first[0] != 0 || p.first[kNumXcd] != items) return fail(SDV2_EINVAL, "plan: items not partitioned");
+  if (ntail > 0 && p.nsplit < 2) return fail(SDV2_EINVAL, "plan: tail items with one split");
+  // every key tile of every item covered once; whole items by one workgroup; partial rows in range
+  std::vector<std::vector<int>> cover(items);
+  std::vector<int> tail_seen(ntail, 0);
+  int wg = 0;
+  for (int b = 0; b < kNumXcd * p.wg_per_xcd; ++b) {
+    WorkItem w;
+    if (!plan_item(p, qtiles, nbatch, b, w)) continue;
+    ++wg;
+    if (w.head < 0 || w.head >= c.num_heads || w.elem < 0 || w.elem >= nbatch || w.qtile < 0 || w.qtile >= qtiles)
+      return fail(SDV2_EINVAL, "plan: workgroup %d decodes out of range", b);
+    const int item = (w.head * nbatch + w.elem) * qtiles + w.qtile;
+    const int x = b % kNumXcd;
+    if (item < p.first[x] || item >= p.first[x + 1]) return fail(SDV2_EINVAL, "plan: item %d off its XCD", item);
+    if ((w.tail < 0) != (w.nsplit == 1) || w.split < 0 || w.split >= w.nsplit)
+      return fail(SDV2_EINVAL, "plan: workgroup %d split %d of %d tail %d", b, w.split, w.nsplit, w.tail);
+    if (w.tail >= 0) {
+      if (w.tail >= ntail) return fail(SDV2_EINVAL, "plan: tail index %d of %d", w.tail, ntail);
+      int h2, e2, q2;
+      plan_tail(p, qtiles, nbatch, w.tail, h2, e2, q2);
+      if (h2 != w.head || e2 != w.elem || q2 != w.qtile) return fail(SDV2_EINVAL, "plan: tail %d maps back wrong", w.tail);
+      ++tail_seen[w.tail];
+    }
+    // the kernels' split of the item's walk (block-causal: it ends at the last own frame the
+    // query tile sees)
+    const int tq_hi = (int)std::min<int64_t>(c.chunk_frames - 1, ((int64_t)w.qtile * kQTile + kQTile - 1) / N);
+    const int tiles_q = (nshared + tq_hi + 1) * tpf;
+    const int t0 = (int)((int64_t)w.split * tiles_q / w.nsplit), t1 = (int)((int64_t)(w.split + 1) * tiles_q / w.nsplit);
+    if (t1 <= t0) return fail(SDV2_EINVAL, "plan: workgroup %d has no key tile", b);
+    for (int t = t0; t < t1; ++t) cover[item].push_back(t);
+  }
+  for (int i = 0; i < items; ++i) {
+    std::vector<int>& v = cover[i];
+    std::sort(v.begin(), v.end());
+    const int q = i % qtiles;
+    const int tq_hi = (int)std::min<int64_t>(c.chunk_frames - 1, ((int64_t)q * kQTile + kQTile - 1) / N);
+    const int tiles_q = (nshared + tq_hi + 1) * tpf;
+    if ((int)v.size() != tiles_q) return fail(SDV2_EINVAL, "plan: item %d covered %zu of %d tiles", i, v.size(), tiles_q);
+    for (int t = 0; t < tiles_q; ++t)
+      if (v[t] != t) return fail(SDV2_EINVAL, "plan: item %d tile %d not covered exactly once", i, t);
+  }
+  for (int t = 0; t < ntail; ++t)
+    if (tail_seen[t] != p.nsplit) return fail(SDV2_EINVAL, "plan: tail item %d has %d of %d splits", t, tail_seen[t], p.nsplit);
+  // the partial results fit the workspace sdv2_cache_size asks for
+  if (plan_partial_bytes(p, c.head_dim, nullptr) > workspace_bytes(c))
+    return fail(SDV2_EINVAL, "plan: partials exceed the workspace");
+  if (nsplit) *nsplit = p.nsplit;
+  if (tail_items) *tail_items = ntail;
+  if (workgroups) *workgroups = wg;
   return ok();
 }
 

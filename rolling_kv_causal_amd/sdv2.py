@@ -67,6 +67,8 @@ _PROTOS = {
     "sdv2_cache_slot_info": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)],
     "sdv2_cache_state": [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "sdv2_debug_fail_hip_call": [_I32],
+    "sdv2_debug_check_plan": [ctypes.POINTER(Config), _I32, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                              ctypes.POINTER(_I32)],
     "sdv2_plan_step": [ctypes.POINTER(Config), _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                        ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
 }
@@ -253,6 +255,14 @@ def sdv2_plan_step(cfg: Config, num_chunks: int, step: int) -> tuple[int, int, i
 
 def sdv2_debug_fail_hip_call(nth: int) -> None:
     _call("sdv2_debug_fail_hip_call", nth)
+
+
+def sdv2_debug_check_plan(cfg: Config, nbatch: int, nshared: int) -> tuple[int, int, int]:
+    """(split count, split query tiles, working workgroups) of the checked plan."""
+    ns, nt, wg = _I32(), _I32(), _I32()
+    _call("sdv2_debug_check_plan", ctypes.byref(cfg), nbatch, nshared, ctypes.byref(ns), ctypes.byref(nt),
+          ctypes.byref(wg))
+    return ns.value, nt.value, wg.value
 
 
 def sdv2_last_error() -> str:

@@ -436,3 +436,35 @@ def test_generator_path_check_follows_branches():
     for f8 in (False, True):
         gen.set_mode(f8)
         gen.check_paths(gen.loop_program())
+
+
+@pytest.mark.parametrize("c", configs.ALL, ids=lambda c: c.name)
+def test_split_plans_cover_every_key_tile_once(c, monkeypatch):
+    # For every state the stream reaches (elements in flight, cached frames present), the work
+    # plan the attention launches is checked by enumerating its workgroups through the kernels'
+    # own decoder: every key tile of every query tile exactly once, partials inside the workspace
+    cfg = sdv2.config_of(c)
+    for forced in (None, "3", "16"):
+        if forced:
+            monkeypatch.setenv("SDV2_NSPLIT", forced)
+        for nb in range(1, c.stream_batch + 1):
+            for shared in range(c.sink_frames + c.window_frames + 1):
+                sdv2.sdv2_debug_check_plan(cfg, nb, shared)
+    monkeypatch.delenv("SDV2_NSPLIT", raising=False)
+    if c.name == "wan14b_512_40layer_b4":
+        # 640 query tiles on 8 x 32 CUs: 512 run whole, 128 split in two (768 workgroups)
+        assert sdv2.sdv2_debug_check_plan(cfg, 4, 9) == (2, 128, 768)
+
+
+def test_split_plans_on_random_shapes():
+    rng = np.random.default_rng(11)
+    for _ in range(150):
+        c = configs.WAN13B_1LAYER.with_(num_heads=int(rng.integers(1, 48)), grid_h=int(rng.integers(1, 40)),
+                                        grid_w=int(rng.integers(1, 60)), sink_frames=int(rng.integers(0, 4)),
+                                        window_frames=int(rng.integers(1, 12)), chunk_frames=int(rng.integers(1, 4)),
+                                        stream_batch=1)
+        c = c.with_(stream_batch=int(rng.integers(1, 8 // c.chunk_frames + 1)))
+        cfg = sdv2.config_of(c)
+        nb = int(rng.integers(1, c.stream_batch + 1))
+        shared = int(rng.integers(0, c.sink_frames + c.window_frames + 1))
+        sdv2.sdv2_debug_check_plan(cfg, nb, shared)
