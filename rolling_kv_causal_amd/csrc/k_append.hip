@@ -63,23 +63,21 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
   static_assert(TILE == kTileKeys || (TILE == kTileKeys / 2 && KV != kKvFP8), "tile");
   constexpr int VSTR = D + (BF16 ? 2 : 1);   // LDS row stride (elements): breaks bank aliasing
   __shared__ T vs[TILE * VSTR];
-  __shared__ float2 tcs[kMaxTPairs];
 
   const int tiles = (a.N + kTileKeys - 1) / kTileKeys * (kTileKeys / TILE);   // padding included
   const int t = blockIdx.x / tiles;                // frame of the chunk
   const int n0 = (blockIdx.x - t * tiles) * TILE, head = blockIdx.y, b = blockIdx.z;
   const int fr = b * a.T + t;                      // frame index within the call
   const int tid = threadIdx.x;
-  if (tid < a.pt) tcs[tid] = a.tcs[fr][tid];
-  __syncthreads();
 
   const int c = tid % CH;
   const int64_t kdst = a.k_layer_off + (int64_t)a.dst_slot[fr] * a.slot_stride +
                        (int64_t)head * a.head_stride;
   constexpr int PASSES = TILE / ROWS;
-  // Every global load of the tile is issued before the first store: q is rotated in place,
-  // so loads placed after a store could not be hoisted by the compiler and each pass would
-  // cost a full memory round trip.
+  // Every global load of the tile is issued before the first store (q is rotated in place, so
+  // loads placed after a store could not be hoisted by the compiler and each pass would cost a
+  // full memory round trip), and the q, k, v rows before the (cos, sin) values, which come
+  // straight from the arguments and tables: nothing waits before the rows are requested.
   uint4 qv[PASSES], kv[PASSES], vv[PASSES];
   float2 cs[PASSES][VEC / 2];
 #pragma unroll
@@ -90,16 +88,22 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
       qv[pass] = *(const uint4*)((const T*)a.q + off);
       kv[pass] = *(const uint4*)((const T*)a.k + off);
       vv[pass] = *(const uint4*)((const T*)a.v + off);
+    } else {                                   // padding tokens of V^T stay zero
+      vv[pass] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int n = n0 + pass * ROWS + tid / CH;
+    if (n < a.N) {
       const int hr = n / a.grid_w, wc = n - hr * a.grid_w;
 #pragma unroll
       for (int j = 0; j < VEC / 2; ++j) {
         const int p = c * (VEC / 2) + j;
-        cs[pass][j] = p < a.pt ? tcs[p]
+        cs[pass][j] = p < a.pt ? a.tcs[fr][p]
                       : p < a.pt + a.ph ? a.tab_h[hr * a.ph + (p - a.pt)]
                                         : a.tab_w[wc * a.pw + (p - a.pt - a.ph)];
       }
-    } else {                                   // padding tokens of V^T stay zero
-      vv[pass] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 #pragma unroll

@@ -274,68 +274,86 @@ hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s) {
 
 // ---- motion: d_t = sqrt(sum (x_t - x_{t-1})^2 / n), fp64 ----------------------------------
 // [NEWS] algorithm item 2 / [WT] motion-aware noise scheduler: the distance between consecutive
-// latent frames.  Pass 1: a block walks kMotionRun consecutive frame pairs of one part of
-// kMotionChunk elements, keeping the previous frame's values in registers, so every frame is
-// read once; per pair it sums (x_t - x_{t-1})^2 in fp64 (lane strides, a butterfly in each
-// wave, the four waves in order).  Pass 2 adds the parts of a frame in order.  A fixed
-// reduction order: results are run-to-run identical.
+// latent frames.  Pass 1: a block walks kMotionRun consecutive frame pairs over one part of
+// kMotionChunk elements, so every frame of the run is read once; each thread keeps the frames
+// of the next kMotionDepth pairs in flight in a ring of registers.  The run is unrolled and
+// branch-free, so every pair waits only for its own frame: tail elements read one fixed element
+// in every frame (difference zero), frames past the run repeat its last frame, and each lane
+// stores its wave's pair sum (lanes other than 0 into a slot of their own).  Per pair the sum of
+// (x_t - x_{t-1})^2 is taken in fp64 (lane strides, a butterfly in each wave, the four waves in
+// order).  Pass 2 adds the parts of a frame in order.  A fixed reduction order: results are
+// run-to-run identical.
 constexpr int kMotionChunk = 4096;   // elements of a part: 16 per thread
 constexpr int kMotionRun = 32;       // frame pairs per block
+constexpr int kMotionDepth = 3;      // frames in flight per thread (with 4 blocks per CU)
 
 int motion_parts(int64_t elems) { return (int)((elems + kMotionChunk - 1) / kMotionChunk); }
 
-template <bool VEC4>
-__global__ __launch_bounds__(256) void motion_partial_kernel(const float* x, int64_t n, int F,
-                                                             double* partials, int parts) {
+// One run of pairs over one part.  TAIL: the part reaches past the frame's end; an
+// out-of-range load reads element 0 of the series in every frame, so its difference is zero.
+template <bool VEC4, bool TAIL>
+__device__ __forceinline__ void motion_run(const float* x, int64_t n, int t0, int pairs,
+                                           int64_t lo, double* red) {
   constexpr int E = kMotionChunk / 256;            // elements per thread
-  __shared__ double red[4][kMotionRun];
-  const int p = blockIdx.x, t0 = blockIdx.y * kMotionRun;   // pairs (t0 + i, t0 + i + 1)
-  const int pairs = F - t0 < kMotionRun ? F - t0 : kMotionRun;
-  const int64_t lo = (int64_t)p * kMotionChunk;
-  float prev[E], cur[E];
+  constexpr int L = VEC4 ? E / 4 : E;              // loads per frame
+  // frame slots (frame t0 + i lives in slot i % NS); the scalar path, with 16 loads per frame,
+  // keeps one frame in flight
+  constexpr int NS = (VEC4 ? kMotionDepth : 1) + 1;
+  const int last = t0 + pairs;                     // last frame of the run
+  float f[NS][E];
   auto load = [&](int t, float* v) {
-    const float* f = x + (int64_t)t * n + lo;
-    if constexpr (VEC4) {                          // n % 4 == 0 and 16-byte aligned frames
+    const int64_t fb = (int64_t)(t < last ? t : last) * n + lo;
 #pragma unroll
-      for (int j = 0; j < E / 4; ++j) {
-        const int64_t i = 4 * (threadIdx.x + 256 * j);
-        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lo + i < n) w = *(const float4*)(f + i);
+    for (int j = 0; j < L; ++j) {
+      const int r = VEC4 ? 4 * ((int)threadIdx.x + 256 * j) : (int)threadIdx.x + 256 * j;
+      // (the multiplier form keeps the tail's choice arithmetic: no branch around the load)
+      const float* ptr = TAIL ? x + (fb + r) * (int64_t)(lo + r < n) : x + fb + r;
+      if constexpr (VEC4) {                        // n % 4 == 0 and 16-byte aligned frames
+        const float4 w = *(const float4*)ptr;
         v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const int64_t i = threadIdx.x + 256 * j;
-        v[j] = lo + i < n ? f[i] : 0.f;
+      } else {
+        v[j] = *ptr;
       }
     }
   };
-  load(t0, prev);
-  double acc[kMotionRun];
 #pragma unroll
-  for (int k = 0; k < kMotionRun; ++k) {
-    acc[k] = 0.0;
-    if (k < pairs) {
-      load(t0 + k + 1, cur);
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const double d = (double)cur[j] - (double)prev[j];
-        acc[k] = fma(d, d, acc[k]);
-        prev[j] = cur[j];
-      }
-    }
-  }
+  for (int i = 0; i < NS; ++i) load(t0 + i, f[i]);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int k = 0; k < kMotionRun; ++k) {
-    const double v = wave_sum(acc[k]);
-    if (lane == 0) red[wave][k] = v;
+  for (int k = 0; k < kMotionRun; ++k) {           // pair k: frames in slots k and k + 1 (mod NS)
+    const float* prev = f[k % NS];
+    const float* cur = f[(k + 1) % NS];
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const double df = (double)cur[j] - (double)prev[j];
+      acc = fma(df, df, acc);
+    }
+    if (k + NS <= kMotionRun) load(t0 + k + NS, f[k % NS]);   // the slot's frame is done
+    // the scheduler keeps each pair's arithmetic between the refills (else it computes as early
+    // as possible and waits for every load right after it is issued)
+    __builtin_amdgcn_sched_barrier(0);
+    const double v = wave_sum(acc);
+    red[lane == 0 && k < pairs ? wave * kMotionRun + k : 4 * kMotionRun + threadIdx.x] = v;
   }
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(256, 4) void motion_partial_kernel(const float* x, int64_t n, int F,
+                                                                double* partials, int parts) {
+  // per-wave pair sums; every lane stores (the others into a slot of their own), so the store
+  // is not a branch the compiler could hoist the next pairs' arithmetic over
+  __shared__ double red[4 * kMotionRun + 256];
+  const int p = blockIdx.x, t0 = blockIdx.y * kMotionRun;   // pairs (t0 + k, t0 + k + 1)
+  const int pairs = F - t0 < kMotionRun ? F - t0 : kMotionRun;
+  const int64_t lo = (int64_t)p * kMotionChunk;
+  if (lo + kMotionChunk <= n) motion_run<VEC4, false>(x, n, t0, pairs, lo, red);
+  else motion_run<VEC4, true>(x, n, t0, pairs, lo, red);
   __syncthreads();
   if ((int)threadIdx.x < pairs) {
-    const int k = threadIdx.x;
-    partials[(int64_t)(t0 + k) * parts + p] = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+    const double* r = red + threadIdx.x;
+    partials[(int64_t)(t0 + threadIdx.x) * parts + p] =
+        ((r[0] + r[kMotionRun]) + r[2 * kMotionRun]) + r[3 * kMotionRun];
   }
 }
 

@@ -324,6 +324,33 @@ def test_motion_l2_and_noise_schedule():
     np.testing.assert_allclose(dist[:2].cpu().numpy(), want2, rtol=1e-12)
 
 
+def test_motion_l2_long_series():
+    """1025 frames of 16x60x104 (the measured series): 32 runs of 32 pairs; 70 frames: a last
+    run of 5 pairs; each frame's last part of 1536 elements takes the tail loads.  The scalar
+    path (unaligned base, 5001 elements: a part of 905) over 40 frames.  Two calls give
+    identical bits (fixed reduction order)."""
+    cfg = configs.WAN13B_480P_B2
+    m = cfg.motion
+    frames = inputs.motion_frames(cfg, frames=1025)
+    x = torch.from_numpy(frames).cuda()
+    for nf in (1025, 70):
+        log(f"motion_l2: {nf} frames of {m.elems} elements")
+        dist = torch.empty(nf - 1, dtype=torch.float64, device="cuda")
+        ws = torch.empty(sdv2.sdv2_motion_workspace_size(nf, m.elems), dtype=torch.uint8, device="cuda")
+        sdv2.sdv2_motion_l2(x[:nf], nf, m.elems, dist, ws)
+        got = dist.cpu().numpy()
+        np.testing.assert_allclose(got, omotion.frame_distances(frames[:nf]), rtol=1e-12, atol=0)
+        sdv2.sdv2_motion_l2(x[:nf], nf, m.elems, dist, ws)
+        assert np.array_equal(dist.cpu().numpy(), got)
+    nf, ne = 40, 5001
+    log(f"motion_l2: {nf} frames of {ne} elements, unaligned")
+    flat = frames.reshape(-1)[1:1 + nf * ne].reshape(nf, ne)
+    dist = torch.empty(nf - 1, dtype=torch.float64, device="cuda")
+    ws = torch.empty(sdv2.sdv2_motion_workspace_size(nf, ne), dtype=torch.uint8, device="cuda")
+    sdv2.sdv2_motion_l2(x.view(-1)[1:1 + nf * ne], nf, ne, dist, ws)
+    np.testing.assert_allclose(dist.cpu().numpy(), omotion.frame_distances(flat), rtol=1e-12, atol=0)
+
+
 def test_repeat_runs_are_bitwise_identical():
     cfg = configs.WAN13B_1LAYER.with_(num_chunks=12)
     outs = []
