@@ -52,6 +52,14 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// 16-byte store with the non-temporal hint: data written once and read by a later launch (from
+// HBM, usually on another XCD) does not displace the L2 lines of the data still being read.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* p, const uint4& w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Workgroup id -> work item such that consecutive work items run on the same XCD (each XCD
 // has its own L2): hardware sends workgroup i to XCD i % 8.  A bijection on [0, G).
 __device__ __forceinline__ int xcd_remap(int bid, int G) {

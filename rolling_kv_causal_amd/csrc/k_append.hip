@@ -8,7 +8,8 @@
 // pw by the column angle of the token (tables in device memory).
 //
 // One workgroup per (frame of the chunk, 64-token tile of the frame, head, element); 16-byte
-// loads and stores throughout.  K rows go to the cache as [token][d]; V goes through LDS and
+// loads and stores throughout, the stores with the non-temporal hint (the attention reads the
+// rows later, from HBM).  K rows go to the cache as [token][d]; V goes through LDS and
 // leaves transposed as [d][token] rows of the tile, so the attention kernel can read V^T
 // fragments contiguously.  Frame t of element b has its own slot and temporal angle.
 #include "common.h"
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
     if (n < a.N) {
       const int64_t off = ((int64_t)(fr * a.N + n) * a.H + head) * D + c * VEC;
       rotate16<BF16>(qv[pass], cs[pass]);
-      *(uint4*)((T*)a.q + off) = qv[pass];
+      store16_nt((T*)a.q + off, qv[pass]);
       if constexpr (KV == kKvFP8) {            // 8 dims -> one 8-byte unit at its e4m3 position
         float kr[8];
         rotate8_f32(kv[pass], cs[pass], kr);
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
         *(uint2*)((TC*)a.kv + kdst + (int64_t)n * D + fp8_pos(c * VEC)) = w;
       } else {
         rotate16<BF16>(kv[pass], cs[pass]);
-        *(uint4*)((TC*)a.kv + kdst + (int64_t)n * D + c * VEC) = kv[pass];
+        store16_nt((TC*)a.kv + kdst + (int64_t)n * D + c * VEC, kv[pass]);
       }
     }
   }
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
       for (int j = 0; j < VEC; ++j) vals[j] = vs[(kc * VEC + j) * VSTR + drow];
       __builtin_memcpy(&w, vals, sizeof(w));
     }
-    *(uint4*)(vdst + (int64_t)drow * a.Npad + kc * TVEC) = w;
+    store16_nt(vdst + (int64_t)drow * a.Npad + kc * TVEC, w);
   }
 }
 

@@ -40,8 +40,9 @@ hipError_t launch_copy_slots(const CopyArgs& a, hipStream_t s) {
 // threshold; rotating every cached key by -delta on the temporal pairs (queries are rotated at
 // the new base by the append) keeps every score unchanged.
 // Work item = one 16-byte chunk of a key row among the first a.cpr chunks, which hold every
-// temporal pair (the rest of the chunk is written back unchanged); consecutive threads take
-// consecutive chunks of a row, then the next row; each thread has four chunks in flight.
+// temporal pair and fill whole 128-byte lines (the other dims are written back unchanged);
+// consecutive threads take consecutive chunks of a row, then the next row; each thread has
+// four chunks in flight; stores carry the non-temporal hint.
 template <int KV>
 __device__ __forceinline__ void rebase_chunk(uint4& w, int c, const float2* cs, int pt) {
   if constexpr (KV == kKvBF16) {
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void rebase_kernel(const RebaseArgs a, int D) 
     for (int u = 0; u < U; ++u)
       if (ptr[u]) {
         rebase_chunk<KV>(w[u], (int)((i0 + u * 256) % a.cpr), cs, a.pt);
-        *ptr[u] = w[u];
+        store16_nt(ptr[u], w[u]);
       }
   }
 }
@@ -281,8 +282,8 @@ hipError_t launch_sink_decide(const SinkArgs& a, hipStream_t s) {
 // in every frame (difference zero), frames past the run repeat its last frame, and each lane
 // stores its wave's pair sum (lanes other than 0 into a slot of their own).  Per pair the sum of
 // (x_t - x_{t-1})^2 is taken in fp64 (lane strides, a butterfly in each wave, the four waves in
-// order).  Pass 2 adds the parts of a frame in order.  A fixed reduction order: results are
-// run-to-run identical.
+// order), into partials[part][pair].  Pass 2 adds the parts of a frame in order.  A fixed
+// reduction order: results are run-to-run identical.
 constexpr int kMotionChunk = 4096;   // elements of a part: 16 per thread
 constexpr int kMotionRun = 32;       // frame pairs per block
 constexpr int kMotionDepth = 3;      // frames in flight per thread (with 4 blocks per CU)
@@ -352,17 +353,26 @@ __global__ __launch_bounds__(256, 4) void motion_partial_kernel(const float* x, 
   __syncthreads();
   if ((int)threadIdx.x < pairs) {
     const double* r = red + threadIdx.x;
-    partials[(int64_t)(t0 + threadIdx.x) * parts + p] =
+    partials[(int64_t)p * F + t0 + threadIdx.x] =
         ((r[0] + r[kMotionRun]) + r[2 * kMotionRun]) + r[3 * kMotionRun];
   }
 }
 
+// partials[p][t]: one thread per frame pair adds the parts in order, eight loads in flight.
 __global__ __launch_bounds__(256) void motion_final_kernel(const double* partials, int parts,
                                                            int F, int64_t n, double* dist) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= F) return;
   double s = 0.0;
-  for (int p = 0; p < parts; ++p) s += partials[(int64_t)t * parts + p];
+  int p = 0;
+  for (; p + 8 <= parts; p += 8) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = partials[(int64_t)(p + i) * F + t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  for (; p < parts; ++p) s += partials[(int64_t)p * F + t];
   dist[t] = sqrt(s / (double)n);
 }
 

@@ -527,6 +527,9 @@ int sdv2_rope_refresh(sdv2_cache* c, int64_t newest_frame, int32_t* applied, voi
       if (cfg.dtype == SDV2_BF16_KV_FP8)
         for (int d = 0; d < 2 * a.pt; ++d) last = std::max(last, fp8_pos(d));
       a.cpr = last / per_chunk + 1;
+      // whole 128-byte lines of the row (the chunks past the temporal dims are written back
+      // unchanged): a write of part of a line makes the memory read the rest of it
+      a.cpr = std::min(cfg.head_dim * (int)c->lay.elem_bytes / 16, (a.cpr + 7) / 8 * 8);
       for (int i = 0; i < ns; ++i) a.slots[i] = slots[i];
       const double delta = (double)(count * T);
       for (int i = 0; i < a.pt; ++i) {
