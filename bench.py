@@ -250,7 +250,7 @@ def hbm_side_runs(c, append_us):
             stats.append(ev["stats"][0].elapsed_time(ev["stats"][1]))
     out["rope_append"] = entry(3 * tensor * eb + tensor * eb + 2 * tensor * kb, append_us, how)
     N = c.tokens
-    nslots = c.sink_frames + c.window_frames
+    nslots = c.window_frames + (0 if c.rope_pin_sinks else c.sink_frames)   # the slots a refresh turns
     pairs_bytes = c.num_layers * nslots * c.num_heads * N * c.rope_dim_t * kb
     out["rebase"] = entry(2 * pairs_bytes, sorted(reb)[2] * 1e3,
                           "refresh with T_reset = 1: every cached key's temporal pairs turned each step")
