@@ -460,7 +460,7 @@ def main():
     if not args.no_hbm:
         log("bench: HBM-bound kernels at the workload's shape")
         hbm = hbm_side_runs(c, g["append_us"])
-        if prof and prof.get("combine_us") and prof.get("combine_bytes"):
+        if prof and prof.get("combine_us") and float(prof.get("combine_bytes") or 0) > 0:
             us, nb = float(prof["combine_us"]), float(prof["combine_bytes"])
             hbm["combine"] = {"bytes_per_call": int(nb), "us": us, "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                               "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
