@@ -121,6 +121,27 @@ def test_small_ragged_streams(kw):
     _stream(cfg, cfg.num_steps, layers=range(cfg.num_layers))
 
 
+def test_sink_decisions_left_on_the_device():
+    # sdv2_sink_replace with h_slot NULL (no host synchronisation): the decision and the copy
+    # happen on the device only.  Every output matches the oracle, whose sinks follow its own
+    # decisions; the fp64 statistics (alpha included) are checked at every commit; the cache
+    # holds the oracle's sink bytes while the library reports the sink slots as unknown.
+    cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5,
+                 grid_w=13, num_heads=2, sink_frames=2, window_frames=3, stream_batch=2, num_chunks=14,
+                 embed_dim=16, sink_threshold=0.2, embed_kind="iid", rope_refresh_period=5,
+                 softmax_scale=128 ** -0.5)
+    h = Harness(cfg, [0], sink_sync=False)
+    replaced = 0
+    for s in range(cfg.num_steps):
+        h.step(s, full=True)
+        h.check_outputs()
+        dec = h.finish_step()
+        replaced += bool(dec and dec["replaced"])
+        h.check_cache()
+    assert h.sinks_unknown and replaced >= 2
+    assert all(h.run.cache.slot_info(j)[0] == -2 for j in range(cfg.sink_frames))
+
+
 def test_split_without_visible_keys_for_some_rows(monkeypatch):
     # Four splits forced over a T' = 2 chunk of 81 tokens (two tiles per frame) with one sink
     # and a window of one: at steady state the walk of the query tile is 8 tiles, and the last

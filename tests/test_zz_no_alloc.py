@@ -1,6 +1,7 @@
 """sdv2_chunk_attention_static (no allocation, static device scratch) against
 sdv2_chunk_attention (create-time workspace): same kernels and split count, so the outputs must
-be bitwise equal.  Two calls in a row, the second on a smaller input, and the size limit."""
+be bitwise equal.  Two calls in a row, the second on a smaller input; the size limit; and
+replays of the call from a captured HIP graph."""
 import numpy as np
 import pytest
 import torch
@@ -80,4 +81,42 @@ def test_static_scratch_refuses_partials_beyond_its_size(monkeypatch):
     sdv2.sdv2_chunk_attention(run.cache.handle, 0, nb, qs[0], out, cfg.softmax_scale)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.count_nonzero(out) > 0
+    run.cache.close()
+
+
+def test_static_entry_point_replays_from_a_hip_graph():
+    # The callers the entry point is for: one chunk-attention call (split-KV: attention and
+    # combine launches, partials in the static array) captured into a HIP graph and replayed.
+    # Before each replay the output is set to NaN and an eager call of its own runs on the same
+    # array, with the program synchronising in between; every replay equals the eager result
+    # of the workspace entry point bit for bit.
+    cfg = configs.TINY_FP32.with_(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
+                                  grid_h=5, grid_w=13, num_heads=3, sink_frames=2, window_frames=3,
+                                  stream_batch=3, rope_refresh_period=0, sink_threshold=None, embed_dim=0,
+                                  embed_kind=None, softmax_scale=128 ** -0.5, name="graph_b3")
+    assert sdv2.sdv2_cache_size(sdv2.config_of(cfg))[2] > 0, "the call must use split-KV partials"
+    run, nb, qs = _steady(cfg, 8, 4)
+    q, h, scale = qs[0], run.cache.handle, cfg.softmax_scale
+    ref = torch.empty_like(q)
+    sdv2.sdv2_chunk_attention(h, 0, nb, q, ref, scale)
+    first = torch.empty_like(q)
+    sdv2.sdv2_chunk_attention_static(h, 0, nb, q, first, scale)     # set-up outside the capture
+    torch.cuda.synchronize()
+    assert torch.equal(first, ref)
+    out = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sdv2.sdv2_chunk_attention_static(h, 0, nb, q, out, scale)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        other = torch.full_like(q, float("nan"))
+        sdv2.sdv2_chunk_attention_static(h, 0, nb, q, other, scale)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref), f"eager call before replay {i}"
+        assert torch.equal(out, ref), f"replay {i}"
+    log(f"graph replays of {cfg.name}: 4 equal to the eager result")
+    del g
     run.cache.close()
