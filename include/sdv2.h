@@ -228,8 +228,12 @@ int sdv2_sink_replace(sdv2_cache* cache, int64_t frame, const float* d_embed,
 /* Batched motion estimate over a stored series ([NEWS] algorithm item 2; [WT] motion-aware
  * noise scheduler; the per-step form is the motion term of sdv2_sink_replace): for t = 1 ..
  * nframes-1, d_dist[t-1] = sqrt(sum_i (x_t[i] - x_{t-1}[i])^2 / elems_per_frame), summed in fp64
- * in a fixed order.  d_frames: fp32 [nframes][elems_per_frame]; d_dist: fp64 [nframes-1];
- * d_workspace: at least sdv2_motion_workspace_size() bytes.  Stateless. */
+ * in a fixed order.  d_frames: fp32 [nframes][elems_per_frame], 4-byte aligned (16-byte
+ * aligned with elems_per_frame % 4 == 0 takes 16-byte loads); d_dist: fp64 [nframes-1];
+ * d_workspace: at least sdv2_motion_workspace_size() bytes (per-part partial sums, contents
+ * unspecified on return); both 8-byte aligned.  Stateless; results are run-to-run identical.
+ * Errors: SDV2_EINVAL for nframes < 2, elems_per_frame < 1, more than 65536 frames, a NULL or
+ * misaligned pointer; SDV2_ENOSPC for a short workspace; nothing is launched then. */
 int sdv2_motion_workspace_size(int32_t nframes, int64_t elems_per_frame, size_t* bytes);
 int sdv2_motion_l2(const float* d_frames, int32_t nframes, int64_t elems_per_frame,
                    double* d_dist, void* d_workspace, size_t workspace_bytes, void* stream);

@@ -8,8 +8,9 @@
 //
 // Kernels here (the head_dim-128 bf16 and e4m3 cache kernel is in k_attention_w64.hip):
 //  * attn_bf16_kernel, bf16 cache with head_dim 64 (split-KV, flash-style): workgroup = 8 waves
-//    x 32 query rows of one (element, head); grid = heads x splits x elements x query tiles,
-//    remapped so that the workgroups sharing one head's K/V run on one XCD (one L2).  K tile
+//    x 32 query rows of one (element, head), a 256-row query tile; the grid follows the work
+//    plan (query tiles dealt to the XCDs in contiguous runs, so the workgroups sharing one
+//    head's K/V run on one XCD and one L2; only an XCD's last round of tiles split).  K tile
 //    [64 keys][d] and V^T tile [d][64 keys] (V is stored transposed in the cache) are staged
 //    through LDS, double-buffered.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K as the A
 //    operand from LDS, Q^T as the B operand held in registers); K rows sit in LDS with bits 2
