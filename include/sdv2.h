@@ -94,6 +94,11 @@ typedef struct sdv2_config {
   int32_t rope_pin_sinks; /* 0: a RoPE refresh rebases every cached key; 1: sinks keep their
                              labels (pinned anchors), only the window is rebased */
   double sink_threshold; /* tau; NaN or -INFINITY = sink refresh off */
+  double key_scale;      /* 0: K is cached as rotated.  > 0 (SDV2_BF16 cache, head_dim 128
+                            only): K is cached as rotated x key_scale x log2(e), rounded once
+                            from fp32, so the attention's exponent needs no per-score product;
+                            every sdv2_chunk_attention on the cache must then pass
+                            scale == key_scale. */
 } sdv2_config;
 
 /* Device layout of the KV cache (element offsets from d_kv, element = 4, 2 or 1 bytes).
@@ -160,7 +165,8 @@ int sdv2_rope_refresh(sdv2_cache* cache, int64_t newest_frame, int32_t* applied,
  * f = chunk*T' + t in rows [t*N, (t+1)*N); first_chunk must equal the number of chunks
  * committed so far and (first_chunk + nbatch)*T' - 1 the newest frame given to
  * sdv2_rope_refresh.  d_q is rotated in place at temporal position f - b0 (row h, col w); k is
- * rotated likewise (e4m3 cache: in fp32, then rounded) and written with v: element 0's frames
+ * rotated likewise (in fp32, then rounded once; with key_scale > 0 multiplied by
+ * key_scale * log2(e) before the rounding) and written with v: element 0's frames
  * into the slots they keep once
  * committed (sink slot f, or ring slot S + f mod (W+T'), which hold no attended frame), the
  * others into their staging slots.  Buffers:
@@ -173,7 +179,8 @@ int sdv2_cache_append(sdv2_cache* cache, int32_t layer, int64_t first_chunk, int
  * Q_rot = d_q_rot as rotated by sdv2_cache_append; inside the own chunk a query of frame t sees
  * the keys of frames 0..t (block-causal).  d_out: [nbatch][T'N][H][d], written.  The
  * workspace given at create time is used for split-KV partial results (calls on one cache
- * must not overlap in time).  The split-KV
+ * must not overlap in time).  On a cache with key_scale > 0, scale must equal key_scale
+ * (SDV2_EINVAL otherwise, nothing launched).  The split-KV
  * count follows a cost model; SDV2_NSPLIT=n (read at create and at each call; clamped to
  * [1, 16] and to the shortest walk) forces it, for tests and tuning: the cache must be created
  * with the variable set, so that the workspace covers the forced count. */

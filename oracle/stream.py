@@ -153,13 +153,16 @@ class OracleStream:
         return [e for e in self.sinks if e is not None] + list(self.window)
 
     # ---- attention of one element ---------------------------------------------------------
-    def attend(self, layer: int, elem: int, q, k, v, rows=None, heads=None, rotated="exact") -> np.ndarray:
+    def attend(self, layer: int, elem: int, q, k, v, rows=None, heads=None, rotated="exact",
+               key_scale=0.0) -> np.ndarray:
         """Output rows of element `elem` at the current step: float64 [len(rows), len(heads), d].
 
         q, k, v are that element's fresh storage arrays [T'N, H, d] (pre-RoPE).  rotated="bf16"
         rounds the rotated queries and keys to bf16 before the product, as a bf16 path stores
         them (reading R13: q_rot and the cached keys are bf16 tensors); the default keeps them
-        exact.
+        exact.  With rotated="bf16" and key_scale > 0 the keys are rounded after a product by
+        the fp32 value of key_scale * log2(e), as a cache created with that key scale holds
+        them, and the product is divided out again.
         """
         cfg = self.cfg
         N, T = cfg.tokens, cfg.chunk_frames
@@ -183,7 +186,11 @@ class OracleStream:
             key_frame.append(np.full(N, g))
         K_all = np.concatenate(k_parts)                            # [L, H, d]
         if rotated == "bf16" and cfg.dtype == "bf16" and not self.kv_fp8:
-            K_all = round_bf16(K_all)
+            if key_scale > 0:
+                kmul = float(np.float32(key_scale * np.log2(np.e)))
+                K_all = round_bf16(K_all * kmul) / kmul
+            else:
+                K_all = round_bf16(K_all)
         V_all = np.concatenate(v_parts)
         key_frame = np.concatenate(key_frame)
 

@@ -145,6 +145,7 @@ struct AppendArgs {
   int dst_slot[kMaxBatch]; // slot of frame t of element b, index b * T + t
   int pt, ph, pw;          // RoPE pairs per axis
   float2 tcs[kMaxBatch][kMaxTPairs];   // temporal (cos, sin) per frame (b * T + t) and pair
+  float kmul;              // factor on rotated k before its rounding (1, or key_scale * log2 e)
 };
 
 struct AttnArgs {
@@ -162,8 +163,9 @@ struct AttnArgs {
   int total_tiles;         // (nshared + T) * tiles_per_frame
   int qtiles;
   WorkPlan plan;
-  float scale_log2;        // softmax scale * log2(e)
+  float scale_log2;        // softmax scale * log2(e); 1 when the keys are cached times it
   float scale;
+  int scaled_keys;         // keys cached times scale * log2(e): the 64-row kernel's program without products
   float scale_log2_inv;    // 1 / scale_log2
   float neg_bias;          // -8 / scale_log2: start of the 64-row kernel's -(m + 8) / scale_log2 blocks
   int slots[kMaxShared];   // cache slots of the shared frames, in attention order

@@ -180,7 +180,9 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None):
     tile's stream, an OR of the words into the lazy-test accumulator.  Masked, every P word is
     ANDed with its mask word (ragged tile and causal), so masked keys weigh and sum to nothing.
     mreg(qb): given only when the rescale recomputes P, the register holding the shift
-    subtracted after the product (one fma).  (The row sums run on the matrix core.)"""
+    subtracted after the product (one fma).  (The row sums run on the matrix core.)
+    SCALED (keys cached times scale_log2, which the host then passes as 1): S is already the
+    exponent, so the exponentials read the accumulator and there is no product."""
     shifted = mreg is not None
     ops = []
     gi = 0
@@ -195,11 +197,15 @@ def softmax_ops(pc, masked, qbs=(0, 1), mreg=None):
                     if shifted:            # S * scale_log2 - shift
                         for j in range(4):
                             ops.append(f"v_fma_f32 {t[j]}, {s_elem(kb, qb, vs[j])}, %[sl], -{mreg(qb)}")
+                        src = t
+                    elif SCALED:           # S = s - m - BIAS already
+                        src = [s_elem(kb, qb, vs[j]) for j in range(4)]
                     else:                  # S * scale_log2 = s * scale_log2 - m - BIAS
                         for j in range(4):
                             ops.append(f"v_mul_f32 {t[j]}, %[sl], {s_elem(kb, qb, vs[j])}")
+                        src = t
                     for j in range(4):
-                        ops.append(f"v_exp_f32 {t[j]}, {t[j]}")
+                        ops.append(f"v_exp_f32 {t[j]}, {src[j]}")
                     words = [p_word(pc, qb, ks, w0), p_word(pc, qb, ks, w0 + 1)]
                     ops.append(f"v_cvt_pk_bf16_f32 {words[0]}, {t[0]}, {t[1]}")
                     ops.append(f"v_cvt_pk_bf16_f32 {words[1]}, {t[2]}, {t[3]}")
@@ -565,10 +571,12 @@ ACC = 246                                        # OR of the tile's P words (laz
 BIAS = 8                                         # P = 2^(s * scale_log2 - m - BIAS)
 
 
-def set_mode(f8):
-    """Program for the e4m3 cache (staged loads widened to bf16) or the bf16 cache."""
-    global F8
+def set_mode(f8, scaled=False):
+    """Program for the e4m3 cache (staged loads widened to bf16) or the bf16 cache; scaled: the
+    bf16 cache holds its keys times scale_log2 (no product per score)."""
+    global F8, SCALED
     F8 = f8
+    SCALED = scaled
 
 
 KTILE = 16384                                    # bytes of a K (or V^T) tile in LDS
@@ -577,6 +585,7 @@ NSLOT = 4                                        # ring slots of K and of V^T ti
 
 BASE = ((84, 86), (88, 90))                      # by parity: SGPR pairs of the K and V^T load bases
 F8 = False                                       # program for the e4m3 cache (set by set_mode)
+SCALED = False                                   # keys cached times scale_log2 (set by set_mode)
 STAGE = 16384                                    # e4m3 staging slot: K tile (8 KB), then V^T tile (8 KB)
 SK, SV = 234, 235                                # e4m3: this lane's staging read addresses (K, V^T)
 WKA, WVA = 232, 236                              # e4m3: widened-chunk write addresses (AGPRs; lo, hi per load)
@@ -733,7 +742,7 @@ def loop_program():
     """The whole tile loop: iterations t = 0 .. n-1 (NSLOT per pass, so that ring slots, P
     buffer and set-up parity are fixed in each copy), then the last PV.  m0 is saved and
     restored."""
-    set_mode(F8)
+    set_mode(F8, SCALED)
     RARE_ID[0] = 0
     lines = ["s_mov_b32 %[m0save], m0"] + init_block()
     # V^T base of tile 1 from the K cursor (tile 1), then vk, vf <- kk, kf and K advances to tile 2
@@ -834,6 +843,8 @@ def main():
            "// kernel as one asm program (register plan, blocks and hazard rules in the generator).", ""]
     set_mode(False)
     out.append(emit("SDV2_W64_LOOP", loop_program()))
+    set_mode(False, scaled=True)
+    out.append(emit("SDV2_W64_LOOP_SK", loop_program()))
     set_mode(True)
     out.append(emit("SDV2_W64_LOOP_FP8", loop_program()))
     set_mode(False)

@@ -18,14 +18,16 @@
 
 namespace sdv2 {
 
+// m: a factor on the rotated values before their rounding (the cache's key scale for k, 1 for
+// q: a product by 1 is exact).
 template <bool BF16>
-__device__ __forceinline__ void rotate16(uint4& w, const float2* cs) {
+__device__ __forceinline__ void rotate16(uint4& w, const float2* cs, float m = 1.f) {
   if constexpr (BF16) {
     uint32_t* u = reinterpret_cast<uint32_t*>(&w);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float x = bf16_bits_to_f32(u[j] & 0xffffu), y = bf16_bits_to_f32(u[j] >> 16);
-      u[j] = pack_bf16x2(x * cs[j].x - y * cs[j].y, x * cs[j].y + y * cs[j].x);
+      u[j] = pack_bf16x2((x * cs[j].x - y * cs[j].y) * m, (x * cs[j].y + y * cs[j].x) * m);
     }
   } else {
     float* f = reinterpret_cast<float*>(&w);
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
                                    pack_fp8x4(kr[4], kr[5], kr[6], kr[7]));
         *(uint2*)((TC*)a.kv + kdst + (int64_t)n * D + fp8_pos(c * VEC)) = w;
       } else {
-        rotate16<BF16>(kv[pass], cs[pass]);
+        rotate16<BF16>(kv[pass], cs[pass], a.kmul);
         store16_nt((TC*)a.kv + kdst + (int64_t)n * D + c * VEC, kv[pass]);
       }
     }

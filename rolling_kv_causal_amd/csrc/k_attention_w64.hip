@@ -1,4 +1,4 @@
-// Chunk attention, bf16 cache, head_dim 128: one wave per SIMD, 64 query rows per wave.
+// Chunk attention, bf16 and e4m3 caches, head_dim 128: one wave per SIMD, 64 query rows per wave.
 //
 // Same operation and split-KV interface as attn_bf16_kernel ([NEWS] method, algorithm item 1;
 // [REPO] core components; [WT] SLO-aware batching scheduler names FlashAttention as the exact
@@ -57,7 +57,9 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) |
 // staging slot (two slots of 16 KB, by iteration parity) and, at the top of the iteration that
 // publishes the tile, widens exactly those bytes to bf16 into the ring slot (exact conversion);
 // the rest of the loop is the bf16 one.
-template <bool F8>
+// SK: bf16 cache whose keys are stored times scale * log2(e): the scores already are the
+// exponent (the host passes scale_log2 = 1) and the program has no product per score.
+template <bool F8, bool SK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_w64_kernel(const AttnArgs a) {
   constexpr int D = 128, KRB = 256, VRB = 128, EB = F8 ? 1 : 2;   // EB: cache bytes per element
@@ -317,6 +319,11 @@ void attn_w64_kernel(const AttnArgs a) {
                  : SDV2_W64_INPUTS, SDV2_W64_PLAN_INPUTS, [ms] "s"(ms), "{v234}"(sk_addr), "{v235}"(sv_addr),
                    "{a[232:235]}"(wk), "{a[236:239]}"(wv)
                  : SDV2_W64_CLOBBERS, "v245", "v246");   // mask word temporary, OR of the P words
+  } else if constexpr (SK) {
+    asm volatile(SDV2_W64_LOOP_SK
+                 : SDV2_W64_OUTPUTS, SDV2_W64_NEGM_OUTPUTS
+                 : SDV2_W64_INPUTS, SDV2_W64_PLAN_INPUTS, [mk] "s"(mk), [mv] "s"(mv)
+                 : SDV2_W64_CLOBBERS, "v245", "v246");   // mask word temporary, OR of the P words
   } else {
     asm volatile(SDV2_W64_LOOP
                  : SDV2_W64_OUTPUTS, SDV2_W64_NEGM_OUTPUTS
@@ -394,9 +401,11 @@ void attn_w64_kernel(const AttnArgs a) {
 hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s) {
   const int grid = kNumXcd * a.plan.wg_per_xcd;
   if (kv == kKvFP8)
-    hipLaunchKernelGGL(attn_w64_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_w64_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.scaled_keys)
+    hipLaunchKernelGGL((attn_w64_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_w64_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_w64_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

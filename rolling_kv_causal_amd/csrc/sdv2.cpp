@@ -99,6 +99,10 @@ int validate(const sdv2_config* c) {
   if (c->rope_pin_sinks != 0 && c->rope_pin_sinks != 1) return fail(SDV2_EINVAL, "rope_pin_sinks must be 0 or 1");
   if (tau_on(*c) && (c->embed_dim < 1 || c->sink_frames < 1))
     return fail(SDV2_EINVAL, "sink refresh needs embed_dim >= 1 and sink_frames >= 1");
+  if (!(c->key_scale >= 0.0) || !std::isfinite(c->key_scale))
+    return fail(SDV2_EINVAL, "key_scale must be finite and >= 0");
+  if (c->key_scale > 0.0 && (c->dtype != SDV2_BF16 || c->head_dim != 128))
+    return fail(SDV2_EINVAL, "key_scale > 0 needs the bf16 cache with head_dim 128");
   // The attention tile loop forms a tile's byte offset inside a layer's K (or V) block as
   // slot * slot_bytes + tile offset in 32-bit scalar arithmetic, with slot_bytes a signed int.
   const int64_t N = (int64_t)c->grid_h * c->grid_w;
@@ -337,6 +341,8 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
   if (!d_q_rot || !d_out) return fail(SDV2_EINVAL, "q_rot and out must not be NULL");
   if (((uintptr_t)d_q_rot | (uintptr_t)d_out) & 15) return fail(SDV2_EINVAL, "q_rot and out must be 16-byte aligned");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(SDV2_EINVAL, "scale must be finite and > 0");
+  if (cfg.key_scale > 0.0 && scale != (float)cfg.key_scale)
+    return fail(SDV2_EINVAL, "scale %g differs from the cache's key_scale %g", (double)scale, cfg.key_scale);
 
   AttnArgs a{};
   a.q = d_q_rot;
@@ -360,7 +366,9 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
   a.plan = make_plan(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
   a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
   a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // keys cached times scale * log2(e): the scores are the exponent already
+  a.scaled_keys = cfg.key_scale > 0.0;
+  a.scale_log2 = a.scaled_keys ? 1.0f : (float)((double)scale * 1.4426950408889634);
   a.scale_log2_inv = 1.0f / a.scale_log2;
   a.neg_bias = -8.0f / a.scale_log2;
   if (cfg.dtype != SDV2_F32 && a.plan.nsplit > 1) {
@@ -604,6 +612,7 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   a.pt = cfg.rope_dim_t / 2;
   a.ph = cfg.rope_dim_h / 2;
   a.pw = cfg.rope_dim_w / 2;
+  a.kmul = cfg.key_scale > 0.0 ? (float)(cfg.key_scale * 1.4426950408889634) : 1.0f;
   for (int b = 0; b < nbatch; ++b)
     for (int t = 0; t < Tc; ++t) {
       const double p = (double)((first_chunk + b) * Tc + t - c->base);   // position f - b0

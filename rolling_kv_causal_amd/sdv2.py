@@ -29,7 +29,7 @@ class Config(ctypes.Structure):
                 ("rope_dim_w", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("rope_refresh_period", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("embed_dim", ctypes.c_int32), ("rope_pin_sinks", ctypes.c_int32),
-                ("sink_threshold", ctypes.c_double)]
+                ("sink_threshold", ctypes.c_double), ("key_scale", ctypes.c_double)]
 
 
 class Layout(ctypes.Structure):
@@ -116,14 +116,15 @@ def _stream(stream) -> int:
 def make_config(*, num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                 chunk_frames=1, stream_batch=1, rope_dim_t, rope_dim_h, rope_dim_w,
                 rope_theta=10000.0, rope_refresh_period=0, dtype="bf16", embed_dim=0,
-                rope_pin_sinks=False, sink_threshold=None, kv_fp8=False, **_ignored) -> Config:
+                rope_pin_sinks=False, sink_threshold=None, kv_fp8=False, key_scale=0.0, **_ignored) -> Config:
     """Build the C config; dtype "bf16"/"fp32" (activations); kv_fp8 with bf16: e4m3 cache;
-    sink_threshold None = sink refresh off."""
+    sink_threshold None = sink refresh off; key_scale > 0: keys cached times it (bf16, d 128)."""
     code = SDV2_F32 if dtype != "bf16" else (SDV2_BF16_KV_FP8 if kv_fp8 else SDV2_BF16)
     return Config(num_layers, num_heads, head_dim, grid_h, grid_w, sink_frames, window_frames,
                   chunk_frames, stream_batch, rope_dim_t, rope_dim_h, rope_dim_w, float(rope_theta),
                   rope_refresh_period, code, embed_dim,
-                  int(bool(rope_pin_sinks)), float("nan") if sink_threshold is None else float(sink_threshold))
+                  int(bool(rope_pin_sinks)), float("nan") if sink_threshold is None else float(sink_threshold),
+                  float(key_scale))
 
 
 def config_of(obj) -> Config:

@@ -65,10 +65,16 @@ class StreamConfig:
     motion: Optional[MotionConfig] = None
     rope_pin_sinks: bool = False      # refresh leaves the sinks' labels pinned (alternative reading)
     kv_fp8: bool = False              # bf16 activations with an OCP e4m3 KV cache
+    scaled_keys: bool = True          # cache option: keys stored times the softmax scale (where allowed)
 
     @property
     def tokens(self) -> int:          # N tokens per latent frame
         return self.grid_h * self.grid_w
+
+    @property
+    def key_scale(self) -> float:     # the cache's key scale: the softmax scale, or 0 (keys as rotated)
+        ok = self.scaled_keys and self.dtype == "bf16" and not self.kv_fp8 and self.head_dim == 128
+        return self.softmax_scale if ok else 0.0
 
     @property
     def chunk_rows(self) -> int:      # T' * N query rows per chunk

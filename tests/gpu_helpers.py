@@ -76,6 +76,7 @@ class Harness:
         # and the host's slot table reports the sink slots as unknown after the first decision
         self.sink_sync = sink_sync
         self.sinks_unknown = False
+        self.kmul = float(np.float32(cfg.key_scale * np.log2(np.e))) if cfg.key_scale > 0 else 1.0
         self.layers = list(layers)
         self.M = cfg.num_chunks if num_chunks is None else num_chunks
         self.ccfg = sdv2.config_of(cfg)
@@ -227,7 +228,8 @@ class Harness:
             for slot, e in entries:
                 self._check_slot_info(slot, e)
                 k_ref = orope.rope_frame(cfg, e.kv[layer][0], e.label)
-                k_got = host64(Kg[slot, :, :N, :].permute(1, 0, 2))
+                # a cache with a key scale holds K times the fp32 value of key_scale * log2(e)
+                k_got = host64(Kg[slot, :, :N, :].permute(1, 0, 2)) / self.kmul
                 assert_close(cfg, k_got, k_ref, f"K slot {slot} frame {e.frame}", scale=1 + r)
                 v_got = Vg[slot, :, :, :N].permute(2, 0, 1).contiguous()
                 if cfg.dtype == "bf16":

@@ -75,6 +75,31 @@ def test_out_of_protocol_calls_change_nothing():
     assert c.slot_info(0) == (0, 0)                                  # frame 0 is the sink
 
 
+def test_scaled_key_cache_refuses_another_scale():
+    # a cache created with a key scale holds its keys times it: an attention call with any other
+    # scale returns SDV2_EINVAL, launches nothing and changes nothing; the matching call runs
+    cfg = configs.TINY_FP32.with_(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
+                                  rope_refresh_period=0, sink_threshold=None, embed_dim=0, embed_kind=None,
+                                  softmax_scale=128 ** -0.5)
+    assert cfg.key_scale == cfg.softmax_scale
+    run = StreamRunner(sdv2.config_of(cfg), cfg.num_chunks, cfg.softmax_scale)
+    c = run.cache
+    shape = (1, cfg.chunk_rows, cfg.num_heads, cfg.head_dim)
+    q, k, v = (torch.randn(shape, device="cuda").to(torch.bfloat16) for _ in range(3))
+    out = torch.zeros_like(q)
+    c.refresh(0)
+    c.append(0, 0, 1, q, k, v)
+    before = snapshot(c)
+    msg = expect(sdv2.SDV2_EINVAL, c.attention, 0, 1, q, out, 2 * cfg.softmax_scale)
+    assert "key_scale" in msg and snapshot(c) == before
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    c.attention(0, 1, q, out, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.count_nonzero(out) > 0
+    run.cache.close()
+
+
 def test_create_fails_cleanly_on_an_injected_hip_error():
     cfg = sdv2.config_of(configs.TINY_FP32)
     kv, meta, ws = sdv2.sdv2_cache_size(cfg)

@@ -61,8 +61,9 @@ def _keys_times_8(steps):
     return qkv
 
 
+@pytest.mark.parametrize("scaled", [True, False], ids=["scaled-keys", "plain-keys"])
 @pytest.mark.parametrize("grid", [(5, 13), (8, 16)], ids=["ragged-tiles", "full-tiles"])
-def test_score_jump_rescales_mid_walk(monkeypatch, grid):
+def test_score_jump_rescales_mid_walk(monkeypatch, grid, scaled):
     # The keys of two committed frames are scaled by 8, so their scores rise far above the
     # running maximum of the tiles walked before them: the lazy rescale (row maximum, O and l
     # scaled, P recomputed) runs at tiles in the middle of the walk, in the masked variant too
@@ -76,16 +77,19 @@ def test_score_jump_rescales_mid_walk(monkeypatch, grid):
     # with weights perturbed by 2^-9 each moves by at most 2^-9 * 2 max|V|): max-abs 2^-7 M,
     # and a mean-abs of 2^-9 M.
     monkeypatch.setattr(inputs, "qkv", _keys_times_8({2, 5}))
+    # (scaled: the cache holds K times the softmax scale (key_scale), rounded after the product,
+    # and the oracle's storage mode rounds it the same way)
     cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
                  grid_h=grid[0], grid_w=grid[1], num_heads=2, sink_frames=1, window_frames=4,
-                 stream_batch=2, num_chunks=10, softmax_scale=128 ** -0.5)
+                 stream_batch=2, num_chunks=10, softmax_scale=128 ** -0.5, scaled_keys=scaled)
+    assert (cfg.key_scale > 0) == scaled
     h = Harness(cfg, [0])
     worst_rel = worst_abs = 0.0
     for s in range(cfg.num_steps):
         h.step(s, full=True)
         for b in range(len(h.st.plan["chunks"])):
             q, k, v = h.np_inputs[(0, b)]
-            ref = h.st.attend(0, b, q, k, v, rotated="bf16")
+            ref = h.st.attend(0, b, q, k, v, rotated="bf16", key_scale=cfg.key_scale)
             got = host64(h.run.out[0, b])
             M = max(1.0, float(np.abs(ref).max()))
             err = np.abs(got - ref)
@@ -111,7 +115,14 @@ def test_score_jump_rescales_mid_walk(monkeypatch, grid):
     dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=11, grid_w=13,
          num_heads=2, sink_frames=1, window_frames=2, stream_batch=2, num_chunks=8,
          softmax_scale=128 ** -0.5),
-], ids=["bf16-ragged-B3-refresh", "bf16-d64-S0", "fp32-d128-W1-B4", "bf16-sinks-iid", "bf16-3-tiles-per-frame"])
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5, grid_w=13,
+         num_heads=3, sink_frames=2, window_frames=3, stream_batch=3, rope_refresh_period=5, num_chunks=14,
+         softmax_scale=128 ** -0.5, scaled_keys=False),
+    dict(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=11, grid_w=13,
+         num_heads=2, sink_frames=1, window_frames=2, stream_batch=2, num_chunks=8,
+         softmax_scale=128 ** -0.5, scaled_keys=False),
+], ids=["bf16-ragged-B3-refresh", "bf16-d64-S0", "fp32-d128-W1-B4", "bf16-sinks-iid", "bf16-3-tiles-per-frame",
+        "bf16-ragged-B3-refresh-plain-keys", "bf16-3-tiles-per-frame-plain-keys"])
 def test_small_ragged_streams(kw):
     # token counts that are not multiples of the 64-key tile or the 128-row query tile,
     # degenerate windows (W = 1, S = 0), B up to 4, and several layers; 143 tokens give three

@@ -240,7 +240,8 @@ def test_generated_asm_writes_only_declared_registers():
         return "\n".join(out)
 
     shared = "".join(macro(m) for m in re.findall(r"#define (SDV2_W64_\w*(?:OUTPUTS|CLOBBERS))\b", src))
-    for prog_name, f8 in (("SDV2_W64_LOOP_FP8", True), ("SDV2_W64_LOOP\n", False)):
+    for prog_name, f8, scaled in (("SDV2_W64_LOOP_FP8", True, False), ("SDV2_W64_LOOP_SK", False, True),
+                                  ("SDV2_W64_LOOP\n", False, False)):
         i = src.index(f"asm volatile({prog_name}")
         stmt = src[i:src.index(");", i)]
         declared = set()
@@ -249,7 +250,7 @@ def test_generated_asm_writes_only_declared_registers():
                 declared |= _asm_register_set(c)
             for c in re.findall(r'"([vas]\d+)"', text):
                 declared |= _asm_register_set(c)
-        gen.F8 = f8
+        gen.set_mode(f8, scaled)
         written = set()
         for line in gen.loop_program():
             t = line.replace(",", " ").split()
@@ -377,12 +378,12 @@ def test_asm_program_scalar_operands_are_sgprs(tmp_path):
     programs = {}
     for name, body in re.findall(r"#define (SDV2_W64_LOOP\w*) \\\n(.*?)(?:\n\n|\Z)", header, re.S):
         programs[name] = [ln for ln in re.findall(r'"(.*?)\\n\\t"', body)]
-    assert set(programs) == {"SDV2_W64_LOOP", "SDV2_W64_LOOP_FP8"}
+    assert set(programs) == {"SDV2_W64_LOOP", "SDV2_W64_LOOP_SK", "SDV2_W64_LOOP_FP8"}
     asm = out.read_text()
     blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", asm, re.S)
     blocks = [[ln.strip() for ln in b.splitlines() if ln.strip() and not ln.strip().startswith(";")] for b in blocks]
     blocks = [b for b in blocks if len(b) > 1000]
-    assert len(blocks) == 2, [len(b) for b in blocks]
+    assert len(blocks) == 3, [len(b) for b in blocks]
 
     def pattern(tmpl):
         parts = re.split(r"(%\[\w+\]|%=)", tmpl.strip())
@@ -433,8 +434,8 @@ def test_generator_path_check_follows_branches():
                                                                    ".Ly:", "s_nop 0"])
     gen.check_paths(ok)
     # the committed programs pass along every path
-    for f8 in (False, True):
-        gen.set_mode(f8)
+    for f8, scaled in ((False, False), (False, True), (True, False)):
+        gen.set_mode(f8, scaled)
         gen.check_paths(gen.loop_program())
 
 
@@ -468,3 +469,29 @@ def test_split_plans_on_random_shapes():
         nb = int(rng.integers(1, c.stream_batch + 1))
         shared = int(rng.integers(0, c.sink_frames + c.window_frames + 1))
         sdv2.sdv2_debug_check_plan(cfg, nb, shared)
+
+
+def test_key_scale_validation():
+    # key_scale > 0 (keys cached times it) only for the bf16 cache at head_dim 128; it must be
+    # finite and >= 0; the scaled cache keeps the layout (same sizes)
+    from synth import configs
+    base = configs.WAN13B_1LAYER
+    assert base.key_scale == base.softmax_scale
+    good = sdv2.config_of(base)
+    plain = sdv2.config_of(base.with_(scaled_keys=False))
+    assert good.key_scale > 0 and plain.key_scale == 0
+    assert sdv2.sdv2_cache_size(good) == sdv2.sdv2_cache_size(plain)
+    for field, value in (("key_scale", -1.0), ("key_scale", float("nan")), ("key_scale", float("inf"))):
+        c = sdv2.config_of(base)
+        setattr(c, field, value)
+        with pytest.raises(sdv2.SDV2Error) as e:
+            sdv2.sdv2_cache_size(c)
+        assert e.value.code == sdv2.SDV2_EINVAL and "key_scale" in str(e.value)
+    for other in (base.with_(kv_fp8=True), base.with_(dtype="fp32"),
+                  base.with_(head_dim=64, rope_dim_t=24, rope_dim_h=20, rope_dim_w=20)):
+        assert other.key_scale == 0          # the workload leaves it off where it is not allowed
+        c = sdv2.config_of(other)
+        c.key_scale = 0.125
+        with pytest.raises(sdv2.SDV2Error) as e:
+            sdv2.sdv2_cache_size(c)
+        assert e.value.code == sdv2.SDV2_EINVAL and "key_scale" in str(e.value)

@@ -184,3 +184,36 @@ def test_round_bf16_pins():
                   -3.0 - q / 2, 2.0 ** -130, 65280.0 + 128.0])
     want = np.array([1.0, 1.0 + q, 1.0, 1.0 + 2 * q, 1.0 + q, -3.0, 2.0 ** -130, 65536.0])
     np.testing.assert_array_equal(round_bf16(x), want)
+
+
+def test_bf16_storage_mode_with_a_key_scale():
+    # rotated="bf16" with key_scale rounds the keys after a product by the fp32 value of
+    # key_scale * log2(e) and divides it out again.  With key_scale = 4 / log2(e) that product is
+    # exactly 4 in fp32, and rounding commutes with a power of two: the outputs equal those of the
+    # unscaled storage mode bit for bit.  With 1/sqrt(128) the keys round at other values: the
+    # outputs differ from the unscaled mode, by no more than the bf16 rounding of the keys moves
+    # them (both stay within that of the exact outputs).
+    cfg = tiny(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, num_heads=2,
+               stream_batch=2, num_chunks=8, softmax_scale=128 ** -0.5)
+    st = ost.OracleStream(cfg, layers=[0])
+    assert float(np.float32(4.0 / np.log2(np.e) * np.log2(np.e))) == 4.0
+    checked = 0
+    for s in range(cfg.num_steps):
+        plan = st.begin_step(s)
+        kv0 = {}
+        for b in range(len(plan["chunks"])):
+            q, k, v = inputs.qkv(cfg, s, 0, b)
+            exact = st.attend(0, b, q, k, v)
+            plain = st.attend(0, b, q, k, v, rotated="bf16")
+            four = st.attend(0, b, q, k, v, rotated="bf16", key_scale=4.0 / np.log2(np.e))
+            scaled = st.attend(0, b, q, k, v, rotated="bf16", key_scale=128 ** -0.5)
+            np.testing.assert_array_equal(four, plain)
+            if s >= 4:
+                assert not np.array_equal(scaled, plain)
+                checked += 1
+            for out in (plain, scaled):
+                assert np.abs(out - exact).max() <= 2e-2
+            if b == 0:
+                kv0[0] = (k, v)
+        st.end_step(kv0, None)
+    assert checked >= 4
