@@ -94,11 +94,14 @@ typedef struct sdv2_config {
   int32_t rope_pin_sinks; /* 0: a RoPE refresh rebases every cached key; 1: sinks keep their
                              labels (pinned anchors), only the window is rebased */
   double sink_threshold; /* tau; NaN or -INFINITY = sink refresh off */
-  double key_scale;      /* 0: K is cached as rotated.  > 0 (SDV2_BF16 cache, head_dim 128
-                            only): K is cached as rotated x key_scale x log2(e), rounded once
-                            from fp32, so the attention's exponent needs no per-score product;
-                            every sdv2_chunk_attention on the cache must then pass
-                            scale == key_scale. */
+  double key_scale;      /* 0: K is cached as rotated (SDV2_BF16, SDV2_F32).  > 0 (head_dim 128;
+                            required for SDV2_BF16_KV_FP8): K is cached as rotated x g, rounded
+                            once from fp32, g = key_scale x log2(e) for the bf16 cache and
+                            key_scale x log2(e) x 2^k for the e4m3 one, k = -floor(log2(
+                            key_scale x log2(e)) + 1/2) (keys keep their range; queries are
+                            then scaled by 2^-k inside the attention, exactly), so the
+                            attention's exponent needs no per-score product; every
+                            sdv2_chunk_attention on the cache must pass scale == key_scale. */
 } sdv2_config;
 
 /* Device layout of the KV cache (element offsets from d_kv, element = 4, 2 or 1 bytes).

@@ -36,6 +36,9 @@ Sources and readings:
   this covers the chunk's own frames as well, since they are read from the cache.  A RoPE
   refresh turns each stored key's temporal pairs by -T_reset and rounds again (the stored
   keys are all the cache has).  Queries, scores and outputs keep their own precision.
+  With a key scale (cfg.key_scale > 0) the cache stores every key times the fp32 factor
+  g = key_scale * log2(e) * 2^k, k = -floor(log2(key_scale * log2(e)) + 1/2) (so that the keys
+  keep their O(1) range in e4m3), rounded after the product; attention divides g out again.
 """
 from __future__ import annotations
 
@@ -63,6 +66,15 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     b = np.asarray(x, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
     b = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def fp8_key_factor(key_scale: float) -> float:
+    """The e4m3 cache's key factor g (module docstring): 1 without a key scale."""
+    if not key_scale > 0:
+        return 1.0
+    c = key_scale * np.log2(np.e)
+    k = -int(np.floor(np.log2(c) + 0.5))
+    return float(np.float32(c * 2.0 ** k))
 
 
 def schedule(cfg, s: int) -> dict:
@@ -112,6 +124,7 @@ class OracleStream:
         self.step = -1
         self.plan = None
         self.kv_fp8 = bool(getattr(cfg, "kv_fp8", False))
+        self.key_mul = fp8_key_factor(getattr(cfg, "key_scale", 0.0)) if self.kv_fp8 else 1.0
 
     # ---- step start: schedule + RoPE refresh ---------------------------------------------
     def begin_step(self, s: int) -> dict:
@@ -138,15 +151,17 @@ class OracleStream:
 
     def _stored(self, K_raw: np.ndarray, V: np.ndarray, label: int):
         """What the cache keeps for a frame at a label: raw K and V (exact mode, RoPE applied
-        when attending), or the rotated key and the value rounded to e4m3."""
+        when attending), or the rotated key (times the key factor) and the value rounded to
+        e4m3."""
         if self.kv_fp8:
-            return ofp8.round_fp8(rope.rope_frame(self.cfg, K_raw, label)), ofp8.round_fp8(V)
+            K = rope.rope_frame(self.cfg, K_raw, label) * self.key_mul
+            return ofp8.round_fp8(K), ofp8.round_fp8(V)
         return K_raw, V
 
     def key_rot(self, e: Entry, layer: int, heads=slice(None)) -> np.ndarray:
         """Rotated key of a cached entry at its label (the given heads)."""
         K = e.kv[layer][0][:, heads]
-        return K if self.kv_fp8 else rope.rope_frame(self.cfg, K, e.label)
+        return K / self.key_mul if self.kv_fp8 else rope.rope_frame(self.cfg, K, e.label)
 
     def cached_entries(self) -> list[Entry]:
         """Distinct cached entries: present sinks, then the window (oldest first)."""
@@ -181,7 +196,7 @@ class OracleStream:
         own_frames = [chunk * T + t for t in range(T)]
         for t, g in enumerate(own_frames):
             own = self._stored(kd[t * N:(t + 1) * N], vd[t * N:(t + 1) * N], g - self.base)
-            k_parts.append(own[0] if self.kv_fp8 else rope.rope_frame(cfg, own[0], g - self.base))
+            k_parts.append(own[0] / self.key_mul if self.kv_fp8 else rope.rope_frame(cfg, own[0], g - self.base))
             v_parts.append(own[1])
             key_frame.append(np.full(N, g))
         K_all = np.concatenate(k_parts)                            # [L, H, d]

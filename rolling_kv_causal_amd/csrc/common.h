@@ -166,6 +166,7 @@ struct AttnArgs {
   float scale_log2;        // softmax scale * log2(e); 1 when the keys are cached times it
   float scale;
   int scaled_keys;         // keys cached times scale * log2(e): the 64-row kernel's program without products
+  float qmul;              // e4m3 cache: queries times this power of two (2^-k of the key factor)
   float scale_log2_inv;    // 1 / scale_log2
   float neg_bias;          // -8 / scale_log2: start of the 64-row kernel's -(m + 8) / scale_log2 blocks
   int slots[kMaxShared];   // cache slots of the shared frames, in attention order

@@ -845,7 +845,7 @@ def main():
     out.append(emit("SDV2_W64_LOOP", loop_program()))
     set_mode(False, scaled=True)
     out.append(emit("SDV2_W64_LOOP_SK", loop_program()))
-    set_mode(True)
+    set_mode(True, scaled=True)
     out.append(emit("SDV2_W64_LOOP_FP8", loop_program()))
     set_mode(False)
     sys.stdout.write("\n".join(out))

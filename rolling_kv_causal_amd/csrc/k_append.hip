@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const AppendArgs a) {
       if constexpr (KV == kKvFP8) {            // 8 dims -> one 8-byte unit at its e4m3 position
         float kr[8];
         rotate8_f32(kv[pass], cs[pass], kr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kr[j] *= a.kmul;   // the cache's key factor, before the rounding
         const uint2 w = make_uint2(pack_fp8x4(kr[0], kr[1], kr[2], kr[3]),
                                    pack_fp8x4(kr[4], kr[5], kr[6], kr[7]));
         *(uint2*)((TC*)a.kv + kdst + (int64_t)n * D + fp8_pos(c * VEC)) = w;

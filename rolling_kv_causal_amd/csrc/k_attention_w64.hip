@@ -56,7 +56,8 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) |
 // F8: e4m3 cache.  Each wave loads its 2 KB share of a K and of a V^T tile (e4m3) into a
 // staging slot (two slots of 16 KB, by iteration parity) and, at the top of the iteration that
 // publishes the tile, widens exactly those bytes to bf16 into the ring slot (exact conversion);
-// the rest of the loop is the bf16 one.
+// the rest of the loop is the bf16 one.  Its keys are stored times key_scale * log2(e) * 2^k
+// and the queries are staged times 2^-k, so its program has no product per score either.
 // SK: bf16 cache whose keys are stored times scale * log2(e): the scores already are the
 // exponent (the host passes scale_log2 = 1) and the program has no product per score.
 template <bool F8, bool SK>
@@ -219,6 +220,21 @@ void attn_w64_kernel(const AttnArgs a) {
     for (int i = 0; i < 32; ++i) {
       q0[i] &= keep0;
       q1[i] &= keep1;
+    }
+  }
+  if constexpr (F8) {
+    // the e4m3 cache stores its keys times key_scale * log2(e) * 2^k: queries times 2^-k (a power
+    // of two: exact in fp32, and the product is a bf16 value, so its top half is exact)
+    const float qm = a.qmul;
+    auto scale2 = [qm](int w) {
+      const float lo = __uint_as_float((uint32_t)w << 16) * qm;
+      const float hi = __uint_as_float((uint32_t)w & 0xffff0000u) * qm;
+      return (int)((__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u));
+    };
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      q0[i] = scale2(q0[i]);
+      q1[i] = scale2(q1[i]);
     }
   }
 
@@ -401,7 +417,7 @@ void attn_w64_kernel(const AttnArgs a) {
 hipError_t launch_attention_w64(const AttnArgs& a, int kv, hipStream_t s) {
   const int grid = kNumXcd * a.plan.wg_per_xcd;
   if (kv == kKvFP8)
-    hipLaunchKernelGGL((attn_w64_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_w64_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
   else if (a.scaled_keys)
     hipLaunchKernelGGL((attn_w64_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   else

@@ -65,6 +65,18 @@ bool tau_on(const sdv2_config& c) {
   return !std::isnan(c.sink_threshold) && c.sink_threshold != -INFINITY;
 }
 
+// Key scaling: k = -floor(log2(key_scale * log2 e) + 1/2); the bf16 cache stores keys times
+// key_scale * log2 e, the e4m3 cache times key_scale * log2 e * 2^k (O(1), keeping e4m3's
+// range), with the queries staged times 2^-k.
+int key_exponent(double key_scale) {
+  return -(int)std::floor(std::log2(key_scale * 1.4426950408889634) + 0.5);
+}
+
+float key_factor(const sdv2_config& c) {
+  const double ks = c.key_scale * 1.4426950408889634;
+  return (float)(c.dtype == SDV2_BF16_KV_FP8 ? std::ldexp(ks, key_exponent(c.key_scale)) : ks);
+}
+
 int validate(const sdv2_config* c) {
   if (!c) return fail(SDV2_EINVAL, "config is NULL");
   if (c->num_layers < 1) return fail(SDV2_EINVAL, "num_layers must be >= 1");
@@ -101,8 +113,10 @@ int validate(const sdv2_config* c) {
     return fail(SDV2_EINVAL, "sink refresh needs embed_dim >= 1 and sink_frames >= 1");
   if (!(c->key_scale >= 0.0) || !std::isfinite(c->key_scale))
     return fail(SDV2_EINVAL, "key_scale must be finite and >= 0");
-  if (c->key_scale > 0.0 && (c->dtype != SDV2_BF16 || c->head_dim != 128))
-    return fail(SDV2_EINVAL, "key_scale > 0 needs the bf16 cache with head_dim 128");
+  if (c->key_scale > 0.0 && (c->dtype == SDV2_F32 || c->head_dim != 128))
+    return fail(SDV2_EINVAL, "key_scale > 0 needs a bf16 or e4m3 cache with head_dim 128");
+  if (c->dtype == SDV2_BF16_KV_FP8 && !(c->key_scale > 0.0))
+    return fail(SDV2_EINVAL, "the e4m3 cache needs key_scale > 0");
   // The attention tile loop forms a tile's byte offset inside a layer's K (or V) block as
   // slot * slot_bytes + tile offset in 32-bit scalar arithmetic, with slot_bytes a signed int.
   const int64_t N = (int64_t)c->grid_h * c->grid_w;
@@ -366,8 +380,10 @@ int attention_call(sdv2_cache* c, int32_t layer, int32_t nbatch, const void* d_q
   a.plan = make_plan(cfg, nbatch, a.total_tiles, (a.nshared + 1) * a.tiles_per_frame);
   a.qtiles = (int)((Tc * c->N + kQTile - 1) / kQTile);
   a.scale = scale;
-  // keys cached times scale * log2(e): the scores are the exponent already
+  // keys cached times scale * log2(e) (e4m3: times 2^k more, queries staged times 2^-k): the
+  // scores are the exponent already
   a.scaled_keys = cfg.key_scale > 0.0;
+  a.qmul = cfg.dtype == SDV2_BF16_KV_FP8 ? std::ldexp(1.0f, -key_exponent(cfg.key_scale)) : 1.0f;
   a.scale_log2 = a.scaled_keys ? 1.0f : (float)((double)scale * 1.4426950408889634);
   a.scale_log2_inv = 1.0f / a.scale_log2;
   a.neg_bias = -8.0f / a.scale_log2;
@@ -612,7 +628,7 @@ int sdv2_cache_append(sdv2_cache* c, int32_t layer, int64_t first_chunk, int32_t
   a.pt = cfg.rope_dim_t / 2;
   a.ph = cfg.rope_dim_h / 2;
   a.pw = cfg.rope_dim_w / 2;
-  a.kmul = cfg.key_scale > 0.0 ? (float)(cfg.key_scale * 1.4426950408889634) : 1.0f;
+  a.kmul = cfg.key_scale > 0.0 ? key_factor(cfg) : 1.0f;
   for (int b = 0; b < nbatch; ++b)
     for (int t = 0; t < Tc; ++t) {
       const double p = (double)((first_chunk + b) * Tc + t - c->base);   // position f - b0

@@ -73,7 +73,7 @@ class StreamConfig:
 
     @property
     def key_scale(self) -> float:     # the cache's key scale: the softmax scale, or 0 (keys as rotated)
-        ok = self.scaled_keys and self.dtype == "bf16" and not self.kv_fp8 and self.head_dim == 128
+        ok = self.scaled_keys and self.dtype == "bf16" and self.head_dim == 128
         return self.softmax_scale if ok else 0.0
 
     @property

@@ -6,6 +6,8 @@ cache, and attention through ``torch.nn.functional.scaled_dot_product_attention`
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -127,6 +129,17 @@ def history_output(cfg, s, elem, layer, sink_frames=None, pinned_sinks=False, fp
     return sdpa(q_rot, np.concatenate(k_parts), np.concatenate(v_parts), cfg.softmax_scale, mask)
 
 
+def e4m3_key_factor(cfg):
+    """The documented key factor of a key-scaled e4m3 cache, from its definition: c =
+    key_scale * log2(e), k = -floor(log2(c) + 1/2), g = fp32(c * 2^k); 1 without a key scale."""
+    ks = getattr(cfg, "key_scale", 0.0)
+    if not ks > 0:
+        return 1.0
+    c = ks * math.log2(math.e)
+    k = -math.floor(math.log2(c) + 0.5)
+    return float(np.float32(math.ldexp(c, k)))
+
+
 def _history_output_fp8(cfg, s, elem, layer, sink_frames):
     T, N, B, S, W = cfg.chunk_frames, cfg.tokens, cfg.stream_batch, cfg.sink_frames, cfg.window_frames
     T_reset = cfg.rope_refresh_period
@@ -135,20 +148,21 @@ def _history_output_fp8(cfg, s, elem, layer, sink_frames):
     sinks = list(range(min(S, n_committed))) if sink_frames is None else list(sink_frames)
     frames = sinks + list(range(max(S, n_committed - W), n_committed))
     b_s = refresh_base(cfg, s)
+    gk = e4m3_key_factor(cfg)                 # keys are stored times gk and read back divided
     k_parts, v_parts, kf = [], [], []
     for f in frames:
         k, v = committed_frame_kv(cfg, f, layer)
         b_c = refresh_base(cfg, f // T + B - 1)
-        key = round_e4m3(frame_rope(cfg, k, f - b_c))
+        key = round_e4m3(gk * frame_rope(cfg, k, f - b_c))
         for _ in range((b_s - b_c) // T_reset if T_reset else 0):
             key = round_e4m3(complex_rope(cfg, key, -T_reset, 0, 0))
-        k_parts.append(key)
+        k_parts.append(key / gk)
         v_parts.append(round_e4m3(v))
         kf.append(np.full(N, -1))
     q, k, v = (to_f64(cfg, a) for a in inputs.qkv(cfg, s, layer, elem))
     for t in range(T):
         g = chunk * T + t
-        k_parts.append(round_e4m3(frame_rope(cfg, k[t * N:(t + 1) * N], g - b_s)))
+        k_parts.append(round_e4m3(gk * frame_rope(cfg, k[t * N:(t + 1) * N], g - b_s)) / gk)
         v_parts.append(round_e4m3(v[t * N:(t + 1) * N]))
         kf.append(np.full(N, g))
     q_rot = np.concatenate([frame_rope(cfg, q[t * N:(t + 1) * N], chunk * T + t - b_s) for t in range(T)])

@@ -153,6 +153,19 @@ def test_sink_decisions_left_on_the_device():
     assert all(h.run.cache.slot_info(j)[0] == -2 for j in range(cfg.sink_frames))
 
 
+@pytest.mark.parametrize("S,W,T", [(3, 60, 1), (2, 60, 2)], ids=["S3-W60-T1", "S2-W60-T2"])
+def test_sixty_four_attended_frames(S, W, T):
+    # the library's limit S + W + T' = 64 (the attended frames' slots fill one 64-lane register):
+    # 65 tokens per frame (two key tiles, the second ragged), the window filled and wrapped, a
+    # refresh every 20 frames; every output of every step, the cache at fill, wrap and the end
+    cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5, grid_w=13,
+                 num_heads=2, sink_frames=S, window_frames=W, chunk_frames=T, stream_batch=2,
+                 num_chunks=(S + W) // T + 12, rope_refresh_period=20, softmax_scale=128 ** -0.5)
+    assert S + W + T == 64
+    fill = (S + W) // T
+    _stream(cfg, cfg.num_steps, cache_check=lambda s: s in (fill - 1, fill + 5, cfg.num_steps - 1))
+
+
 def test_split_without_visible_keys_for_some_rows(monkeypatch):
     # Four splits forced over a T' = 2 chunk of 81 tokens (two tiles per frame) with one sink
     # and a window of one: at steady state the walk of the query tile is 8 tiles, and the last

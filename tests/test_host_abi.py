@@ -240,7 +240,7 @@ def test_generated_asm_writes_only_declared_registers():
         return "\n".join(out)
 
     shared = "".join(macro(m) for m in re.findall(r"#define (SDV2_W64_\w*(?:OUTPUTS|CLOBBERS))\b", src))
-    for prog_name, f8, scaled in (("SDV2_W64_LOOP_FP8", True, False), ("SDV2_W64_LOOP_SK", False, True),
+    for prog_name, f8, scaled in (("SDV2_W64_LOOP_FP8", True, True), ("SDV2_W64_LOOP_SK", False, True),
                                   ("SDV2_W64_LOOP\n", False, False)):
         i = src.index(f"asm volatile({prog_name}")
         stmt = src[i:src.index(");", i)]
@@ -434,7 +434,7 @@ def test_generator_path_check_follows_branches():
                                                                    ".Ly:", "s_nop 0"])
     gen.check_paths(ok)
     # the committed programs pass along every path
-    for f8, scaled in ((False, False), (False, True), (True, False)):
+    for f8, scaled in ((False, False), (False, True), (True, True)):
         gen.set_mode(f8, scaled)
         gen.check_paths(gen.loop_program())
 
@@ -487,11 +487,18 @@ def test_key_scale_validation():
         with pytest.raises(sdv2.SDV2Error) as e:
             sdv2.sdv2_cache_size(c)
         assert e.value.code == sdv2.SDV2_EINVAL and "key_scale" in str(e.value)
-    for other in (base.with_(kv_fp8=True), base.with_(dtype="fp32"),
-                  base.with_(head_dim=64, rope_dim_t=24, rope_dim_h=20, rope_dim_w=20)):
+    for other in (base.with_(dtype="fp32"), base.with_(head_dim=64, rope_dim_t=24, rope_dim_h=20, rope_dim_w=20)):
         assert other.key_scale == 0          # the workload leaves it off where it is not allowed
         c = sdv2.config_of(other)
         c.key_scale = 0.125
         with pytest.raises(sdv2.SDV2Error) as e:
             sdv2.sdv2_cache_size(c)
         assert e.value.code == sdv2.SDV2_EINVAL and "key_scale" in str(e.value)
+    # the e4m3 cache requires it
+    fp8 = sdv2.config_of(base.with_(kv_fp8=True))
+    assert fp8.key_scale == base.softmax_scale
+    sdv2.sdv2_cache_size(fp8)
+    fp8.key_scale = 0.0
+    with pytest.raises(sdv2.SDV2Error) as e:
+        sdv2.sdv2_cache_size(fp8)
+    assert e.value.code == sdv2.SDV2_EINVAL and "key_scale" in str(e.value)

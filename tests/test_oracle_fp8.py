@@ -58,6 +58,32 @@ def _fp8_cfg(**kw):
     return TINY_FP32.with_(**base)
 
 
+def _fp8_scaled_cfg(**kw):
+    # head_dim 128 with the softmax scale as key scale: keys stored times the factor g
+    base = dict(head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, softmax_scale=128 ** -0.5)
+    base.update(kw)
+    cfg = _fp8_cfg(**base)
+    assert cfg.key_scale == cfg.softmax_scale
+    return cfg
+
+
+def test_key_factor_has_its_documented_form():
+    # g = key_scale * log2(e) * 2^k with k = -floor(log2(key_scale * log2(e)) + 1/2): g in
+    # [2^-1/2, 2^1/2] and key_scale * log2(e) / g a power of two; 4 / log2(e) gives g = 1 and
+    # no key scale gives 1
+    from oracle.stream import fp8_key_factor
+    assert fp8_key_factor(0.0) == 1.0
+    assert fp8_key_factor(4.0 / np.log2(np.e)) == 1.0
+    for ks in (128 ** -0.5, 64 ** -0.5, 1.0, 0.3, 5.0, 1e-3):
+        g = fp8_key_factor(ks)
+        c = ks * np.log2(np.e)
+        assert 2 ** -0.5 <= g <= 2 ** 0.5, (ks, g)
+        e = np.log2(c / g)
+        assert abs(e - np.round(e)) < 1e-6, (ks, g)           # a power of two up to fp32 rounding of g
+        assert g == brute.e4m3_key_factor(TINY_FP32.with_(dtype="bf16", head_dim=128, rope_dim_t=44,
+                                                           rope_dim_h=42, rope_dim_w=42, softmax_scale=ks))
+
+
 def test_brute_rounding_agrees_with_the_table_encoder():
     # two routes to e4m3 rounding (binade quantum vs nearest-table search) on values that
     # include every midpoint, both signs, subnormals and saturation
@@ -69,11 +95,13 @@ def test_brute_rounding_agrees_with_the_table_encoder():
     np.testing.assert_array_equal(brute.round_e4m3(x), fp8.round_fp8(x))
 
 
-@pytest.mark.parametrize("T,B,period", [(1, 1, 3), (1, 2, 3), (2, 2, 4), (1, 3, 0)])
-def test_fp8_stream_equals_history_fold(T, B, period):
+@pytest.mark.parametrize("T,B,period,scaled", [(1, 1, 3, False), (1, 2, 3, False), (2, 2, 4, False),
+                                               (1, 3, 0, False), (1, 2, 3, True), (2, 2, 4, True)])
+def test_fp8_stream_equals_history_fold(T, B, period, scaled):
     # every output at every step equals attention over keys rebuilt from the frame history:
     # commit-time rounding, one turn-back and rounding per refresh since, all relative to b0(s)
-    cfg = _fp8_cfg(chunk_frames=T, stream_batch=B, rope_refresh_period=period)
+    # (scaled: each key times the key factor before its roundings, divided out when attending)
+    cfg = (_fp8_scaled_cfg if scaled else _fp8_cfg)(chunk_frames=T, stream_batch=B, rope_refresh_period=period)
     st, outs = brute.run_oracle(cfg)
     assert (len(st.refresh_log) > 2) == (period > 0)
     for s in range(cfg.num_steps):
@@ -87,10 +115,14 @@ def ost_schedule(cfg, s):
     return ost.schedule(cfg, s)
 
 
-def test_fp8_cached_keys_are_e4m3_and_near_the_exact_rotation():
+@pytest.mark.parametrize("scaled", [False, True])
+def test_fp8_cached_keys_are_e4m3_and_near_the_exact_rotation(scaled):
     # stored keys and values are e4m3 values; each key pair is within the rounding errors of
-    # its commit and of each refresh since of the exact rotation at the current label
-    cfg = _fp8_cfg(window_frames=4, rope_refresh_period=2, num_chunks=12)
+    # its commit and of each refresh since of the exact rotation at the current label (scaled:
+    # of the exact rotation times the key factor g)
+    cfg = (_fp8_scaled_cfg if scaled else _fp8_cfg)(window_frames=4, rope_refresh_period=2, num_chunks=12)
+    g = brute.e4m3_key_factor(cfg)
+    assert (g != 1.0) == scaled
     st, _ = brute.run_oracle(cfg)
     r = len(st.refresh_log)
     assert r >= 4
@@ -99,7 +131,7 @@ def test_fp8_cached_keys_are_e4m3_and_near_the_exact_rotation():
         assert np.array_equal(fp8.round_fp8(K), K) and np.array_equal(fp8.round_fp8(V), V)
         k_raw, v_raw = brute.committed_frame_kv(cfg, e.frame, 0)
         np.testing.assert_array_equal(V, fp8.round_fp8(v_raw))
-        exact = brute.frame_rope(cfg, k_raw, e.label)
+        exact = g * brute.frame_rope(cfg, k_raw, e.label)
         err = np.hypot(K[..., 0::2] - exact[..., 0::2], K[..., 1::2] - exact[..., 1::2])
         norm = np.hypot(exact[..., 0::2], exact[..., 1::2])
         assert np.all(err <= (r + 1) * (2.0 ** -4 * 1.1 * norm + 2.0 ** -9)), e.frame
