@@ -12,8 +12,11 @@ and, interleaved with the MFMAs from the 20th on (S^T of key block 0 is complete
 stored bf16 queries unchanged and the first QK MFMA of a chain accumulates onto the
 -(m + BIAS) / scale_log2 block, so scale_log2 * S (one fp32 product per score) is the exponent;
 the P words are ORed for the lazy test, and eight 16x16x32 MFMAs add the previous tile's P row
-sums into l.  The e4m3 program differs only in its loads (staged,
-then widened to bf16 at the top of the iteration).
+sums into l.  Three programs: SDV2_W64_LOOP as described; SDV2_W64_LOOP_SK for a bf16 cache
+whose keys carry scale_log2 (the host passes scale_log2 = 1 and the exponentials read S
+directly: no product); SDV2_W64_LOOP_FP8 for the e4m3 cache, which carries it too (with the
+queries staged times a power of two), and differs from SK only in its loads (staged, then
+widened to bf16 at the top of the iteration).
 
 Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
 moves them; the loop is generated once per phase, so the ring slots of K(t) (ph) and V^T(t-1)

@@ -30,7 +30,8 @@
 // Softmax: base 2 with a lazy running maximum m per row.  Q is staged as stored (bf16) and the
 // first QK MFMA of each chain accumulates onto a block holding -(m + 8) / c, c = scale *
 // log2(e), so one fp32 product by c turns the MFMA result into the exponent: P = 2^(s c - m -
-// 8), the factor 2^-8 cancelling between O and l.  Only when some P word of a tile reaches 2 (a score
+// 8), the factor 2^-8 cancelling between O and l.  A cache whose keys carry c (SK, e4m3) runs
+// with c = 1 and a program without the product.  Only when some P word of a tile reaches 2 (a score
 // 9 above m, a NaN or an infinity), or a row has no maximum yet, is the row maximum taken and
 // O, l rescaled.  The row sums l are MFMAs over P with a selector operand.  Masks (ragged last
 // tile of a frame, block-causal own frames) are applied to the packed P words by AND.
@@ -93,7 +94,8 @@ void attn_w64_kernel(const AttnArgs a) {
   const int tq_wave = wrow / a.N;             // lowest frame of the wave's rows
 
   // Q^T operands: lane (g, r) holds Q[row][16 kd + 8g .. +7] as dwords 4kd..4kd+3 of q[qb],
-  // the stored bf16 values unchanged (the softmax scale is applied to each score in fp32).
+  // the stored bf16 values unchanged (the softmax scale is applied to each score in fp32, or
+  // carried by the keys; the e4m3 program scales them by a power of two below).
   i32x32 q0, q1;
   {
     const uint16_t* qb0 = (const uint16_t*)a.q + ((int64_t)(elem * R + (valid[0] ? row[0] : 0)) * a.H + head) * D + 8 * g;
