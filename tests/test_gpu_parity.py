@@ -7,9 +7,11 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import Harness, assert_close, host64, log, sample_rows
+from gpu_helpers import Harness, assert_close, dev, host64, log, sample_rows
 from oracle import motion as omotion
+from oracle import stream as ost
 from rolling_kv_causal_amd import sdv2
+from rolling_kv_causal_amd.stream import StreamRunner
 from synth import configs, inputs
 
 pytestmark = pytest.mark.gpu
@@ -164,6 +166,50 @@ def test_sixty_four_attended_frames(S, W, T):
     assert S + W + T == 64
     fill = (S + W) // T
     _stream(cfg, cfg.num_steps, cache_check=lambda s: s in (fill - 1, fill + 5, cfg.num_steps - 1))
+
+
+@pytest.mark.parametrize("kv_fp8,heads", [(False, 255), (True, 510)], ids=["bf16", "e4m3"])
+def test_layer_block_at_the_4gib_limit(kv_fp8, heads):
+    # 64 slots (S + W + T' = 1 + 62 + 1) of `heads` x 1024 tokens x 128 dims: a layer's K block
+    # of 4.28e9 bytes, just under the library's 2^32 limit, so once the ring has filled the tile
+    # loop's 32-bit slot offsets pass 2^31, and the refreshes at frames 32 and 64 rebase the
+    # whole block.  The first, middle and last heads carry the seeded inputs the oracle sees
+    # (a 3-head stream: heads are independent); the others are random on the device.  Every row
+    # of those heads at the fill step, after the wrap (the second refresh) and at the end.
+    base = configs.WAN13B_1LAYER.with_(sink_frames=1, window_frames=62, num_chunks=70, kv_fp8=kv_fp8)
+    big, small = base.with_(num_heads=heads), base.with_(num_heads=3)
+    ccfg = sdv2.config_of(big)
+    lay = sdv2.sdv2_cache_layout(ccfg)
+    block = lay.slots * lay.slot_stride * lay.elem_bytes
+    assert lay.slots == 64 and 2 ** 31 + 2 ** 30 < block < 2 ** 32, block
+    hsel = [0, heads // 2, heads - 1]
+    run = StreamRunner(ccfg, big.num_chunks, big.softmax_scale)
+    st = ost.OracleStream(small, layers=[0])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    worst = 0.0
+    for s in range(big.num_steps):
+        plan = st.begin_step(s)
+        q, k, v = inputs.qkv(small, s, 0, 0)
+
+        def qkv(s_, layer, nb):
+            out = []
+            for x in (q, k, v):
+                t = torch.randn((nb, big.chunk_rows, heads, big.head_dim), generator=gen, device="cuda")
+                t = (t * (big.q_prescale if x is q else 1.0)).to(torch.bfloat16)
+                t[0][:, hsel] = dev(small, x)
+                out.append(t)
+            return tuple(out)
+
+        info = run.step(s, qkv)
+        assert info["refreshed"] == sum(1 for (s_, _) in st.refresh_log if s_ == s)
+        if s in (62, 64, big.num_steps - 1):
+            log(f"4 GiB block ({'e4m3' if kv_fp8 else 'bf16'}, {heads} heads): step {s}, every row of heads {hsel}")
+            ref = st.attend(0, 0, q, k, v)
+            worst = max(worst, assert_close(small, host64(run.out[0, 0][:, hsel]), ref, f"out step {s}"))
+        st.end_step({0: (k, v)})
+    assert [f for (_, f) in st.refresh_log] == [32, 64]
+    log(f"4 GiB block: worst max-abs {worst:.3g}")
 
 
 def test_split_without_visible_keys_for_some_rows(monkeypatch):
@@ -372,8 +418,9 @@ def test_motion_l2_and_noise_schedule():
 def test_motion_l2_long_series():
     """1025 frames of 16x60x104 (the measured series): 32 runs of 32 pairs; 70 frames: a last
     run of 5 pairs; each frame's last part of 1536 elements takes the tail loads.  The scalar
-    path (unaligned base, 5001 elements: a part of 905) over 40 frames.  Two calls give
-    identical bits (fixed reduction order)."""
+    path (unaligned base, 5001 elements: a part of 905) over 40 frames; one pair, frames of a
+    single tail part (100 and 3 elements) and of one element.  Two calls give identical bits
+    (fixed reduction order)."""
     cfg = configs.WAN13B_480P_B2
     m = cfg.motion
     frames = inputs.motion_frames(cfg, frames=1025)
@@ -387,6 +434,14 @@ def test_motion_l2_long_series():
         np.testing.assert_allclose(got, omotion.frame_distances(frames[:nf]), rtol=1e-12, atol=0)
         sdv2.sdv2_motion_l2(x[:nf], nf, m.elems, dist, ws)
         assert np.array_equal(dist.cpu().numpy(), got)
+    # degenerate sizes: one pair; one part that is all tail (100 and 3 elements); one element
+    for nf, ne, off in ((2, 99840, 0), (5, 100, 0), (4, 3, 1), (3, 1, 0)):
+        log(f"motion_l2: {nf} frames of {ne} elements, offset {off}")
+        flat = frames.reshape(-1)[off:off + nf * ne].reshape(nf, ne)
+        dist = torch.empty(nf - 1, dtype=torch.float64, device="cuda")
+        ws = torch.empty(sdv2.sdv2_motion_workspace_size(nf, ne), dtype=torch.uint8, device="cuda")
+        sdv2.sdv2_motion_l2(x.view(-1)[off:off + nf * ne], nf, ne, dist, ws)
+        np.testing.assert_allclose(dist.cpu().numpy(), omotion.frame_distances(flat), rtol=1e-12, atol=0)
     nf, ne = 40, 5001
     log(f"motion_l2: {nf} frames of {ne} elements, unaligned")
     flat = frames.reshape(-1)[1:1 + nf * ne].reshape(nf, ne)
