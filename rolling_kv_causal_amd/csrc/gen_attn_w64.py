@@ -15,24 +15,26 @@ the P words are ORed for the lazy test, and eight 16x16x32 MFMAs add the previou
 sums into l.  Three programs: SDV2_W64_LOOP as described; SDV2_W64_LOOP_SK for a bf16 cache
 whose keys carry scale_log2 (the host passes scale_log2 = 1 and the exponentials read S
 directly: no product); SDV2_W64_LOOP_FP8 for the e4m3 cache, which carries it too (with the
-queries staged times a power of two), and differs from SK only in its loads (staged, then
-widened to bf16 at the top of the iteration).
+queries staged times a power of two), and differs from SK only in its loads: staged by one
+iteration, widened to bf16 in the first gaps of the next one.
 
 Iteration t, t mod 4 = phase ph (every state register is an asm operand, so the compiler never
 moves them; the loop is generated once per phase, so the ring slots of K(t) (ph) and V^T(t-1)
 (ph - 1) are immediate offsets of the fragment reads):
-  wait for the loads of iteration t-2 (e4m3: widen this wave's staged share of K(t), V^T(t-1)
-    into the bf16 ring), barrier; branch on mflag(t) to the masked variant
+  bf16: wait for the loads of iteration t-2; barrier (e4m3: every wave has written its share of
+    K(t), V^T(t-1), widened in iteration t-1); branch on mflag(t) to the masked variant
   tile block: QK(t), PV(t-1) with P buffer pp, softmax(t) into buffer 1-pp, this wave's tile
     loads (K(t+2), V^T(t+1); bf16 eight of 1 KB into the ring, e4m3 four into the staging
-    slot of parity ph mod 2) spread over the stream, and, in the free issue slots of the QK
+    slot of parity ph mod 2) spread over the stream, e4m3: the widening of this wave's staged
+    K(t+1), V^T(t) (loaded in iteration t-1) into ring slots ph + 1 and ph in the gaps before the
+    softmax, in the registers of the P buffer it is about to fill, and, in the free issue slots of the QK
     part, the scalar set-up of iteration t+1 (load cursors and global bases, the walk cursor
     and mflag of tile t+1); then the lazy test (trig != 0: some P word of the tile is >= 2 or
     not finite, or some row has no maximum yet)
   trig != 0 (out of line): the rescale: masked row max, m, alpha, O and l scaled (not while
     no row of the block has a maximum), P of the tile recomputed into buffer 1-pp, the -m
     blocks rewritten
-After the loop the last PV (e4m3: after widening V^T(n-1)).  Set-up values alternate between
+After the loop the last PV.  (e4m3: before the loop, K(0) and the zeroed V^T(-1) are widened.)  Set-up values alternate between
 two register sets by iteration parity, so the loads of iteration t read one set while the
 stream writes the other.  The masked variant ANDs every P word with its mask word: the
 ragged-tile mask (keys >= nvalid) times the row block's causal mask (own frame tk after the
@@ -54,6 +56,7 @@ Register plan (per lane):
   a[192:223]  mask words per (qb, word);  a[224:227] 8g, frame per qb, (lane ^ 32) * 4
   a[228:231]  row-sum selector
   e4m3 only:  v[234:235] staging read addresses; a[232:239] widened-chunk write addresses
+              (read into v[188:195] for the widening)
   s[84:91]    global bases of the K and V^T tile loads, two sets by iteration parity
 
 Hazards kept by construction (gfx950, counted in issued instructions): an MFMA result is read
@@ -80,6 +83,8 @@ WAIT_EVERY = 4                                   # one LDS wait per this many fr
 READ_START = 2                                   # fragment reads issued before the first MFMA
 NEXT_GAP = ["<next gap>"]                        # unit marker: continue the chunk after the next MFMA
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
+WIDEN_CAP = 8                                    # ... and the e4m3 widening (set-up included)
+WIDEN_END = 16                                   # e4m3: first gap of the set-up, after most of the widening
 
 
 def o_reg(db, qb):
@@ -249,7 +254,7 @@ def mask_setup():
     return lines
 
 
-def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
+def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=(), widen=()):
     """Reads KA ahead of their MFMAs (after a ramp: READ_START reads before the first MFMA, then
     two per MFMA pair until KA are in flight); VALU ops spread evenly over the MFMAs from index
     valu_from on.  dma maps a read index i to (m0 setup, tile load): the setup follows the MFMA
@@ -258,9 +263,15 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
     extra: (first gap, units) chunks of scalar bookkeeping, placed in order and one chunk after
     the other; a unit (a few instructions, closed in its use of SCC) goes into the gap after an
     MFMA, from the chunk's first gap on, into the first gap with room for it (at most GAP_CAP
-    instructions besides the MFMA), so the wave can issue it while the matrix core works."""
+    instructions besides the MFMA), so the wave can issue it while the matrix core works.
+    widen: (first gap, unit) pairs (e4m3), placed in order after the set-up, each from its first
+    gap on into the first gap with room (WIDEN_CAP), all before the softmax's first gap.  Waits
+    are written as marks and resolved at the end: lgkmcnt(@Fi) waits for fragment read i and
+    lgkmcnt(@Wj) for widening read j, counting every LDS op issued after it (LDS ops complete in
+    order); vmcnt(@Pj) waits for load j of the previous iteration's four (e4m3), counting the
+    loads this stream has issued since."""
     dma = dma or {}
-    lines = []
+    out = []                                     # (line, tag): tags name the reads waited for
     # reads issued after the MFMA pair of read i: KA ahead in the steady state; the stream starts
     # with READ_START reads and catches up by one extra read per pair, so the four waves leaving
     # the barrier together do not queue 32 reads at the LDS at once
@@ -273,17 +284,17 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
         nr = upto
     assert nr == len(reads)
     for i in range(first):
-        lines.append(read_instr(reads[i], i % RING, ph))
-    issued = first
+        out.append((read_instr(reads[i], i % RING, ph), f"F{i}"))
     # LDS waits: before the MFMA pair of read i when read i is not yet covered; a wait covers
     # reads up to i + WAIT_EVERY - 1, but not those issued after the previous pair (during the
-    # ramp they would stall the wave), and at least read i.  waits[i] = lgkmcnt operand.
+    # ramp they would stall the wave), and at least read i.  waits[i] = last read covered.
     waits, done, n_issued = {}, 0, first
     for i in range(len(reads)):
         if i >= done:
             recent = len(after[i - 1]) if i else 0
             done = max(i + 1, min(i + WAIT_EVERY, n_issued - recent))
-            waits[i] = min(n_issued - done, 15)
+            # (at most 15 reads may stay in flight)
+            waits[i] = max(done, n_issued - 15) - 1
         n_issued += len(after[i])
     n_mfma = 2 * len(reads)
     fixed = [0] * n_mfma                         # read, wait and load instructions after MFMA g
@@ -304,9 +315,9 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
     load = [per[g] + fixed[g] for g in range(n_mfma)]
     placed = [[] for _ in range(n_mfma)]
     g = 0
-    for first, units in extra:
+    for first_gap, units in extra:
         # chunks one after another: they share the scratch SGPRs x and y
-        g = max(g, first)
+        g = max(g, first_gap)
         for u in units:
             if u == NEXT_GAP:                    # the rest of the chunk goes after the next MFMA
                 g = min(g + 1, n_mfma - 1)
@@ -315,27 +326,58 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=()):
                 g += 1
             placed[g] += u
             load[g] += len(u)
+    wplaced = [[] for _ in range(n_mfma)]
+    g = 0
+    for first_gap, u in widen:
+        g = max(g, first_gap)
+        while g < valu_from and load[g] + len(u) > WIDEN_CAP:
+            g += 1
+        assert g < valu_from, "the widening must end before the softmax reuses its registers"
+        wplaced[g] += u
+        load[g] += len(u)
     vi = 0
     for i, r in enumerate(reads):
         if i in waits:
-            lines.append(f"s_waitcnt lgkmcnt({waits[i]})")
+            out.append((f"s_waitcnt lgkmcnt(@F{waits[i]})", None))
         for j, m in enumerate(mfma_pair(r, i % RING, pp)):
-            lines.append(m)
+            out.append((m, None))
             for _ in range(per[2 * i + j]):
-                lines.append(valu[vi])
+                out.append((valu[vi], None))
                 vi += 1
-            lines += placed[2 * i + j]
+            out += [(x, None) for x in placed[2 * i + j]]
+            out += [(x, None) if isinstance(x, str) else x for x in wplaced[2 * i + j]]
         if i in dma:
-            lines.append(dma[i][0])
+            out.append((dma[i][0], None))
         for j in after[i]:
-            lines.append(read_instr(reads[j], j % RING, ph))
-            issued += 1
+            out.append((read_instr(reads[j], j % RING, ph), f"F{j}"))
         if i in dma and not after[i]:
-            lines.append("s_nop 0")
+            out.append(("s_nop 0", None))
         if i in dma:
-            lines.append(dma[i][1])
+            out.append((dma[i][1], None))
     assert vi == len(valu)
-    lines.append("s_waitcnt lgkmcnt(0)")
+    out.append(("s_waitcnt lgkmcnt(0)", None))
+    return resolve_waits(out)
+
+
+def resolve_waits(out):
+    """Lines with their wait marks replaced: lgkmcnt(@tag) by the number of LDS ops issued after
+    the tagged one (at most 15: waiting for more is safe), vmcnt(@Pj) by 3 - j plus the tile
+    loads issued since the stream began."""
+    lines, lds, loads = [], [], 0
+    for text, tag in out:
+        op = text.split()[0]
+        if "lgkmcnt(@" in text:
+            want = text.split("(@")[1].rstrip(")")
+            n = len(lds) - 1 - lds.index(want)
+            text = f"s_waitcnt lgkmcnt({min(n, 15)})"
+        elif "vmcnt(@P" in text:
+            j = int(text.split("(@P")[1].rstrip(")"))
+            text = f"s_waitcnt vmcnt({3 - j + loads})"
+        if op.startswith("ds_"):
+            lds.append(tag)
+        if op.startswith("global_load"):
+            loads += 1
+        lines.append(text)
     return lines
 
 
@@ -348,8 +390,10 @@ def tile_block(ph, masked):
     pp = 1 - par
     pc = 1 - pp
     lines = mask_setup() if masked else []
-    extra = [(0, v_setup(1 - par)), (0, cursor_shift()), (0, k_setup(1 - par, 3)),
-             (0, walk_setup(1 - par, False))]
+    # (e4m3: after the widening, which takes the first gaps)
+    g0 = WIDEN_END if F8 else 0
+    extra = [(g0, v_setup(1 - par)), (g0, cursor_shift()), (g0, k_setup(1 - par, 3)),
+             (g0, walk_setup(1 - par, False))]
     valu = softmax_ops(pc, masked)
     # l += row sums of P(t-1) (buffer pp, complete), one MFMA after every other group
     sums = [rowsum_mfma(pp, qb, ks) for ks in range(4) for qb in range(2)]
@@ -361,7 +405,8 @@ def tile_block(ph, masked):
             if gcount % 2 == 1 and sums:
                 out.append(sums.pop(0))
     valu = out + sums
-    lines += stream(k_reads() + v_reads(), pp, ph, valu, tile_loads(ph), SM_FROM, extra)
+    lines += stream(k_reads() + v_reads(), pp, ph, valu, tile_loads(ph), SM_FROM, extra,
+                    widen_units(ph, pc) if F8 else ())
     # lazy test: some P word >= 2 (a score 9 above m, or not finite), or a row without m
     return lines + [f"v_and_b32 v{TMP}, 0x40004000, v{ACC}",
                     f"v_cmp_ne_u32 vcc, 0, v{TMP}",
@@ -597,14 +642,14 @@ WKA, WVA = 232, 236                              # e4m3: widened-chunk write add
 def tile_loads(ph):
     """Read index -> (m0 setup, load) of this wave's tile loads in iteration phase ph: bf16,
     four 1 KB K loads (after reads 1, 5, 9, 13) into ring slot ph + 2 and four V^T loads (after
-    reads 17, 21, 25, 29) into slot ph + 1; e4m3, two of each (after reads 1, 9 and 17, 25)
-    into staging slot ph mod 2.  m0 holds the LDS destination, the SGPR pair of parity ph mod 2
+    reads 17, 21, 25, 29) into slot ph + 1; e4m3, two of each (after reads 1, 3 and 5, 7:
+    early, so that they land before the next iteration widens them) into staging slot ph mod 2.  m0 holds the LDS destination, the SGPR pair of parity ph mod 2
     the global tile base and v[236:243] the lane offsets."""
     par = ph % 2
     d = {}
     if F8:
-        kinds = ((1, "ms", (ph % 2) * STAGE, BASE[par][0], KOFF), (17, "ms", (ph % 2) * STAGE + STAGE // 2, BASE[par][1], VOFF))
-        n, step = 2, 8
+        kinds = ((1, "ms", (ph % 2) * STAGE, BASE[par][0], KOFF), (5, "ms", (ph % 2) * STAGE + STAGE // 2, BASE[par][1], VOFF))
+        n, step = 2, 2
     else:
         kinds = ((1, "mk", ((ph + 2) % NSLOT) * KTILE, BASE[par][0], KOFF),
                  (17, "mv", ((ph + 1) % NSLOT) * KTILE, BASE[par][1], VOFF))
@@ -616,14 +661,14 @@ def tile_loads(ph):
     return d
 
 
-def widen_block(ph, k=True):
-    """e4m3, top of iteration phase ph: this wave's staged bytes of K(t) and V^T(t-1) (staging
-    slot ph mod 2, loaded two iterations ago) widened to bf16 into ring slots ph and ph - 1.
-    A staged 16-byte chunk c = 2p + h of a row holds, in the cache's byte order, elements
+def widen_block(ph):
+    """e4m3, before the loop (ph = 0): this wave's staged bytes of K(0) and of the zeroed V^T(-1)
+    (staging slot 0, the prologue's first loads) widened to bf16 into ring slots 0 and 3.  A
+    staged 16-byte chunk c = 2p + h of a row holds, in the cache's byte order, elements
     32p + 8h + [0, 8) and 32p + 16 + 8h + [0, 8): the bf16 chunks 4p + h (lo) and 4p + 2 + h
     (hi), whose LDS addresses wait in a[232:239]."""
     stage = (ph % 2) * STAGE
-    parts = ([("K", i) for i in range(2)] if k else []) + [("V", i) for i in range(2)]
+    parts = [("K", i) for i in range(2)] + [("V", i) for i in range(2)]
     lines = []
     for j, (kind, i) in enumerate(parts):
         addr, off = (SK, stage + i * 1024) if kind == "K" else (SV, stage + i * 1024)
@@ -648,6 +693,56 @@ def widen_block(ph, k=True):
                          f"offset:{slot * KTILE}")
     lines.append("s_waitcnt lgkmcnt(0)")
     return lines
+
+
+def widen_units(ph, pc):
+    """e4m3, iteration phase ph: this wave's staged bytes of K(t+1) and V^T(t) (staging slot
+    (ph + 1) mod 2, loaded by the previous iteration) widened to bf16 into ring slots ph + 1 (K)
+    and ph (V^T), in the gaps before the softmax: as (first gap, unit) pairs for stream().
+    Registers: P buffer pc, whose P(t-2) is dead until the softmax writes P(t) there, holds
+    chunk j = (K0, K1, V0, V1) in its 8 registers R..R+7: the staged 16 bytes are read into
+    R+4..R+7 and widened in place (bf16 pair 2dw + sel from staged word dw: each word is read
+    by both of its conversions before a later one overwrites it); the temporaries hold the
+    write addresses.  K is widened first: its loads were issued earliest."""
+    stage = ((ph + 1) % 2) * STAGE
+    base = p_base(pc)
+    units = []
+
+    def at(gap, *ins):
+        units.append((gap, list(ins)))
+
+    def addresses(kind, gap):                  # write addresses of (kind, 0) and (kind, 1)
+        a0, t0 = (WKA, TMP) if kind == "K" else (WVA, TMP + 4)
+        for h in range(2):
+            at(gap, *[f"v_accvgpr_read_b32 v{t0 + 2 * h + x}, a{a0 + 2 * h + x}" for x in range(2)])
+
+    def read(j, gap):
+        kind, i = ("K", "K", "V", "V")[j], j % 2
+        R = base + 8 * j
+        at(gap, f"s_waitcnt vmcnt(@P{j})",
+           (f"ds_read_b128 v[{R + 4}:{R + 7}], v{SK if kind == 'K' else SV} offset:{stage + i * 1024}", f"W{j}"))
+
+    def widen(j, gap):
+        kind = ("K", "K", "V", "V")[j]
+        R = base + 8 * j
+        slot = (ph + 1) % NSLOT if kind == "K" else ph % NSLOT
+        cv = [f"v_cvt_scalef32_pk_bf16_fp8 v{R + 2 * dw + sel}, v{R + 4 + dw}, 1.0" + (" op_sel:[1,0,0]" if sel else "")
+              for dw in range(4) for sel in range(2)]
+        at(gap, (f"s_waitcnt lgkmcnt(@W{j})", None), cv[0], cv[1])
+        for k in range(2, 8, 2):
+            at(gap, cv[k], cv[k + 1])
+        for h in range(2):
+            at(gap, f"ds_write_b128 v{TMP + 2 * j + h}, v[{R + 4 * h}:{R + 4 * h + 3}] offset:{slot * KTILE}")
+
+    # the four reads first (the loads landed most of an iteration ago), each chunk's conversion
+    # a few gaps after its read (LDS latency)
+    addresses("K", 0)
+    for j in range(4):
+        read(j, 1 + j)
+    addresses("V", 5)
+    for j in range(4):
+        widen(j, 6 + 2 * j)
+    return units
 
 
 def k_setup(par, ahead):
@@ -721,9 +816,9 @@ def iteration(ph):
     """Iteration t < n of phase ph = t mod NSLOT (P buffer pp = 1 - ph mod 2 read by PV(t-1),
     P(t) written into the other).  The masked tile block and the rescale are out of line."""
     par, tag = ph % 2, "abcd"[ph]
-    return [# loads of iteration t-2 (K(t), V^T(t-1)) in (e4m3: staged, widened by this wave);
-            # every wave is done with iteration t-1's slots
-            f"s_waitcnt vmcnt({4 if F8 else 8})"] + (widen_block(ph) if F8 else []) + ["s_barrier",
+    # bf16: the loads of iteration t-2 (K(t), V^T(t-1)) are in; e4m3: this wave's widening of
+    # them (the previous iteration's stream) is written.  Every wave is done with iteration t-1.
+    return ([] if F8 else ["s_waitcnt vmcnt(8)"]) + ["s_barrier",
             f"s_cmp_eq_u32 %[mflag{par}], 0", f"s_cbranch_scc0 .Lw64_m{tag}_%="] + \
         tile_block(ph, False) + \
         [f".Lw64_td{tag}_%=:",
@@ -756,6 +851,10 @@ def loop_program():
     lines += sum((u for u in walk_setup(0, False) if u != NEXT_GAP), []) + v1 + \
         ["s_mov_b32 %[vk], %[kk]", "s_mov_b32 %[vf], %[kf]"] + \
         sum((u for u in k_setup(0, 2) if u != NEXT_GAP), [])
+    if F8:
+        # staging slot 0 (K(0) and a zeroed V^T half, the prologue's first loads) into ring slots
+        # 0 and 3; slot 1 (K(1), V^T(0)) is widened by iteration 0
+        lines += ["s_waitcnt vmcnt(4)"] + widen_block(0)
     lines += [".Lw64_loop_%=:"]
     for ph in range(NSLOT):
         lines += iteration(ph)
@@ -766,9 +865,8 @@ def loop_program():
     for ph in range(1, NSLOT):
         lines += [f"s_cmp_eq_u32 %[x], {ph}", f"s_cbranch_scc1 .Lw64_pv{ph}_%="]
     for ph in range(NSLOT):
-        # e4m3: V^T(n-1) widened first
-        lines += ([f".Lw64_pv{ph}_%=:"] if ph else []) + (widen_block(ph, k=False) if F8 else []) + \
-            ["s_barrier"] + pv_only_block(ph) + ["s_branch .Lw64_fin_%="]
+        lines += ([f".Lw64_pv{ph}_%=:"] if ph else []) + ["s_barrier"] + pv_only_block(ph) + \
+            ["s_branch .Lw64_fin_%="]
     for ph in range(NSLOT):
         lines += out_of_line(ph)
     lines += [".Lw64_fin_%=:", "s_mov_b32 m0, %[m0save]"]
@@ -834,6 +932,77 @@ def check_paths(lines, history=64, depth=3):
         walk(lab, [], 1)
 
 
+def check_staging(iterations=10, masked=(2, 5)):
+    """e4m3: run the loads, waits and LDS traffic of the tile loop as one wave executes them
+    (the prologue's six loads, the widening before the loop, iterations 0 .. iterations-1,
+    masked at the given ones, the last PV) and check the data each LDS read finds: a staged
+    chunk is read only once its load is counted complete by a vmcnt wait and holds the tile the
+    widening expects (iteration t widens K(t+1) and V^T(t)); the fragment reads of iteration t
+    find K(t) and V^T(t-1) in the bf16 ring, the last PV V^T(n-1).  The other waves' share is
+    the same with its own addresses, and the barrier at each iteration's top orders the waves."""
+    assert F8
+    pending = [((0, 0), ("K", 0)), ((0, 1), ("K", 0)), ((1, 0), ("K", 1)), ((1, 1), ("K", 1)),
+               ((1, 8), ("V", 0)), ((1, 9), ("V", 0))]
+    staged = {(0, 8): ("V", -1), (0, 9): ("V", -1)}          # zeroed by the prologue: V^T(-1)
+    ring, regs, addr_kind = {}, {}, {}
+    m0 = None
+
+    def run(lines, t, expect_k, expect_v):
+        nonlocal pending, m0
+        for l in lines:
+            tok = l.replace(",", " ").split()
+            if not tok or l.startswith(".L"):
+                continue
+            op = tok[0]
+            if op == "s_add_u32" and tok[1] == "m0":
+                m0 = int(tok[3]) if tok[2] == "%[ms]" else (m0 + int(tok[3]) if tok[2] == "m0" else None)
+            elif op.startswith("global_load_lds"):
+                part = (m0 // STAGE, (m0 % STAGE) // 1024)
+                what = ("K", t + 2) if tok[1] in (f"v{KOFF}", f"v{KOFF + 1}") else ("V", t + 1)
+                pending.append((part, what))
+                staged.pop(part, None)
+            elif op == "s_waitcnt" and "vmcnt(" in l:
+                n = int(l.split("vmcnt(")[1].split(")")[0])
+                for part, what in (pending[:len(pending) - n] if n else pending):
+                    staged[part] = what
+                pending = pending[len(pending) - n:] if n else []
+            elif op == "v_accvgpr_read_b32" and tok[2] in [f"a{WKA + i}" for i in range(4)] + [f"a{WVA + i}" for i in range(4)]:
+                addr_kind[tok[1]] = "K" if int(tok[2][1:]) < WVA else "V"
+            elif op == "ds_read_b128":
+                lo = int(tok[1][2:].split(":")[0])
+                off = int(tok[3].split(":")[1])
+                if tok[2] in (f"v{SK}", f"v{SV}"):
+                    part = (off // STAGE, (off % STAGE) // 1024 + (8 if tok[2] == f"v{SV}" else 0))
+                    assert part in staged, (t, l, "reads a staged chunk whose load may not have landed")
+                    want = expect_k if tok[2] == f"v{SK}" else expect_v
+                    assert staged[part] == want, (t, l, staged[part], want)
+                    for r in range(lo, lo + 4):
+                        regs[r] = staged[part]
+                else:
+                    kind = "K" if KADDR <= int(tok[2][1:]) < KADDR + 8 else "V"
+                    want = ("K", t) if kind == "K" else ("V", t - 1)
+                    assert ring.get((kind, off // KTILE)) == want, (t, l, ring.get((kind, off // KTILE)), want)
+            elif op == "v_cvt_scalef32_pk_bf16_fp8":
+                regs[int(tok[1][1:])] = regs[int(tok[2][1:])]
+            elif op == "ds_write_b128":
+                lo = int(tok[2][2:].split(":")[0])
+                vals = {regs.get(r) for r in range(lo, lo + 4)}
+                assert len(vals) == 1, (t, l, vals)
+                what = vals.pop()
+                assert what[0] == addr_kind[tok[1]], (t, l, what)
+                ring[(what[0], int(tok[3].split(":")[1]) // KTILE)] = what
+
+    lines = loop_program()
+    pre = lines[:lines.index(".Lw64_loop_%=:")]
+    run(pre, -1, ("K", 0), ("V", -1))
+    for t in range(iterations):
+        ph = t % NSLOT
+        body = tile_block(ph, t in masked)
+        run(["s_barrier"] + body, t, ("K", t + 1), ("V", t))
+    ph = iterations % NSLOT
+    run(["s_waitcnt vmcnt(0)", "s_barrier"] + pv_only_block(ph), iterations, None, None)
+
+
 def emit(name, lines):
     check_hazards([l for l in lines if not l.startswith(".L")])
     check_paths(lines)
@@ -849,6 +1018,7 @@ def main():
     set_mode(False, scaled=True)
     out.append(emit("SDV2_W64_LOOP_SK", loop_program()))
     set_mode(True, scaled=True)
+    check_staging()
     out.append(emit("SDV2_W64_LOOP_FP8", loop_program()))
     set_mode(False)
     sys.stdout.write("\n".join(out))

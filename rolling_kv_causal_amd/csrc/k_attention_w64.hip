@@ -193,9 +193,9 @@ void attn_w64_kernel(const AttnArgs a) {
 
   // Prologue: V^T slot 3 (read as V(-1) with P(-1) = 0) zeroed; K(0) into slot 0, K(1) into
   // slot 1 (K(0) again when n = 1: the loop counts the loads in flight at its start), V(0)
-  // into slot 0.  e4m3: the V^T half of staging slot 0 is zeroed instead (the top of iteration
-  // 0 widens it into V^T slot 3); K(0) goes to staging slot 0, K(1) and V(0) to slot 1, as if
-  // loaded by iterations -2 and -1.
+  // into slot 0.  e4m3: the V^T half of staging slot 0 is zeroed instead (the program widens
+  // it into V^T slot 3 with K(0) before its loop); K(0) goes to staging slot 0, K(1) and V(0)
+  // to slot 1, as if loaded by iterations -2 and -1, in the order the program's load waits count.
   if constexpr (F8) {
 #pragma unroll
     for (int i = 0; i < STAGE / 2 / (256 * 16); ++i)

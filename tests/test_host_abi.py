@@ -314,6 +314,52 @@ def test_generator_hazard_check_rejects_a_missing_lds_wait():
         gen.check_hazards(lines[:waits[1]] + lines[waits[1] + 1:])
 
 
+def test_generator_staging_check_rejects_planted_mistakes():
+    # The e4m3 program widens each staged tile in the stream of the iteration after its loads;
+    # check_staging runs one wave's loads, waits and LDS traffic.  It passes the committed
+    # program and rejects: a vmcnt wait one load short, the widening reading the other staging
+    # slot, and K(t+1) widened into the ring slot K(t) is being read from.
+    import importlib.util
+    import pathlib
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_stage", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    gen.set_mode(True, scaled=True)
+    gen.check_staging()
+    resolve, units = gen.resolve_waits, gen.widen_units
+
+    def short_wait(out):
+        return [f"s_waitcnt vmcnt({int(l.split('(')[1].rstrip(')')) + 1})" if l.startswith("s_waitcnt vmcnt") else l
+                for l in resolve(out)]
+
+    def edit_units(fix):
+        def f(ph, pc):
+            return [(g, [fix(ph, x) for x in u]) for g, u in units(ph, pc)]
+        return f
+
+    def other_stage(ph, x):
+        line = x[0] if isinstance(x, tuple) else x
+        if line.startswith("ds_read_b128") and (f"v{gen.SK}" in line or f"v{gen.SV}" in line):
+            off = int(line.split("offset:")[1])
+            line = line.split("offset:")[0] + f"offset:{off ^ gen.STAGE}"
+        return (line, x[1]) if isinstance(x, tuple) else line
+
+    def k_into_read_slot(ph, x):
+        if isinstance(x, str) and x.startswith("ds_write_b128") and int(x.split()[1].rstrip(",")[1:]) < gen.TMP + 4:
+            return x.split("offset:")[0] + f"offset:{(ph % gen.NSLOT) * gen.KTILE}"
+        return x
+
+    for name, attr, plant in (("short vmcnt", "resolve_waits", short_wait),
+                              ("other staging slot", "widen_units", edit_units(other_stage)),
+                              ("K over the slot being read", "widen_units", edit_units(k_into_read_slot))):
+        setattr(gen, attr, plant)
+        with pytest.raises(AssertionError):
+            gen.check_staging()
+        setattr(gen, attr, resolve if attr == "resolve_waits" else units)
+    gen.check_staging()
+
+
 def test_layer_blocks_over_the_32_bit_offset_range_are_rejected():
     # The attention tile loop forms offsets inside a layer's K or V block in 32 bits: a layer
     # block of 4 GiB or more, or a slot of 2 GiB or more, is refused at validation.
