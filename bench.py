@@ -9,8 +9,9 @@ tensors of the workload's shapes, generated before the timed region.
 Prints one JSON line.  `value` is the attention work of the step (algorithmic FLOPs,
 4 * nbatch * H * N * L * d per layer with L = (S + W + 1) * N keys) divided by the step time.
 `roofline` scores the attention call (split-KV kernel + combine) against the bf16 MFMA peak;
-its duration is the time of a batch of back-to-back attention calls, by HIP events on the
-library's stream, over the calls in the batch.  `hbm_kernels` scores the HBM-bound kernels
+its duration comes from HIP events on the library's stream around each attention call of the
+timed steps (workloads of 8 or more layers; a single-layer workload, whose step the host
+cannot keep ahead of, times a batch of back-to-back calls instead).  `hbm_kernels` scores the HBM-bound kernels
 (append, rebase, sink copy, split combine, motion reduction) against 8 TB/s.  `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the host cores.
 
@@ -107,11 +108,12 @@ class Stepper:
         from rolling_kv_causal_amd import sdv2
         return sdv2.config_of(c)
 
-    def step(self, ev=None, attn_repeat=1):
+    def step(self, ev=None, attn_repeat=1, calls=None):
         """One step.  ev: dict of event pairs to record around the append batch, the attention
         batch (all layers back to back, each call repeated attn_repeat times), the refresh and
         the end-of-step chunk statistics / sink refresh.  Without ev, append and attention
-        alternate per layer as in a DiT forward."""
+        alternate per layer as in a DiT forward; calls: then a dict of "append" and "attention"
+        lists, one event pair per layer each, recorded around each call."""
         c, run = self.c, self.run
         first, nb, commit, newest = run.plan(self.s)
         st = self.sets[self.s % len(self.sets)]
@@ -133,8 +135,15 @@ class Stepper:
         else:
             for layer in range(c.num_layers):
                 q, k, v = st[layer]
+                if calls:
+                    calls["append"][layer][0].record()
                 run.cache.append(layer, first, nb, q[:nb], k[:nb], v[:nb])
+                if calls:
+                    calls["append"][layer][1].record()
+                    calls["attention"][layer][0].record()
                 run.cache.attention(layer, nb, q[:nb], run.out[layer, :nb], run.scale)
+                if calls:
+                    calls["attention"][layer][1].record()
         if commit >= 0:
             run.cache.commit(commit)
             last = (commit + 1) * c.chunk_frames - 1            # the chunk's last frame
@@ -156,23 +165,33 @@ def events(names):
 
 
 def run_gpu(c, steps, warmup):
-    """Whole-step time, then a pass with events around batched calls (per-kernel figures)."""
+    """Whole-step time; per-call append and attention times from HIP events around each call
+    inside the timed steps (workloads of 8 or more layers, where the host enqueues far ahead of
+    the GPU), else from a pass with events around batched calls."""
     import torch
     torch.cuda.set_device(0)
     st = Stepper(c)
     fill = c.sink_frames + c.window_frames + c.stream_batch + 1
     for _ in range(fill + warmup):
         st.step()
+    per_call = c.num_layers >= 8
+    calls = [{k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(c.num_layers)] for k in ("append", "attention")}
+             for _ in range(steps)] if per_call else [None] * steps
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
-        st.step()
+    for i in range(steps):
+        st.step(calls=calls[i])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / steps
+    med = lambda v: sorted(v)[len(v) // 2] if v else None
+    if per_call:
+        mean_ms = lambda pairs: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        inside = {k: med([mean_ms(cl[k]) for cl in calls]) * 1e3 for k in ("append", "attention")}
     # batched pass: events around the append batch and the attention batch of each step; a
     # single-layer workload repeats its attention call so that a batch holds several calls
     repeat = max(1, 8 // c.num_layers)
@@ -189,11 +208,22 @@ def run_gpu(c, steps, warmup):
                 acc[n].append(a.elapsed_time(b))
             except (RuntimeError, ValueError):    # the pair was not recorded this step
                 pass
-    med = lambda v: sorted(v)[len(v) // 2] if v else None
     attn_ms = med(acc["attention"])
+    if per_call:
+        timing = (f"HIP events on the library's stream around each of the {c.num_layers} attention calls of "
+                  f"each timed step (append and attention alternating per layer); median over the {steps} steps "
+                  "of the mean per call")
+    else:
+        timing = (f"HIP events on the library's stream around {c.num_layers * repeat} back-to-back attention "
+                  "calls per step (median of the batched steps)")
     return {"ms_per_step": ms_step, "wall_s": wall,
-            "attention_us": attn_ms * 1e3 / (c.num_layers * repeat), "attention_calls_per_batch": c.num_layers * repeat,
+            "attention_us": inside["attention"] if per_call else attn_ms * 1e3 / (c.num_layers * repeat),
+            "attention_timing": timing,
+            "attention_batched_us": attn_ms * 1e3 / (c.num_layers * repeat),
+            # the append (HBM-bound, 50 us or less) from the back-to-back batch: a per-call event
+            # pair adds the few microseconds between the previous kernel's end and its start
             "append_us": med(acc["append"]) * 1e3 / c.num_layers,
+            "append_in_step_us": inside["append"] if per_call else None,
             "stats_us": None if not acc["stats"] else med(acc["stats"]) * 1e3,
             "refreshes": st.run.cache.state()[2]}
 
@@ -355,6 +385,50 @@ def calibration_copy(nbytes=1 << 30):
     log(f"bench: calibration copy of {nbytes} bytes done")
 
 
+def reference_rates(c, n=20, warmup=5):
+    """Library rates on this GPU for context: torch.matmul bf16 (hipBLASLt) on square GEMMs and
+    PyTorch's scaled_dot_product_attention (flash and memory-efficient backends) on the
+    workload's attention shape (B x H heads, T'N queries, every visible key, one call per layer
+    without the block-causal mask).  HIP events around n calls after warmup calls."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n * 1e-3
+
+    out = {"gemm_bf16": {}, "sdpa_bf16": {}}
+    for M in (8192, 16384):
+        a = torch.randn(M, M, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(M, M, device="cuda", dtype=torch.bfloat16)
+        t = timed(lambda: torch.matmul(a, b))
+        out["gemm_bf16"][str(M)] = {"us": round(t * 1e6, 1), "tflops": round(2 * M ** 3 / t / 1e12, 1)}
+        del a, b
+    L = visible_keys(c, c.chunk_frames - 1)
+    q = torch.randn(c.stream_batch, c.num_heads, c.chunk_rows, c.head_dim, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(c.stream_batch, c.num_heads, L, c.head_dim, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    flops = 4.0 * c.stream_batch * c.num_heads * c.chunk_rows * L * c.head_dim
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel(backend):
+                t = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
+            out["sdpa_bf16"][name] = {"us": round(t * 1e6, 1), "tflops": round(flops / t / 1e12, 1)}
+        except RuntimeError as ex:                 # backend not built for this GPU
+            out["sdpa_bf16"][name] = {"unavailable": str(ex)[:120]}
+    out["sdpa_shape"] = {"batch": c.stream_batch, "heads": c.num_heads, "queries": c.chunk_rows, "keys": L,
+                         "head_dim": c.head_dim}
+    return out
+
+
 SLO_GRID = [(1, 1), (2, 1), (4, 1), (8, 1), (1, 2), (2, 2), (4, 2), (1, 4), (2, 4), (1, 8)]
 
 
@@ -391,6 +465,8 @@ def main():
                     help="pinned-sink RoPE refresh: the refresh rebases only the window")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="OCP e4m3 KV cache (bf16 queries, scores and outputs)")
+    ap.add_argument("--reference-rates", action="store_true",
+                    help="print library rates on this GPU (bf16 GEMM, PyTorch SDPA on the workload's shape)")
     ap.add_argument("--target-fps", type=float, default=30.0)
     ap.add_argument("--deadline-ms", type=float, default=100.0)
     args = ap.parse_args()
@@ -407,6 +483,9 @@ def main():
         c = c.with_(rope_pin_sinks=True)
     if args.kv_fp8:
         c = c.with_(kv_fp8=True, name=c.name + "_kvfp8")
+    if args.reference_rates:
+        print(json.dumps({"workload": c.name, **reference_rates(c)}), flush=True)
+        return
     if args.slo_table:
         print(json.dumps(slo_table(c, min(args.steps, 20), min(args.warmup, 5), args.target_fps,
                                    args.deadline_ms * 1e-3)), flush=True)
@@ -432,8 +511,8 @@ def main():
                          "attn_w64_kernel" if c.dtype == "bf16" and c.head_dim == 128 else
                          "attn_bf16_kernel" if c.dtype == "bf16" else "attn_f32_kernel"),
             "flops_per_call": wn["flops_per_layer"], "avg_call_us": round(attn_us, 3),
-            "timing": f"HIP events on the library's stream around {g['attention_calls_per_batch']} back-to-back "
-                      "attention calls per step (median of the batched steps)"}
+            "timing": g["attention_timing"],
+            "back_to_back_call_us": round(g["attention_batched_us"], 3)}
     if prof:
         roof["profile_call_us"] = prof.get("call_us")
         roof["profile_kernel_us"] = prof.get("kernel_us")
