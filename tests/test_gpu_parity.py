@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import random_configs
 from gpu_helpers import Harness, assert_close, dev, host64, log, sample_rows
 from oracle import motion as omotion
 from oracle import stream as ost
@@ -210,6 +211,19 @@ def test_layer_block_at_the_4gib_limit(kv_fp8, heads):
         st.end_step({0: (k, v)})
     assert [f for (_, f) in st.refresh_log] == [32, 64]
     log(f"4 GiB block: worst max-abs {worst:.3g}")
+
+
+@pytest.mark.parametrize("seed", random_configs.SEEDS)
+def test_random_small_streams(seed):
+    # seeded random configurations across the library's limits (tests/random_configs.py): every
+    # output of every step, the cache at the end
+    cfg = random_configs.random_config(seed)
+    log(f"{cfg.name}: {cfg.dtype}{' e4m3 cache' if cfg.kv_fp8 else ''} d {cfg.head_dim} rope "
+        f"{cfg.rope_dim_t}/{cfg.rope_dim_h}/{cfg.rope_dim_w} grid {cfg.grid_h}x{cfg.grid_w} H {cfg.num_heads} "
+        f"layers {cfg.num_layers} S {cfg.sink_frames} W {cfg.window_frames} T' {cfg.chunk_frames} "
+        f"B {cfg.stream_batch} refresh {cfg.rope_refresh_period} pinned {cfg.rope_pin_sinks} "
+        f"tau {cfg.sink_threshold} key scale {cfg.key_scale:.3g}")
+    _stream(cfg, cfg.num_steps, cache_check=lambda s: s == cfg.num_steps - 1)
 
 
 def test_split_without_visible_keys_for_some_rows(monkeypatch):

@@ -314,6 +314,20 @@ def test_generator_hazard_check_rejects_a_missing_lds_wait():
         gen.check_hazards(lines[:waits[1]] + lines[waits[1] + 1:])
 
 
+def test_random_stream_configs_are_valid():
+    # the seeded random configurations of the GPU parity sweep are inside the library's limits,
+    # and every work plan their streams reach covers each key tile once
+    import random_configs
+    for seed in random_configs.SEEDS:
+        c = random_configs.random_config(seed)
+        cfg = sdv2.config_of(c)
+        sdv2.sdv2_config_validate(cfg)
+        for nb in range(1, c.stream_batch + 1):
+            for shared in range(c.sink_frames + c.window_frames + 1):
+                if c.dtype == "bf16" and c.head_dim == 128:
+                    sdv2.sdv2_debug_check_plan(cfg, nb, shared)
+
+
 def test_generator_staging_check_rejects_planted_mistakes():
     # The e4m3 program widens each staged tile in the stream of the iteration after its loads;
     # check_staging runs one wave's loads, waits and LDS traffic.  It passes the committed
