@@ -37,4 +37,13 @@ def random_config(seed: int):
         scaled_keys=bool(r.integers(3)))
 
 
+def forced_splits(seed: int):
+    """A split-KV count forced on the stream (the SDV2_NSPLIT knob) for some bf16 head_dim-128
+    configurations, else None (the work plan's own choice)."""
+    c = random_config(seed)
+    if c.dtype != "bf16" or c.head_dim != 128:
+        return None
+    return [None, 2, 3, 5][seed % 4]
+
+
 SEEDS = list(range(24))

@@ -214,15 +214,18 @@ def test_layer_block_at_the_4gib_limit(kv_fp8, heads):
 
 
 @pytest.mark.parametrize("seed", random_configs.SEEDS)
-def test_random_small_streams(seed):
-    # seeded random configurations across the library's limits (tests/random_configs.py): every
-    # output of every step, the cache at the end
+def test_random_small_streams(seed, monkeypatch):
+    # seeded random configurations across the library's limits (tests/random_configs.py), some
+    # with a forced split-KV count: every output of every step, the cache at the end
     cfg = random_configs.random_config(seed)
+    nsplit = random_configs.forced_splits(seed)
+    if nsplit:
+        monkeypatch.setenv("SDV2_NSPLIT", str(nsplit))
     log(f"{cfg.name}: {cfg.dtype}{' e4m3 cache' if cfg.kv_fp8 else ''} d {cfg.head_dim} rope "
         f"{cfg.rope_dim_t}/{cfg.rope_dim_h}/{cfg.rope_dim_w} grid {cfg.grid_h}x{cfg.grid_w} H {cfg.num_heads} "
         f"layers {cfg.num_layers} S {cfg.sink_frames} W {cfg.window_frames} T' {cfg.chunk_frames} "
         f"B {cfg.stream_batch} refresh {cfg.rope_refresh_period} pinned {cfg.rope_pin_sinks} "
-        f"tau {cfg.sink_threshold} key scale {cfg.key_scale:.3g}")
+        f"tau {cfg.sink_threshold} key scale {cfg.key_scale:.3g} forced splits {nsplit}")
     _stream(cfg, cfg.num_steps, cache_check=lambda s: s == cfg.num_steps - 1)
 
 

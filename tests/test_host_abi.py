@@ -314,14 +314,20 @@ def test_generator_hazard_check_rejects_a_missing_lds_wait():
         gen.check_hazards(lines[:waits[1]] + lines[waits[1] + 1:])
 
 
-def test_random_stream_configs_are_valid():
+def test_random_stream_configs_are_valid(monkeypatch):
     # the seeded random configurations of the GPU parity sweep are inside the library's limits,
-    # and every work plan their streams reach covers each key tile once
+    # and every work plan their streams reach (with the forced split counts) covers each key
+    # tile once
     import random_configs
     for seed in random_configs.SEEDS:
         c = random_configs.random_config(seed)
         cfg = sdv2.config_of(c)
         sdv2.sdv2_config_validate(cfg)
+        nsplit = random_configs.forced_splits(seed)
+        if nsplit:
+            monkeypatch.setenv("SDV2_NSPLIT", str(nsplit))
+        else:
+            monkeypatch.delenv("SDV2_NSPLIT", raising=False)
         for nb in range(1, c.stream_batch + 1):
             for shared in range(c.sink_frames + c.window_frames + 1):
                 if c.dtype == "bf16" and c.head_dim == 128:
