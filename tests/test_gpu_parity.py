@@ -325,12 +325,13 @@ def test_fp8_kv_wan14b_40layer_b4_full_size():
 
 
 def test_wan13b_30layer_t2b2_full_size():
-    # split-KV with block-causal query tiles: splits of frame-0 rows end before own frame 1
+    # split-KV with block-causal query tiles: splits of frame-0 rows end before own frame 1;
+    # every row, head and element (2 x 2048 x 12) of layers 0 and 29 at the last step
     cfg = configs.WAN13B_30LAYER_T2B2
     checked = {1, 9, 10}
     rows = sample_rows(cfg.chunk_rows, n=32, seed=4)
     _stream(cfg, 11, layers=(0, 29), check=lambda s: s in checked, rows=rows,
-            cache_check=lambda s: s in checked)
+            cache_check=lambda s: s in checked, all_rows_at={10})
 
 
 def test_wan13b_single_layer_full_size():
@@ -345,19 +346,22 @@ def test_wan13b_single_layer_full_size():
 
 
 def test_wan13b_30layer_b4_full_size():
+    # sampled rows; every row, head and element (4 x 1024 x 12) of layers 0 and 29 at the last step
     cfg = configs.WAN13B_30LAYER_B4
     checked = {3, 12, 13}
     rows = sample_rows(cfg.tokens, n=24, seed=1)
     _stream(cfg, 14, layers=(0, 29), check=lambda s: s in checked, rows=rows,
-            cache_check=lambda s: s in checked)
+            cache_check=lambda s: s in checked, all_rows_at={13})
 
 
 def test_wan13b_480p_b2_full_size_with_refresh():
+    # sampled rows through the refresh; every row, head and element (2 x 1560 x 12) of layers 0
+    # and 29 at the first step after it
     cfg = configs.WAN13B_480P_B2
     checked = {2, 10, 24, 25}
     rows = sample_rows(cfg.tokens, n=24, seed=2)
     h = _stream(cfg, 26, layers=(0, 29), check=lambda s: s in checked, rows=rows,
-                cache_check=lambda s: s in checked)
+                cache_check=lambda s: s in checked, all_rows_at={25})
     assert h.st.refresh_log == [(24, 24)]
     assert h.stats_checked == 24                # the motion term of commits 1..24 (frame 0 has none)
 
