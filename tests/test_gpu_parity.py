@@ -302,11 +302,13 @@ def test_fp8_kv_cache(kw):
 
 
 def test_fp8_kv_wan13b_single_layer_full_size():
-    # the headline shape with an e4m3 cache, through the refresh at frame 32
+    # the single-layer shape with an e4m3 cache, through the refresh at frame 32; every row and
+    # head at the step after it
     cfg = configs.WAN13B_1LAYER.with_(kv_fp8=True)
     checked = {1, 9, 31, 32, 33}
     rows = sample_rows(cfg.tokens, n=48, seed=5)
-    h = _stream(cfg, 34, check=lambda s: s in checked, rows=rows, cache_check=lambda s: s in checked)
+    h = _stream(cfg, 34, check=lambda s: s in checked, rows=rows, cache_check=lambda s: s in checked,
+                all_rows_at={33})
     assert h.st.refresh_log == [(32, 32)]
 
 
@@ -317,8 +319,11 @@ def test_fp8_kv_wan14b_40layer_b4_full_size():
     for s in range(12):
         full = s in (3, 11)
         h.step(s, full=full)
-        if full:
+        if s == 3:
             h.check_outputs(rows=rows, heads=np.arange(0, 40, 3))
+        elif full:
+            log(f"{cfg.name} e4m3: step {s}, all rows, heads and elements of layer 39")
+            h.check_outputs()
         h.finish_step()
         if full:
             h.check_cache()
