@@ -55,9 +55,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // F8: e4m3 cache.  Each wave loads its 2 KB share of a K and of a V^T tile (e4m3) into a
-// staging slot (two slots of 16 KB, by iteration parity) and, at the top of the iteration that
-// publishes the tile, widens exactly those bytes to bf16 into the ring slot (exact conversion);
-// the rest of the loop is the bf16 one.  Its keys are stored times key_scale * log2(e) * 2^k
+// staging slot (two slots of 16 KB, by iteration parity), and the next iteration widens exactly
+// those bytes to bf16 into the ring slots (exact conversion) in the gaps of its stream before the
+// softmax; the rest of the loop is the bf16 one.  Its keys are stored times key_scale * log2(e) * 2^k
 // and the queries are staged times 2^-k, so its program has no product per score either.
 // SK: bf16 cache whose keys are stored times scale * log2(e): the scores already are the
 // exponent (the host passes scale_log2 = 1) and the program has no product per score.
