@@ -9,9 +9,10 @@ tensors of the workload's shapes, generated before the timed region.
 Prints one JSON line.  `value` is the attention work of the step (algorithmic FLOPs,
 4 * nbatch * H * N * L * d per layer with L = (S + W + 1) * N keys) divided by the step time.
 `roofline` scores the attention call (split-KV kernel + combine) against the bf16 MFMA peak;
-its duration comes from HIP events on the library's stream around each attention call of the
-timed steps (workloads of 8 or more layers; a single-layer workload, whose step the host
-cannot keep ahead of, times a batch of back-to-back calls instead).  `hbm_kernels` scores the HBM-bound kernels
+its duration comes from HIP events on the library's stream around each attention call of steps
+run after the timed ones, in the same order (workloads of 8 or more layers; a single-layer
+workload, whose step the host cannot keep ahead of, times a batch of back-to-back calls
+instead).  No event sits inside the timed steps.  `hbm_kernels` scores the HBM-bound kernels
 (append, rebase, sink copy, split combine, motion reduction) against 8 TB/s.  `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the host cores.
 
@@ -112,8 +113,8 @@ class Stepper:
         """One step.  ev: dict of event pairs to record around the append batch, the attention
         batch (all layers back to back, each call repeated attn_repeat times), the refresh and
         the end-of-step chunk statistics / sink refresh.  Without ev, append and attention
-        alternate per layer as in a DiT forward; calls: then a dict of "append" and "attention"
-        lists, one event pair per layer each, recorded around each call."""
+        alternate per layer as in a DiT forward; calls: then a dict whose "attention" list holds
+        one event pair per layer, recorded around each attention call."""
         c, run = self.c, self.run
         first, nb, commit, newest = run.plan(self.s)
         st = self.sets[self.s % len(self.sets)]
@@ -135,11 +136,8 @@ class Stepper:
         else:
             for layer in range(c.num_layers):
                 q, k, v = st[layer]
-                if calls:
-                    calls["append"][layer][0].record()
                 run.cache.append(layer, first, nb, q[:nb], k[:nb], v[:nb])
                 if calls:
-                    calls["append"][layer][1].record()
                     calls["attention"][layer][0].record()
                 run.cache.attention(layer, nb, q[:nb], run.out[layer, :nb], run.scale)
                 if calls:
@@ -165,39 +163,43 @@ def events(names):
 
 
 def run_gpu(c, steps, warmup):
-    """Whole-step time; per-call append and attention times from HIP events around each call
-    inside the timed steps (workloads of 8 or more layers, where the host enqueues far ahead of
-    the GPU), else from a pass with events around batched calls."""
+    """Whole-step time over the timed steps (no event inside them: an event record between two
+    calls delays the next kernel by several microseconds); then per-call attention times from
+    HIP events around each attention call of further steps of the same kind (workloads of 8 or
+    more layers, where the host enqueues far ahead of the GPU), else from a pass with events
+    around batched calls."""
     import torch
     torch.cuda.set_device(0)
     st = Stepper(c)
     fill = c.sink_frames + c.window_frames + c.stream_batch + 1
     for _ in range(fill + warmup):
         st.step()
-    per_call = c.num_layers >= 8
-    calls = [{k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(c.num_layers)] for k in ("append", "attention")}
-             for _ in range(steps)] if per_call else [None] * steps
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for i in range(steps):
-        st.step(calls=calls[i])
+    for _ in range(steps):
+        st.step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / steps
     med = lambda v: sorted(v)[len(v) // 2] if v else None
+    per_call = c.num_layers >= 8
+    npass = max(3, min(10, steps // 2))
     if per_call:
+        calls = [{"attention": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                                for _ in range(c.num_layers)]} for _ in range(npass)]
+        for cl in calls:
+            st.step(calls=cl)
+        torch.cuda.synchronize()
         mean_ms = lambda pairs: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-        inside = {k: med([mean_ms(cl[k]) for cl in calls]) * 1e3 for k in ("append", "attention")}
+        in_step_us = med([mean_ms(cl["attention"]) for cl in calls]) * 1e3
     # batched pass: events around the append batch and the attention batch of each step; a
     # single-layer workload repeats its attention call so that a batch holds several calls
     repeat = max(1, 8 // c.num_layers)
     names = ("refresh", "append", "attention", "stats")
     acc = {n: [] for n in names}
-    npass = max(3, min(10, steps // 2))
     for _ in range(npass):
         ev = events(names)
         st.step(ev, attn_repeat=repeat)
@@ -211,19 +213,18 @@ def run_gpu(c, steps, warmup):
     attn_ms = med(acc["attention"])
     if per_call:
         timing = (f"HIP events on the library's stream around each of the {c.num_layers} attention calls of "
-                  f"each timed step (append and attention alternating per layer); median over the {steps} steps "
-                  "of the mean per call")
+                  f"{npass} steps run after the timed ones (append and attention alternating per layer, as "
+                  "in the timed steps); median over the steps of the mean per call")
     else:
         timing = (f"HIP events on the library's stream around {c.num_layers * repeat} back-to-back attention "
                   "calls per step (median of the batched steps)")
     return {"ms_per_step": ms_step, "wall_s": wall,
-            "attention_us": inside["attention"] if per_call else attn_ms * 1e3 / (c.num_layers * repeat),
+            "attention_us": in_step_us if per_call else attn_ms * 1e3 / (c.num_layers * repeat),
             "attention_timing": timing,
             "attention_batched_us": attn_ms * 1e3 / (c.num_layers * repeat),
             # the append (HBM-bound, 50 us or less) from the back-to-back batch: a per-call event
             # pair adds the few microseconds between the previous kernel's end and its start
             "append_us": med(acc["append"]) * 1e3 / c.num_layers,
-            "append_in_step_us": inside["append"] if per_call else None,
             "stats_us": None if not acc["stats"] else med(acc["stats"]) * 1e3,
             "refreshes": st.run.cache.state()[2]}
 
