@@ -41,7 +41,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-ATTN_SOURCES = ("k_attention.hip", "k_attention_w64.hip", "attn_w64_asm.h", "attn_tiles.h")
+# the attention kernels, their shared definitions and the host code that sizes their launches
+# (the split-KV work plan): a profile taken on other sources is not used
+ATTN_SOURCES = ("k_attention.hip", "k_attention_w64.hip", "attn_w64_asm.h", "attn_tiles.h", "common.h", "sdv2.cpp")
 
 
 def attn_source_hash() -> str:

@@ -149,13 +149,13 @@ sdv2_layout make_layout(const sdv2_config& c) {
 // full rounds of 32, the rest split into k key ranges) costs, on the slowest XCD, its rounds x
 // (tiles per workgroup x one 64-key tile step + the workgroup's prologue and epilogue), plus
 // the bf16 partial results the tail items write and the combine reads back.  The constants are
-// measured on MI355X with the 64-row kernel: about 1.6 us per tile step of a 256-row workgroup
+// measured on MI355X with the 64-row kernel: about 1.5 us per tile step of a 256-row workgroup
 // with every CU busy, 8 us of prologue/epilogue per round and ~5 TB/s for the partial traffic.
 // A round that leaves CUs idle runs at a higher clock (the chip is power-bound): its tile step
-// is shorter by kClockGain x the idle fraction (1.45 us measured at 3/4 occupancy).
+// is shorter by kClockGain x the idle fraction (1.26 us measured at 3/4 occupancy).
 constexpr int kCuPerXcd = 32;
 constexpr int kMaxSplit = 16;
-constexpr double kTileUs = 1.6, kRoundUs = 8.0, kClockGain = 0.38;
+constexpr double kTileUs = 1.51, kRoundUs = 8.0, kClockGain = 0.66;
 constexpr double kPartialBytesPerUs = 5.0e6, kCombineUs = 6.0;
 
 // Rounds of n workgroups of `tiles` tiles each on one XCD.
