@@ -169,6 +169,20 @@ def test_sixty_four_attended_frames(S, W, T):
     _stream(cfg, cfg.num_steps, cache_check=lambda s: s in (fill - 1, fill + 5, cfg.num_steps - 1))
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "e4m3"])
+def test_sixteen_sinks_widest_temporal_rope_and_full_batch(kv_fp8):
+    # the other limits at once: S = 16 sinks (the most the library takes) under sink refresh,
+    # rope_dim_t = 64 (32 temporal pairs, the most) with a refresh every 5 frames, B T' = 8
+    # (B = 4, T' = 2); every output of every step, the cache at fill, after refreshes and at the end
+    cfg = _small(dtype="bf16", head_dim=128, rope_dim_t=64, rope_dim_h=32, rope_dim_w=32, grid_h=6, grid_w=11,
+                 num_heads=2, sink_frames=16, window_frames=3, chunk_frames=2, stream_batch=4, kv_fp8=kv_fp8,
+                 num_chunks=16, rope_refresh_period=5, embed_dim=16, sink_threshold=0.5, embed_kind="iid",
+                 softmax_scale=128 ** -0.5)
+    h = _stream(cfg, cfg.num_steps, cache_check=lambda s: s in (8, 12, cfg.num_steps - 1))
+    assert len(h.st.refresh_log) >= 4
+    assert sum(1 for d, _ in h.decisions.values() if d["replaced"]) >= 1
+
+
 @pytest.mark.parametrize("kv_fp8,heads", [(False, 255), (True, 510)], ids=["bf16", "e4m3"])
 def test_layer_block_at_the_4gib_limit(kv_fp8, heads):
     # 64 slots (S + W + T' = 1 + 62 + 1) of `heads` x 1024 tokens x 128 dims: a layer's K block
