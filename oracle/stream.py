@@ -133,20 +133,26 @@ class OracleStream:
         self.plan = schedule(self.cfg, s)
         T_reset = self.cfg.rope_refresh_period
         f_new = self.plan["newest_frame"]
+        n = 0
         while T_reset > 0 and f_new is not None and f_new - self.base >= T_reset:
             self.base += T_reset
+            n += 1
+            self.refresh_log.append((s, self.base))
+        if n:
+            # one refresh event per step: when the newest frame passes several periods at once
+            # (T' > T_reset), the labels drop by the whole n T_reset and stored e4m3 keys turn
+            # back by it once, with one rounding
             moved = self.window if self.cfg.rope_pin_sinks else self.cached_entries()
             for e in moved:
-                e.label -= T_reset
+                e.label -= n * T_reset
                 if self.kv_fp8:
-                    e.kv = {layer: (self._turn_back(K, T_reset), V) for layer, (K, V) in e.kv.items()}
-            self.refresh_log.append((s, self.base))
+                    e.kv = {layer: (self._turn_back(K, n * T_reset), V) for layer, (K, V) in e.kv.items()}
         return self.plan
 
-    def _turn_back(self, K: np.ndarray, T_reset: int) -> np.ndarray:
-        """Stored (rotated, e4m3) keys of a frame whose label drops by T_reset: the temporal
-        pairs turn by -T_reset * omega (the row and column pairs by angle 0), then round."""
-        phi = rope.angles(self.cfg, -float(T_reset), 0.0, 0.0)
+    def _turn_back(self, K: np.ndarray, delta: int) -> np.ndarray:
+        """Stored (rotated, e4m3) keys of a frame whose label drops by delta: the temporal
+        pairs turn by -delta * omega (the row and column pairs by angle 0), then round."""
+        phi = rope.angles(self.cfg, -float(delta), 0.0, 0.0)
         return ofp8.round_fp8(rope.rotate_pairs(K, phi))
 
     def _stored(self, K_raw: np.ndarray, V: np.ndarray, label: int):

@@ -152,10 +152,14 @@ def _history_output_fp8(cfg, s, elem, layer, sink_frames):
     k_parts, v_parts, kf = [], [], []
     for f in frames:
         k, v = committed_frame_kv(cfg, f, layer)
-        b_c = refresh_base(cfg, f // T + B - 1)
+        c_step = f // T + B - 1                   # the step that committed frame f
+        b_c = refresh_base(cfg, c_step)
         key = round_e4m3(gk * frame_rope(cfg, k, f - b_c))
-        for _ in range((b_s - b_c) // T_reset if T_reset else 0):
-            key = round_e4m3(complex_rope(cfg, key, -T_reset, 0, 0))
+        # each later step whose base moved turns the stored key back by that step's move, once
+        for s2 in range(c_step + 1, s + 1):
+            d = refresh_base(cfg, s2) - refresh_base(cfg, s2 - 1)
+            if d:
+                key = round_e4m3(complex_rope(cfg, key, -d, 0, 0))
         k_parts.append(key / gk)
         v_parts.append(round_e4m3(v))
         kf.append(np.full(N, -1))

@@ -96,11 +96,14 @@ def test_brute_rounding_agrees_with_the_table_encoder():
 
 
 @pytest.mark.parametrize("T,B,period,scaled", [(1, 1, 3, False), (1, 2, 3, False), (2, 2, 4, False),
-                                               (1, 3, 0, False), (1, 2, 3, True), (2, 2, 4, True)])
+                                               (1, 3, 0, False), (1, 2, 3, True), (2, 2, 4, True),
+                                               (3, 2, 2, False), (3, 1, 2, True)])
 def test_fp8_stream_equals_history_fold(T, B, period, scaled):
     # every output at every step equals attention over keys rebuilt from the frame history:
-    # commit-time rounding, one turn-back and rounding per refresh since, all relative to b0(s)
-    # (scaled: each key times the key factor before its roundings, divided out when attending)
+    # commit-time rounding, then one turn-back and rounding for each later step whose base
+    # moved, by that step's move (T' > T_reset: some steps pass two periods at once), all
+    # relative to b0(s) (scaled: each key times the key factor before its roundings, divided
+    # out when attending)
     cfg = (_fp8_scaled_cfg if scaled else _fp8_cfg)(chunk_frames=T, stream_batch=B, rope_refresh_period=period)
     st, outs = brute.run_oracle(cfg)
     assert (len(st.refresh_log) > 2) == (period > 0)
