@@ -34,7 +34,7 @@ def random_config(seed: int):
         num_chunks=(S + W) // T + 3 + B, q_prescale=1.0 if scale < 1 else 1.0 / math.sqrt(d), softmax_scale=scale,
         embed_dim=16 if sink_refresh else 0, sink_threshold=float(r.choice([0.2, 0.5])) if sink_refresh else None,
         embed_kind="iid" if sink_refresh else None, rope_pin_sinks=S >= 1 and bool(r.integers(2)),
-        scaled_keys=bool(r.integers(3)))
+        scaled_keys=bool(r.integers(3)) or kind == "e4m3")   # (the e4m3 cache needs its key scale)
 
 
 def forced_splits(seed: int):
