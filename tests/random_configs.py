@@ -46,4 +46,4 @@ def forced_splits(seed: int):
     return [None, 2, 3, 5][seed % 4]
 
 
-SEEDS = list(range(40))
+SEEDS = list(range(100))
