@@ -154,18 +154,27 @@ void attn_w64_kernel(const AttnArgs a) {
   };
 
   // Global->LDS loads.  bf16: wave w fills 1 KB pieces w*LD .. w*LD+LD-1 of each ring tile.
-  // e4m3: wave w loads K rows 16w + 8i + lane / 8 (chunk lane % 8) and V^T rows 32w + 16i +
-  // lane / 4 (chunk lane % 4), i = 0, 1, in lane order into its 2 KB of the staging slot.
+  // e4m3: wave w loads 16-byte chunks of K rows 16w + 8i + [0, 8) and V^T rows 32w + 16i +
+  // [0, 16), i = 0, 1, lane l taking chunk kc8 of K row kr (vc8 of V^T row vr) below, into its
+  // 2 KB of the staging slot in lane order.  The widened write of a lane's chunk lands at the
+  // row's swizzled bf16 chunks; the LDS serves a 16-byte write 8 lanes (128 bytes) at a time, so
+  // each group of 8 lanes pairs 4 chunks of a row with 4 of a row whose swizzle differs in bit 1
+  // (K rows r and r + 2, V^T rows r and r + 4): their positions mod 128 bytes are disjoint and
+  // every write is free of bank conflicts (in row order two rows of a group collide).
+  const int g8 = lane >> 3, sub = (lane >> 2) & 1;
+  const int kr = (0x5410 >> (4 * (g8 >> 1)) & 15) + 2 * sub;     // row pairs {0,2} {1,3} {4,6} {5,7}
+  const int kc8 = (lane & 3) + 4 * (sub ^ (g8 & 1));
+  const int vr = ((g8 & 3) | ((g8 & 4) << 1)) + 4 * sub, vc8 = lane & 3;
   uint32_t koff[LD], voff[LD];
   int kr8[LD], vr8[LD];
 #pragma unroll
   for (int i = 0; i < LD; ++i) {
     int Rr, c;
     if constexpr (F8) {
-      kr8[i] = 16 * wave + 8 * i + (lane >> 3);
-      koff[i] = (uint32_t)(perm_key(kr8[i]) * D + (lane & 7) * 16);
-      vr8[i] = 32 * wave + 16 * i + (lane >> 2);
-      voff[i] = (uint32_t)(vr8[i] * a.Npad + (lane & 3) * 16);
+      kr8[i] = 16 * wave + 8 * i + kr;
+      koff[i] = (uint32_t)(perm_key(kr8[i]) * D + kc8 * 16);
+      vr8[i] = 32 * wave + 16 * i + vr;
+      voff[i] = (uint32_t)(vr8[i] * a.Npad + vc8 * 16);
     } else {
       lds_chunk_inv<KRB>((wave * LD + i) * 64 + lane, Rr, c);
       koff[i] = (uint32_t)(perm_key(Rr) * KRB + c * 16);
@@ -326,7 +335,6 @@ void attn_w64_kernel(const AttnArgs a) {
     i32x4 wk, wv;
 #pragma unroll
     for (int i = 0; i < LD; ++i) {
-      const int kc8 = lane & 7, vc8 = lane & 3;
       wk[2 * i] = (int)((uint32_t)(uintptr_t)ldsK + lds_chunk<KRB>(kr8[i], 4 * (kc8 >> 1) + (kc8 & 1)));
       wk[2 * i + 1] = (int)((uint32_t)(uintptr_t)ldsK + lds_chunk<KRB>(kr8[i], 4 * (kc8 >> 1) + 2 + (kc8 & 1)));
       wv[2 * i] = (int)((uint32_t)(uintptr_t)ldsV + lds_chunk<VRB>(vr8[i], 4 * (vc8 >> 1) + (vc8 & 1)));
