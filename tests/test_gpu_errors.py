@@ -147,15 +147,18 @@ class FailFirst:
         return wrapped
 
 
-def test_injected_hip_failures_leave_the_stream_intact():
+def test_injected_hip_failures_leave_the_stream_intact(monkeypatch):
     # bf16, two layers, refresh every 3 frames, sink refresh with i.i.d. embeddings, B = 2 and
-    # split-KV: every entry point that launches fails once per call, then succeeds; outputs,
-    # cache, decisions and statistics still match the oracle at every step
+    # split-KV (three splits forced: attention and combine launches): every entry point that
+    # launches fails once per call, then succeeds; outputs, cache, decisions and statistics
+    # still match the oracle at every step
+    monkeypatch.setenv("SDV2_NSPLIT", "3")
     cfg = configs.TINY_FP32.with_(dtype="bf16", head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42,
                                   grid_h=5, grid_w=13, num_heads=2, num_layers=2, sink_frames=1,
                                   window_frames=2, stream_batch=2, rope_refresh_period=3, num_chunks=8,
                                   embed_dim=16, sink_threshold=0.2, embed_kind="iid",
                                   softmax_scale=128 ** -0.5)
+    assert sdv2.sdv2_cache_size(sdv2.config_of(cfg))[2] > 0      # the forced splits are in effect
     h = Harness(cfg, range(cfg.num_layers))
     proxy = FailFirst(h.run.cache)
     h.run.cache = proxy

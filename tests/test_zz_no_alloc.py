@@ -50,9 +50,9 @@ def _compare(cfg, steps, seed):
     return nb
 
 
-def test_static_scratch_matches_workspace_then_a_smaller_call():
+def test_static_scratch_matches_workspace_then_a_smaller_call(monkeypatch):
     # 1.3B single layer: five splits (16 MB of partials), then a smaller ragged stream (65
-    # tokens, B = 3, four splits forced by size) on the same GPU's array
+    # tokens, B = 3, four splits forced) on the same GPU's array
     big = configs.WAN13B_1LAYER
     kv, meta, ws = sdv2.sdv2_cache_size(sdv2.config_of(big))
     assert ws > 0, "the workload must use split-KV partials"
@@ -62,6 +62,7 @@ def test_static_scratch_matches_workspace_then_a_smaller_call():
                                     grid_h=5, grid_w=13, num_heads=3, sink_frames=2, window_frames=3,
                                     stream_batch=3, rope_refresh_period=0, sink_threshold=None, embed_dim=0,
                                     embed_kind=None, softmax_scale=128 ** -0.5, name="small_b3")
+    monkeypatch.setenv("SDV2_NSPLIT", "4")
     assert 0 < sdv2.sdv2_cache_size(sdv2.config_of(small))[2] < ws
     _compare(small, 8, 2)
 
@@ -84,7 +85,7 @@ def test_static_scratch_refuses_partials_beyond_its_size(monkeypatch):
     run.cache.close()
 
 
-def test_static_entry_point_replays_from_a_hip_graph():
+def test_static_entry_point_replays_from_a_hip_graph(monkeypatch):
     # The callers the entry point is for: one chunk-attention call (split-KV: attention and
     # combine launches, partials in the static array) captured into a HIP graph and replayed.
     # Before each replay the output is set to NaN and an eager call of its own runs on the same
@@ -94,6 +95,7 @@ def test_static_entry_point_replays_from_a_hip_graph():
                                   grid_h=5, grid_w=13, num_heads=3, sink_frames=2, window_frames=3,
                                   stream_batch=3, rope_refresh_period=0, sink_threshold=None, embed_dim=0,
                                   embed_kind=None, softmax_scale=128 ** -0.5, name="graph_b3")
+    monkeypatch.setenv("SDV2_NSPLIT", "4")                        # four splits forced
     assert sdv2.sdv2_cache_size(sdv2.config_of(cfg))[2] > 0, "the call must use split-KV partials"
     run, nb, qs = _steady(cfg, 8, 4)
     q, h, scale = qs[0], run.cache.handle, cfg.softmax_scale
