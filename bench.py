@@ -15,6 +15,10 @@ workload, whose step the host cannot keep ahead of, times a batch of back-to-bac
 instead).  No event sits inside the timed steps.  `hbm_kernels` scores the HBM-bound kernels
 (append, rebase, sink copy, split combine, motion reduction) against 8 TB/s.  `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the host cores.
+`reference_rates` (bf16 workloads, after the timed steps) times torch.matmul's square bf16 GEMM
+(hipBLASLt) and PyTorch's SDPA on the workload's attention shape on the same GPU;
+`roofline.frac_of_measured_gemm` divides `achieved` by the 16384^3 GEMM's rate, a measured
+second denominator beside the published peak.
 
 The default workload is the largest single-GPU one: the Wan-14B-shaped 40-layer stack with a
 stream batch of 4 and the sink refresh.
@@ -470,6 +474,8 @@ def main():
                     help="OCP e4m3 KV cache (bf16 queries, scores and outputs)")
     ap.add_argument("--reference-rates", action="store_true",
                     help="print library rates on this GPU (bf16 GEMM, PyTorch SDPA on the workload's shape)")
+    ap.add_argument("--no-reference-rates", action="store_true",
+                    help="leave the library reference rates out of the line")
     ap.add_argument("--target-fps", type=float, default=30.0)
     ap.add_argument("--deadline-ms", type=float, default=100.0)
     args = ap.parse_args()
@@ -549,6 +555,13 @@ def main():
                               "how": f"rocprofv3 kernel trace, profiles/attn_trace_{c.name}.md "
                                      f"({prof.get('nsplit')} split partials read, output written)"}
         out["hbm_kernels"] = hbm
+    if not args.no_reference_rates and c.dtype == "bf16":
+        log("bench: library reference rates (bf16 GEMM, PyTorch SDPA) on this GPU")
+        ref = reference_rates(c, n=10, warmup=3)
+        gemm = ref["gemm_bf16"]["16384"]["tflops"]
+        roof["measured_gemm_tflops"] = gemm
+        roof["frac_of_measured_gemm"] = round(achieved / gemm, 4)
+        out["reference_rates"] = ref
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline(c)
