@@ -938,23 +938,27 @@ def check_staging(iterations=10, masked=(2, 5)):
     masked at the given ones, the last PV) and check the data each LDS read finds: a staged
     chunk is read only once its load is counted complete by a vmcnt wait and holds the tile the
     widening expects (iteration t widens K(t+1) and V^T(t)); the fragment reads of iteration t
-    find K(t) and V^T(t-1) in the bf16 ring, the last PV V^T(n-1).  The other waves' share is
-    the same with its own addresses, and the barrier at each iteration's top orders the waves."""
+    find K(t) and V^T(t-1) in the bf16 ring, the last PV V^T(n-1), written by the widening
+    before a barrier; a widened write goes into a ring slot only after a barrier has passed since
+    the slot's last read.  The other waves' share is the same with its own addresses, and the
+    barrier at each iteration's top orders the waves."""
     assert F8
     pending = [((0, 0), ("K", 0)), ((0, 1), ("K", 0)), ((1, 0), ("K", 1)), ((1, 1), ("K", 1)),
                ((1, 8), ("V", 0)), ((1, 9), ("V", 0))]
     staged = {(0, 8): ("V", -1), (0, 9): ("V", -1)}          # zeroed by the prologue: V^T(-1)
-    ring, regs, addr_kind = {}, {}, {}
-    m0 = None
+    ring, regs, addr_kind, last_read = {}, {}, {}, {}
+    m0, barriers = None, 0
 
     def run(lines, t, expect_k, expect_v):
-        nonlocal pending, m0
+        nonlocal pending, m0, barriers
         for l in lines:
             tok = l.replace(",", " ").split()
             if not tok or l.startswith(".L"):
                 continue
             op = tok[0]
-            if op == "s_add_u32" and tok[1] == "m0":
+            if op == "s_barrier":
+                barriers += 1
+            elif op == "s_add_u32" and tok[1] == "m0":
                 m0 = int(tok[3]) if tok[2] == "%[ms]" else (m0 + int(tok[3]) if tok[2] == "m0" else None)
             elif op.startswith("global_load_lds"):
                 part = (m0 // STAGE, (m0 % STAGE) // 1024)
@@ -981,7 +985,10 @@ def check_staging(iterations=10, masked=(2, 5)):
                 else:
                     kind = "K" if KADDR <= int(tok[2][1:]) < KADDR + 8 else "V"
                     want = ("K", t) if kind == "K" else ("V", t - 1)
-                    assert ring.get((kind, off // KTILE)) == want, (t, l, ring.get((kind, off // KTILE)), want)
+                    what, when = ring.get((kind, off // KTILE), (None, None))
+                    assert what == want, (t, l, what, want)
+                    assert when < barriers, (t, l, "reads a widened tile no barrier has passed since")
+                    last_read[(kind, off // KTILE)] = barriers
             elif op == "v_cvt_scalef32_pk_bf16_fp8":
                 regs[int(tok[1][1:])] = regs[int(tok[2][1:])]
             elif op == "ds_write_b128":
@@ -990,7 +997,9 @@ def check_staging(iterations=10, masked=(2, 5)):
                 assert len(vals) == 1, (t, l, vals)
                 what = vals.pop()
                 assert what[0] == addr_kind[tok[1]], (t, l, what)
-                ring[(what[0], int(tok[3].split(":")[1]) // KTILE)] = what
+                key = (what[0], int(tok[3].split(":")[1]) // KTILE)
+                assert last_read.get(key, -1) < barriers, (t, l, "widens into a slot read since the last barrier")
+                ring[key] = (what, barriers)
 
     lines = loop_program()
     pre = lines[:lines.index(".Lw64_loop_%=:")]
@@ -1001,6 +1010,82 @@ def check_staging(iterations=10, masked=(2, 5)):
         run(["s_barrier"] + body, t, ("K", t + 1), ("V", t))
     ph = iterations % NSLOT
     run(["s_waitcnt vmcnt(0)", "s_barrier"] + pv_only_block(ph), iterations, None, None)
+
+
+def check_ring(iterations=10, masked=(2, 5), rare=(3, 5)):
+    """bf16: run the tile loads, waits, barriers and LDS reads of the tile loop as one wave
+    executes them (the prologue's loads of K(0) and K(1) into ring slots 0 and 1 and of V^T(0)
+    into slot 0 with V^T(-1) zeroed in slot 3, iterations 0 .. iterations-1, masked and rescaled
+    at the given ones, the last PV) and check the ring protocol.  A fragment read of iteration t
+    finds K(t) (V^T(t-1)) in its slot: this wave's four 1 KB pieces of that tile were loaded
+    there, counted complete by a vmcnt wait, and a barrier has passed since (every wave runs
+    this program on its own pieces, so then every piece is in).  A tile load goes into a slot
+    only after a barrier has passed since the slot's last read, and no LDS op is in flight at a
+    barrier."""
+    assert not F8
+    pending = [((kind, slot, p), what) for kind, slot, what in
+               (("K", 0, ("K", 0)), ("K", 1, ("K", 1)), ("V", 0, ("V", 0))) for p in range(4)]
+    done, visible, last_read = {}, {("V", 3): ("V", -1)}, {}
+    state = {"barriers": 0, "lds": 0, "m0": None}
+
+    def run(lines, t):
+        nonlocal pending
+        for l in lines:
+            tok = l.replace(",", " ").split()
+            if not tok or l.startswith(".L"):
+                continue
+            op = tok[0]
+            if op == "s_add_u32" and tok[1] == "m0":
+                if tok[2] in ("%[mk]", "%[mv]"):
+                    state["m0"] = ("K" if tok[2] == "%[mk]" else "V", int(tok[3]))
+                elif tok[2] == "m0" and state["m0"]:
+                    state["m0"] = (state["m0"][0], state["m0"][1] + int(tok[3]))
+                else:
+                    state["m0"] = None
+            elif op.startswith("global_load_lds"):
+                assert state["m0"], (t, l, "m0 does not hold a ring address")
+                kind, off = state["m0"]
+                key = (kind, off // KTILE)
+                assert last_read.get(key, -1) < state["barriers"], (t, l, "a load into a slot read since the last barrier")
+                pending.append(((kind, off // KTILE, (off % KTILE) // 1024), ("K", t + 2) if kind == "K" else ("V", t + 1)))
+                visible.pop(key, None)
+            elif op == "s_waitcnt" and "vmcnt(" in l:
+                n = int(l.split("vmcnt(")[1].split(")")[0])
+                for piece, what in pending[:max(0, len(pending) - n)]:
+                    done[piece] = what
+                pending = pending[max(0, len(pending) - n):]
+            elif op == "s_waitcnt" and "lgkmcnt(" in l:
+                state["lds"] = min(state["lds"], int(l.split("lgkmcnt(")[1].split(")")[0]))
+            elif op == "s_barrier":
+                assert state["lds"] == 0, (t, "LDS ops in flight at a barrier")
+                state["barriers"] += 1
+                busy = {piece[:2] for piece, _ in pending}
+                for kind in "KV":
+                    for sl in range(NSLOT):
+                        w = {done.get((kind, sl, p)) for p in range(4)}
+                        if len(w) == 1 and None not in w and (kind, sl) not in busy:
+                            visible[(kind, sl)] = w.pop()
+            elif op == "ds_read_b128":
+                a, off = int(tok[2][1:]), int(tok[3].split(":")[1])
+                kind = "K" if KADDR <= a < KADDR + 8 else "V"
+                assert kind == "K" or VADDR <= a < VADDR + 4, (t, l)
+                key = (kind, off // KTILE)
+                want = ("K", t) if kind == "K" else ("V", t - 1)
+                assert visible.get(key) == want, (t, l, visible.get(key), want)
+                last_read[key] = state["barriers"]
+                state["lds"] += 1
+            elif op.startswith("ds_"):
+                state["lds"] += 1
+
+    lines = loop_program()
+    run(lines[:lines.index(".Lw64_loop_%=:")], -1)
+    for t in range(iterations):
+        ph = t % NSLOT
+        top = iteration(ph)
+        top = top[:next(i for i, l in enumerate(top) if l.startswith("s_cbranch_scc0 .Lw64_m")) + 1]
+        body = tile_block(ph, t in masked) + (rare_block(ph % 2, t in masked) if t in rare else [])
+        run(top + body, t)
+    run(["s_waitcnt vmcnt(0)", "s_barrier"] + pv_only_block(iterations % NSLOT), iterations)
 
 
 def emit(name, lines):
@@ -1014,8 +1099,10 @@ def main():
     out = ["// Generated by gen_attn_w64.py; do not edit.  The tile loop of the 64-row attention",
            "// kernel as one asm program (register plan, blocks and hazard rules in the generator).", ""]
     set_mode(False)
+    check_ring()
     out.append(emit("SDV2_W64_LOOP", loop_program()))
     set_mode(False, scaled=True)
+    check_ring()
     out.append(emit("SDV2_W64_LOOP_SK", loop_program()))
     set_mode(True, scaled=True)
     check_staging()

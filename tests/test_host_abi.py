@@ -380,6 +380,59 @@ def test_generator_staging_check_rejects_planted_mistakes():
     gen.check_staging()
 
 
+def test_generator_ring_check_rejects_planted_mistakes():
+    # The bf16 programs load each K and V^T tile straight into an LDS ring slot two iterations
+    # ahead; check_ring runs one wave's loads, waits, barriers and fragment reads.  It passes
+    # both committed bf16 programs and rejects: the iteration's vmcnt wait one load short, the
+    # barrier left out, K(t+2) loaded into the slot K(t+1) is about to be read from, V^T(t+1)
+    # loaded into the slot V^T(t-1) is being read from, and the stream's last fragment read moved
+    # after its final LDS wait (still in flight at the next barrier).
+    import importlib.util
+    import pathlib
+    csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
+    spec = importlib.util.spec_from_file_location("gen_attn_w64_ring", csrc / "gen_attn_w64.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    for scaled in (False, True):
+        gen.set_mode(False, scaled=scaled)
+        gen.check_ring()
+    iteration, loads, resolve = gen.iteration, gen.tile_loads, gen.resolve_waits
+
+    def short_wait(ph):
+        return [l.replace("vmcnt(8)", "vmcnt(9)") for l in iteration(ph)]
+
+    def no_barrier(ph):
+        return [l for l in iteration(ph) if l != "s_barrier"]
+
+    def slot_shift(kind, delta):
+        def f(ph):
+            base = "%[mk]" if kind == "K" else "%[mv]"
+            d = {}
+            for i, (setup, load) in loads(ph).items():
+                if setup.startswith(f"s_add_u32 m0, {base},"):
+                    off = int(setup.split(",")[-1])
+                    setup = f"s_add_u32 m0, {base}, {(off + delta * gen.KTILE) % (gen.NSLOT * gen.KTILE)}"
+                d[i] = (setup, load)
+            return d
+        return f
+
+    def read_after_last_wait(out):
+        lines = resolve(out)
+        last = max(i for i, l in enumerate(lines) if l.startswith("ds_read_b128"))
+        return lines[:last] + lines[last + 1:] + [lines[last]]
+
+    for name, attr, plant in (("short vmcnt", "iteration", short_wait),
+                              ("no barrier", "iteration", no_barrier),
+                              ("K one slot early", "tile_loads", slot_shift("K", -1)),
+                              ("V^T two slots late", "tile_loads", slot_shift("V", 2)),
+                              ("a read in flight at the barrier", "resolve_waits", read_after_last_wait)):
+        setattr(gen, attr, plant)
+        with pytest.raises(AssertionError):
+            gen.check_ring()
+        setattr(gen, attr, {"iteration": iteration, "tile_loads": loads, "resolve_waits": resolve}[attr])
+    gen.check_ring()
+
+
 def test_layer_blocks_over_the_32_bit_offset_range_are_rejected():
     # The attention tile loop forms offsets inside a layer's K or V block in 32 bits: a layer
     # block of 4 GiB or more, or a slot of 2 GiB or more, is refused at validation.
