@@ -55,7 +55,10 @@ def _decode(cfg, raw, shape):
          num_chunks=8, softmax_scale=128 ** -0.5, num_layers=2),
     dict(dtype="fp32", head_dim=64, grid_h=3, grid_w=7, num_heads=2, sink_frames=1, window_frames=2,
          stream_batch=2, rope_refresh_period=3, num_chunks=8),
-], ids=["bf16-B3-refresh", "bf16-T2-block-causal", "fp32-d64"])
+    dict(dtype="bf16", kv_fp8=True, head_dim=128, rope_dim_t=44, rope_dim_h=42, rope_dim_w=42, grid_h=5,
+         grid_w=13, num_heads=2, sink_frames=1, window_frames=3, stream_batch=2, rope_refresh_period=4,
+         num_chunks=10, softmax_scale=128 ** -0.5, num_layers=2),
+], ids=["bf16-B3-refresh", "bf16-T2-block-causal", "fp32-d64", "e4m3-cache"])
 def test_stream_from_plain_c_matches_the_oracle(kw, tmp_path):
     base = dict(rope_refresh_period=0, sink_threshold=None, embed_dim=0, embed_kind=None)
     base.update(kw)
