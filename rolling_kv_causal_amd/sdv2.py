@@ -8,7 +8,6 @@ call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import pathlib
 from typing import Optional
 
