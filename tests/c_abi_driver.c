@@ -5,9 +5,13 @@
  *   c_abi_driver <inputs> <outputs>
  *
  * <inputs>:  the sdv2_config struct as laid out in sdv2.h, int64 num_chunks, float scale, then
- *            for every step with a non-empty stream batch (schedule from sdv2_plan_step) and
- *            every layer: q, k, v, each [nbatch][T'N][H][d] in the activation dtype.
- * <outputs>: for the same steps and layers, the attention output [nbatch][T'N][H][d].
+ *            for every step with a non-empty stream batch (schedule from sdv2_plan_step): for
+ *            every layer q, k, v, each [nbatch][T'N][H][d] in the activation dtype, and, when
+ *            the step commits a chunk and embed_dim > 0, that chunk's fp32 embedding.
+ * <outputs>: for the same steps and layers, the attention output [nbatch][T'N][H][d], and
+ *            after each commit with an embedding the sink decision: int64 slot (j* if
+ *            replaced, else -1, also when no decision was taken), double alpha_j* (1 when no
+ *            decision was taken).
  * Exit status 0 on success; any failing call prints its sdv2_last_error() text and exits 1.
  */
 #include <hip/hip_runtime_api.h>
@@ -82,6 +86,13 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipMalloc(&d_o, max_bytes));
   char* h = (char*)malloc(max_bytes);
   if (!h) return 1;
+  float* d_embed = NULL;
+  float* h_embed = NULL;
+  if (cfg.embed_dim > 0) {
+    CHECK_HIP(hipMalloc((void**)&d_embed, sizeof(float) * cfg.embed_dim));
+    h_embed = (float*)malloc(sizeof(float) * cfg.embed_dim);
+    if (!h_embed) return 1;
+  }
 
   const int64_t num_steps = num_chunks + cfg.stream_batch - 1;
   int steps_run = 0;
@@ -106,12 +117,26 @@ int main(int argc, char** argv) {
       CHECK_HIP(hipStreamSynchronize(stream));
       if (fwrite(h, 1, bytes, out) != bytes) return 1;
     }
-    if (commit >= 0) CHECK_SDV2(sdv2_cache_commit(cache, commit, stream));
+    if (commit >= 0) {
+      CHECK_SDV2(sdv2_cache_commit(cache, commit, stream));
+      if (cfg.embed_dim > 0) {
+        read_exact(in, h_embed, sizeof(float) * cfg.embed_dim);
+        CHECK_HIP(hipMemcpyAsync(d_embed, h_embed, sizeof(float) * cfg.embed_dim, hipMemcpyHostToDevice, stream));
+        int32_t slot = -3;                    /* the call always writes it */
+        double alpha = 0.0;
+        const int64_t last_frame = (commit + 1) * cfg.chunk_frames - 1;
+        CHECK_SDV2(sdv2_sink_replace(cache, last_frame, d_embed, NULL, NULL, 0, NULL, &slot, &alpha, stream));
+        const int64_t slot64 = slot;
+        if (fwrite(&slot64, sizeof slot64, 1, out) != 1 || fwrite(&alpha, sizeof alpha, 1, out) != 1) return 1;
+      }
+    }
     ++steps_run;
   }
   CHECK_HIP(hipStreamSynchronize(stream));
   CHECK_SDV2(sdv2_cache_destroy(cache));
   free(h);
+  free(h_embed);
+  if (d_embed) hipFree(d_embed);
   hipFree(d_q);
   hipFree(d_k);
   hipFree(d_v);
