@@ -82,6 +82,7 @@ SM_FROM = 20                                     # first MFMA followed by softma
 WAIT_EVERY = 4                                   # one LDS wait per this many fragment reads
 READ_START = 2                                   # fragment reads issued before the first MFMA
 NEXT_GAP = ["<next gap>"]                        # unit marker: continue the chunk after the next MFMA
+LATE = "<late>"                                  # widen unit marker: issue after its MFMA pair's fragment reads
 GAP_CAP = 5                                      # instructions between two MFMAs the set-up may fill up to
 WIDEN_CAP = 8                                    # ... and the e4m3 widening (set-up included)
 WIDEN_END = 16                                   # e4m3: first gap of the set-up, after most of the widening
@@ -265,7 +266,9 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=(), widen=()):
     MFMA, from the chunk's first gap on, into the first gap with room for it (at most GAP_CAP
     instructions besides the MFMA), so the wave can issue it while the matrix core works.
     widen: (first gap, unit) pairs (e4m3), placed in order after the set-up, each from its first
-    gap on into the first gap with room (WIDEN_CAP), all before the softmax's first gap.  Waits
+    gap on into the first gap with room (WIDEN_CAP), all before the softmax's first gap; a unit
+    that starts with LATE goes, on a cursor of its own, after the fragment reads that follow the
+    MFMA pair of its first gap, one such unit per pair.  Waits
     are written as marks and resolved at the end: lgkmcnt(@Fi) waits for fragment read i and
     lgkmcnt(@Wj) for widening read j, counting every LDS op issued after it (LDS ops complete in
     order); vmcnt(@Pj) waits for load j of the previous iteration's four (e4m3), counting the
@@ -327,8 +330,17 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=(), widen=()):
             placed[g] += u
             load[g] += len(u)
     wplaced = [[] for _ in range(n_mfma)]
-    g = 0
+    late = [[] for _ in range(len(reads))]       # issued after the fragment reads of MFMA pair i
+    g, gl = 0, 0
     for first_gap, u in widen:
+        if u and u[0] == LATE:
+            gl = max(gl, first_gap)
+            while late[gl // 2]:
+                gl += 2
+            assert gl < valu_from, "the widening must end before the softmax reuses its registers"
+            late[gl // 2] += u[1:]
+            load[gl | 1] += len(u) - 1
+            continue
         g = max(g, first_gap)
         while g < valu_from and load[g] + len(u) > WIDEN_CAP:
             g += 1
@@ -354,6 +366,7 @@ def stream(reads, pp, ph, valu, dma=None, valu_from=0, extra=(), widen=()):
             out.append(("s_nop 0", None))
         if i in dma:
             out.append((dma[i][1], None))
+        out += [(x, None) for x in late[i]]
     assert vi == len(valu)
     out.append(("s_waitcnt lgkmcnt(0)", None))
     return resolve_waits(out)
@@ -703,7 +716,10 @@ def widen_units(ph, pc):
     chunk j = (K0, K1, V0, V1) in its 8 registers R..R+7: the staged 16 bytes are read into
     R+4..R+7 and widened in place (bf16 pair 2dw + sel from staged word dw: each word is read
     by both of its conversions before a later one overwrites it); the temporaries hold the
-    write addresses.  K is widened first: its loads were issued earliest."""
+    write addresses.  K is widened first: its loads were issued earliest.  The eight widened
+    writes go one per MFMA pair, pairs 2 to 9, each after the pair's fragment reads: LDS ops
+    complete in order, and writes issued ahead of fragment reads (two per gap, as first
+    written) held those reads back; placed behind them the 14B call ran 3-4 % faster."""
     stage = ((ph + 1) % 2) * STAGE
     base = p_base(pc)
     units = []
@@ -732,16 +748,17 @@ def widen_units(ph, pc):
         for k in range(2, 8, 2):
             at(gap, cv[k], cv[k + 1])
         for h in range(2):
-            at(gap, f"ds_write_b128 v{TMP + 2 * j + h}, v[{R + 4 * h}:{R + 4 * h + 3}] offset:{slot * KTILE}")
+            at(5 + 4 * j + 2 * h, LATE,
+               f"ds_write_b128 v{TMP + 2 * j + h}, v[{R + 4 * h}:{R + 4 * h + 3}] offset:{slot * KTILE}")
 
     # the four reads first (the loads landed most of an iteration ago), each chunk's conversion
-    # a few gaps after its read (LDS latency)
+    # a few gaps after its read (LDS latency), its two writes in later pairs
     addresses("K", 0)
     for j in range(4):
         read(j, 1 + j)
-    addresses("V", 5)
+    addresses("V", 2)
     for j in range(4):
-        widen(j, 6 + 2 * j)
+        widen(j, 2 + 2 * j)
     return units
 
 
