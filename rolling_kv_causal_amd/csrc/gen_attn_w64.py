@@ -1013,6 +1013,7 @@ def check_staging(iterations=10, masked=(2, 5)):
                 vals = {regs.get(r) for r in range(lo, lo + 4)}
                 assert len(vals) == 1, (t, l, vals)
                 what = vals.pop()
+                assert what is not None, (t, l, "writes registers no widening has filled")
                 assert what[0] == addr_kind[tok[1]], (t, l, what)
                 key = (what[0], int(tok[3].split(":")[1]) // KTILE)
                 assert last_read.get(key, -1) < barriers, (t, l, "widens into a slot read since the last barrier")

@@ -338,7 +338,8 @@ def test_generator_staging_check_rejects_planted_mistakes():
     # The e4m3 program widens each staged tile in the stream of the iteration after its loads;
     # check_staging runs one wave's loads, waits and LDS traffic.  It passes the committed
     # program and rejects: a vmcnt wait one load short, the widening reading the other staging
-    # slot, and K(t+1) widened into the ring slot K(t) is being read from.
+    # slot, K(t+1) widened into the ring slot K(t) is being read from, and a widened write of
+    # registers whose conversion comes later.
     import importlib.util
     import pathlib
     csrc = pathlib.Path(sdv2.__file__).resolve().parent / "csrc"
@@ -365,6 +366,13 @@ def test_generator_staging_check_rejects_planted_mistakes():
             line = line.split("offset:")[0] + f"offset:{off ^ gen.STAGE}"
         return (line, x[1]) if isinstance(x, tuple) else line
 
+    def early_write(ph, x):
+        # K0's low half written from the registers of V1, whose conversions come later
+        if isinstance(x, str) and x.startswith(f"ds_write_b128 v{gen.TMP},"):
+            lo = int(x.split("v[")[1].split(":")[0])
+            return x.replace(f"v[{lo}:{lo + 3}]", f"v[{lo + 24}:{lo + 27}]")
+        return x
+
     def k_into_read_slot(ph, x):
         if isinstance(x, str) and x.startswith("ds_write_b128") and int(x.split()[1].rstrip(",")[1:]) < gen.TMP + 4:
             return x.split("offset:")[0] + f"offset:{(ph % gen.NSLOT) * gen.KTILE}"
@@ -372,7 +380,8 @@ def test_generator_staging_check_rejects_planted_mistakes():
 
     for name, attr, plant in (("short vmcnt", "resolve_waits", short_wait),
                               ("other staging slot", "widen_units", edit_units(other_stage)),
-                              ("K over the slot being read", "widen_units", edit_units(k_into_read_slot))):
+                              ("K over the slot being read", "widen_units", edit_units(k_into_read_slot)),
+                              ("a write before its conversion", "widen_units", edit_units(early_write))):
         setattr(gen, attr, plant)
         with pytest.raises(AssertionError):
             gen.check_staging()
